@@ -1,0 +1,191 @@
+/*
+ * kmeans.h -- C ABI of the MI355X (gfx950) exact Lloyd K-Means library.
+ *
+ * Citations name the page "Flash-KMeans: Fast and Memory-Efficient Exact
+ * K-Means" (gist.science summary of paper 2603.09229): "tech §n" is a section
+ * of its technical summary, "pop §n" one of its popular explainer.
+ *
+ * What the library computes.  Standard Lloyd K-Means, exactly (the page keeps
+ * the K-Means formula and adds no approximation: tech §2 opening, tech §3).
+ * The page leaves these rules open; this library fixes them:
+ *   - distance: squared Euclidean;
+ *   - assignment: nearest centroid, the LOWEST index wins a tie;
+ *   - update: new centroid = mean of its assigned points; a cluster with no
+ *     point keeps its previous centroid bit for bit;
+ *   - one iteration = one assignment followed by one update; `iters` runs
+ *     exactly that many (no tolerance, no early exit).
+ *
+ * Precision.  X may be fp32, bf16 or fp16.  Centroids are always fp32.  For
+ * 16-bit X the distance contraction runs on the matrix cores with fp32
+ * accumulation against the fp32 centroids rounded once per assignment to X's
+ * type (round to nearest, ties to even); sums and means are accumulated in
+ * fp32.  Near-equal distances (relative gap around 1e-6 of ||x||^2 + ||c||^2)
+ * may resolve differently from exact arithmetic.
+ *
+ * Conventions for every entry point:
+ *   - Layout: X is N x D row-major (element type `dt`), C is K x D row-major
+ *     fp32, assignment vectors are int32[N], counts int32[K].  X must be
+ *     4-byte aligned (16-byte alignment with D*sizeof(elem) % 16 == 0 enables
+ *     vector loads); every other pointer 4-byte aligned (`objective` 8).
+ *   - Memory: "device" pointers are HIP device memory (e.g. torch CUDA tensors
+ *     on ROCm); "pinned host" pointers come from hipHostMalloc (torch's
+ *     pin_memory()).  The caller owns every buffer; the library never
+ *     allocates or frees memory.  Scratch space is the caller's workspace
+ *     `ws` (device memory of at least kmeans_workspace_bytes() bytes, any
+ *     content, 256-byte aligned); it must not be used by anything else while
+ *     the call's work runs.
+ *   - Streams: `stream` is a hipStream_t (NULL = the default stream).  All
+ *     work is enqueued asynchronously on it; results are ready once the
+ *     stream is synchronised.  The library never synchronises the host
+ *     (kmeans_fit_streamed returns once its last chunk is enqueued).
+ *   - Limits: 1 <= N < 2^31, 1 <= K < 2^31, 1 <= D <= 512 for 16-bit X and
+ *     1 <= D <= 256 for fp32 X (other D: KM_ERR_UNSUPPORTED).  K > N is
+ *     allowed (the extra clusters stay empty).  N = 0 is accepted and does
+ *     nothing except the documented output of an empty update.
+ *   - Errors: arguments, dtype and workspace size are checked synchronously
+ *     before any HIP call, so a failed check enqueues nothing.  A failed
+ *     launch returns KM_ERR_HIP.  Faults inside kernels surface at the
+ *     caller's next synchronisation.  No C++ exception crosses this ABI.
+ *     kmeans_last_error() gives a message for the last failure on the
+ *     calling thread.
+ *   - Reentrancy: calls are thread-safe given distinct workspaces.  The only
+ *     global state is the optional kernel-timing registry.
+ */
+#ifndef MEANS_CLUSTERING_AMD_KMEANS_H
+#define MEANS_CLUSTERING_AMD_KMEANS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum km_dtype { KM_F32 = 0, KM_BF16 = 1, KM_F16 = 2 } km_dtype;
+
+typedef enum km_status {
+  KM_OK = 0,
+  KM_ERR_INVALID_VALUE = 1, /* null pointer, size out of range, misalignment, bad dtype */
+  KM_ERR_UNSUPPORTED = 2,   /* valid but not supported here (D too large) */
+  KM_ERR_WORKSPACE = 3,     /* ws is NULL or ws_bytes smaller than required */
+  KM_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} km_status;
+
+typedef enum km_op {
+  KM_OP_ASSIGN = 0,
+  KM_OP_UPDATE = 1,
+  KM_OP_FIT = 2,
+  KM_OP_FIT_STREAMED = 3,
+  KM_OP_SORT = 4
+} km_op;
+
+/*
+ * Workspace bytes needed by entry point `op` for the given sizes (N is the
+ * number of points; for KM_OP_FIT_STREAMED `chunk_rows` is the chunk size and
+ * N may be any value).  Returns 0 if the arguments are invalid.
+ */
+size_t kmeans_workspace_bytes(km_op op, int64_t N, int64_t D, int64_t K, km_dtype dt, int64_t chunk_rows);
+
+/*
+ * kmeans_assign -- FlashAssign (tech §2.1): nearest centroid of every point,
+ * fused with the distance computation so that no N x K distance matrix is
+ * ever written (HBM traffic O(Nd + Kd), tech §2.1 "effect").
+ *   X        device, N x D, type dt                         (read)
+ *   C        device, K x D fp32 centroids                   (read)
+ *   assign   device int32[N]: index of the nearest centroid (written)
+ *   min_dist device fp32[N] or NULL: squared distance to that centroid,
+ *            computed as ||x||^2 - 2 x.c + ||c||^2 in fp32, clamped at 0
+ */
+km_status kmeans_assign(const void* X, km_dtype dt, int64_t N, int64_t D, const float* C, int64_t K,
+                        int32_t* assign, float* min_dist, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kmeans_sort_by_cluster -- the explicit inverse map of Sort-Inverse Update
+ * (tech §2.2 "explicit inverse mapping"): a stable argsort of the assignment
+ * vector by cluster id, plus each cluster's segment boundaries.
+ *   assign   device int32[N] cluster ids                    (read)
+ *   perm     device int32[N]: point indices grouped by ascending cluster id,
+ *            ascending point index within a cluster; a point whose id is
+ *            outside [0, K) is listed inside cluster K-1's range with bit 31
+ *            set (its index is perm & 0x7fffffff)           (written)
+ *   offsets  device int32[K+1] or NULL: cluster k occupies perm[offsets[k] ..
+ *            offsets[k+1]); offsets[K] = N                  (written)
+ */
+km_status kmeans_sort_by_cluster(const int32_t* assign, int64_t N, int64_t K, int32_t* perm, int32_t* offsets,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kmeans_update -- Sort-Inverse Update (tech §2.2): argsort of the assignment
+ * vector, segment boundaries, then a segmented reduction over the sorted
+ * order with no atomic operation anywhere (the page's variant issues atomics
+ * only at segment boundaries; here boundary pieces are summed by a fixed-
+ * order pass, so results are deterministic).
+ *   X       device, N x D, type dt                          (read)
+ *   assign  device int32[N] cluster ids; ids outside [0, K) are ignored
+ *   C_prev  device K x D fp32: centroids kept by empty clusters (read)
+ *   C_new   device K x D fp32: means (written; may alias C_prev)
+ *   counts  device int32[K] or NULL: points per cluster     (written)
+ */
+km_status kmeans_update(const void* X, km_dtype dt, int64_t N, int64_t D, const int32_t* assign, int64_t K,
+                        const float* C_prev, float* C_new, int32_t* counts, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/*
+ * kmeans_fit -- `iters` Lloyd iterations with X resident in device memory;
+ * each iteration is kmeans_assign followed by kmeans_update, all enqueued on
+ * `stream` with no host synchronisation.
+ *   C          device K x D fp32: initial centroids in, C^iters out
+ *   assign     device int32[N] or NULL: assignment of the last iteration
+ *   counts     device int32[K] or NULL: counts that formed C^iters
+ *   objective  device double[iters] or NULL: objective[t] = sum of squared
+ *              distances of iteration t's assignment (fp32 terms, fp64 sum)
+ *   iters = 0 leaves every output untouched.
+ */
+km_status kmeans_fit(const void* X, km_dtype dt, int64_t N, int64_t D, int64_t K, float* C, int32_t iters,
+                     int32_t* assign, int32_t* counts, double* objective, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/*
+ * kmeans_fit_streamed -- Lloyd iterations for X that stays in pinned host
+ * memory (tech §2.3 "chunked stream overlap"): every iteration copies X to
+ * the device in chunks of `chunk_rows` rows on `copy_stream`, two device
+ * buffers in rotation, while `compute_stream` assigns the previous chunk and
+ * accumulates its per-cluster sums; the means are formed once per iteration.
+ *   X_host       pinned host, N x D, type dt                 (read)
+ *   C            device K x D fp32: initial centroids in, C^iters out
+ *   assign_host  pinned host int32[N] or NULL: assignment of the last
+ *                iteration (copied back chunk by chunk)
+ *   counts       device int32[K] or NULL
+ *   objective    device double[iters] or NULL (as kmeans_fit)
+ *   compute_stream, copy_stream: distinct hipStream_t (NULL allowed for
+ *                compute_stream only).  On return all work is enqueued;
+ *                synchronise compute_stream before reading any output.
+ */
+km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_t D, int64_t K, float* C,
+                              int32_t iters, int64_t chunk_rows, int32_t* assign_host, int32_t* counts,
+                              double* objective, void* ws, size_t ws_bytes, void* compute_stream,
+                              void* copy_stream);
+
+/* Short constant description of a status code. */
+const char* kmeans_status_string(km_status s);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* kmeans_last_error(void);
+
+/*
+ * Kernel timing (for measurement, off by default).  While enabled, every
+ * kernel phase a call enqueues is bracketed by HIP events on the stream it
+ * runs on.  kmeans_timing_read() waits for the recorded events and returns
+ * the summed milliseconds and the number of timed launches of one phase:
+ * "prep", "assign", "sort", "segments", "reduce", "finalize", "objective",
+ * "h2d", "d2h".  kmeans_timing_reset() forgets all records.
+ */
+km_status kmeans_timing_enable(int enable);
+km_status kmeans_timing_read(const char* phase, double* total_ms, int64_t* launches);
+km_status kmeans_timing_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MEANS_CLUSTERING_AMD_KMEANS_H */

@@ -1,0 +1,260 @@
+"""Exact Lloyd K-Means on MI355X (gfx950): Python binding of ``libkmeans_amd.so``.
+
+A thin ctypes layer over the C ABI declared in ``include/kmeans.h``: it
+checks tensor types, passes pointers, sizes and the current HIP stream, and
+hands the library a device workspace.  Every step of the computation runs in
+the library's HIP kernels; there is no CPU or PyTorch fallback, and using this
+module without the built library raises an error.
+
+Citations name the page "Flash-KMeans: Fast and Memory-Efficient Exact
+K-Means" (gist.science summary of paper 2603.09229); "tech §n" is a section
+of its technical summary.
+
+Entry points (all tensors on one ROCm device unless stated):
+  assign(X, C)                       nearest centroid per point   (tech §2.1 FlashAssign)
+  sort_by_cluster(a, K)              stable argsort + boundaries  (tech §2.2 inverse map)
+  update(X, a, C_prev)               means, empty keeps previous  (tech §2.2 Sort-Inverse Update)
+  fit(X, C0, iters)                  Lloyd iterations, X resident
+  fit_streamed(X_host, C0, iters, chunk_rows)   X in pinned host memory (tech §2.3 chunked overlap)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkmeans_amd.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "kmeans.h")
+
+KM_F32, KM_BF16, KM_F16 = 0, 1, 2
+KM_OP_ASSIGN, KM_OP_UPDATE, KM_OP_FIT, KM_OP_FIT_STREAMED, KM_OP_SORT = 0, 1, 2, 3, 4
+STATUS = {0: "KM_OK", 1: "KM_ERR_INVALID_VALUE", 2: "KM_ERR_UNSUPPORTED", 3: "KM_ERR_WORKSPACE", 4: "KM_ERR_HIP"}
+_DT = {torch.float32: KM_F32, torch.bfloat16: KM_BF16, torch.float16: KM_F16}
+
+
+class KMeansError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def _bind(lib):
+    i64, vp, c_int, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "kmeans_workspace_bytes": (sz, [c_int, i64, i64, i64, c_int, i64]),
+        "kmeans_assign": (c_int, [vp, c_int, i64, i64, vp, i64, vp, vp, vp, sz, vp]),
+        "kmeans_sort_by_cluster": (c_int, [vp, i64, i64, vp, vp, vp, sz, vp]),
+        "kmeans_update": (c_int, [vp, c_int, i64, i64, vp, i64, vp, vp, vp, vp, sz, vp]),
+        "kmeans_fit": (c_int, [vp, c_int, i64, i64, i64, vp, ctypes.c_int32, vp, vp, vp, vp, sz, vp]),
+        "kmeans_fit_streamed": (c_int, [vp, c_int, i64, i64, i64, vp, ctypes.c_int32, i64, vp, vp, vp, vp, sz, vp,
+                                        vp]),
+        "kmeans_status_string": (ctypes.c_char_p, [c_int]),
+        "kmeans_last_error": (ctypes.c_char_p, []),
+        "kmeans_timing_enable": (c_int, [c_int]),
+        "kmeans_timing_read": (c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]),
+        "kmeans_timing_reset": (c_int, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+def lib():
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                                   "(python -m means_clustering_amd.build)")
+            _lib = _bind(ctypes.CDLL(LIB_PATH))
+        return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/kmeans.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(kmeans_\w+)\s*\(", text, re.M)))
+
+
+def _check(status: int):
+    if status != 0:
+        raise KMeansError(status, lib().kmeans_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dtype(X: torch.Tensor) -> int:
+    if X.dtype not in _DT:
+        raise TypeError(f"X must be float32, bfloat16 or float16, got {X.dtype}")
+    return _DT[X.dtype]
+
+
+def workspace_bytes(op: int, N: int, D: int, K: int, dtype=torch.bfloat16, chunk_rows: int = 0) -> int:
+    return int(lib().kmeans_workspace_bytes(op, N, D, K, _DT[dtype], chunk_rows))
+
+
+class Workspace:
+    """A reusable device scratch buffer for the library's calls."""
+
+    def __init__(self, device=None):
+        self.device = torch.device(device) if device is not None else None
+        self.buf = None
+
+    def get(self, nbytes: int, device) -> torch.Tensor:
+        nbytes = max(int(nbytes), 256)
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != torch.device(device):
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        return self.buf
+
+
+_default_ws: dict = {}
+
+
+def _ws(ws: Workspace | None, nbytes: int, device) -> torch.Tensor:
+    if ws is None:
+        ws = _default_ws.setdefault(str(device), Workspace(device))
+    return ws.get(nbytes, device)
+
+
+def _need(X: torch.Tensor, C: torch.Tensor):
+    if not X.is_cuda or not C.is_cuda:
+        raise ValueError("X and C must be device tensors")
+    if X.dim() != 2 or C.dim() != 2 or X.shape[1] != C.shape[1]:
+        raise ValueError("X must be N x D and C K x D")
+    if C.dtype != torch.float32:
+        raise TypeError("centroids must be float32")
+    if not X.is_contiguous() or not C.is_contiguous():
+        raise ValueError("X and C must be contiguous")
+
+
+def assign(X: torch.Tensor, C: torch.Tensor, min_dist: bool = False, out: torch.Tensor | None = None,
+           ws: Workspace | None = None):
+    """Nearest centroid of every row of X (FlashAssign). Returns (assign int32[N], dist fp32[N] or None)."""
+    _need(X, C)
+    N, D = X.shape
+    K = C.shape[0]
+    a = out if out is not None else torch.empty(N, dtype=torch.int32, device=X.device)
+    d = torch.empty(N, dtype=torch.float32, device=X.device) if min_dist else None
+    nb = workspace_bytes(KM_OP_ASSIGN, N, D, K, X.dtype)
+    w = _ws(ws, nb, X.device)
+    _check(lib().kmeans_assign(_ptr(X), _dtype(X), N, D, _ptr(C), K, _ptr(a), _ptr(d), _ptr(w), w.numel(),
+                               ctypes.c_void_p(_stream(X.device))))
+    return a, d
+
+
+def sort_by_cluster(a: torch.Tensor, K: int, ws: Workspace | None = None):
+    """Stable argsort of cluster ids. Returns (perm int32[N], offsets int32[K+1])."""
+    if a.dtype != torch.int32 or not a.is_cuda or a.dim() != 1 or not a.is_contiguous():
+        raise ValueError("a must be a contiguous int32 device vector")
+    N = a.shape[0]
+    perm = torch.empty(N, dtype=torch.int32, device=a.device)
+    off = torch.empty(K + 1, dtype=torch.int32, device=a.device)
+    nb = int(lib().kmeans_workspace_bytes(KM_OP_SORT, N, 1, K, KM_F32, 0))
+    w = _ws(ws, nb, a.device)
+    _check(lib().kmeans_sort_by_cluster(_ptr(a), N, K, _ptr(perm), _ptr(off), _ptr(w), w.numel(),
+                                        ctypes.c_void_p(_stream(a.device))))
+    return perm, off
+
+
+def update(X: torch.Tensor, a: torch.Tensor, C_prev: torch.Tensor, out: torch.Tensor | None = None,
+           ws: Workspace | None = None):
+    """Sort-Inverse Update. Returns (C_new fp32[K, D], counts int32[K])."""
+    _need(X, C_prev)
+    if a.dtype != torch.int32 or a.shape != (X.shape[0],) or not a.is_contiguous():
+        raise ValueError("a must be a contiguous int32 vector of length N")
+    N, D = X.shape
+    K = C_prev.shape[0]
+    C_new = out if out is not None else torch.empty_like(C_prev)
+    counts = torch.empty(K, dtype=torch.int32, device=X.device)
+    nb = workspace_bytes(KM_OP_UPDATE, N, D, K, X.dtype)
+    w = _ws(ws, nb, X.device)
+    _check(lib().kmeans_update(_ptr(X), _dtype(X), N, D, _ptr(a), K, _ptr(C_prev), _ptr(C_new), _ptr(counts),
+                               _ptr(w), w.numel(), ctypes.c_void_p(_stream(X.device))))
+    return C_new, counts
+
+
+def fit(X: torch.Tensor, C0: torch.Tensor, iters: int, objective: bool = False, inplace: bool = False,
+        ws: Workspace | None = None, assign_out: torch.Tensor | None = None,
+        counts_out: torch.Tensor | None = None, objective_out: torch.Tensor | None = None):
+    """Lloyd iterations with X in device memory.
+
+    Returns (C, assign, counts, objective-or-None); C is C0 itself when ``inplace``.
+    Preallocated ``*_out`` tensors are used as given (no allocation in the call).
+    """
+    _need(X, C0)
+    N, D = X.shape
+    K = C0.shape[0]
+    C = C0 if inplace else C0.clone()
+    a = assign_out if assign_out is not None else torch.empty(N, dtype=torch.int32, device=X.device)
+    counts = counts_out if counts_out is not None else torch.empty(K, dtype=torch.int32, device=X.device)
+    obj = objective_out
+    if objective and obj is None:
+        obj = torch.empty(max(iters, 1), dtype=torch.float64, device=X.device)
+    nb = workspace_bytes(KM_OP_FIT, N, D, K, X.dtype)
+    w = _ws(ws, nb, X.device)
+    _check(lib().kmeans_fit(_ptr(X), _dtype(X), N, D, K, _ptr(C), int(iters), _ptr(a), _ptr(counts), _ptr(obj),
+                            _ptr(w), w.numel(), ctypes.c_void_p(_stream(X.device))))
+    return C, a, counts, (obj[:iters] if obj is not None else None)
+
+
+def fit_streamed(X_host: torch.Tensor, C0: torch.Tensor, iters: int, chunk_rows: int, copy_stream=None,
+                 want_assign: bool = True, objective: bool = False, ws: Workspace | None = None):
+    """Lloyd iterations with X in pinned host memory, streamed in chunks.
+
+    Returns (C, assign_host int32[N] pinned or None, counts, objective-or-None).
+    The call returns once all work is enqueued on the current stream.
+    """
+    if X_host.is_cuda or not X_host.is_pinned():
+        raise ValueError("X_host must be a pinned host tensor")
+    if not C0.is_cuda or C0.dtype != torch.float32 or X_host.dim() != 2 or X_host.shape[1] != C0.shape[1]:
+        raise ValueError("C0 must be a K x D float32 device tensor matching X_host")
+    N, D = X_host.shape
+    K = C0.shape[0]
+    dev = C0.device
+    C = C0.clone()
+    a = torch.empty(N, dtype=torch.int32, pin_memory=True) if want_assign else None
+    counts = torch.empty(K, dtype=torch.int32, device=dev)
+    obj = torch.empty(max(iters, 1), dtype=torch.float64, device=dev) if objective else None
+    nb = workspace_bytes(KM_OP_FIT_STREAMED, N, D, K, X_host.dtype, chunk_rows)
+    w = _ws(ws, nb, dev)
+    cs = copy_stream if copy_stream is not None else torch.cuda.Stream(dev)
+    _check(lib().kmeans_fit_streamed(_ptr(X_host), _dtype(X_host), N, D, K, _ptr(C), int(iters), int(chunk_rows),
+                                     _ptr(a), _ptr(counts), _ptr(obj), _ptr(w), w.numel(),
+                                     ctypes.c_void_p(_stream(dev)), ctypes.c_void_p(cs.cuda_stream)))
+    return C, a, counts, (obj[:iters] if obj is not None else None)
+
+
+def timing_enable(on: bool = True):
+    _check(lib().kmeans_timing_enable(1 if on else 0))
+
+
+def timing_reset():
+    _check(lib().kmeans_timing_reset())
+
+
+def timing_read(phase: str):
+    """(total milliseconds, launches) recorded for one kernel phase (waits for its events)."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(lib().kmeans_timing_read(phase.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+PHASES = ("prep", "assign", "sort", "segments", "reduce", "finalize", "objective", "h2d", "d2h")

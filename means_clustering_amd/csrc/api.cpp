@@ -1,0 +1,535 @@
+// C ABI of the K-Means library: argument checks, workspace carving, the
+// per-iteration launch sequence and the chunked host-streaming pipeline.
+//
+// Citations name the page "Flash-KMeans: Fast and Memory-Efficient Exact
+// K-Means" (gist.science summary of paper 2603.09229); "tech §n" is a section
+// of its technical summary.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <utility>
+#include <vector>
+
+#include "../../include/kmeans.h"
+#include "km_internal.hpp"
+
+using namespace km;
+
+// --------------------------------------------------------------- errors ----
+
+static thread_local std::string g_last_error;
+
+static km_status fail(km_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+#define KM_HIP(call)                                                                               \
+  do {                                                                                             \
+    hipError_t e_ = (call);                                                                        \
+    if (e_ != hipSuccess) return fail(KM_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+// --------------------------------------------------------------- timing ----
+
+namespace {
+struct TimingRegistry {
+  std::mutex mu;
+  bool enabled = false;
+  std::unordered_map<std::string, std::vector<std::pair<hipEvent_t, hipEvent_t>>> rec;
+};
+TimingRegistry& timing() {
+  static TimingRegistry r;
+  return r;
+}
+
+// Brackets the launches made by `fn` with events on `stream` when timing is on.
+template <class F>
+hipError_t timed(const char* phase, hipStream_t stream, F&& fn) {
+  TimingRegistry& T = timing();
+  bool on;
+  {
+    std::lock_guard<std::mutex> g(T.mu);
+    on = T.enabled;
+  }
+  if (!on) return fn();
+  hipEvent_t a, b;
+  hipError_t e = hipEventCreate(&a);
+  if (e != hipSuccess) return e;
+  e = hipEventCreate(&b);
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(a, stream);
+  if (e != hipSuccess) return e;
+  e = fn();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, stream);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> g(T.mu);
+  T.rec[phase].emplace_back(a, b);
+  return hipSuccess;
+}
+}  // namespace
+
+#define KM_TIMED(phase, stream, body)                                                     \
+  do {                                                                                    \
+    hipError_t e_ = timed(phase, stream, [&]() -> hipError_t { body; });                  \
+    if (e_ != hipSuccess) return fail(KM_ERR_HIP, std::string(phase) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+// ---------------------------------------------------------- validation ----
+
+static bool dtype_ok(km_dtype dt) { return dt == KM_F32 || dt == KM_BF16 || dt == KM_F16; }
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p) % a == 0; }
+static const int64_t kMaxN = (int64_t)1 << 31;
+
+static km_status check_sizes(int64_t N, int64_t D, int64_t K, km_dtype dt, bool need_d) {
+  if (!dtype_ok(dt)) return fail(KM_ERR_INVALID_VALUE, "dtype must be KM_F32, KM_BF16 or KM_F16");
+  if (N < 0 || N >= kMaxN) return fail(KM_ERR_INVALID_VALUE, "N must satisfy 0 <= N < 2^31");
+  if (K < 1 || K >= kMaxN) return fail(KM_ERR_INVALID_VALUE, "K must satisfy 1 <= K < 2^31");
+  if (need_d) {
+    if (D < 1) return fail(KM_ERR_INVALID_VALUE, "D must be >= 1");
+    const int64_t dmax = (int64_t)kMaxKB * frag_depth(dt);
+    if (D > dmax)
+      return fail(KM_ERR_UNSUPPORTED, "D=" + std::to_string(D) + " exceeds the supported maximum " +
+                                          std::to_string(dmax) + " for this dtype");
+    if (K * D >= kMaxN * 64) return fail(KM_ERR_UNSUPPORTED, "K*D too large");
+  }
+  return KM_OK;
+}
+
+// ----------------------------------------------------------- geometry -----
+
+static AssignGeom assign_geom(int64_t N, int64_t D, int64_t K, km_dtype dt) {
+  AssignGeom g;
+  g.dt = (int)dt;
+  g.N = N;
+  g.D = D;
+  g.K = K;
+  g.KB = (int)((D + frag_depth(dt) - 1) / frag_depth(dt));
+  g.Kpad = pad_up(K, kPadK);
+  return g;
+}
+
+static SortGeom sort_geom(int64_t N, int64_t K) {
+  SortGeom g;
+  g.N = N;
+  g.K = K;
+  int kb = 0;
+  while (kb < 31 && ((int64_t)1 << kb) <= K - 1) ++kb;
+  if (kb < 1) kb = 1;
+  g.kbits = kb;
+  g.npass = (kb + 7) / 8;
+  const int base = kb / g.npass, rem = kb % g.npass;
+  for (int p = 0; p < 4; ++p) g.bits[p] = p < g.npass ? base + (p < rem ? 1 : 0) : 0;
+  g.nblk = (N + kSortBlock - 1) / kSortBlock;
+  int64_t m = 1;
+  for (int p = 0; p < g.npass; ++p) {
+    const int64_t len = ((int64_t)1 << g.bits[p]) * g.nblk;
+    if (len > m) m = len;
+  }
+  g.count_len = m;
+  return g;
+}
+
+// Bump allocator over the caller's workspace (256-byte aligned pieces).
+struct Carve {
+  uint8_t* base;
+  size_t used = 0;
+  explicit Carve(void* b) : base((uint8_t*)b) {}
+  template <class T>
+  T* take(size_t count) {
+    used = (used + 255) / 256 * 256;
+    T* p = base ? (T*)(base + used) : nullptr;
+    used += count * sizeof(T);
+    return p;
+  }
+};
+
+struct SortBufs {
+  int32_t *key_a, *val_a, *key_b, *val_b;
+  uint32_t *counts, *scan_part;
+  int32_t* off;
+};
+
+static SortBufs carve_sort(Carve& c, const SortGeom& g) {
+  SortBufs b;
+  const size_t n = (size_t)(g.N > 0 ? g.N : 1);
+  b.key_a = c.take<int32_t>(n);
+  b.val_a = c.take<int32_t>(n);
+  b.key_b = c.take<int32_t>(n);
+  b.val_b = c.take<int32_t>(n);
+  b.counts = c.take<uint32_t>((size_t)g.count_len);
+  b.scan_part = c.take<uint32_t>((size_t)scan_part_len(g.count_len));
+  b.off = c.take<int32_t>((size_t)g.K + 1);
+  return b;
+}
+
+struct UpdateBufs {
+  SortBufs s;
+  float* carry_sum;
+  int32_t* carry_cnt;
+};
+
+static UpdateBufs carve_update(Carve& c, const SortGeom& g, int64_t D, km_dtype dt) {
+  UpdateBufs u;
+  u.s = carve_sort(c, g);
+  const int64_t ntiles = (g.N + kSegTile - 1) / kSegTile;
+  u.carry_sum = c.take<float>((size_t)(ntiles > 0 ? ntiles : 1) * 2 * (size_t)reduce_dc((int)dt, D));
+  u.carry_cnt = c.take<int32_t>((size_t)(ntiles > 0 ? ntiles : 1) * 2);
+  return u;
+}
+
+struct FitBufs {
+  void* frag;
+  UpdateBufs u;
+  int32_t* assign;
+  float* min_dist;
+  double* obj_part;
+};
+
+static FitBufs carve_fit(Carve& c, int64_t N, int64_t D, int64_t K, km_dtype dt) {
+  FitBufs f;
+  f.frag = c.take<uint8_t>(assign_geom(N, D, K, dt).frag_bytes());
+  f.u = carve_update(c, sort_geom(N, K), D, dt);
+  const size_t n = (size_t)(N > 0 ? N : 1);
+  f.assign = c.take<int32_t>(n);
+  f.min_dist = c.take<float>(n);
+  f.obj_part = c.take<double>((size_t)objective_partials(N));
+  return f;
+}
+
+struct StreamBufs {
+  FitBufs f;  // sized for one chunk
+  void* xbuf[2];
+  float* acc_sum;
+  int64_t* acc_cnt;
+};
+
+static StreamBufs carve_streamed(Carve& c, int64_t rows, int64_t D, int64_t K, km_dtype dt) {
+  StreamBufs s;
+  s.f = carve_fit(c, rows, D, K, dt);
+  const size_t xb = (size_t)rows * (size_t)D * (size_t)dtype_size((int)dt);
+  s.xbuf[0] = c.take<uint8_t>(xb);
+  s.xbuf[1] = c.take<uint8_t>(xb);
+  s.acc_sum = c.take<float>((size_t)K * (size_t)D);
+  s.acc_cnt = c.take<int64_t>((size_t)K);
+  return s;
+}
+
+static size_t workspace_bytes_impl(km_op op, int64_t N, int64_t D, int64_t K, km_dtype dt, int64_t chunk_rows) {
+  Carve c(nullptr);
+  switch (op) {
+    case KM_OP_ASSIGN: c.take<uint8_t>(assign_geom(N, D, K, dt).frag_bytes()); break;
+    case KM_OP_SORT: carve_sort(c, sort_geom(N, K)); break;
+    case KM_OP_UPDATE: carve_update(c, sort_geom(N, K), D, dt); break;
+    case KM_OP_FIT: carve_fit(c, N, D, K, dt); break;
+    case KM_OP_FIT_STREAMED: {
+      const int64_t rows = chunk_rows < N ? chunk_rows : (N > 0 ? N : 1);
+      carve_streamed(c, rows, D, K, dt);
+      break;
+    }
+    default: return 0;
+  }
+  return (c.used + 255) / 256 * 256;
+}
+
+static km_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return KM_OK;
+  if (!ws) return fail(KM_ERR_WORKSPACE, "workspace pointer is NULL");
+  if (!aligned(ws, 256)) return fail(KM_ERR_INVALID_VALUE, "workspace must be 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(KM_ERR_WORKSPACE, "workspace too small: " + std::to_string(ws_bytes) + " < " + std::to_string(need));
+  return KM_OK;
+}
+
+// ---------------------------------------------------- launch sequences ----
+
+static km_status run_assign(const void* X, km_dtype dt, int64_t N, int64_t D, const float* C, int64_t K,
+                            int32_t* assign, float* min_dist, void* frag, hipStream_t s) {
+  const AssignGeom g = assign_geom(N, D, K, dt);
+  KM_TIMED("prep", s, return launch_prep(C, K, D, (int)dt, g.KB, g.Kpad, frag, s));
+  if (N > 0)
+    KM_TIMED("assign", s, return launch_flash_assign(X, (int)dt, N, D, g.KB, frag, g.Kpad, assign, min_dist, s));
+  return KM_OK;
+}
+
+// Argsort + boundaries; returns the sorted keys and values (the inverse map).
+static km_status run_sort(const int32_t* assign, int64_t N, int64_t K, const SortBufs& b, int32_t* perm_out,
+                          int32_t** keys, int32_t** vals, hipStream_t s) {
+  const SortGeom g = sort_geom(N, K);
+  // ping-pong through set a / set b; the last pass may write the caller's perm
+  int32_t* kf = (g.npass % 2) ? b.key_a : b.key_b;
+  int32_t* vf = perm_out ? perm_out : ((g.npass % 2) ? b.val_a : b.val_b);
+  KM_TIMED("sort", s, return launch_argsort(g, assign, b.key_a, b.val_a, b.key_b, b.val_b, kf, vf, b.counts,
+                                            b.scan_part, s));
+  *keys = kf;
+  *vals = vf;
+  KM_TIMED("segments", s, return launch_boundaries(kf, N, K, b.off, s));
+  return KM_OK;
+}
+
+static km_status run_update(const void* X, km_dtype dt, int64_t N, int64_t D, const int32_t* assign, int64_t K,
+                            const float* C_prev, float* C_new, int32_t* counts, const UpdateBufs& u, int mode,
+                            float* acc_sum, int64_t* acc_cnt, hipStream_t s) {
+  int32_t *keys = nullptr, *vals = nullptr;
+  km_status st = run_sort(assign, N, K, u.s, nullptr, &keys, &vals, s);
+  if (st != KM_OK) return st;
+  ReduceArgs a;
+  a.X = X;
+  a.dt = (int)dt;
+  a.N = N;
+  a.D = D;
+  a.K = K;
+  a.keys = keys;
+  a.vals = vals;
+  a.off = u.s.off;
+  a.carry_sum = u.carry_sum;
+  a.carry_cnt = u.carry_cnt;
+  a.mode = mode;
+  a.C_prev = C_prev;
+  a.C_new = C_new;
+  a.counts = counts;
+  a.acc_sum = acc_sum;
+  a.acc_cnt = acc_cnt;
+  KM_TIMED("reduce", s, return launch_segment_reduce(a, s));
+  KM_TIMED("finalize", s, return launch_fixup(a, s));
+  return KM_OK;
+}
+
+// ------------------------------------------------------------ entry points --
+
+extern "C" {
+
+size_t kmeans_workspace_bytes(km_op op, int64_t N, int64_t D, int64_t K, km_dtype dt, int64_t chunk_rows) {
+  const bool need_d = op != KM_OP_SORT;
+  if (check_sizes(N, need_d ? D : 1, K, op == KM_OP_SORT ? KM_F32 : dt, need_d) != KM_OK) return 0;
+  if (op == KM_OP_FIT_STREAMED && chunk_rows < 1) return 0;
+  return workspace_bytes_impl(op, N, D, K, dt, chunk_rows);
+}
+
+km_status kmeans_assign(const void* X, km_dtype dt, int64_t N, int64_t D, const float* C, int64_t K, int32_t* assign,
+                        float* min_dist, void* ws, size_t ws_bytes, void* stream) {
+  km_status st = check_sizes(N, D, K, dt, true);
+  if (st != KM_OK) return st;
+  if (!C || (N > 0 && (!X || !assign))) return fail(KM_ERR_INVALID_VALUE, "X, C and assign must be non-NULL");
+  if (!aligned(X, dt == KM_F32 ? 4 : 2) || !aligned(C, 4) || !aligned(assign, 4) || !aligned(min_dist, 4))
+    return fail(KM_ERR_INVALID_VALUE, "misaligned pointer");
+  st = check_ws(ws, ws_bytes, workspace_bytes_impl(KM_OP_ASSIGN, N, D, K, dt, 0));
+  if (st != KM_OK) return st;
+  Carve c(ws);
+  void* frag = c.take<uint8_t>(assign_geom(N, D, K, dt).frag_bytes());
+  return run_assign(X, dt, N, D, C, K, assign, min_dist, frag, (hipStream_t)stream);
+}
+
+km_status kmeans_sort_by_cluster(const int32_t* assign, int64_t N, int64_t K, int32_t* perm, int32_t* offsets,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  km_status st = check_sizes(N, 1, K, KM_F32, false);
+  if (st != KM_OK) return st;
+  if (N > 0 && (!assign || !perm)) return fail(KM_ERR_INVALID_VALUE, "assign and perm must be non-NULL");
+  if (!aligned(assign, 4) || !aligned(perm, 4) || !aligned(offsets, 4))
+    return fail(KM_ERR_INVALID_VALUE, "misaligned pointer");
+  st = check_ws(ws, ws_bytes, workspace_bytes_impl(KM_OP_SORT, N, 1, K, KM_F32, 0));
+  if (st != KM_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  Carve c(ws);
+  const SortBufs b = carve_sort(c, sort_geom(N, K));
+  int32_t *keys = nullptr, *vals = nullptr;
+  if (N > 0) {
+    st = run_sort(assign, N, K, b, perm, &keys, &vals, s);
+    if (st != KM_OK) return st;
+  } else {
+    KM_TIMED("segments", s, return launch_boundaries(b.key_a, 0, K, b.off, s));
+  }
+  if (offsets) KM_HIP(hipMemcpyAsync(offsets, b.off, sizeof(int32_t) * (size_t)(K + 1), hipMemcpyDeviceToDevice, s));
+  return KM_OK;
+}
+
+km_status kmeans_update(const void* X, km_dtype dt, int64_t N, int64_t D, const int32_t* assign, int64_t K,
+                        const float* C_prev, float* C_new, int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
+  km_status st = check_sizes(N, D, K, dt, true);
+  if (st != KM_OK) return st;
+  if (!C_prev || !C_new || (N > 0 && (!X || !assign)))
+    return fail(KM_ERR_INVALID_VALUE, "X, assign, C_prev and C_new must be non-NULL");
+  if (!aligned(X, dt == KM_F32 ? 4 : 2) || !aligned(assign, 4) || !aligned(C_prev, 4) || !aligned(C_new, 4) ||
+      !aligned(counts, 4))
+    return fail(KM_ERR_INVALID_VALUE, "misaligned pointer");
+  st = check_ws(ws, ws_bytes, workspace_bytes_impl(KM_OP_UPDATE, N, D, K, dt, 0));
+  if (st != KM_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  Carve c(ws);
+  const UpdateBufs u = carve_update(c, sort_geom(N, K), D, dt);
+  if (N == 0) {  // every cluster is empty: keep C_prev
+    if (counts) KM_HIP(launch_zero(counts, sizeof(int32_t) * (size_t)K, s));
+    if (C_new != C_prev)
+      KM_HIP(hipMemcpyAsync(C_new, C_prev, sizeof(float) * (size_t)(K * D), hipMemcpyDeviceToDevice, s));
+    return KM_OK;
+  }
+  return run_update(X, dt, N, D, assign, K, C_prev, C_new, counts, u, MODE_MEAN, nullptr, nullptr, s);
+}
+
+km_status kmeans_fit(const void* X, km_dtype dt, int64_t N, int64_t D, int64_t K, float* C, int32_t iters,
+                     int32_t* assign, int32_t* counts, double* objective, void* ws, size_t ws_bytes, void* stream) {
+  km_status st = check_sizes(N, D, K, dt, true);
+  if (st != KM_OK) return st;
+  if (iters < 0) return fail(KM_ERR_INVALID_VALUE, "iters must be >= 0");
+  if (!C || (N > 0 && !X)) return fail(KM_ERR_INVALID_VALUE, "X and C must be non-NULL");
+  if (!aligned(X, dt == KM_F32 ? 4 : 2) || !aligned(C, 4) || !aligned(assign, 4) || !aligned(counts, 4) ||
+      !aligned(objective, 8))
+    return fail(KM_ERR_INVALID_VALUE, "misaligned pointer");
+  st = check_ws(ws, ws_bytes, workspace_bytes_impl(KM_OP_FIT, N, D, K, dt, 0));
+  if (st != KM_OK) return st;
+  if (iters == 0) return KM_OK;
+  hipStream_t s = (hipStream_t)stream;
+  Carve c(ws);
+  const FitBufs f = carve_fit(c, N, D, K, dt);
+  int32_t* a = assign ? assign : f.assign;
+  for (int32_t t = 0; t < iters; ++t) {
+    st = run_assign(X, dt, N, D, C, K, a, objective ? f.min_dist : nullptr, f.frag, s);
+    if (st != KM_OK) return st;
+    if (objective) KM_TIMED("objective", s, return launch_objective(f.min_dist, N, f.obj_part, objective + t, 0, s));
+    if (N == 0) {
+      if (counts) KM_HIP(launch_zero(counts, sizeof(int32_t) * (size_t)K, s));
+      continue;
+    }
+    st = run_update(X, dt, N, D, a, K, C, C, counts, f.u, MODE_MEAN, nullptr, nullptr, s);
+    if (st != KM_OK) return st;
+  }
+  return KM_OK;
+}
+
+km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_t D, int64_t K, float* C,
+                              int32_t iters, int64_t chunk_rows, int32_t* assign_host, int32_t* counts,
+                              double* objective, void* ws, size_t ws_bytes, void* compute_stream,
+                              void* copy_stream) {
+  km_status st = check_sizes(N, D, K, dt, true);
+  if (st != KM_OK) return st;
+  if (iters < 0) return fail(KM_ERR_INVALID_VALUE, "iters must be >= 0");
+  if (chunk_rows < 1) return fail(KM_ERR_INVALID_VALUE, "chunk_rows must be >= 1");
+  if (!C || (N > 0 && !X_host)) return fail(KM_ERR_INVALID_VALUE, "X_host and C must be non-NULL");
+  if (!copy_stream || copy_stream == compute_stream)
+    return fail(KM_ERR_INVALID_VALUE, "copy_stream must be a non-NULL stream distinct from compute_stream");
+  if (!aligned(X_host, dt == KM_F32 ? 4 : 2) || !aligned(C, 4) || !aligned(assign_host, 4) ||
+      !aligned(counts, 4) || !aligned(objective, 8))
+    return fail(KM_ERR_INVALID_VALUE, "misaligned pointer");
+  st = check_ws(ws, ws_bytes, workspace_bytes_impl(KM_OP_FIT_STREAMED, N, D, K, dt, chunk_rows));
+  if (st != KM_OK) return st;
+  if (iters == 0) return KM_OK;
+  hipStream_t cs = (hipStream_t)compute_stream, xs = (hipStream_t)copy_stream;
+  const int64_t rows = chunk_rows < N ? chunk_rows : (N > 0 ? N : 1);
+  Carve c(ws);
+  const StreamBufs b = carve_streamed(c, rows, D, K, dt);
+  const int64_t nchunks = N > 0 ? (N + rows - 1) / rows : 0;
+  const size_t es = (size_t)dtype_size((int)dt);
+  const AssignGeom g = assign_geom(rows, D, K, dt);
+
+  hipEvent_t ready[2], freed[2];
+  for (int i = 0; i < 2; ++i) {
+    KM_HIP(hipEventCreateWithFlags(&ready[i], hipEventDisableTiming));
+    KM_HIP(hipEventCreateWithFlags(&freed[i], hipEventDisableTiming));
+  }
+  struct EventGuard {
+    hipEvent_t* r;
+    hipEvent_t* f;
+    ~EventGuard() {
+      for (int i = 0; i < 2; ++i) {
+        (void)hipEventDestroy(r[i]);
+        (void)hipEventDestroy(f[i]);
+      }
+    }
+  } guard{ready, freed};
+
+  int64_t seq = 0;  // global chunk counter: buffer = seq % 2
+  for (int32_t t = 0; t < iters; ++t) {
+    KM_TIMED("prep", cs, return launch_prep(C, K, D, (int)dt, g.KB, g.Kpad, b.f.frag, cs));
+    KM_HIP(launch_zero(b.acc_sum, sizeof(float) * (size_t)(K * D), cs));
+    KM_HIP(launch_zero(b.acc_cnt, sizeof(int64_t) * (size_t)K, cs));
+    if (objective && nchunks == 0) KM_HIP(launch_zero(objective + t, sizeof(double), cs));
+    for (int64_t ch = 0; ch < nchunks; ++ch, ++seq) {
+      const int buf = (int)(seq % 2);
+      const int64_t r0 = ch * rows;
+      const int64_t nr = (N - r0) < rows ? (N - r0) : rows;
+      // copy stream: wait until the compute of the chunk that last used this buffer is done
+      if (seq >= 2) KM_HIP(hipStreamWaitEvent(xs, freed[buf], 0));
+      KM_TIMED("h2d", xs,
+               return hipMemcpyAsync(b.xbuf[buf], (const uint8_t*)X_host + (size_t)r0 * (size_t)D * es,
+                                     (size_t)nr * (size_t)D * es, hipMemcpyHostToDevice, xs));
+      KM_HIP(hipEventRecord(ready[buf], xs));
+      // compute stream: assign the chunk, then fold its per-cluster sums into the totals
+      KM_HIP(hipStreamWaitEvent(cs, ready[buf], 0));
+      KM_TIMED("assign", cs,
+               return launch_flash_assign(b.xbuf[buf], (int)dt, nr, D, g.KB, b.f.frag, g.Kpad, b.f.assign,
+                                          objective ? b.f.min_dist : nullptr, cs));
+      if (objective)
+        KM_TIMED("objective", cs,
+                 return launch_objective(b.f.min_dist, nr, b.f.obj_part, objective + t, ch > 0 ? 1 : 0, cs));
+      const UpdateBufs u = b.f.u;
+      st = run_update(b.xbuf[buf], dt, nr, D, b.f.assign, K, nullptr, nullptr, nullptr, u, MODE_ACCUM, b.acc_sum,
+                      b.acc_cnt, cs);
+      if (st != KM_OK) return st;
+      if (assign_host && t == iters - 1)
+        KM_TIMED("d2h", cs,
+                 return hipMemcpyAsync(assign_host + r0, b.f.assign, sizeof(int32_t) * (size_t)nr,
+                                       hipMemcpyDeviceToHost, cs));
+      KM_HIP(hipEventRecord(freed[buf], cs));
+    }
+    KM_TIMED("finalize", cs, return launch_finalize_accum(b.acc_sum, b.acc_cnt, K, D, C, counts, cs));
+  }
+  return KM_OK;
+}
+
+const char* kmeans_status_string(km_status s) {
+  switch (s) {
+    case KM_OK: return "success";
+    case KM_ERR_INVALID_VALUE: return "invalid argument";
+    case KM_ERR_UNSUPPORTED: return "unsupported shape";
+    case KM_ERR_WORKSPACE: return "workspace missing or too small";
+    case KM_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* kmeans_last_error(void) { return g_last_error.c_str(); }
+
+km_status kmeans_timing_enable(int enable) {
+  TimingRegistry& T = timing();
+  std::lock_guard<std::mutex> g(T.mu);
+  T.enabled = enable != 0;
+  return KM_OK;
+}
+
+km_status kmeans_timing_read(const char* phase, double* total_ms, int64_t* launches) {
+  if (!phase || !total_ms || !launches) return fail(KM_ERR_INVALID_VALUE, "NULL argument");
+  TimingRegistry& T = timing();
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+  {
+    std::lock_guard<std::mutex> g(T.mu);
+    auto it = T.rec.find(phase);
+    if (it != T.rec.end()) ev = it->second;
+  }
+  double sum = 0.0;
+  for (auto& p : ev) {
+    KM_HIP(hipEventSynchronize(p.second));
+    float ms = 0.0f;
+    KM_HIP(hipEventElapsedTime(&ms, p.first, p.second));
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = (int64_t)ev.size();
+  return KM_OK;
+}
+
+km_status kmeans_timing_reset(void) {
+  TimingRegistry& T = timing();
+  std::lock_guard<std::mutex> g(T.mu);
+  for (auto& kv : T.rec)
+    for (auto& p : kv.second) {
+      (void)hipEventDestroy(p.first);
+      (void)hipEventDestroy(p.second);
+    }
+  T.rec.clear();
+  return KM_OK;
+}
+
+}  // extern "C"

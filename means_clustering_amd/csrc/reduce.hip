@@ -1,0 +1,435 @@
+// Segmented reduction of Sort-Inverse Update, boundary fix-up, finalisation
+// and the fp64 objective.
+//
+// Citations name the page "Flash-KMeans: Fast and Memory-Efficient Exact
+// K-Means" (gist.science summary of paper 2603.09229); "tech §n" is a section
+// of its technical summary.
+//
+// tech §2.2: after the argsort, the points of a cluster are contiguous in the
+// sorted order, so each worker reduces contiguous same-cluster segments on
+// chip and touches global memory only at segment boundaries.  Re-designed for
+// CDNA4 with no atomics at all:
+//   * the sorted order is cut into tiles of kSegTile positions; one "lane
+//     group" (G lanes, 16 bytes of a row each) walks a tile in order,
+//     gathering X[perm[i]] rows and accumulating in fp32 registers;
+//   * a segment that starts and ends inside the tile is finished right there
+//     (mean written, or added to the running totals when streaming);
+//   * a segment cut by a tile edge leaves a partial sum in one of the tile's
+//     two carry slots (slot 0: the tile's first id, slot 1: its last id);
+//   * the fix-up pass gives every cut segment one workgroup that adds its
+//     carry pieces in a fixed order (strided per thread row, then a fixed
+//     tree), so results do not depend on scheduling.
+// Atomic count: zero, against the page's O((K + N/B_N) d) boundary atomics.
+#include "km_internal.hpp"
+
+namespace km {
+
+typedef unsigned u32x4_r __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void widen(const u32x4_r& v, int dt, float* out) {
+  if (dt == DT_F32) {
+    out[0] = __uint_as_float(v.x);
+    out[1] = __uint_as_float(v.y);
+    out[2] = __uint_as_float(v.z);
+    out[3] = __uint_as_float(v.w);
+  } else if (dt == DT_BF16) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      out[2 * e] = __uint_as_float(w[e] << 16);
+      out[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+  } else {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      out[2 * e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[e] & 0xffffu));
+      out[2 * e + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[e] >> 16));
+    }
+  }
+}
+
+int64_t reduce_dc(int dt, int64_t D) {
+  const int64_t epl = dt == DT_F32 ? 4 : 8;
+  const int64_t nch = (D + epl - 1) / epl;
+  int64_t g = 1;
+  while (g < nch && g < 64) g <<= 1;
+  const int64_t cpl = (nch + g - 1) / g;
+  return g * cpl * epl;
+}
+
+// 16 bytes of row `row`, elements [c0, c0 + EPL), zero beyond D.
+template <int ES>
+__device__ __forceinline__ u32x4_r load_chunk(const uint8_t* __restrict__ X, int64_t row, int D, int c0, bool vec_ok) {
+  constexpr int EPL = 16 / ES;
+  u32x4_r v = {0u, 0u, 0u, 0u};
+  if (c0 >= D) return v;
+  const uint8_t* r = X + (size_t)row * (size_t)D * ES;
+  if (vec_ok && c0 + EPL <= D) return *reinterpret_cast<const u32x4_r*>(r + (size_t)c0 * ES);
+  uint32_t w[4] = {0, 0, 0, 0};
+  if (ES == 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (c0 + e < D) w[e] = reinterpret_cast<const uint32_t*>(r)[c0 + e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (c0 + e < D) w[e >> 1] |= (uint32_t)reinterpret_cast<const uint16_t*>(r)[c0 + e] << (16 * (e & 1));
+  }
+  return u32x4_r{w[0], w[1], w[2], w[3]};
+}
+
+struct SegParams {
+  const uint8_t* X;
+  int dt;
+  int64_t N;
+  int D;
+  int64_t K;
+  bool vec_ok;
+  const int32_t* keys;
+  const int32_t* vals;
+  const int32_t* off;
+  float* carry_sum;
+  int32_t* carry_cnt;
+  int Dc;
+  int mode;
+  const float* C_prev;
+  float* C_new;
+  int32_t* counts;
+  float* acc_sum;
+  int64_t* acc_cnt;
+};
+
+// Write a finished segment (or a carry piece) held by one lane group.
+template <int EPL, int CPL, int G>
+__device__ __forceinline__ void flush_piece(const SegParams& P, int64_t tile, int64_t ps, int64_t pe, int32_t first_key,
+                                            int32_t k, const float (&acc)[CPL][EPL], int32_t cnt, int j) {
+  if (k < 0 || k >= P.K) return;  // sorted ids lie in [0, K)
+  const int64_t s = P.off[k], e = P.off[k + 1];
+  if (s >= ps && e <= pe) {  // whole segment inside this tile: final here
+    if (P.mode == MODE_MEAN) {
+      if (j == 0 && P.counts) P.counts[k] = cnt;
+      const float fcnt = (float)cnt;
+#pragma unroll
+      for (int q = 0; q < CPL; ++q) {
+        const int c0 = (j + q * G) * EPL;
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) {
+          const int c = c0 + x;
+          if (c < P.D) {
+            const int64_t o = (int64_t)k * P.D + c;
+            P.C_new[o] = cnt > 0 ? acc[q][x] / fcnt : P.C_prev[o];
+          }
+        }
+      }
+    } else {
+      if (j == 0) P.acc_cnt[k] += cnt;
+#pragma unroll
+      for (int q = 0; q < CPL; ++q) {
+        const int c0 = (j + q * G) * EPL;
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) {
+          const int c = c0 + x;
+          if (c < P.D) P.acc_sum[(int64_t)k * P.D + c] += acc[q][x];
+        }
+      }
+    }
+  } else {  // cut by a tile edge: leave a carry piece
+    const int slot = k == first_key ? 0 : 1;
+    float* dst = P.carry_sum + (tile * 2 + slot) * (int64_t)P.Dc;
+    if (j == 0) P.carry_cnt[tile * 2 + slot] = cnt;
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) {
+      const int c0 = (j + q * G) * EPL;
+#pragma unroll
+      for (int x = 0; x < EPL; ++x) dst[c0 + x] = acc[q][x];
+    }
+  }
+}
+
+template <int ES, int CPL, int G>
+__global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
+  constexpr int EPL = 16 / ES;
+  constexpr int U = G < 8 ? G : 8;  // rows in flight per lane group
+  const int j = threadIdx.x % G;
+  const int lgbase = (threadIdx.x & 63) & ~(G - 1);
+  const int64_t tile = (int64_t)blockIdx.x * (256 / G) + threadIdx.x / G;
+  const int64_t ps = tile * kSegTile;
+  if (ps >= P.N) return;
+  const int64_t pe = ps + kSegTile < P.N ? ps + kSegTile : P.N;
+  const int32_t first_key = P.keys[ps];
+
+  float acc[CPL][EPL];
+#pragma unroll
+  for (int q = 0; q < CPL; ++q)
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) acc[q][x] = 0.0f;
+  int32_t cnt = 0;
+  int32_t cur = first_key;
+
+  for (int64_t p0 = ps; p0 < pe; p0 += G) {
+    const int64_t mypos = p0 + j;
+    const int32_t kj = mypos < pe ? P.keys[mypos] : 0;
+    const int32_t vj = mypos < pe ? P.vals[mypos] : (int32_t)kInvalidFlag;
+    for (int b0 = 0; b0 < G; b0 += U) {
+      if (p0 + b0 >= pe) break;
+      u32x4_r xr[U][CPL];
+      int32_t kk[U];
+      bool ok[U], in[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int b = b0 + u;
+        const int32_t v = __shfl(vj, lgbase + b);
+        kk[u] = __shfl(kj, lgbase + b);
+        in[u] = p0 + b < pe;
+        const int64_t row = (int64_t)((uint32_t)v & ~kInvalidFlag);
+        ok[u] = in[u] && v >= 0 && row < P.N;
+#pragma unroll
+        for (int q = 0; q < CPL; ++q)
+          xr[u][q] = ok[u] ? load_chunk<ES>(P.X, row, P.D, (j + q * G) * EPL, P.vec_ok) : u32x4_r{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (in[u]) {
+          if (kk[u] != cur) {
+            flush_piece<EPL, CPL, G>(P, tile, ps, pe, first_key, cur, acc, cnt, j);
+            cur = kk[u];
+            cnt = 0;
+#pragma unroll
+            for (int q = 0; q < CPL; ++q)
+#pragma unroll
+              for (int x = 0; x < EPL; ++x) acc[q][x] = 0.0f;
+          }
+          cnt += ok[u] ? 1 : 0;
+#pragma unroll
+          for (int q = 0; q < CPL; ++q) {
+            float f[EPL];
+            widen(xr[u][q], P.dt, f);
+#pragma unroll
+            for (int x = 0; x < EPL; ++x) acc[q][x] += f[x];
+          }
+        }
+      }
+    }
+  }
+  flush_piece<EPL, CPL, G>(P, tile, ps, pe, first_key, cur, acc, cnt, j);
+}
+
+// One workgroup per cluster: segments cut by tile edges are summed from their
+// carry pieces in a fixed order; empty clusters keep their centroid.
+__global__ __launch_bounds__(256) void fixup_kernel(SegParams P) {
+  __shared__ float red[256 * 4];
+  __shared__ int32_t redc[256];
+  const int64_t k = blockIdx.x;
+  const int64_t s = P.off[k], e = P.off[k + 1];
+  if (s < 0 || e > P.N || s > e) return;  // boundaries are monotone in [0, N]
+  if (s == e) {
+    if (P.mode == MODE_MEAN) {
+      if (threadIdx.x == 0 && P.counts) P.counts[k] = 0;
+      if (P.C_new != P.C_prev)
+        for (int c = threadIdx.x; c < P.D; c += 256) P.C_new[k * P.D + c] = P.C_prev[k * P.D + c];
+    }
+    return;
+  }
+  const int64_t t0 = s / kSegTile, t1 = (e - 1) / kSegTile;
+  if (t0 == t1) return;  // finished by segment_reduce_kernel
+  const int gc = P.Dc / 4;  // float4 columns of a carry piece (Dc is a multiple of 4, at most 512)
+  const int R = 256 / gc;   // thread rows
+  const int r = threadIdx.x / gc, c4 = threadIdx.x % gc;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  int32_t n = 0;
+  if (r < R) {
+    for (int64_t t = t0 + r; t <= t1; t += R) {
+      const int slot = (t == t0 && s != t0 * kSegTile) ? 1 : 0;
+      const float4 v = *reinterpret_cast<const float4*>(P.carry_sum + (t * 2 + slot) * (int64_t)P.Dc + c4 * 4);
+      a0 += v.x;
+      a1 += v.y;
+      a2 += v.z;
+      a3 += v.w;
+      if (c4 == 0) n += P.carry_cnt[t * 2 + slot];
+    }
+  }
+  red[threadIdx.x * 4 + 0] = a0;
+  red[threadIdx.x * 4 + 1] = a1;
+  red[threadIdx.x * 4 + 2] = a2;
+  red[threadIdx.x * 4 + 3] = a3;
+  redc[threadIdx.x] = n;
+  __syncthreads();
+  for (int stride = R / 2; stride > 0; stride >>= 1) {
+    if (r < stride) {
+      const int o = (r + stride) * gc + c4;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) red[threadIdx.x * 4 + x] += red[o * 4 + x];
+      if (c4 == 0) redc[threadIdx.x] += redc[o];
+    }
+    __syncthreads();
+  }
+  const int32_t total = redc[0];
+  if (r == 0) {
+    for (int x = 0; x < 4; ++x) {
+      const int c = c4 * 4 + x;
+      if (c >= P.D) continue;
+      const int64_t o = k * P.D + c;
+      const float sum = red[threadIdx.x * 4 + x];
+      if (P.mode == MODE_MEAN)
+        P.C_new[o] = total > 0 ? sum / (float)total : P.C_prev[o];
+      else
+        P.acc_sum[o] += sum;
+    }
+    if (c4 == 0) {
+      if (P.mode == MODE_MEAN) {
+        if (P.counts) P.counts[k] = total;
+      } else {
+        P.acc_cnt[k] += total;
+      }
+    }
+  }
+}
+
+static SegParams make_params(const ReduceArgs& a) {
+  SegParams P;
+  P.X = (const uint8_t*)a.X;
+  P.dt = a.dt;
+  P.N = a.N;
+  P.D = (int)a.D;
+  P.K = a.K;
+  const int es = dtype_size(a.dt);
+  P.vec_ok = (((uintptr_t)a.X) % 16 == 0) && ((a.D * es) % 16 == 0);
+  P.keys = a.keys;
+  P.vals = a.vals;
+  P.off = a.off;
+  P.carry_sum = a.carry_sum;
+  P.carry_cnt = a.carry_cnt;
+  P.Dc = (int)reduce_dc(a.dt, a.D);
+  P.mode = a.mode;
+  P.C_prev = a.C_prev;
+  P.C_new = a.C_new;
+  P.counts = a.counts;
+  P.acc_sum = a.acc_sum;
+  P.acc_cnt = a.acc_cnt;
+  return P;
+}
+
+template <int ES, int CPL, int G>
+static void launch_seg(const SegParams& P, hipStream_t s) {
+  const int64_t ntiles = (P.N + kSegTile - 1) / kSegTile;
+  const int64_t per_block = 256 / G;
+  hipLaunchKernelGGL((segment_reduce_kernel<ES, CPL, G>), dim3((unsigned)((ntiles + per_block - 1) / per_block)),
+                     dim3(256), 0, s, P);
+}
+
+hipError_t launch_segment_reduce(const ReduceArgs& a, hipStream_t stream) {
+  if (a.N == 0) return hipSuccess;
+  const SegParams P = make_params(a);
+  const int es = dtype_size(a.dt);
+  const int epl = 16 / es;
+  const int64_t nch = (a.D + epl - 1) / epl;
+  int g = 1;
+  while (g < nch && g < 64) g <<= 1;
+  const int cpl = (int)((nch + g - 1) / g);
+  // D <= 512 (16-bit) or 256 (fp32) gives at most 64 chunks: cpl == 1 always.
+  if (cpl != 1) return hipErrorInvalidValue;
+#define KM_SEG(ES_, G_) \
+  if (es == ES_ && g == G_) { launch_seg<ES_, 1, G_>(P, stream); return hipGetLastError(); }
+  KM_SEG(2, 1) KM_SEG(2, 2) KM_SEG(2, 4) KM_SEG(2, 8) KM_SEG(2, 16) KM_SEG(2, 32) KM_SEG(2, 64)
+  KM_SEG(4, 1) KM_SEG(4, 2) KM_SEG(4, 4) KM_SEG(4, 8) KM_SEG(4, 16) KM_SEG(4, 32) KM_SEG(4, 64)
+#undef KM_SEG
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fixup(const ReduceArgs& a, hipStream_t stream) {
+  if (a.K == 0) return hipSuccess;
+  const SegParams P = make_params(a);
+  hipLaunchKernelGGL(fixup_kernel, dim3((unsigned)a.K), dim3(256), 0, stream, P);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- streaming --
+
+__global__ void finalize_accum_kernel(const float* __restrict__ acc_sum, const int64_t* __restrict__ acc_cnt,
+                                      int64_t K, int64_t D, float* __restrict__ C, int32_t* __restrict__ counts) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= K * D) return;
+  const int64_t k = i / D;
+  const int64_t n = acc_cnt[k];
+  if (n > 0) C[i] = acc_sum[i] / (float)n;
+  if (counts && i % D == 0) counts[k] = (int32_t)n;
+}
+
+hipError_t launch_finalize_accum(const float* acc_sum, const int64_t* acc_cnt, int64_t K, int64_t D, float* C,
+                                 int32_t* counts, hipStream_t stream) {
+  const int64_t n = K * D;
+  const int tpb = 256;
+  hipLaunchKernelGGL(finalize_accum_kernel, dim3((unsigned)((n + tpb - 1) / tpb)), dim3(tpb), 0, stream, acc_sum,
+                     acc_cnt, K, D, C, counts);
+  return hipGetLastError();
+}
+
+__global__ void zero_kernel(uint32_t* __restrict__ p, int64_t words) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// Fill with zeros by a kernel (never hipMemsetAsync, so callers may capture it in a graph).
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
+  const int64_t words = (int64_t)(bytes / 4);
+  if (words == 0) return hipSuccess;
+  int64_t blocks = (words + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (uint32_t*)p, words);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- objective --
+
+constexpr int kObjThreads = 256;
+constexpr int kObjItems = 16;
+
+__global__ __launch_bounds__(kObjThreads) void objective_partial_kernel(const float* __restrict__ v, int64_t n,
+                                                                        double* __restrict__ part) {
+  __shared__ double red[kObjThreads];
+  const int64_t base = ((int64_t)blockIdx.x * kObjThreads + threadIdx.x) * kObjItems;
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < kObjItems; ++i)
+    if (base + i < n) s += (double)v[base + i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int st = kObjThreads / 2; st > 0; st >>= 1) {
+    if ((int)threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(kObjThreads) void objective_final_kernel(const double* __restrict__ part, int64_t np,
+                                                                      double* __restrict__ out, int accumulate) {
+  __shared__ double red[kObjThreads];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < np; i += kObjThreads) s += part[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int st = kObjThreads / 2; st > 0; st >>= 1) {
+    if ((int)threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[0] = (accumulate ? out[0] : 0.0) + red[0];
+}
+
+int64_t objective_partials(int64_t n) {
+  const int64_t per = (int64_t)kObjThreads * kObjItems;
+  return (n + per - 1) / per + 1;
+}
+
+hipError_t launch_objective(const float* v, int64_t n, double* partials, double* out, int accumulate,
+                            hipStream_t stream) {
+  const int64_t per = (int64_t)kObjThreads * kObjItems;
+  const int64_t np = (n + per - 1) / per;
+  if (np > 0)
+    hipLaunchKernelGGL(objective_partial_kernel, dim3((unsigned)np), dim3(kObjThreads), 0, stream, v, n, partials);
+  hipLaunchKernelGGL(objective_final_kernel, dim3(1), dim3(kObjThreads), 0, stream, (const double*)partials, np, out,
+                     accumulate);
+  return hipGetLastError();
+}
+
+}  // namespace km

@@ -192,9 +192,11 @@ def init_centroids(w: Workload, X: np.ndarray | None = None) -> np.ndarray:
     idx = init_indices(w)
     if X is not None:
         rows = X[idx]
-    else:
-        rows = np.concatenate([points(w, int(i), 1) for i in idx]) if len(idx) else \
-            np.empty((0, w.D), dtype=np.float32 if w.dtype == "f32" else np.uint16)
+    else:  # regenerate the chosen rows one by one (index-addressable generator)
+        cent = centers(w)
+        rows = np.empty((len(idx), w.D), dtype=np.float32 if w.dtype == "f32" else np.uint16)
+        for r, i in enumerate(idx):
+            points_into(w, rows[r:].ctypes.data, int(i), 1, cent=cent)
     return rows.astype(np.float32) if w.dtype == "f32" else bf16_bits_to_f32(rows)
 
 

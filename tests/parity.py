@@ -1,0 +1,83 @@
+"""Comparison of the HIP library's results with the fp64 oracle (test helper).
+
+The bar (the library's stated contract for exact Lloyd K-Means):
+  * assignments: a point may differ from the oracle only if the oracle's gap
+    between its best and second-best distance is at most
+    1e-4 * (||x||^2 + 1), and such near-tie differences stay below 0.01% of
+    the points (both sides score the same rounded centroids);
+  * counts: equal to the histogram of the library's own assignments, and to
+    the oracle's counts whenever the assignments agree;
+  * centroids: the oracle recomputes the update from the library's own
+    assignments (so a near-tie flip cannot leak into the comparison); the
+    error max_k ||c_k - c*_k||_inf / max(||c*_k||_inf, 1e-6) must stay within
+    1e-4 for fp32 X and 2e-3 for 16-bit X; empty clusters match bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+CENTROID_TOL = {"f32": 1e-4, "bf16": 2e-3, "f16": 2e-3}
+GAP_REL = 1e-4
+MAX_NEAR_TIE_FRAC = 1e-4
+
+
+def x_to_numpy(X: torch.Tensor):
+    """Stored values of a device X as numpy + the oracle's storage name."""
+    if X.dtype == torch.float32:
+        return X.cpu().numpy(), "f32"
+    if X.dtype == torch.bfloat16:
+        return X.cpu().view(torch.int16).numpy().view(np.uint16), "bf16"
+    if X.dtype == torch.float16:
+        return X.cpu().numpy(), "f16"
+    raise TypeError(X.dtype)
+
+
+def x_from_numpy(Xn: np.ndarray, xdtype: str, device) -> torch.Tensor:
+    if xdtype == "bf16":
+        return torch.from_numpy(Xn.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(Xn).to(device)
+
+
+def check_assign(Xn, xdtype, C_state, a_gpu, rows=None, label=""):
+    """Assignment of rows `rows` (all if None) against the oracle on the same centroid state."""
+    Xs = Xn if rows is None else Xn[rows]
+    a_ref, d1, d2 = oracle.assign(Xs, np.asarray(C_state, dtype=np.float64), xdtype)
+    a_gpu = np.asarray(a_gpu if rows is None else a_gpu[rows])
+    mism = np.nonzero(a_gpu != a_ref)[0]
+    xn = (oracle.decode(Xs, xdtype) ** 2).sum(axis=1)
+    gap = d2 - d1
+    allowed = gap[mism] <= GAP_REL * (xn[mism] + 1.0)
+    assert allowed.all(), (f"{label}: {int((~allowed).sum())} mismatches beyond the near-tie gap, e.g. rows "
+                           f"{mism[~allowed][:5].tolist()} gpu {a_gpu[mism[~allowed][:5]].tolist()} "
+                           f"oracle {a_ref[mism[~allowed][:5]].tolist()} gap {gap[mism[~allowed][:5]].tolist()}")
+    assert len(mism) <= MAX_NEAR_TIE_FRAC * len(Xs) + 1e-9 or len(mism) == 0, \
+        f"{label}: {len(mism)} near-tie mismatches of {len(Xs)} points"
+    return len(mism), a_ref
+
+
+def centroid_error(C_gpu, C_ref):
+    C_gpu = np.asarray(C_gpu, dtype=np.float64)
+    C_ref = np.asarray(C_ref, dtype=np.float64)
+    num = np.abs(C_gpu - C_ref).max(axis=1)
+    den = np.maximum(np.abs(C_ref).max(axis=1), 1e-6)
+    return float((num / den).max()) if len(num) else 0.0
+
+
+def check_update(Xn, xdtype, a_gpu, C_prev, C_gpu, counts_gpu, label=""):
+    """Update from the library's own assignments against the oracle's update from the same assignments."""
+    K = C_prev.shape[0]
+    C_ref, n_ref = oracle.update(Xn, np.asarray(a_gpu, dtype=np.int32), K, np.asarray(C_prev, dtype=np.float64),
+                                 xdtype)
+    a = np.asarray(a_gpu)
+    valid = (a >= 0) & (a < K)
+    assert np.array_equal(np.asarray(counts_gpu), np.bincount(a[valid], minlength=K)), f"{label}: counts"
+    assert np.array_equal(np.asarray(counts_gpu), n_ref), f"{label}: counts vs oracle"
+    empty = n_ref == 0
+    assert np.array_equal(np.asarray(C_gpu)[empty], np.asarray(C_prev, dtype=np.float32)[empty]), \
+        f"{label}: empty clusters must keep their centroid bit for bit"
+    err = centroid_error(np.asarray(C_gpu)[~empty], C_ref[~empty])
+    assert err <= CENTROID_TOL[xdtype], f"{label}: centroid error {err:.3e} > {CENTROID_TOL[xdtype]}"
+    return err

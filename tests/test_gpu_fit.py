@@ -1,0 +1,111 @@
+"""Lloyd iterations (kmeans_fit, kmeans_fit_streamed) against the fp64 oracle, iteration by iteration."""
+import numpy as np
+import pytest
+import torch
+
+import means_clustering_amd as km
+import oracle
+import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _workload(name, **kw):
+    w = synth.WORKLOADS[name].scaled(**kw)
+    Xn = synth.points(w)
+    C0 = synth.init_centroids(w, Xn)
+    return w, Xn, C0
+
+
+def _teacher_forced(Xn, xdtype, C0, T, label, streamed_chunk=None):
+    """Run T single iterations on the GPU; check each against the oracle fed the GPU's own state."""
+    X = parity.x_from_numpy(Xn, xdtype, DEV)
+    C = torch.from_numpy(C0).to(DEV)
+    max_err, flips = 0.0, 0
+    for t in range(T):
+        print(f"[fit] {label} iteration {t}", flush=True)
+        C_prev = C.cpu().numpy()
+        if streamed_chunk is None:
+            C, a, counts, obj = km.fit(X, C, 1, objective=True)
+        else:
+            Xh = X.cpu().pin_memory()
+            C, a, counts, obj = km.fit_streamed(Xh, C, 1, streamed_chunk, objective=True)
+        torch.cuda.synchronize()
+        an = a.cpu().numpy() if a.is_cuda else a.numpy()
+        nm, _ = parity.check_assign(Xn, xdtype, C_prev, an, label=f"{label} it{t}")
+        flips += nm
+        max_err = max(max_err, parity.check_update(Xn, xdtype, an, C_prev, C.cpu().numpy(),
+                                                   counts.cpu().numpy(), label=f"{label} it{t}"))
+        # objective: sum of the fp32 distances, against the fp64 distances to the same centroids
+        _, d1, _ = oracle.assign(Xn, C_prev.astype(np.float64), xdtype)
+        J = float(obj.cpu().numpy()[0])
+        assert abs(J - d1.sum()) <= 1e-5 * d1.sum() + 1e-6, (J, d1.sum())
+    return max_err, flips
+
+
+def test_fit_small_mixture_fp32():
+    w, Xn, C0 = _workload("c1", N=3000, K=40)
+    _teacher_forced(Xn, "f32", C0, 6, "c1-like fp32")
+
+
+def test_fit_small_mixture_bf16():
+    w, Xn, C0 = _workload("c2", N=20000, K=256)
+    _teacher_forced(Xn, "bf16", C0, 5, "c2-like bf16")
+
+
+def test_fit_skewed_bf16():
+    w, Xn, C0 = _workload("c4", N=60000, K=512)
+    _teacher_forced(Xn, "bf16", C0, 4, "c4-like zipf")
+
+
+def test_fit_unit_sphere_bf16():
+    w, Xn, C0 = _workload("c3", N=20000, K=2048)
+    _teacher_forced(Xn, "bf16", C0, 3, "c3-like sphere")
+
+
+@pytest.mark.parametrize("chunk", [7, 1000, 4096, 100_000])
+def test_fit_streamed_matches_oracle(chunk):
+    w, Xn, C0 = _workload("c4", N=9000, K=300)
+    _teacher_forced(Xn, "bf16", C0, 2, f"streamed chunk={chunk}", streamed_chunk=chunk)
+
+
+def test_fit_resume_and_determinism():
+    w, Xn, C0 = _workload("c2", N=50000, K=512)
+    X = parity.x_from_numpy(Xn, "bf16", DEV)
+    C0t = torch.from_numpy(C0).to(DEV)
+    C6, a6, n6, obj6 = km.fit(X, C0t, 6, objective=True)
+    C6b, a6b, n6b, _ = km.fit(X, C0t, 6)
+    Cs = C0t
+    objs = []
+    for t in range(6):  # resume from the state after every iteration
+        Cs, a1, n1, o1 = km.fit(X, Cs, 1, objective=True)
+        objs.append(o1)
+    torch.cuda.synchronize()
+    assert torch.equal(C6, C6b) and torch.equal(a6, a6b) and torch.equal(n6, n6b)
+    assert torch.equal(C6, Cs) and torch.equal(a6, a1) and torch.equal(n6, n1)
+    assert torch.equal(obj6, torch.cat(objs))
+
+
+def test_fit_zero_iterations_and_fixed_point():
+    g = torch.Generator().manual_seed(1)
+    cen = torch.tensor([[0.0, 0.0], [10.0, 0.0], [0.0, 10.0]])
+    off = torch.tensor([[1.0, 0.0], [-1.0, 0.0], [0.0, 1.0], [0.0, -1.0]])
+    X = (cen[:, None, :] + off[None]).reshape(-1, 2)[torch.randperm(12, generator=g)].to(DEV)
+    C, a, n, obj = km.fit(X, cen.to(DEV), 0)
+    torch.cuda.synchronize()
+    assert torch.equal(C.cpu(), cen)
+    C, a, n, obj = km.fit(X, cen.to(DEV), 3, objective=True)
+    torch.cuda.synchronize()
+    assert torch.equal(C.cpu(), cen) and n.cpu().tolist() == [4, 4, 4]
+    assert obj.cpu().tolist() == [12.0, 12.0, 12.0]
+
+
+def test_fit_trajectory_1d():
+    X = torch.tensor([[0.0], [1.0], [10.0], [11.0]], device=DEV)
+    C, a, n, obj = km.fit(X, torch.tensor([[0.0], [1.0]], device=DEV), 3, objective=True)
+    torch.cuda.synchronize()
+    assert C.cpu().flatten().tolist() == [0.5, 10.5]
+    assert a.cpu().tolist() == [0, 0, 1, 1]
+    np.testing.assert_allclose(obj.cpu().numpy(), [181.0, 194.0 / 9.0, 1.0], rtol=1e-5)

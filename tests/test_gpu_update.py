@@ -1,0 +1,97 @@
+"""Sort-Inverse Update (kmeans_update) against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import means_clustering_amd as km
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def _run(X, a_np, C_prev, label, inplace=False):
+    print(f"[update] {label} N={X.shape[0]} D={X.shape[1]} K={C_prev.shape[0]} {X.dtype}", flush=True)
+    a = torch.from_numpy(a_np.astype(np.int32)).to(DEV)
+    prev_np = C_prev.cpu().numpy().copy()
+    if inplace:
+        C_new, counts = km.update(X, a, C_prev, out=C_prev)
+    else:
+        C_new, counts = km.update(X, a, C_prev)
+    torch.cuda.synchronize()
+    Xn, xdt = parity.x_to_numpy(X)
+    return parity.check_update(Xn, xdt, a_np, prev_np, C_new.cpu().numpy(), counts.cpu().numpy(), label=label)
+
+
+def _x(N, D, xdtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(N, D, generator=g) * 2).to(TORCH_DT[xdtype]).to(DEV)
+
+
+@pytest.mark.parametrize("xdtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("shape", [(1, 1, 1), (100, 3, 7), (1000, 32, 64), (20000, 128, 1024), (5000, 64, 5000),
+                                   (3001, 200, 50), (700, 512, 9), (12345, 96, 4096)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_update_random(shape, xdtype):
+    N, D, K = shape
+    if xdtype == "f32" and D > 256:
+        pytest.skip("fp32 supports D <= 256")
+    X = _x(N, D, xdtype, seed=N + D + K)
+    rng = np.random.default_rng(N * 3 + K)
+    a = rng.integers(0, K, N)
+    C_prev = torch.randn(K, D, generator=torch.Generator().manual_seed(K)).to(DEV)
+    _run(X, a, C_prev, f"random {shape} {xdtype}")
+
+
+def test_update_hot_cluster_spanning_many_tiles():
+    X = _x(400_000, 64, "bf16", seed=1)
+    rng = np.random.default_rng(2)
+    a = np.where(rng.random(400_000) < 0.7, 5, rng.integers(0, 4096, 400_000))
+    C_prev = torch.randn(4096, 64).to(DEV)
+    _run(X, a, C_prev, "70% of points in cluster 5")
+
+
+def test_update_all_points_one_cluster_and_empty_rest():
+    X = _x(300_000, 128, "bf16", seed=3)
+    a = np.full(300_000, 2)
+    C_prev = torch.randn(17, 128).to(DEV)
+    _run(X, a, C_prev, "single cluster")
+
+
+def test_update_zipf_inplace():
+    X = _x(250_000, 64, "bf16", seed=4)
+    rng = np.random.default_rng(5)
+    w = 1.0 / np.arange(1, 4097) ** 1.2
+    a = rng.choice(4096, size=250_000, p=w / w.sum())
+    C_prev = torch.randn(4096, 64).to(DEV)
+    _run(X, a, C_prev, "zipf in place", inplace=True)
+
+
+def test_update_invalid_ids_are_ignored():
+    X = _x(10_000, 32, "f32", seed=6)
+    rng = np.random.default_rng(7)
+    a = rng.integers(0, 100, 10_000)
+    a[::13] = -1
+    a[1::17] = 100
+    a[2::19] = 2**31 - 1
+    C_prev = torch.randn(100, 32).to(DEV)
+    _run(X, a, C_prev, "invalid ids")
+
+
+def test_update_empty_input_keeps_centroids():
+    X = torch.empty(0, 16, dtype=torch.bfloat16, device=DEV)
+    C_prev = torch.randn(5, 16).to(DEV)
+    C_new, counts = km.update(X, torch.empty(0, dtype=torch.int32, device=DEV), C_prev)
+    torch.cuda.synchronize()
+    assert torch.equal(C_new, C_prev) and counts.cpu().tolist() == [0] * 5
+
+
+def test_update_deterministic():
+    X = _x(300_000, 128, "bf16", seed=8)
+    a = torch.from_numpy(np.random.default_rng(9).integers(0, 1024, 300_000).astype(np.int32)).to(DEV)
+    C_prev = torch.randn(1024, 128).to(DEV)
+    c1, n1 = km.update(X, a, C_prev)
+    c2, n2 = km.update(X, a, C_prev)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2) and torch.equal(n1, n2)
