@@ -19,7 +19,9 @@ SOURCES = ["csrc/flash_assign.hip", "csrc/sort.hip", "csrc/reduce.hip", "csrc/ap
 ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 instructions.
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-          "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
+          "-packed-fp32-ops", "-Wno-unused-command-line-argument",
+          # MFMA results in ordinary VGPRs: the argmax epilogue reads them without accumulator copies
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def _hipcc() -> str:

@@ -90,7 +90,7 @@ static km_status check_sizes(int64_t N, int64_t D, int64_t K, km_dtype dt, bool 
   if (K < 1 || K >= kMaxN) return fail(KM_ERR_INVALID_VALUE, "K must satisfy 1 <= K < 2^31");
   if (need_d) {
     if (D < 1) return fail(KM_ERR_INVALID_VALUE, "D must be >= 1");
-    const int64_t dmax = (int64_t)kMaxKB * frag_depth(dt);
+    const int64_t dmax = dt == KM_F32 ? kMaxD32 : kMaxD16;
     if (D > dmax)
       return fail(KM_ERR_UNSUPPORTED, "D=" + std::to_string(D) + " exceeds the supported maximum " +
                                           std::to_string(dmax) + " for this dtype");
@@ -102,14 +102,7 @@ static km_status check_sizes(int64_t N, int64_t D, int64_t K, km_dtype dt, bool 
 // ----------------------------------------------------------- geometry -----
 
 static AssignGeom assign_geom(int64_t N, int64_t D, int64_t K, km_dtype dt) {
-  AssignGeom g;
-  g.dt = (int)dt;
-  g.N = N;
-  g.D = D;
-  g.K = K;
-  g.KB = (int)((D + frag_depth(dt) - 1) / frag_depth(dt));
-  g.Kpad = pad_up(K, kPadK);
-  return g;
+  return make_assign_geom(N, D, K, (int)dt);
 }
 
 static SortGeom sort_geom(int64_t N, int64_t K) {
@@ -249,9 +242,8 @@ static km_status check_ws(void* ws, size_t ws_bytes, size_t need) {
 static km_status run_assign(const void* X, km_dtype dt, int64_t N, int64_t D, const float* C, int64_t K,
                             int32_t* assign, float* min_dist, void* frag, hipStream_t s) {
   const AssignGeom g = assign_geom(N, D, K, dt);
-  KM_TIMED("prep", s, return launch_prep(C, K, D, (int)dt, g.KB, g.Kpad, frag, s));
-  if (N > 0)
-    KM_TIMED("assign", s, return launch_flash_assign(X, (int)dt, N, D, g.KB, frag, g.Kpad, assign, min_dist, s));
+  KM_TIMED("prep", s, return launch_prep(g, C, frag, s));
+  if (N > 0) KM_TIMED("assign", s, return launch_flash_assign(g, X, N, frag, assign, min_dist, s));
   return KM_OK;
 }
 
@@ -442,7 +434,7 @@ km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_
 
   int64_t seq = 0;  // global chunk counter: buffer = seq % 2
   for (int32_t t = 0; t < iters; ++t) {
-    KM_TIMED("prep", cs, return launch_prep(C, K, D, (int)dt, g.KB, g.Kpad, b.f.frag, cs));
+    KM_TIMED("prep", cs, return launch_prep(g, C, b.f.frag, cs));
     KM_HIP(launch_zero(b.acc_sum, sizeof(float) * (size_t)(K * D), cs));
     KM_HIP(launch_zero(b.acc_cnt, sizeof(int64_t) * (size_t)K, cs));
     if (objective && nchunks == 0) KM_HIP(launch_zero(objective + t, sizeof(double), cs));
@@ -459,7 +451,7 @@ km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_
       // compute stream: assign the chunk, then fold its per-cluster sums into the totals
       KM_HIP(hipStreamWaitEvent(cs, ready[buf], 0));
       KM_TIMED("assign", cs,
-               return launch_flash_assign(b.xbuf[buf], (int)dt, nr, D, g.KB, b.f.frag, g.Kpad, b.f.assign,
+               return launch_flash_assign(g, b.xbuf[buf], nr, b.f.frag, b.f.assign,
                                           objective ? b.f.min_dist : nullptr, cs));
       if (objective)
         KM_TIMED("objective", cs,

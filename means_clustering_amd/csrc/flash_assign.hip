@@ -22,14 +22,19 @@
 //
 // Structure (tech §2.1 "online argmin", "tiled streaming", "double buffering",
 // re-designed for CDNA4):
-//   * a wavefront owns NB x 16 points and keeps their operand fragments in
+//   * 16-bit X uses v_mfma_f32_32x32x16 (32 centroids x 32 points per
+//     instruction; on gfx950 the 16x16x32 shape runs at half this rate);
+//     fp32 X uses v_mfma_f32_16x16x4_f32;
+//   * a wavefront owns NB point groups and keeps their operand fragments in
 //     VGPRs for the whole centroid sweep (X is read from HBM exactly once);
-//   * centroids stream through LDS in tiles of CT x 16, double-buffered:
+//   * centroids stream through LDS in tiles of CT groups, double-buffered:
 //     tile t+1 is fetched from L2/HBM into registers while tile t feeds the
 //     matrix cores, then stored to the other LDS buffer (one barrier a tile);
-//   * each lane keeps (best score, tile-relative selector) for its points in
-//     registers; the four lanes that hold the same point merge once at the
-//     end, so ties resolve to the lowest centroid index.
+//   * the accumulator of each MFMA chain starts at the centroid's bias, so
+//     the matrix cores deliver the score and the vector ALUs only keep the
+//     running (best score, selector) per lane in registers;
+//   * the lanes that hold the same point merge once at the end (ties go to
+//     the lowest centroid index).
 #include <math.h>
 
 #include "km_internal.hpp"
@@ -39,6 +44,7 @@ namespace km {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
@@ -58,161 +64,92 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-// Value of the centroid coordinate as the contraction sees it.
-__device__ __forceinline__ float quantize(float c, int dt) {
-  if (dt == DT_BF16) return bf16_bits_to_f32(f32_to_bf16_bits(c));
-  if (dt == DT_F16) return f16_bits_to_f32(f32_to_f16_bits(c));
-  return c;
-}
-
 // ---------------------------------------------------------------- prep ----
 
-// One thread per 16-byte fragment (group g, depth block kb, lane).  Group g
-// occupies KB*64 + 4 consecutive 16-byte slots: its fragments, then its 16
-// bias values (written by prep_bias_kernel).
-__global__ void prep_frag_kernel(const float* __restrict__ C, int64_t K, int64_t D, int dt, int KB,
-                                 int64_t total, uint4* __restrict__ frag) {
-  int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (tid >= total) return;
-  const int lane = (int)(tid & 63);
-  const int64_t t2 = tid >> 6;
-  const int kb = (int)(t2 % KB);
-  const int64_t g = t2 / KB;
-  const int64_t CT = assign_cfg(KB).CT;
-  const int64_t slot = (g / CT) * tile_slots(KB) + (g % CT) * group_slots(KB) + (int64_t)kb * 64 + lane;
-  const int64_t k = g * kGroupRows + (lane & 15);
-  uint32_t w[4];
-  if (dt == DT_F32) {
-    const int64_t d0 = (int64_t)kb * 16 + (lane >> 4) * 4;
+// One wavefront per centroid group: quantise the group's rows into fragment
+// blocks, and write -||Q(c)||^2/2 (fp32, from the quantised values) in the
+// order the FlashAssign lanes read it; padding rows get zero fragments and a
+// bias of -inf, so they can never be selected.
+__global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ C, int64_t K, int D, int dt, AssignCfg cfg,
+                                                   int64_t groups, u32x4_t* __restrict__ frag) {
+  const int lane = threadIdx.x & 63;
+  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (g >= groups) return;
+  const bool wide = cfg.rows == 32;
+  const int rsel = wide ? (lane & 31) : (lane & 15);
+  const int part = wide ? (lane >> 5) : (lane >> 4);  // which 8 (wide) or 4 (narrow) depth values
+  const int64_t row = g * cfg.rows + rsel;
+  const bool live = row < K;
+  u32x4_t* gdst = frag + (g / cfg.CT) * cfg.tile_slots() + (g % cfg.CT) * cfg.group_slots();
+  float ss = 0.0f;
+  for (int kb = 0; kb < cfg.KB; ++kb) {
+    uint32_t w[4];
+    if (wide) {
+      const int d0 = kb * kFragDepth + part * 8;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t d = d0 + e;
-      w[e] = __float_as_uint((k < K && d < D) ? C[k * D + d] : 0.0f);
+      for (int e = 0; e < 4; ++e) {
+        const int da = d0 + 2 * e, db = da + 1;
+        const float ca = (live && da < D) ? C[row * D + da] : 0.0f;
+        const float cb = (live && db < D) ? C[row * D + db] : 0.0f;
+        const uint32_t qa = dt == DT_BF16 ? f32_to_bf16_bits(ca) : f32_to_f16_bits(ca);
+        const uint32_t qb = dt == DT_BF16 ? f32_to_bf16_bits(cb) : f32_to_f16_bits(cb);
+        const float fa = dt == DT_BF16 ? bf16_bits_to_f32(qa) : f16_bits_to_f32(qa);
+        const float fb = dt == DT_BF16 ? bf16_bits_to_f32(qb) : f16_bits_to_f32(qb);
+        ss = fmaf(fa, fa, ss);
+        ss = fmaf(fb, fb, ss);
+        w[e] = qa | (qb << 16);
+      }
+    } else {
+      const int d0 = kb * kFragDepth + part * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = d0 + e;
+        const float c = (live && d < D) ? C[row * D + d] : 0.0f;
+        ss = fmaf(c, c, ss);
+        w[e] = __float_as_uint(c);
+      }
     }
+    gdst[kb * 64 + lane] = u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+  // total over the lanes that hold the same row
+  if (wide) {
+    ss += __shfl_xor(ss, 32);
   } else {
-    const int64_t d0 = (int64_t)kb * 32 + (lane >> 4) * 8;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      uint32_t lo = 0, hi = 0;
-      const int64_t da = d0 + 2 * e, db = d0 + 2 * e + 1;
-      const float ca = (k < K && da < D) ? C[k * D + da] : 0.0f;
-      const float cb = (k < K && db < D) ? C[k * D + db] : 0.0f;
-      lo = dt == DT_BF16 ? f32_to_bf16_bits(ca) : f32_to_f16_bits(ca);
-      hi = dt == DT_BF16 ? f32_to_bf16_bits(cb) : f32_to_f16_bits(cb);
-      w[e] = lo | (hi << 16);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+  }
+  float* bias = reinterpret_cast<float*>(gdst + cfg.KB * 64);
+  if (part == 0) {
+    const float b = live ? -0.5f * ss : -INFINITY;
+    if (wide) {  // lane half h reads rows 8j + 4h + r as its 16 accumulator values
+      const int j = rsel >> 3, h = (rsel >> 2) & 1, r = rsel & 3;
+      bias[h * 16 + j * 4 + r] = b;
+    } else {  // lane quad q reads rows 4q .. 4q+3
+      bias[rsel] = b;
     }
   }
-  frag[slot] = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// bias_k = -||Q(c_k)||^2 / 2 in fp32 (ascending coordinate order), -inf for
-// padding rows; stored after the fragments of its group, 16 floats a group.
-__global__ void prep_bias_kernel(const float* __restrict__ C, int64_t K, int64_t D, int dt, int KB, int64_t Kpad,
-                                 float* __restrict__ frag_f) {
-  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= Kpad) return;
-  const int64_t g = k / kGroupRows;
-  const int64_t CT = assign_cfg(KB).CT;
-  float* dst = frag_f + ((g / CT) * tile_slots(KB) + (g % CT) * group_slots(KB) + (int64_t)KB * 64) * 4 +
-               (k % kGroupRows);
-  if (k >= K) {
-    *dst = -INFINITY;
-    return;
-  }
-  float s = 0.0f;
-  for (int64_t d = 0; d < D; ++d) {
-    const float q = quantize(C[k * D + d], dt);
-    s = fmaf(q, q, s);
-  }
-  *dst = -0.5f * s;
-}
-
-hipError_t launch_prep(const float* C, int64_t K, int64_t D, int dt, int KB, int64_t Kpad, void* frag,
-                       hipStream_t stream) {
-  const int64_t total = (Kpad / kGroupRows) * KB * 64;
-  const int tpb = 256;
-  hipLaunchKernelGGL(prep_frag_kernel, dim3((unsigned)((total + tpb - 1) / tpb)), dim3(tpb), 0, stream, C, K, D,
-                     dt, KB, total, (uint4*)frag);
-  hipLaunchKernelGGL(prep_bias_kernel, dim3((unsigned)((Kpad + tpb - 1) / tpb)), dim3(tpb), 0, stream, C, K, D, dt,
-                     KB, Kpad, (float*)frag);
+hipError_t launch_prep(const AssignGeom& g, const float* C, void* frag, hipStream_t stream) {
+  const int64_t groups = g.groups();
+  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)((groups + 3) / 4)), dim3(256), 0, stream, C, g.K, (int)g.D, g.dt,
+                     g.cfg, groups, (u32x4_t*)frag);
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------- FlashAssign ----
+// ------------------------------------------------------- point fragments ----
 
-template <int DT>
-struct FragTraits;
-template <>
-struct FragTraits<DT_BF16> {
-  static constexpr int EPL = 8, FB = 32, ES = 2;
-  static __device__ __forceinline__ f32x4_t mma(u32x4_t a, u32x4_t b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                   c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ float sumsq(u32x4_t v) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    float s = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a = bf16_bits_to_f32(w[e] & 0xffffu), b = bf16_bits_to_f32(w[e] >> 16);
-      s = fmaf(a, a, s);
-      s = fmaf(b, b, s);
-    }
-    return s;
-  }
-};
-template <>
-struct FragTraits<DT_F16> {
-  static constexpr int EPL = 8, FB = 32, ES = 2;
-  static __device__ __forceinline__ f32x4_t mma(u32x4_t a, u32x4_t b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
-                                                  0, 0, 0);
-  }
-  static __device__ __forceinline__ float sumsq(u32x4_t v) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    float s = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a = f16_bits_to_f32(w[e] & 0xffffu), b = f16_bits_to_f32(w[e] >> 16);
-      s = fmaf(a, a, s);
-      s = fmaf(b, b, s);
-    }
-    return s;
-  }
-};
-template <>
-struct FragTraits<DT_F32> {
-  static constexpr int EPL = 4, FB = 16, ES = 4;
-  static __device__ __forceinline__ f32x4_t mma(u32x4_t a, u32x4_t b, f32x4_t c) {
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
-    return c;
-  }
-  static __device__ __forceinline__ float sumsq(u32x4_t v) {
-    const float a = __uint_as_float(v.x), b = __uint_as_float(v.y), c = __uint_as_float(v.z),
-                d = __uint_as_float(v.w);
-    float s = 0.0f;
-    s = fmaf(a, a, s);
-    s = fmaf(b, b, s);
-    s = fmaf(c, c, s);
-    s = fmaf(d, d, s);
-    return s;
-  }
-};
-
-// 16 bytes of point p, depth values [d0, d0 + EPL); zero beyond D or N.
-template <int DT>
+// 16 bytes of row p, elements [d0, d0 + 16/ES); zero beyond D or N.
+template <int ES>
 __device__ __forceinline__ u32x4_t load_point_frag(const uint8_t* __restrict__ X, int64_t p, int64_t N, int D, int d0,
-                                                 bool vec_ok) {
-  using T = FragTraits<DT>;
+                                                   bool vec_ok) {
+  constexpr int EPL = 16 / ES;
   u32x4_t v = {0u, 0u, 0u, 0u};
   if (p >= N || d0 >= D) return v;
-  const uint8_t* row = X + (size_t)p * (size_t)D * T::ES;
-  if (vec_ok && d0 + T::EPL <= D) return *reinterpret_cast<const u32x4_t*>(row + (size_t)d0 * T::ES);
+  const uint8_t* row = X + (size_t)p * (size_t)D * ES;
+  if (vec_ok && d0 + EPL <= D) return *reinterpret_cast<const u32x4_t*>(row + (size_t)d0 * ES);
   uint32_t w[4] = {0, 0, 0, 0};
-  if (T::ES == 4) {
+  if (ES == 4) {
     const uint32_t* r = reinterpret_cast<const uint32_t*>(row);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -226,16 +163,306 @@ __device__ __forceinline__ u32x4_t load_point_frag(const uint8_t* __restrict__ X
   return u32x4_t{w[0], w[1], w[2], w[3]};
 }
 
-template <int DT, int KB, int NB, int W, int CT>
-__global__ __launch_bounds__(W * 64) void flash_assign_kernel(const uint8_t* __restrict__ X, int64_t N, int D,
-                                                              bool vec_ok, const u32x4_t* __restrict__ frag,
-                                                              int ntiles, int32_t* __restrict__ assign,
-                                                              float* __restrict__ min_dist) {
-  using T = FragTraits<DT>;
-  constexpr int GS = (int)group_slots(KB);  // 16-byte slots per centroid group: fragments, then 16 biases
-  constexpr int TS = (int)tile_slots(KB);   // slots per tile, a multiple of the thread count
+template <int DT>
+__device__ __forceinline__ float sumsq16(u32x4_t v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float s = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a = DT == DT_BF16 ? bf16_bits_to_f32(w[e] & 0xffffu) : f16_bits_to_f32(w[e] & 0xffffu);
+    const float b = DT == DT_BF16 ? bf16_bits_to_f32(w[e] >> 16) : f16_bits_to_f32(w[e] >> 16);
+    s = fmaf(a, a, s);
+    s = fmaf(b, b, s);
+  }
+  return s;
+}
+
+template <int DT>
+__device__ __forceinline__ f32x16_t mma32(u32x4_t a, u32x4_t b, f32x16_t c) {
+  if constexpr (DT == DT_BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                   0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                  0, 0, 0);
+}
+
+// ------------------------------------------------- FlashAssign, 16-bit X ----
+//
+// MFMA 32x32x16 layout: lane l supplies A row (l % 32) and B column (l % 32),
+// 8 depth values each (the same depth values for A and B, so the contraction
+// is exact whatever order the hardware sums them in); the result lane l holds
+// column (l % 32) and rows 8j + 4(l/32) + r as accumulator element 4j + r.
+// So a lane scores one point against 16 centroids per instruction group, in
+// ascending centroid order, and lanes l and l ^ 32 share the point.
+
+// Running-argmax update with one score: if v > best then (best, rel) = (v, E).
+// Three VALU instructions: the comparison lands in VCC and the element index
+// E is an inline constant, so no selector has to be copied into a vector
+// register.  `rel` counts from the base of the group being scanned (callers
+// rebase it by -16 per group).  A NaN score never wins ("not greater than").
+template <int E>
+__device__ __forceinline__ void argmax_update(float v, float& best, int& rel) {
+  asm("v_cmp_ngt_f32 vcc, %2, %0\n\t"
+      "v_cndmask_b32 %0, %2, %0, vcc\n\t"
+      "v_cndmask_b32 %1, %3, %1, vcc"
+      : "+v"(best), "+v"(rel)
+      : "v"(v), "I"(E)
+      : "vcc");
+}
+
+template <int E, int NB>
+__device__ __forceinline__ void argmax_all(const f32x16_t (&in)[NB], float (&best)[NB], int (&rel)[NB]) {
+#pragma unroll
+  for (int g = 0; g < NB; ++g) argmax_update<E>(in[g][E], best[g], rel[g]);
+}
+
+// Elements [E0, E1) of the previous group's scores.
+template <int E0, int E1, int NB>
+__device__ __forceinline__ void argmax_range(const f32x16_t (&in)[NB], float (&best)[NB], int (&rel)[NB]) {
+  if constexpr (E0 < E1 && E0 < 16) {
+    argmax_all<E0, NB>(in, best, rel);
+    argmax_range<E0 + 1, E1, NB>(in, best, rel);
+  }
+}
+
+__device__ __forceinline__ f32x16_t bias_of(const u32x4_t* bp) {
+  const u32x4_t b0 = bp[0], b1 = bp[1], b2 = bp[2], b3 = bp[3];
+  return f32x16_t{__uint_as_float(b0.x), __uint_as_float(b0.y), __uint_as_float(b0.z), __uint_as_float(b0.w),
+                  __uint_as_float(b1.x), __uint_as_float(b1.y), __uint_as_float(b1.z), __uint_as_float(b1.w),
+                  __uint_as_float(b2.x), __uint_as_float(b2.y), __uint_as_float(b2.z), __uint_as_float(b2.w),
+                  __uint_as_float(b3.x), __uint_as_float(b3.y), __uint_as_float(b3.z), __uint_as_float(b3.w)};
+}
+
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Lazy running argmax, fast part: fold a share of the previous group's 16
+// scores into a running group maximum m (exact, 1 instruction per 2 scores).
+template <int E0, int E1, int NB>
+__device__ __forceinline__ void fold_range(const f32x16_t (&in)[NB], float (&m)[NB]) {
+  if constexpr (E0 < E1 && E0 < 16) {
+    if constexpr (E0 + 1 < E1 && E0 + 1 < 16) {
+#pragma unroll
+      for (int g = 0; g < NB; ++g) m[g] = max3f(m[g], in[g][E0], in[g][E0 + 1]);
+      fold_range<E0 + 2, E1, NB>(in, m);
+    } else {
+#pragma unroll
+      for (int g = 0; g < NB; ++g) m[g] = max3f(m[g], in[g][E0], in[g][E0]);
+      fold_range<E0 + 1, E1, NB>(in, m);
+    }
+  }
+}
+
+// Lazy running argmax, slow part: only when some lane's group maximum beats
+// its running best does the wavefront scan the group's scores exactly; the
+// result is the same as scanning every group exactly (a group whose maximum
+// does not exceed the best cannot change the lowest-index argmax).
+template <int NB>
+__device__ __forceinline__ void lazy_resolve(const f32x16_t (&in)[NB], const float (&m)[NB], float (&best)[NB],
+                                             int (&rel)[NB]) {
+  bool imp = false;
+#pragma unroll
+  for (int g = 0; g < NB; ++g) imp |= m[g] > best[g];
+  if (__builtin_amdgcn_ballot_w64(imp)) argmax_range<0, 16, NB>(in, best, rel);
+}
+
+// One pipeline stage: the MFMAs of one 32-centroid group into `out`, depth
+// block by depth block, each block fenced together with its share of the
+// running-argmax update over the previous group's scores `in`, so the matrix
+// cores and the vector ALUs of one wavefront overlap.  `a0`/`bias` hold the
+// group's first A fragment and its bias (fetched by the caller); the next
+// depth block's fragment is fetched one step ahead.
+template <int KB, int NB, int KBI, bool LAZY>
+__device__ __forceinline__ void epilogue_share(const f32x16_t (&in)[NB], float (&best)[NB], int (&rel)[NB],
+                                               float (&m)[NB]) {
+  constexpr int per = (16 + KB - 1) / KB;  // epilogue elements per depth block
+  if constexpr (LAZY)
+    fold_range<KBI * per, (KBI + 1) * per, NB>(in, m);
+  else
+    argmax_range<KBI * per, (KBI + 1) * per, NB>(in, best, rel);
+}
+
+template <int DT, int KB, int NB, bool LAZY, bool epi, int KBI = 0>
+__device__ __forceinline__ void pipeline_steps(const u32x4_t* __restrict__ grp, int lane, u32x4_t a,
+                                               const f32x16_t& bias, const u32x4_t (&xb)[NB][KB],
+                                               f32x16_t (&out)[NB], const f32x16_t (&in)[NB], float (&best)[NB],
+                                               int (&rel)[NB], float (&m)[NB]) {
+  if constexpr (KBI < KB) {
+    u32x4_t a_next;
+    if constexpr (KBI + 1 < KB) a_next = grp[(KBI + 1) * 64 + lane];
+    if constexpr (epi) {
+      if constexpr (KBI == 0) {
+#pragma unroll
+        for (int g = 0; g < NB; ++g) {
+          rel[g] -= 16;  // selectors now count from this group's base
+          m[g] = -INFINITY;
+        }
+      }
+      epilogue_share<KB, NB, KBI, LAZY>(in, best, rel, m);
+    }
+#pragma unroll
+    for (int g = 0; g < NB; ++g) out[g] = mma32<DT>(a, xb[g][KBI], KBI == 0 ? bias : out[g]);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (KBI + 1 < KB)
+      pipeline_steps<DT, KB, NB, LAZY, epi, KBI + 1>(grp, lane, a_next, bias, xb, out, in, best, rel, m);
+    else if constexpr (epi && LAZY)
+      lazy_resolve<NB>(in, m, best, rel);
+  }
+}
+
+// Copy one centroid tile (TS 16-byte slots) from global memory straight into
+// LDS: each lane moves 16 bytes per instruction, and a wavefront fills 64
+// consecutive slots starting at a wave-uniform LDS address, so no VGPRs hold
+// the data in flight.  Completion is awaited with s_waitcnt before the
+// barrier that publishes the tile.
+template <int TS, int NTHR>
+__device__ __forceinline__ void tile_dma(const u32x4_t* __restrict__ src, u32x4_t* lds_tile, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < TS / NTHR; ++i) {
+    const int base = i * NTHR + wave * 64;
+    __builtin_amdgcn_global_load_lds((const void*)(src + base + lane),
+                                     (__attribute__((address_space(3))) void*)(lds_tile + base), 16, 0, 0);
+  }
+}
+
+template <int NB>
+__device__ __forceinline__ void drain_epilogue(const f32x16_t (&in)[NB], float (&best)[NB], int (&rel)[NB]) {
+#pragma unroll
+  for (int g = 0; g < NB; ++g) rel[g] -= 16;
+  argmax_range<0, 16, NB>(in, best, rel);
+}
+
+template <int DT, int KB, bool LAZY>
+__global__ __launch_bounds__(wide_cfg(KB).W * 64) void flash_assign_wide_kernel(
+    const uint8_t* __restrict__ X, int64_t N, int D, bool vec_ok, const u32x4_t* __restrict__ frag, int ntiles,
+    int32_t* __restrict__ assign, float* __restrict__ min_dist) {
+  constexpr AssignCfg cfg = wide_cfg(KB);
+  constexpr int NB = cfg.NB, CT = cfg.CT, W = cfg.W;
+  constexpr int GS = (int)cfg.group_slots();
+  constexpr int TS = (int)cfg.tile_slots();
   constexpr int NTHR = W * 64;
-  constexpr int CPT = TS / NTHR;            // 16-byte copies per thread per tile
+  constexpr int CPT = TS / NTHR;
+  static_assert(TS % NTHR == 0 && TS >= CT * GS, "tile padding");
+  static_assert(CT % 2 == 0, "groups alternate between two accumulator sets");
+  __shared__ u32x4_t lds[2][TS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 31;
+  const int h = lane >> 5;
+  const int64_t wbase = ((int64_t)blockIdx.x * W + wave) * (NB * 32);
+
+  // Point fragments: read once from HBM, kept in VGPRs for the whole sweep.
+  u32x4_t xb[NB][KB];
+  float xn[NB];
+#pragma unroll
+  for (int g = 0; g < NB; ++g) {
+    const int64_t p = wbase + g * 32 + col;
+    float s = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      xb[g][kb] = load_point_frag<2>(X, p, N, D, kb * kFragDepth + h * 8, vec_ok);
+      s += sumsq16<DT>(xb[g][kb]);
+    }
+    s += __shfl_xor(s, 32);
+    xn[g] = s;
+  }
+
+  // best score per point group and lane; `rel` = selected element counted
+  // from the base of the group most recently scanned (rebased by -16 a group;
+  // the start value stays far below any real selection)
+  float best[NB];
+  int rel[NB];
+#pragma unroll
+  for (int g = 0; g < NB; ++g) {
+    best[g] = -INFINITY;
+    rel[g] = -(1 << 30);
+  }
+
+  // tile 0 into LDS
+  tile_dma<TS, NTHR>(frag, &lds[0][0], wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // Group q's scores land in acc0 (q even) or acc1 (q odd); the stage that
+  // computes group q also folds group q-1 into the running argmax.
+  f32x16_t acc0[NB], acc1[NB];
+  float m[NB];  // running maximum of the group being folded (lazy argmax)
+  for (int t = 0; t < ntiles; ++t) {
+    const u32x4_t* tile = &lds[t & 1][0];
+    // the next tile streams into the other buffer while this one is used
+    if (t + 1 < ntiles) tile_dma<TS, NTHR>(frag + (size_t)(t + 1) * TS, &lds[(t + 1) & 1][0], wave, lane);
+#pragma unroll
+    for (int c = 0; c < CT; c += 2) {
+      const u32x4_t* g0 = tile + c * GS;
+      const u32x4_t* g1 = g0 + GS;
+      const u32x4_t a00 = g0[lane];
+      const f32x16_t bias0 = bias_of(g0 + KB * 64 + h * 4);
+      if (c == 0 && t == 0)
+        pipeline_steps<DT, KB, NB, LAZY, false>(g0, lane, a00, bias0, xb, acc0, acc1, best, rel, m);
+      else
+        pipeline_steps<DT, KB, NB, LAZY, true>(g0, lane, a00, bias0, xb, acc0, acc1, best, rel, m);
+      const u32x4_t a10 = g1[lane];
+      const f32x16_t bias1 = bias_of(g1 + KB * 64 + h * 4);
+      pipeline_steps<DT, KB, NB, LAZY, true>(g1, lane, a10, bias1, xb, acc1, acc0, best, rel, m);
+    }
+    if (t + 1 < ntiles) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the next tile has landed
+      __syncthreads();                // ... and everyone's; this tile is no longer read
+    }
+  }
+  drain_epilogue<NB>(acc1, best, rel);
+
+  const int last_base = (ntiles * CT - 1) * 16;  // selector base of the final group
+#pragma unroll
+  for (int g = 0; g < NB; ++g) {
+    float b = best[g];
+    const int sg = last_base + rel[g];
+    int k = b == -INFINITY ? INT32_MAX : (sg >> 4) * 32 + ((sg & 15) >> 2) * 8 + h * 4 + (sg & 3);
+    const float ob = __shfl_xor(b, 32);
+    const int ok = __shfl_xor(k, 32);
+    if (ob > b || (ob == b && ok < k)) {
+      b = ob;
+      k = ok;
+    }
+    if (k == INT32_MAX) k = 0;  // no finite score (NaN input): index 0
+    const int64_t p = wbase + g * 32 + col;
+    if (h == 0 && p < N) {
+      assign[p] = k;
+      if (min_dist) min_dist[p] = fmaxf(xn[g] - 2.0f * b, 0.0f);
+    }
+  }
+}
+
+// --------------------------------------------------- FlashAssign, fp32 X ----
+//
+// MFMA 16x16x4 f32 layout: lane l supplies A row (l % 16) and B column
+// (l % 16), one depth value each; a fragment holds the four depth values of
+// four consecutive instructions.  The result lane l holds column (l % 16) and
+// rows 4(l/16) + r; lanes l, l^16, l^32, l^48 share the point.
+
+__device__ __forceinline__ f32x4_t mma16_f32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+  return c;
+}
+
+template <int KB>
+__global__ __launch_bounds__(narrow_cfg(KB).W * 64) void flash_assign_narrow_kernel(
+    const uint8_t* __restrict__ X, int64_t N, int D, bool vec_ok, const u32x4_t* __restrict__ frag, int ntiles,
+    int32_t* __restrict__ assign, float* __restrict__ min_dist) {
+  constexpr AssignCfg cfg = narrow_cfg(KB);
+  constexpr int NB = cfg.NB, CT = cfg.CT, W = cfg.W;
+  constexpr int GS = (int)cfg.group_slots();
+  constexpr int TS = (int)cfg.tile_slots();
+  constexpr int NTHR = W * 64;
+  constexpr int CPT = TS / NTHR;
   static_assert(TS % NTHR == 0 && TS >= CT * GS, "tile padding");
   __shared__ u32x4_t lds[2][TS];
 
@@ -245,7 +472,6 @@ __global__ __launch_bounds__(W * 64) void flash_assign_kernel(const uint8_t* __r
   const int quad = lane >> 4;
   const int64_t wbase = ((int64_t)blockIdx.x * W + wave) * (NB * 16);
 
-  // Point fragments: read once from HBM, kept in VGPRs for the whole sweep.
   u32x4_t xb[NB][KB];
   float xn[NB];
 #pragma unroll
@@ -254,8 +480,12 @@ __global__ __launch_bounds__(W * 64) void flash_assign_kernel(const uint8_t* __r
     float s = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      xb[g][kb] = load_point_frag<DT>(X, p, N, D, kb * T::FB + quad * T::EPL, vec_ok);
-      s += T::sumsq(xb[g][kb]);
+      xb[g][kb] = load_point_frag<4>(X, p, N, D, kb * kFragDepth + quad * 4, vec_ok);
+      const u32x4_t v = xb[g][kb];
+      s = fmaf(__uint_as_float(v.x), __uint_as_float(v.x), s);
+      s = fmaf(__uint_as_float(v.y), __uint_as_float(v.y), s);
+      s = fmaf(__uint_as_float(v.z), __uint_as_float(v.z), s);
+      s = fmaf(__uint_as_float(v.w), __uint_as_float(v.w), s);
     }
     s += __shfl_xor(s, 16);
     s += __shfl_xor(s, 32);
@@ -283,7 +513,7 @@ __global__ __launch_bounds__(W * 64) void flash_assign_kernel(const uint8_t* __r
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const bool more = t + 1 < ntiles;
-    if (more) {  // next tile in flight while this one feeds the matrix cores
+    if (more) {
       const u32x4_t* src = frag + (size_t)(t + 1) * TS + threadIdx.x;
 #pragma unroll
       for (int i = 0; i < CPT; ++i) stage[i] = src[i * NTHR];
@@ -300,10 +530,10 @@ __global__ __launch_bounds__(W * 64) void flash_assign_kernel(const uint8_t* __r
       for (int g = 0; g < NB; ++g) {
         f32x4_t acc = bias4;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) acc = T::mma(a[kb], xb[g][kb], acc);
+        for (int kb = 0; kb < KB; ++kb) acc = mma16_f32(a[kb], xb[g][kb], acc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if (acc[i] > best[g]) {  // strict: the first (lowest) index among equals stays
+          if (acc[i] > best[g]) {
             best[g] = acc[i];
             sel[g] = s0 + i;
           }
@@ -317,11 +547,10 @@ __global__ __launch_bounds__(W * 64) void flash_assign_kernel(const uint8_t* __r
     __syncthreads();
   }
 
-  // Merge the four lanes that hold the same point; ties go to the lower index.
 #pragma unroll
   for (int g = 0; g < NB; ++g) {
     float b = best[g];
-    int k = sel[g] < 0 ? INT32_MAX : (sel[g] >> 2) * kGroupRows + quad * 4 + (sel[g] & 3);
+    int k = sel[g] < 0 ? INT32_MAX : (sel[g] >> 2) * 16 + quad * 4 + (sel[g] & 3);
 #pragma unroll
     for (int off = 16; off <= 32; off <<= 1) {
       const float ob = __shfl_xor(b, off);
@@ -331,7 +560,7 @@ __global__ __launch_bounds__(W * 64) void flash_assign_kernel(const uint8_t* __r
         k = ok;
       }
     }
-    if (k == INT32_MAX) k = 0;  // no finite score (NaN input): index 0
+    if (k == INT32_MAX) k = 0;
     const int64_t p = wbase + g * 16 + col;
     if (quad == 0 && p < N) {
       assign[p] = k;
@@ -340,41 +569,64 @@ __global__ __launch_bounds__(W * 64) void flash_assign_kernel(const uint8_t* __r
   }
 }
 
+// --------------------------------------------------------------- launch ----
+
 template <int DT, int KB>
-static hipError_t launch_fa(const void* X, int64_t N, int64_t D, const void* frag, int64_t Kpad, int32_t* assign,
-                            float* min_dist, hipStream_t stream) {
-  constexpr int NB = assign_cfg(KB).NB;
-  constexpr int CT = assign_cfg(KB).CT;
-  constexpr int W = assign_cfg(KB).W;
-  const int64_t pts = (int64_t)W * NB * 16;
-  const int64_t nblk = (N + pts - 1) / pts;
-  const int ntiles = (int)(Kpad / (CT * kGroupRows));
-  const bool vec_ok = (((uintptr_t)X) % 16 == 0) && ((D * FragTraits<DT>::ES) % 16 == 0);
-  hipLaunchKernelGGL((flash_assign_kernel<DT, KB, NB, W, CT>), dim3((unsigned)nblk), dim3(W * 64), 0, stream,
-                     (const uint8_t*)X, N, (int)D, vec_ok, (const u32x4_t*)frag, ntiles, assign, min_dist);
+static hipError_t launch_wide(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
+                              float* min_dist, hipStream_t s) {
+  constexpr AssignCfg cfg = wide_cfg(KB);
+  const int64_t pts = (int64_t)cfg.W * cfg.NB * 32;
+  const bool vec_ok = (((uintptr_t)X) % 16 == 0) && ((g.D * 2) % 16 == 0);
+  const dim3 grid((unsigned)((N + pts - 1) / pts)), block(cfg.W * 64);
+  if (g.lazy)
+    hipLaunchKernelGGL((flash_assign_wide_kernel<DT, KB, true>), grid, block, 0, s, (const uint8_t*)X, N, (int)g.D,
+                       vec_ok, (const u32x4_t*)frag, (int)g.ntiles(), assign, min_dist);
+  else
+    hipLaunchKernelGGL((flash_assign_wide_kernel<DT, KB, false>), grid, block, 0, s, (const uint8_t*)X, N,
+                       (int)g.D, vec_ok, (const u32x4_t*)frag, (int)g.ntiles(), assign, min_dist);
+  return hipGetLastError();
+}
+
+template <int KB>
+static hipError_t launch_narrow(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
+                                float* min_dist, hipStream_t s) {
+  constexpr AssignCfg cfg = narrow_cfg(KB);
+  const int64_t pts = (int64_t)cfg.W * cfg.NB * 16;
+  const bool vec_ok = (((uintptr_t)X) % 16 == 0) && ((g.D * 4) % 16 == 0);
+  hipLaunchKernelGGL((flash_assign_narrow_kernel<KB>), dim3((unsigned)((N + pts - 1) / pts)), dim3(cfg.W * 64), 0, s,
+                     (const uint8_t*)X, N, (int)g.D, vec_ok, (const u32x4_t*)frag, (int)g.ntiles(), assign,
+                     min_dist);
   return hipGetLastError();
 }
 
 template <int DT>
-static hipError_t dispatch_kb(int KB, const void* X, int64_t N, int64_t D, const void* frag, int64_t Kpad,
-                              int32_t* assign, float* min_dist, hipStream_t s) {
-  switch (KB) {
+static hipError_t dispatch_wide(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
+                                float* min_dist, hipStream_t s) {
+  switch (g.cfg.KB) {
 #define KM_CASE(n) \
-  case n: return launch_fa<DT, n>(X, N, D, frag, Kpad, assign, min_dist, s);
+  case n: return launch_wide<DT, n>(g, X, N, frag, assign, min_dist, s);
     KM_CASE(1) KM_CASE(2) KM_CASE(3) KM_CASE(4) KM_CASE(5) KM_CASE(6) KM_CASE(7) KM_CASE(8)
-    KM_CASE(9) KM_CASE(10) KM_CASE(11) KM_CASE(12) KM_CASE(13) KM_CASE(14) KM_CASE(15) KM_CASE(16)
+    KM_CASE(10) KM_CASE(12) KM_CASE(14) KM_CASE(16) KM_CASE(20) KM_CASE(24) KM_CASE(28) KM_CASE(32)
 #undef KM_CASE
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_flash_assign(const void* X, int dt, int64_t N, int64_t D, int KB, const void* frag,
-                               int64_t Kpad, int32_t* assign, float* min_dist, hipStream_t stream) {
+hipError_t launch_flash_assign(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
+                               float* min_dist, hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  switch (dt) {
-    case DT_BF16: return dispatch_kb<DT_BF16>(KB, X, N, D, frag, Kpad, assign, min_dist, stream);
-    case DT_F16: return dispatch_kb<DT_F16>(KB, X, N, D, frag, Kpad, assign, min_dist, stream);
-    case DT_F32: return dispatch_kb<DT_F32>(KB, X, N, D, frag, Kpad, assign, min_dist, stream);
+  switch (g.dt) {
+    case DT_BF16: return dispatch_wide<DT_BF16>(g, X, N, frag, assign, min_dist, stream);
+    case DT_F16: return dispatch_wide<DT_F16>(g, X, N, frag, assign, min_dist, stream);
+    case DT_F32:
+      switch (g.cfg.KB) {
+#define KM_CASE(n) \
+  case n: return launch_narrow<n>(g, X, N, frag, assign, min_dist, stream);
+        KM_CASE(1) KM_CASE(2) KM_CASE(3) KM_CASE(4) KM_CASE(5) KM_CASE(6) KM_CASE(7) KM_CASE(8)
+        KM_CASE(9) KM_CASE(10) KM_CASE(11) KM_CASE(12) KM_CASE(13) KM_CASE(14) KM_CASE(15) KM_CASE(16)
+#undef KM_CASE
+        default: return hipErrorInvalidValue;
+      }
     default: return hipErrorInvalidValue;
   }
 }

@@ -18,50 +18,98 @@ inline int dtype_size(int dt) { return dt == DT_F32 ? 4 : 2; }
 
 // ---------------------------------------------------------------------------
 // Centroid fragments.  The contraction x . c runs on the matrix cores with the
-// centroids as the A operand (16 rows) and the points as the B operand (16
-// columns).  A "fragment block" is what one wavefront feeds one group of
-// MFMAs: 64 lanes x 16 bytes, covering 16 centroids x FB depth values, where
-// FB = 32 for 16-bit data (v_mfma_f32_16x16x32_{bf16,f16}: 8 values per lane)
-// and FB = 16 for fp32 (four v_mfma_f32_16x16x4_f32: 4 values per lane).
-// Lane l holds centroid (l % 16) and depth values [FB*kb + EPL*(l/16), +EPL).
-// Fragments are stored [group g][depth block kb][lane][16 bytes], so a
-// centroid tile is one contiguous run of bytes: copying it to LDS and reading
-// it back are both lane-linear 16-byte accesses.
+// centroids as the A operand and the points as the B operand.  Two layouts:
+//   * 16-bit X ("wide"): v_mfma_f32_32x32x16_{bf16,f16}; a centroid group is
+//     32 rows, a fragment block covers 32 rows x 16 depth values (lane l:
+//     row l % 32, depth 16*kb + 8*(l/32) .. +7, 16 bytes);
+//   * fp32 X ("narrow"): four v_mfma_f32_16x16x4_f32; a group is 16 rows, a
+//     fragment block covers 16 rows x 16 depth values (lane l: row l % 16,
+//     depth 16*kb + 4*(l/16) .. +3, 16 bytes).
+// A group is stored as its KB fragment blocks (64 lanes x 16 bytes each),
+// then its bias values -||c||^2/2 (32 or 16 floats, in the order the lanes
+// read them).  Groups are packed into tiles of CT groups, each tile padded to
+// a whole number of 16-byte copies per thread, so streaming a tile into LDS
+// is one contiguous, unconditional copy and every LDS read is lane-linear.
 // ---------------------------------------------------------------------------
-constexpr int kGroupRows = 16;     // centroids per fragment group
+constexpr int kFragDepth = 16;     // depth values per fragment block (both layouts)
 constexpr int kPadK = 128;         // K is padded to a multiple of this (>= any tile)
-constexpr int kMaxKB = 16;         // depth blocks supported: D <= 512 (16-bit), D <= 256 (fp32)
+constexpr int kMaxD16 = 512;       // D limit for 16-bit X
+constexpr int kMaxD32 = 256;       // D limit for fp32 X
 
-inline int frag_depth(int dt) { return dt == DT_F32 ? 16 : 32; }
-inline int64_t pad_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
-
-// FlashAssign launch shape for a given number of depth blocks KB:
-//   NB  16-point groups per wavefront (register-resident point fragments),
-//   CT  16-centroid groups per LDS tile,
-//   W   wavefronts per workgroup.
+// Launch shape of one FlashAssign instantiation.
 struct AssignCfg {
-  int NB, CT, W;
+  int rows;   // centroids per group (32 wide, 16 narrow)
+  int KB;     // fragment blocks per group
+  int NB;     // point groups per wavefront (32 points wide, 16 narrow)
+  int CT;     // centroid groups per LDS tile
+  int W;      // wavefronts per workgroup
+  constexpr int64_t bias_slots() const { return rows / 4; }
+  constexpr int64_t group_slots() const { return (int64_t)KB * 64 + bias_slots(); }
+  constexpr int64_t tile_slots() const {
+    return (CT * group_slots() + W * 64 - 1) / (W * 64) * (W * 64);
+  }
 };
-constexpr AssignCfg assign_cfg(int KB) {
-  return AssignCfg{KB <= 4 ? 4 : (KB <= 8 ? 2 : 1), KB <= 2 ? 8 : (KB <= 4 ? 4 : (KB <= 8 ? 2 : 1)), 4};
+
+// Depth blocks actually instantiated for 16-bit X (D padded up to 16 * one of these).
+constexpr int kWideKB[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16, 20, 24, 28, 32};
+
+// Build-time knobs for tile sweeps (defaults are the shipped configuration).
+#ifndef KM_WIDE_NB_SMALL
+#define KM_WIDE_NB_SMALL 2  // point groups per wavefront for D <= 64
+#endif
+#ifndef KM_WIDE_NB_MID
+#define KM_WIDE_NB_MID 2    // ... for 64 < D <= 128
+#endif
+#ifndef KM_WIDE_W
+#define KM_WIDE_W 4         // wavefronts per workgroup
+#endif
+#ifndef KM_WIDE_CT
+#define KM_WIDE_CT 2        // centroid groups per LDS tile for 64 < D <= 256 (even)
+#endif
+constexpr AssignCfg wide_cfg(int KB) {
+  return AssignCfg{32, KB, KB <= 4 ? KM_WIDE_NB_SMALL : (KB <= 8 ? KM_WIDE_NB_MID : (KB <= 16 ? 2 : 1)),
+                   KB <= 4 ? 4 : (KB <= 16 ? KM_WIDE_CT : 2), KM_WIDE_W};
 }
-// 16-byte slots of one centroid group: KB*64 fragments, then 4 slots of bias.
-constexpr int64_t group_slots(int KB) { return (int64_t)KB * 64 + 4; }
-// 16-byte slots of one tile, padded so every thread of the block copies the
-// same number of slots.
-constexpr int64_t tile_slots(int KB) {
-  return (assign_cfg(KB).CT * group_slots(KB) + assign_cfg(KB).W * 64 - 1) / (assign_cfg(KB).W * 64) *
-         (assign_cfg(KB).W * 64);
+constexpr AssignCfg narrow_cfg(int KB) {
+  return AssignCfg{16, KB, KB <= 4 ? 4 : (KB <= 8 ? 2 : 1), KB <= 2 ? 8 : (KB <= 4 ? 4 : (KB <= 8 ? 2 : 1)), 4};
 }
+
+inline int wide_kb(int64_t D) {
+  const int need = (int)((D + kFragDepth - 1) / kFragDepth);
+  for (int kb : kWideKB)
+    if (kb >= need) return kb;
+  return -1;
+}
+inline int64_t pad_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 struct AssignGeom {
   int dt;
   int64_t N, D, K;
-  int KB;          // depth blocks = ceil(D / FB)
   int64_t Kpad;    // K rounded up to kPadK
-  int64_t ntiles() const { return Kpad / ((int64_t)assign_cfg(KB).CT * kGroupRows); }
-  size_t frag_bytes() const { return (size_t)ntiles() * (size_t)tile_slots(KB) * 16; }
+  AssignCfg cfg;
+  bool lazy;       // argmax by group maxima first (pays off when the centroid sweep is long)
+  int64_t groups() const { return Kpad / cfg.rows; }
+  int64_t ntiles() const { return groups() / cfg.CT; }
+  size_t frag_bytes() const { return (size_t)ntiles() * (size_t)cfg.tile_slots() * 16; }
 };
+
+inline AssignGeom make_assign_geom(int64_t N, int64_t D, int64_t K, int dt) {
+  AssignGeom g;
+  g.dt = dt;
+  g.N = N;
+  g.D = D;
+  g.K = K;
+  g.Kpad = pad_up(K, kPadK);
+  if (dt == DT_F32)
+    g.cfg = narrow_cfg((int)((D + kFragDepth - 1) / kFragDepth));
+  else
+    g.cfg = wide_cfg(wide_kb(D));
+  // A group whose maximum does not beat a lane's running best costs one max3
+  // per two scores instead of a full compare-and-select; with many groups such
+  // groups dominate (measured on gfx950: better from about 256 groups of 32).
+  g.lazy = dt != DT_F32 && g.groups() >= 256;
+  return g;
+}
 
 // ---------------------------------------------------------------------------
 // Sort-inverse update geometry.
@@ -85,11 +133,10 @@ struct SortGeom {
 // ---------------------------------------------------------------------------
 // Launchers (all asynchronous on `stream`; they return the launch status).
 // ---------------------------------------------------------------------------
-hipError_t launch_prep(const float* C, int64_t K, int64_t D, int dt, int KB, int64_t Kpad, void* frag,
-                       hipStream_t stream);
+hipError_t launch_prep(const AssignGeom& g, const float* C, void* frag, hipStream_t stream);
 
-hipError_t launch_flash_assign(const void* X, int dt, int64_t N, int64_t D, int KB, const void* frag, int64_t Kpad,
-                               int32_t* assign, float* min_dist, hipStream_t stream);
+hipError_t launch_flash_assign(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
+                               float* min_dist, hipStream_t stream);
 
 // Radix argsort of cluster ids.  keys_in: the assignment vector.  The passes
 // ping-pong through (key_a, val_a) and (key_b, val_b); the last pass writes
