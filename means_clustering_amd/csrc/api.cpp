@@ -113,10 +113,10 @@ static SortGeom sort_geom(int64_t N, int64_t K) {
   while (kb < 31 && ((int64_t)1 << kb) <= K - 1) ++kb;
   if (kb < 1) kb = 1;
   g.kbits = kb;
-  g.npass = (kb + 7) / 8;
+  g.npass = (kb + kMaxDigitBits - 1) / kMaxDigitBits;
   const int base = kb / g.npass, rem = kb % g.npass;
-  for (int p = 0; p < 4; ++p) g.bits[p] = p < g.npass ? base + (p < rem ? 1 : 0) : 0;
-  g.nblk = (N + kSortBlock - 1) / kSortBlock;
+  for (int p = 0; p < 6; ++p) g.bits[p] = p < g.npass ? base + (p < rem ? 1 : 0) : 0;
+  g.nblk = (N + kRadixBlock - 1) / kRadixBlock;
   int64_t m = 1;
   for (int p = 0; p < g.npass; ++p) {
     const int64_t len = ((int64_t)1 << g.bits[p]) * g.nblk;

@@ -66,26 +66,27 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
 
 // ---------------------------------------------------------------- prep ----
 
-// One wavefront per centroid group: quantise the group's rows into fragment
-// blocks, and write -||Q(c)||^2/2 (fp32, from the quantised values) in the
-// order the FlashAssign lanes read it; padding rows get zero fragments and a
-// bias of -inf, so they can never be selected.
+// One workgroup (4 wavefronts) per centroid group: wavefront w quantises the
+// group's depth blocks w, w+4, ... into fragment blocks; the partial sums of
+// squares of the quantised values meet in LDS, and -||Q(c)||^2/2 (fp32) is
+// written in the order the FlashAssign lanes read it.  Padding rows get zero
+// fragments and a bias of -inf, so they can never be selected.
 __global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ C, int64_t K, int D, int dt, AssignCfg cfg,
                                                    int64_t groups, u32x4_t* __restrict__ frag) {
-  const int lane = threadIdx.x & 63;
-  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (g >= groups) return;
+  __shared__ float part[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t g = blockIdx.x;
   const bool wide = cfg.rows == 32;
   const int rsel = wide ? (lane & 31) : (lane & 15);
-  const int part = wide ? (lane >> 5) : (lane >> 4);  // which 8 (wide) or 4 (narrow) depth values
+  const int piece = wide ? (lane >> 5) : (lane >> 4);  // which 8 (wide) or 4 (narrow) depth values
   const int64_t row = g * cfg.rows + rsel;
   const bool live = row < K;
   u32x4_t* gdst = frag + (g / cfg.CT) * cfg.tile_slots() + (g % cfg.CT) * cfg.group_slots();
   float ss = 0.0f;
-  for (int kb = 0; kb < cfg.KB; ++kb) {
+  for (int kb = wave; kb < cfg.KB; kb += 4) {
     uint32_t w[4];
     if (wide) {
-      const int d0 = kb * kFragDepth + part * 8;
+      const int d0 = kb * kFragDepth + piece * 8;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int da = d0 + 2 * e, db = da + 1;
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ C, 
         w[e] = qa | (qb << 16);
       }
     } else {
-      const int d0 = kb * kFragDepth + part * 4;
+      const int d0 = kb * kFragDepth + piece * 4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int d = d0 + e;
@@ -111,29 +112,34 @@ __global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ C, 
     }
     gdst[kb * 64 + lane] = u32x4_t{w[0], w[1], w[2], w[3]};
   }
-  // total over the lanes that hold the same row
-  if (wide) {
-    ss += __shfl_xor(ss, 32);
-  } else {
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
-  }
-  float* bias = reinterpret_cast<float*>(gdst + cfg.KB * 64);
-  if (part == 0) {
-    const float b = live ? -0.5f * ss : -INFINITY;
-    if (wide) {  // lane half h reads rows 8j + 4h + r as its 16 accumulator values
-      const int j = rsel >> 3, h = (rsel >> 2) & 1, r = rsel & 3;
-      bias[h * 16 + j * 4 + r] = b;
-    } else {  // lane quad q reads rows 4q .. 4q+3
-      bias[rsel] = b;
+  part[wave][lane] = ss;
+  __syncthreads();
+  if (wave == 0) {
+    // fixed order: the four wavefronts, then the lanes that hold the same row
+    float t = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+    if (wide) {
+      t += __shfl_xor(t, 32);
+    } else {
+      t += __shfl_xor(t, 16);
+      t += __shfl_xor(t, 32);
+    }
+    float* bias = reinterpret_cast<float*>(gdst + cfg.KB * 64);
+    if (piece == 0) {
+      const float b = live ? -0.5f * t : -INFINITY;
+      if (wide) {  // lane half h reads rows 8j + 4h + r as its 16 accumulator values
+        const int j = rsel >> 3, h = (rsel >> 2) & 1, r = rsel & 3;
+        bias[h * 16 + j * 4 + r] = b;
+      } else {  // lane quad q reads rows 4q .. 4q+3
+        bias[rsel] = b;
+      }
     }
   }
 }
 
 hipError_t launch_prep(const AssignGeom& g, const float* C, void* frag, hipStream_t stream) {
   const int64_t groups = g.groups();
-  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)((groups + 3) / 4)), dim3(256), 0, stream, C, g.K, (int)g.D, g.dt,
-                     g.cfg, groups, (u32x4_t*)frag);
+  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)groups), dim3(256), 0, stream, C, g.K, (int)g.D, g.dt, g.cfg, groups,
+                     (u32x4_t*)frag);
   return hipGetLastError();
 }
 

@@ -114,10 +114,17 @@ inline AssignGeom make_assign_geom(int64_t N, int64_t D, int64_t K, int dt) {
 // ---------------------------------------------------------------------------
 // Sort-inverse update geometry.
 // ---------------------------------------------------------------------------
-constexpr int kSortThreads = 256;            // 4 wavefronts
-constexpr int kSortItems = 16;               // keys per thread
-constexpr int kSortBlock = kSortThreads * kSortItems;  // 4096 keys per block
-constexpr int kSegTile = 256;                // sorted positions per segment tile
+#ifndef KM_SEG_TILE
+#define KM_SEG_TILE 128   // sorted positions per segment tile
+#endif
+#ifndef KM_SEG_U
+#define KM_SEG_U 16       // rows in flight per lane group in the segmented reduction
+#endif
+constexpr int kRadixThreads = 256;
+constexpr int kRadixItems = 32;              // consecutive keys per thread
+constexpr int kRadixBlock = kRadixThreads * kRadixItems;  // keys per block (block positions fit in 16 bits)
+constexpr int kMaxDigitBits = 6;             // digits of at most 64 values per pass
+constexpr int kSegTile = KM_SEG_TILE;
 constexpr uint32_t kInvalidFlag = 0x80000000u;  // marks a point whose cluster id was out of range
 
 struct SortGeom {
@@ -125,8 +132,8 @@ struct SortGeom {
   int64_t K;
   int kbits;        // bits of the largest valid id (K - 1), at least 1
   int npass;        // radix passes
-  int bits[4];      // digit width of each pass
-  int64_t nblk;     // key blocks of kSortBlock
+  int bits[6];      // digit width of each pass
+  int64_t nblk;     // key blocks of kRadixBlock
   int64_t count_len;  // max over passes of (2^bits * nblk)
 };
 

@@ -100,13 +100,14 @@ struct SegParams {
   int64_t* acc_cnt;
 };
 
-// Write a finished segment (or a carry piece) held by one lane group.
+// Write a finished segment (or a carry piece) held by one lane group.  A
+// segment is finished here when it both starts and ends inside this tile
+// (`complete`, known from the id changes the walk has seen).
 template <int EPL, int CPL, int G>
-__device__ __forceinline__ void flush_piece(const SegParams& P, int64_t tile, int64_t ps, int64_t pe, int32_t first_key,
-                                            int32_t k, const float (&acc)[CPL][EPL], int32_t cnt, int j) {
+__device__ __forceinline__ void flush_piece(const SegParams& P, int64_t tile, int32_t first_key, int32_t k,
+                                            bool complete, const float (&acc)[CPL][EPL], int32_t cnt, int j) {
   if (k < 0 || k >= P.K) return;  // sorted ids lie in [0, K)
-  const int64_t s = P.off[k], e = P.off[k + 1];
-  if (s >= ps && e <= pe) {  // whole segment inside this tile: final here
+  if (complete) {
     if (P.mode == MODE_MEAN) {
       if (j == 0 && P.counts) P.counts[k] = cnt;
       const float fcnt = (float)cnt;
@@ -150,7 +151,7 @@ __device__ __forceinline__ void flush_piece(const SegParams& P, int64_t tile, in
 template <int ES, int CPL, int G>
 __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
   constexpr int EPL = 16 / ES;
-  constexpr int U = G < 8 ? G : 8;  // rows in flight per lane group
+  constexpr int U = G < KM_SEG_U ? G : KM_SEG_U;  // rows in flight per lane group
   const int j = threadIdx.x % G;
   const int lgbase = (threadIdx.x & 63) & ~(G - 1);
   const int64_t tile = (int64_t)blockIdx.x * (256 / G) + threadIdx.x / G;
@@ -158,6 +159,8 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
   if (ps >= P.N) return;
   const int64_t pe = ps + kSegTile < P.N ? ps + kSegTile : P.N;
   const int32_t first_key = P.keys[ps];
+  const int32_t before_key = ps > 0 ? P.keys[ps - 1] : -1;   // id just before the tile
+  const int32_t after_key = pe < P.N ? P.keys[pe] : -1;      // id just after the tile
 
   float acc[CPL][EPL];
 #pragma unroll
@@ -166,6 +169,7 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
     for (int x = 0; x < EPL; ++x) acc[q][x] = 0.0f;
   int32_t cnt = 0;
   int32_t cur = first_key;
+  bool started = before_key != first_key;  // the current segment began inside this tile
 
   for (int64_t p0 = ps; p0 < pe; p0 += G) {
     const int64_t mypos = p0 + j;
@@ -191,10 +195,11 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (in[u]) {
-          if (kk[u] != cur) {
-            flush_piece<EPL, CPL, G>(P, tile, ps, pe, first_key, cur, acc, cnt, j);
+          if (kk[u] != cur) {  // the current segment ends inside the tile
+            flush_piece<EPL, CPL, G>(P, tile, first_key, cur, started, acc, cnt, j);
             cur = kk[u];
             cnt = 0;
+            started = true;
 #pragma unroll
             for (int q = 0; q < CPL; ++q)
 #pragma unroll
@@ -212,75 +217,95 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
       }
     }
   }
-  flush_piece<EPL, CPL, G>(P, tile, ps, pe, first_key, cur, acc, cnt, j);
+  flush_piece<EPL, CPL, G>(P, tile, first_key, cur, started && after_key != cur, acc, cnt, j);
 }
 
-// One workgroup per cluster: segments cut by tile edges are summed from their
-// carry pieces in a fixed order; empty clusters keep their centroid.
+// Segments cut by tile edges are summed from their carry pieces; empty
+// clusters keep their centroid.  One wavefront per cluster, 16 clusters a
+// workgroup.  Lanes split into R rows x (Dc/4) float4 columns; row r adds the
+// pieces of tiles t0+r, t0+r+R, ... and the rows are combined by a fixed
+// shuffle tree, so the order of additions never depends on scheduling.
+constexpr int kFixupPerWave = 1;
+template <int CPL>  // float4 columns per lane: 2 only when a piece has 128 of them
 __global__ __launch_bounds__(256) void fixup_kernel(SegParams P) {
-  __shared__ float red[256 * 4];
-  __shared__ int32_t redc[256];
-  const int64_t k = blockIdx.x;
-  const int64_t s = P.off[k], e = P.off[k + 1];
-  if (s < 0 || e > P.N || s > e) return;  // boundaries are monotone in [0, N]
-  if (s == e) {
-    if (P.mode == MODE_MEAN) {
-      if (threadIdx.x == 0 && P.counts) P.counts[k] = 0;
-      if (P.C_new != P.C_prev)
-        for (int c = threadIdx.x; c < P.D; c += 256) P.C_new[k * P.D + c] = P.C_prev[k * P.D + c];
-    }
-    return;
-  }
-  const int64_t t0 = s / kSegTile, t1 = (e - 1) / kSegTile;
-  if (t0 == t1) return;  // finished by segment_reduce_kernel
-  const int gc = P.Dc / 4;  // float4 columns of a carry piece (Dc is a multiple of 4, at most 512)
-  const int R = 256 / gc;   // thread rows
-  const int r = threadIdx.x / gc, c4 = threadIdx.x % gc;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  int32_t n = 0;
-  if (r < R) {
-    for (int64_t t = t0 + r; t <= t1; t += R) {
-      const int slot = (t == t0 && s != t0 * kSegTile) ? 1 : 0;
-      const float4 v = *reinterpret_cast<const float4*>(P.carry_sum + (t * 2 + slot) * (int64_t)P.Dc + c4 * 4);
-      a0 += v.x;
-      a1 += v.y;
-      a2 += v.z;
-      a3 += v.w;
-      if (c4 == 0) n += P.carry_cnt[t * 2 + slot];
-    }
-  }
-  red[threadIdx.x * 4 + 0] = a0;
-  red[threadIdx.x * 4 + 1] = a1;
-  red[threadIdx.x * 4 + 2] = a2;
-  red[threadIdx.x * 4 + 3] = a3;
-  redc[threadIdx.x] = n;
-  __syncthreads();
-  for (int stride = R / 2; stride > 0; stride >>= 1) {
-    if (r < stride) {
-      const int o = (r + stride) * gc + c4;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) red[threadIdx.x * 4 + x] += red[o * 4 + x];
-      if (c4 == 0) redc[threadIdx.x] += redc[o];
-    }
-    __syncthreads();
-  }
-  const int32_t total = redc[0];
-  if (r == 0) {
-    for (int x = 0; x < 4; ++x) {
-      const int c = c4 * 4 + x;
-      if (c >= P.D) continue;
-      const int64_t o = k * P.D + c;
-      const float sum = red[threadIdx.x * 4 + x];
-      if (P.mode == MODE_MEAN)
-        P.C_new[o] = total > 0 ? sum / (float)total : P.C_prev[o];
-      else
-        P.acc_sum[o] += sum;
-    }
-    if (c4 == 0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gc = P.Dc / 4;                    // float4 columns of a carry piece (power of two, <= 128)
+  const int lpr = gc < 64 ? gc : 64;          // lanes per row
+  const int R = 64 / lpr;                     // rows
+  constexpr int cpl = CPL;
+  const int r = lane / lpr, c0 = lane % lpr;
+  for (int i = 0; i < kFixupPerWave; ++i) {
+    const int64_t k = ((int64_t)blockIdx.x * 4 + wave) * kFixupPerWave + i;
+    if (k >= P.K) return;
+    const int64_t s = P.off[k], e = P.off[k + 1];
+    if (s < 0 || e > P.N || s > e) continue;  // boundaries are monotone in [0, N]
+    if (s == e) {
       if (P.mode == MODE_MEAN) {
-        if (P.counts) P.counts[k] = total;
-      } else {
-        P.acc_cnt[k] += total;
+        if (lane == 0 && P.counts) P.counts[k] = 0;
+        if (P.C_new != P.C_prev)
+          for (int c = lane; c < P.D; c += 64) P.C_new[k * P.D + c] = P.C_prev[k * P.D + c];
+      }
+      continue;
+    }
+    const int64_t t0 = s / kSegTile, t1 = (e - 1) / kSegTile;
+    if (t0 == t1) continue;  // finished by segment_reduce_kernel
+    float a[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    int32_t n = 0;
+    constexpr int UNR = 4;  // pieces in flight per lane
+    for (int64_t tb = t0 + r; tb <= t1; tb += (int64_t)R * UNR) {
+      float4 v[UNR][2];
+      int32_t cc[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int64_t t = tb + (int64_t)u * R;
+        cc[u] = 0;
+        v[u][0] = v[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (t <= t1) {
+          const int slot = (t == t0 && s != t0 * kSegTile) ? 1 : 0;
+          const float* piece = P.carry_sum + (t * 2 + slot) * (int64_t)P.Dc;
+#pragma unroll
+          for (int cl = 0; cl < cpl; ++cl) v[u][cl] = *reinterpret_cast<const float4*>(piece + (c0 + cl * lpr) * 4);
+          cc[u] = P.carry_cnt[t * 2 + slot];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {  // ascending tile order within the row
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl) {
+          a[cl][0] += v[u][cl].x;
+          a[cl][1] += v[u][cl].y;
+          a[cl][2] += v[u][cl].z;
+          a[cl][3] += v[u][cl].w;
+        }
+        n += cc[u];
+      }
+    }
+    for (int off = lpr; off < 64; off <<= 1) {  // fixed tree over the rows
+#pragma unroll
+      for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) a[cl][x] += __shfl_xor(a[cl][x], off);
+      n += __shfl_xor(n, off);
+    }
+    if (r == 0) {
+#pragma unroll
+      for (int cl = 0; cl < cpl; ++cl)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int c = (c0 + cl * lpr) * 4 + x;
+          if (c >= P.D) continue;
+          const int64_t o = k * P.D + c;
+          if (P.mode == MODE_MEAN)
+            P.C_new[o] = n > 0 ? a[cl][x] / (float)n : P.C_prev[o];
+          else
+            P.acc_sum[o] += a[cl][x];
+        }
+      if (c0 == 0) {
+        if (P.mode == MODE_MEAN) {
+          if (P.counts) P.counts[k] = n;
+        } else {
+          P.acc_cnt[k] += n;
+        }
       }
     }
   }
@@ -340,7 +365,12 @@ hipError_t launch_segment_reduce(const ReduceArgs& a, hipStream_t stream) {
 hipError_t launch_fixup(const ReduceArgs& a, hipStream_t stream) {
   if (a.K == 0) return hipSuccess;
   const SegParams P = make_params(a);
-  hipLaunchKernelGGL(fixup_kernel, dim3((unsigned)a.K), dim3(256), 0, stream, P);
+  const int64_t per_block = 4 * kFixupPerWave;
+  const dim3 grid((unsigned)((a.K + per_block - 1) / per_block));
+  if (P.Dc / 4 > 64)
+    hipLaunchKernelGGL(fixup_kernel<2>, grid, dim3(256), 0, stream, P);
+  else
+    hipLaunchKernelGGL(fixup_kernel<1>, grid, dim3(256), 0, stream, P);
   return hipGetLastError();
 }
 

@@ -8,243 +8,346 @@
 // tech §2.2 sorts the assignment vector (argsort) so that the points of each
 // cluster become contiguous; the update then reduces contiguous segments
 // instead of scattering.  Here the sort is an LSD radix sort over the bits of
-// the largest cluster id, at most 8 bits a pass, passes of balanced width.
-// Nothing in it uses a global atomic, so a hot cluster (many points with one
-// id) costs no contention: inside a wavefront, lanes with equal digits are
-// found with ballots, the lowest such lane (the "leader") advances the wave's
-// private LDS counter for that digit once for the whole group, and per-block
-// digit counts become global destinations through an exclusive scan.  Every
-// step is a deterministic function of the input, and equal ids keep ascending
-// point order (stable), which fixes the summation order of the update.
+// the largest cluster id, at most 6 bits a pass, passes of balanced width.
+// Nothing in it uses an atomic, so a hot cluster (many points with one id)
+// costs no contention.  Ranking inside a block of kRadixBlock keys: every
+// thread owns kRadixItems consecutive keys and a private 16-bit counter per
+// digit in LDS; counting its own keys in order gives each key its rank among
+// the thread's keys of that digit, and one exclusive scan over the counters in
+// (digit, thread) order turns them into block-wide ranks that keep the input
+// order of equal digits (stable).  Per-block digit counts then become global
+// destinations through a device-wide exclusive scan.  Every step is a
+// deterministic function of the input, which fixes the summation order of
+// the update.
 #include "km_internal.hpp"
 
 namespace km {
 
-constexpr int kSortWaves = kSortThreads / 64;
-constexpr int kRounds = kSortItems;  // a wave handles kRounds x 64 consecutive keys
+// ----------------------------------------------------------- block rank --
 
-// Lanes of this wavefront whose `bits`-bit digit equals this lane's (active lanes only).
-__device__ __forceinline__ uint64_t match_digit(uint32_t d, int bits, bool active) {
-  uint64_t m = __ballot(active);
-  for (int b = 0; b < bits; ++b) {
-    const bool bit = (d >> b) & 1u;
-    const uint64_t v = __ballot(active && bit);
-    m &= bit ? v : ~v;
-  }
-  return m;
+constexpr int kRadixWords = (1 << kMaxDigitBits) * kRadixThreads / 2;  // 16-bit counters, two a word
+constexpr int kRadixPadded = kRadixWords + kRadixWords / 32;             // + one pad word per 32
+
+// LDS word of the counter of (digit d, thread t): counters are laid out in
+// (digit, thread) order, two to a 32-bit word, with one pad word after every
+// 32 so the raking scan's per-thread chunks fall in different banks.
+__device__ __forceinline__ int ctr_word(int f) {
+  const int w = f >> 1;
+  return w + (w >> 5);
 }
 
-__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+__device__ __forceinline__ uint32_t ctr_get(const uint32_t* ctr, int f) {
+  return (ctr[ctr_word(f)] >> (16 * (f & 1))) & 0xffffu;
 }
 
-// Key and value of sorted-input position pos for this pass.  Pass 0 reads the
-// caller's assignment vector: ids outside [0, K) become K-1 with the invalid
-// flag in the value, and the value is the point index itself.
-__device__ __forceinline__ void load_kv(const int32_t* __restrict__ keys, const int32_t* __restrict__ vals,
-                                        bool first, int64_t pos, int64_t K, int32_t& key, int32_t& val) {
-  key = keys[pos];
-  if (first) {
-    val = (int32_t)pos;
-    if ((uint32_t)key >= (uint32_t)K) {
-      key = (int32_t)(K - 1);
-      val = (int32_t)((uint32_t)pos | kInvalidFlag);
-    }
-  } else {
-    val = vals[pos];
-  }
-}
-
-// Per-block digit counts: counts[d * nblk + b].
-__global__ __launch_bounds__(kSortThreads) void radix_count_kernel(const int32_t* __restrict__ keys, int64_t N,
-                                                                   int64_t K, int first, int shift, int bits,
-                                                                   int64_t nblk, uint32_t* __restrict__ counts) {
-  __shared__ uint32_t cnt[kSortWaves][256];
+// Exclusive scan of one value per thread across the block; returns the total.
+__device__ __forceinline__ uint32_t block_scan_excl(uint32_t v, uint32_t& excl, uint32_t* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int R = 1 << bits;
-  for (int i = threadIdx.x; i < kSortWaves * 256; i += kSortThreads) (&cnt[0][0])[i] = 0;
-  __syncthreads();
-  const int64_t b = blockIdx.x;
-  const int64_t base = b * kSortBlock + (int64_t)wave * (kRounds * 64);
-  for (int r = 0; r < kRounds; ++r) {
-    const int64_t pos = base + r * 64 + lane;
-    const bool active = pos < N;
-    uint32_t d = 0;
-    if (active) {
-      int32_t key = keys[pos];
-      if (first && (uint32_t)key >= (uint32_t)K) key = (int32_t)(K - 1);
-      d = ((uint32_t)key >> shift) & (uint32_t)(R - 1);
-    }
-    const uint64_t m = match_digit(d, bits, active);
-    if (active && lanes_below(m) == 0) cnt[wave][d] += (uint32_t)__popcll(m);  // one leader per digit
-    __builtin_amdgcn_wave_barrier();
-  }
-  __syncthreads();
-  for (int d = threadIdx.x; d < R; d += kSortThreads) {
-    uint32_t s = 0;
-#pragma unroll
-    for (int w = 0; w < kSortWaves; ++w) s += cnt[w][d];
-    counts[(int64_t)d * nblk + b] = s;
-  }
-}
-
-// Stable scatter: destination = scanned block base + earlier waves + rank in wave.
-__global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(const int32_t* __restrict__ keys_in,
-                                                                     const int32_t* __restrict__ vals_in, int64_t N,
-                                                                     int64_t K, int first, int shift, int bits,
-                                                                     int64_t nblk,
-                                                                     const uint32_t* __restrict__ offsets,
-                                                                     int32_t* __restrict__ keys_out,
-                                                                     int32_t* __restrict__ vals_out) {
-  __shared__ uint32_t cnt[kSortWaves][256];
-  __shared__ uint32_t gbase[256];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int R = 1 << bits;
-  for (int i = threadIdx.x; i < kSortWaves * 256; i += kSortThreads) (&cnt[0][0])[i] = 0;
-  const int64_t b = blockIdx.x;
-  for (int d = threadIdx.x; d < R; d += kSortThreads) gbase[d] = offsets[(int64_t)d * nblk + b];
-  __syncthreads();
-
-  const int64_t base = b * kSortBlock + (int64_t)wave * (kRounds * 64);
-  int32_t key[kRounds], val[kRounds];
-  uint32_t rank[kRounds];
-#pragma unroll
-  for (int r = 0; r < kRounds; ++r) {
-    const int64_t pos = base + r * 64 + lane;
-    const bool active = pos < N;
-    key[r] = 0;
-    val[r] = 0;
-    uint32_t d = 0;
-    if (active) {
-      load_kv(keys_in, vals_in, first, pos, K, key[r], val[r]);
-      d = ((uint32_t)key[r] >> shift) & (uint32_t)(R - 1);
-    }
-    const uint64_t m = match_digit(d, bits, active);
-    const uint32_t below = lanes_below(m);
-    uint32_t before = 0;
-    if (active) before = cnt[wave][d];
-    __builtin_amdgcn_wave_barrier();
-    if (active && below == 0) cnt[wave][d] = before + (uint32_t)__popcll(m);
-    __builtin_amdgcn_wave_barrier();
-    rank[r] = before + below;
-  }
-  __syncthreads();
-  // exclusive prefix over waves for every digit, plus the block's global base
-  for (int d = threadIdx.x; d < R; d += kSortThreads) {
-    uint32_t run = gbase[d];
-#pragma unroll
-    for (int w = 0; w < kSortWaves; ++w) {
-      const uint32_t c = cnt[w][d];
-      cnt[w][d] = run;
-      run += c;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < kRounds; ++r) {
-    const int64_t pos = base + r * 64 + lane;
-    if (pos < N) {
-      const uint32_t d = ((uint32_t)key[r] >> shift) & (uint32_t)(R - 1);
-      const uint32_t dst = cnt[wave][d] + rank[r];
-      if (dst < (uint64_t)N) {  // always true for a consistent scan; keeps any inconsistency in bounds
-        keys_out[dst] = key[r];
-        vals_out[dst] = val[r];
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------------- scan --
-
-constexpr int kScanThreads = 1024;
-constexpr int kScanItems = 16;
-constexpr int64_t kScanTile = (int64_t)kScanThreads * kScanItems;
-
-// Exclusive scan of v[] across the block (each thread holds kScanItems
-// consecutive values); returns the block total.
-__device__ uint32_t block_exclusive_scan(uint32_t (&v)[kScanItems], uint32_t carry, uint32_t* lds_waves) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < kScanItems; ++i) {
-    const uint32_t t = v[i];
-    v[i] = s;
-    s += t;
-  }
-  uint32_t x = s;
+  uint32_t x = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const uint32_t y = __shfl_up(x, off);
     if (lane >= off) x += y;
   }
-  if (lane == 63) lds_waves[wave] = x;
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  uint32_t before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kRadixThreads / 64; ++w) {
+    const uint32_t sw = wsum[w];
+    if (w < wave) before += sw;
+    total += sw;
+  }
+  excl = before + x - v;
+  __syncthreads();
+  return total;
+}
+
+// Stable ranks of this block's keys by BITS-bit digit.  d[i] is the digit of
+// the thread's i-th key (valid[i] false: not a key).  On return rank[i] is
+// the key's position in the block sorted by digit, and start[dd] (LDS, R+1
+// entries) the first position of digit dd.
+template <int BITS>
+__device__ __forceinline__ void block_rank(const uint32_t (&d)[kRadixItems], const bool (&valid)[kRadixItems],
+                                           uint32_t* ctr, uint32_t* wsum, uint32_t* start,
+                                           uint32_t (&rank)[kRadixItems]) {
+  constexpr int R = 1 << BITS;
+  constexpr int T = kRadixThreads;
+  const int t = threadIdx.x;
+  for (int i = t; i < kRadixPadded; i += T) ctr[i] = 0;
+  __syncthreads();
+  // count own keys in order: rank among this thread's keys of the same digit
+  uint16_t* c16 = reinterpret_cast<uint16_t*>(ctr);
+#pragma unroll
+  for (int i = 0; i < kRadixItems; ++i) {
+    if (valid[i]) {
+      const int f = (int)d[i] * T + t;
+      const int h = ctr_word(f) * 2 + (f & 1);
+      const uint32_t c = c16[h];
+      rank[i] = c;
+      c16[h] = (uint16_t)(c + 1);
+    }
+  }
+  __syncthreads();
+  // raking exclusive scan over the R*T counters in (digit, thread) order:
+  // thread t owns the flat counters [t*R, t*R + R)
+  constexpr int CH = R;  // counters per thread
+  uint32_t loc[CH];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    loc[j] = ctr_get(ctr, t * CH + j);
+    sum += loc[j];
+  }
+  uint32_t excl;
+  block_scan_excl(sum, excl, wsum);
+  uint32_t run = excl;
+#pragma unroll
+  for (int j = 0; j < CH; j += 2) {
+    const uint32_t lo = run;
+    run += loc[j];
+    const uint32_t hi = run;
+    run += loc[j + 1];
+    ctr[ctr_word(t * CH + j)] = lo | (hi << 16);  // block positions fit in 16 bits
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kRadixItems; ++i)
+    if (valid[i]) rank[i] += ctr_get(ctr, (int)d[i] * T + t);
+  for (int dd = t; dd < R; dd += T) start[dd] = ctr_get(ctr, dd * T);
+  if (t == T - 1) start[R] = run;  // the last thread's running sum is the block's key count
+  __syncthreads();
+}
+
+// Keys (and values) of this thread: kRadixItems consecutive positions.
+// Pass 0 reads the caller's assignment vector: ids outside [0, K) become K-1
+// with the invalid flag in the value, and the value is the point index itself.
+__device__ __forceinline__ void load_block_keys(const int32_t* __restrict__ keys, const int32_t* __restrict__ vals,
+                                                bool first, int64_t N, int64_t K, int64_t base,
+                                                int32_t (&key)[kRadixItems], int32_t (&val)[kRadixItems],
+                                                bool (&valid)[kRadixItems], bool want_vals) {
+  const int64_t p0 = base + (int64_t)threadIdx.x * kRadixItems;
+  if (p0 + kRadixItems <= N && ((reinterpret_cast<uintptr_t>(keys + p0) & 15) == 0)) {
+    const int4* k4 = reinterpret_cast<const int4*>(keys + p0);
+#pragma unroll
+    for (int i = 0; i < kRadixItems / 4; ++i) {
+      const int4 v = k4[i];
+      key[4 * i] = v.x;
+      key[4 * i + 1] = v.y;
+      key[4 * i + 2] = v.z;
+      key[4 * i + 3] = v.w;
+    }
+    if (want_vals && !first) {
+      const int4* v4 = reinterpret_cast<const int4*>(vals + p0);
+#pragma unroll
+      for (int i = 0; i < kRadixItems / 4; ++i) {
+        const int4 v = v4[i];
+        val[4 * i] = v.x;
+        val[4 * i + 1] = v.y;
+        val[4 * i + 2] = v.z;
+        val[4 * i + 3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kRadixItems; ++i) valid[i] = true;
+  } else {
+#pragma unroll
+    for (int i = 0; i < kRadixItems; ++i) {
+      const int64_t pos = p0 + i;
+      valid[i] = pos < N;
+      key[i] = valid[i] ? keys[pos] : 0;
+      if (want_vals && !first) val[i] = valid[i] ? vals[pos] : 0;
+    }
+  }
+  if (first) {
+#pragma unroll
+    for (int i = 0; i < kRadixItems; ++i) {
+      const int64_t pos = p0 + i;
+      val[i] = (int32_t)pos;
+      if ((uint32_t)key[i] >= (uint32_t)K) {
+        key[i] = (int32_t)(K - 1);
+        val[i] = (int32_t)((uint32_t)pos | kInvalidFlag);
+      }
+    }
+  }
+}
+
+// Per-block digit counts: counts[d * nblk + b].
+template <int BITS>
+__global__ __launch_bounds__(kRadixThreads) void radix_count_kernel(const int32_t* __restrict__ keys, int64_t N,
+                                                                    int64_t K, int first, int shift, int64_t nblk,
+                                                                    uint32_t* __restrict__ counts) {
+  constexpr int R = 1 << BITS;
+  __shared__ uint32_t ctr[kRadixPadded];
+  __shared__ uint32_t wsum[kRadixThreads / 64];
+  __shared__ uint32_t start[R + 1];
+  const int64_t b = blockIdx.x;
+  int32_t key[kRadixItems], val[kRadixItems];
+  bool valid[kRadixItems];
+  load_block_keys(keys, nullptr, first, N, K, b * kRadixBlock, key, val, valid, false);
+  uint32_t d[kRadixItems], rank[kRadixItems];
+#pragma unroll
+  for (int i = 0; i < kRadixItems; ++i) d[i] = ((uint32_t)key[i] >> shift) & (uint32_t)(R - 1);
+  block_rank<BITS>(d, valid, ctr, wsum, start, rank);
+  for (int dd = threadIdx.x; dd < R; dd += kRadixThreads) counts[(int64_t)dd * nblk + b] = start[dd + 1] - start[dd];
+}
+
+// Stable scatter: destination = scanned global base of (digit, block) + rank
+// within the digit.  The block's keys, then its values, are first placed in
+// LDS in sorted order (reusing the counter space), then written out with
+// consecutive lanes on consecutive block positions, so each digit's run
+// leaves as contiguous stores rather than scattered words.
+static_assert(kRadixPadded >= kRadixBlock, "staging reuses the counter space");
+template <int BITS>
+__global__ __launch_bounds__(kRadixThreads) void radix_scatter_kernel(const int32_t* __restrict__ keys_in,
+                                                                      const int32_t* __restrict__ vals_in, int64_t N,
+                                                                      int64_t K, int first, int shift, int64_t nblk,
+                                                                      const uint32_t* __restrict__ offsets,
+                                                                      int32_t* __restrict__ keys_out,
+                                                                      int32_t* __restrict__ vals_out) {
+  constexpr int R = 1 << BITS;
+  __shared__ uint32_t ctr[kRadixPadded];
+  __shared__ uint32_t wsum[kRadixThreads / 64];
+  __shared__ uint32_t start[R + 1];
+  __shared__ uint32_t gbase[R];
+  const int64_t b = blockIdx.x;
+  for (int dd = threadIdx.x; dd < R; dd += kRadixThreads) gbase[dd] = offsets[(int64_t)dd * nblk + b];
+  int32_t key[kRadixItems], val[kRadixItems];
+  bool valid[kRadixItems];
+  load_block_keys(keys_in, vals_in, first, N, K, b * kRadixBlock, key, val, valid, true);
+  uint32_t d[kRadixItems], rank[kRadixItems];
+#pragma unroll
+  for (int i = 0; i < kRadixItems; ++i) d[i] = ((uint32_t)key[i] >> shift) & (uint32_t)(R - 1);
+  block_rank<BITS>(d, valid, ctr, wsum, start, rank);
+  const uint32_t nkeys = start[R];
+  int32_t* stage = reinterpret_cast<int32_t*>(ctr);
+  // keys in sorted order; remember each striped position's destination
+#pragma unroll
+  for (int i = 0; i < kRadixItems; ++i)
+    if (valid[i]) stage[rank[i]] = key[i];
+  __syncthreads();
+  uint32_t dst[kRadixItems];
+#pragma unroll
+  for (int i = 0; i < kRadixItems; ++i) {
+    const uint32_t p = (uint32_t)(i * kRadixThreads + threadIdx.x);
+    dst[i] = 0xffffffffu;
+    if (p < nkeys) {
+      const int32_t k = stage[p];
+      const uint32_t dg = ((uint32_t)k >> shift) & (uint32_t)(R - 1);
+      dst[i] = gbase[dg] + (p - start[dg]);
+      if (dst[i] < (uint64_t)N) keys_out[dst[i]] = k;  // always true for a consistent scan
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kRadixItems; ++i)
+    if (valid[i]) stage[rank[i]] = val[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kRadixItems; ++i) {
+    const uint32_t p = (uint32_t)(i * kRadixThreads + threadIdx.x);
+    if (p < nkeys && dst[i] < (uint64_t)N) vals_out[dst[i]] = stage[p];
+  }
+}
+
+// ------------------------------------------------------------------- scan --
+//
+// Exclusive scan of the (digit, block) counts.  A tile is 1024 threads x 4
+// consecutive values, loaded and stored as one 16-byte vector per thread
+// (a wavefront touches 1 KiB of contiguous memory per instruction).
+
+constexpr int kScanThreads = 1024;
+constexpr int64_t kScanTile = (int64_t)kScanThreads * 4;
+
+// Exclusive scan of one value per thread across the 1024-thread block; returns the total.
+__device__ uint32_t scan_block(uint32_t v, uint32_t& excl, uint32_t* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
   __syncthreads();
   if (wave == 0) {
     constexpr int NW = kScanThreads / 64;
-    uint32_t w = lane < NW ? lds_waves[lane] : 0;
+    const uint32_t w = lane < NW ? wsum[lane] : 0u;
     uint32_t z = w;
 #pragma unroll
     for (int off = 1; off < NW; off <<= 1) {
       const uint32_t y = __shfl_up(z, off);
       if (lane >= off) z += y;
     }
-    if (lane < NW) lds_waves[NW + lane] = z - w;  // exclusive wave prefix
-    if (lane == NW - 1) lds_waves[2 * NW] = z;    // block total
+    if (lane < NW) wsum[NW + lane] = z - w;  // exclusive prefix of each wavefront
+    if (lane == NW - 1) wsum[2 * NW] = z;    // block total
   }
   __syncthreads();
-  const uint32_t pre = carry + lds_waves[kScanThreads / 64 + wave] + (x - s);
-#pragma unroll
-  for (int i = 0; i < kScanItems; ++i) v[i] += pre;
-  const uint32_t total = lds_waves[2 * (kScanThreads / 64)];
+  excl = wsum[kScanThreads / 64 + wave] + x - v;
+  const uint32_t total = wsum[2 * (kScanThreads / 64)];
   __syncthreads();
   return total;
 }
 
-// Sum of each tile of kScanTile values.
+__device__ __forceinline__ uint4 load4(const uint32_t* a, int64_t i, int64_t n) {
+  if (i + 4 <= n) return *reinterpret_cast<const uint4*>(a + i);
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (i < n) v.x = a[i];
+  if (i + 1 < n) v.y = a[i + 1];
+  if (i + 2 < n) v.z = a[i + 2];
+  return v;
+}
+
+__device__ __forceinline__ void store4(uint32_t* a, int64_t i, int64_t n, uint4 v) {
+  if (i + 4 <= n) {
+    *reinterpret_cast<uint4*>(a + i) = v;
+    return;
+  }
+  if (i < n) a[i] = v.x;
+  if (i + 1 < n) a[i + 1] = v.y;
+  if (i + 2 < n) a[i + 2] = v.z;
+}
+
+// Scan one tile in place with carry-in `carry`; returns the tile total.
+__device__ uint32_t scan_tile(uint32_t* a, int64_t n, int64_t t0, uint32_t carry, uint32_t* wsum) {
+  const int64_t i = t0 + (int64_t)threadIdx.x * 4;
+  uint4 v = load4(a, i, n);
+  const uint32_t s = v.x + v.y + v.z + v.w;
+  uint32_t excl;
+  const uint32_t total = scan_block(s, excl, wsum);
+  const uint32_t b = carry + excl;
+  const uint4 o = make_uint4(b, b + v.x, b + v.x + v.y, b + v.x + v.y + v.z);
+  store4(a, i, n, o);
+  return total;
+}
+
+// Sum of each tile.
 __global__ __launch_bounds__(kScanThreads) void scan_reduce_kernel(const uint32_t* __restrict__ a, int64_t n,
                                                                    uint32_t* __restrict__ part) {
-  __shared__ uint32_t lds[2 * (kScanThreads / 64) + 1];
-  uint32_t v[kScanItems];
-  const int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
-#pragma unroll
-  for (int i = 0; i < kScanItems; ++i) v[i] = base + i < n ? a[base + i] : 0u;
-  const uint32_t total = block_exclusive_scan(v, 0u, lds);
+  __shared__ uint32_t wsum[2 * (kScanThreads / 64) + 1];
+  const int64_t i = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * 4;
+  const uint4 v = load4(a, i, n);
+  uint32_t excl;
+  const uint32_t total = scan_block(v.x + v.y + v.z + v.w, excl, wsum);
   if (threadIdx.x == 0) part[blockIdx.x] = total;
 }
 
-// In-place exclusive scan of a[0..n) by one block, tile after tile with a carry.
+// In-place exclusive scan of a[0..n) by one block, tile after tile.
 __global__ __launch_bounds__(kScanThreads) void scan_single_kernel(uint32_t* __restrict__ a, int64_t n) {
-  __shared__ uint32_t lds[2 * (kScanThreads / 64) + 1];
+  __shared__ uint32_t wsum[2 * (kScanThreads / 64) + 1];
   uint32_t carry = 0;
-  for (int64_t t0 = 0; t0 < n; t0 += kScanTile) {
-    uint32_t v[kScanItems];
-    const int64_t base = t0 + (int64_t)threadIdx.x * kScanItems;
-#pragma unroll
-    for (int i = 0; i < kScanItems; ++i) v[i] = base + i < n ? a[base + i] : 0u;
-    const uint32_t total = block_exclusive_scan(v, carry, lds);
-#pragma unroll
-    for (int i = 0; i < kScanItems; ++i)
-      if (base + i < n) a[base + i] = v[i];
-    carry += total;
-  }
+  for (int64_t t0 = 0; t0 < n; t0 += kScanTile) carry += scan_tile(a, n, t0, carry, wsum);
 }
 
 // In-place exclusive scan of each tile, offset by the scanned tile sums.
 __global__ __launch_bounds__(kScanThreads) void scan_apply_kernel(uint32_t* __restrict__ a, int64_t n,
                                                                   const uint32_t* __restrict__ part) {
-  __shared__ uint32_t lds[2 * (kScanThreads / 64) + 1];
-  uint32_t v[kScanItems];
-  const int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
-#pragma unroll
-  for (int i = 0; i < kScanItems; ++i) v[i] = base + i < n ? a[base + i] : 0u;
-  block_exclusive_scan(v, part[blockIdx.x], lds);
-#pragma unroll
-  for (int i = 0; i < kScanItems; ++i)
-    if (base + i < n) a[base + i] = v[i];
+  __shared__ uint32_t wsum[2 * (kScanThreads / 64) + 1];
+  scan_tile(a, n, (int64_t)blockIdx.x * kScanTile, part[blockIdx.x], wsum);
 }
 
 static hipError_t launch_scan(uint32_t* a, int64_t n, uint32_t* part, hipStream_t s) {
-  if (n <= 4 * kScanTile) {
+  if (n <= kScanTile) {
     hipLaunchKernelGGL(scan_single_kernel, dim3(1), dim3(kScanThreads), 0, s, a, n);
     return hipGetLastError();
   }
@@ -272,12 +375,28 @@ hipError_t launch_argsort(const SortGeom& g, const int32_t* keys_in, int32_t* ke
     const bool last = p == g.npass - 1;
     int32_t* kout = last ? key_final : (p % 2 == 0 ? key_a : key_b);
     int32_t* vout = last ? val_final : (p % 2 == 0 ? val_a : val_b);
-    hipLaunchKernelGGL(radix_count_kernel, dim3((unsigned)g.nblk), dim3(kSortThreads), 0, stream, kin, g.N, g.K,
-                       first, shift, bits, g.nblk, counts);
+    switch (bits) {
+#define KM_PASS(B)                                                                                                 \
+  case B:                                                                                                          \
+    hipLaunchKernelGGL((radix_count_kernel<B>), dim3((unsigned)g.nblk), dim3(kRadixThreads), 0, stream, kin, g.N, \
+                       g.K, first, shift, g.nblk, counts);                                                        \
+    break;
+      KM_PASS(1) KM_PASS(2) KM_PASS(3) KM_PASS(4) KM_PASS(5) KM_PASS(6)
+#undef KM_PASS
+      default: return hipErrorInvalidValue;
+    }
     hipError_t e = launch_scan(counts, ((int64_t)1 << bits) * g.nblk, scan_part, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(radix_scatter_kernel, dim3((unsigned)g.nblk), dim3(kSortThreads), 0, stream, kin, vin, g.N,
-                       g.K, first, shift, bits, g.nblk, (const uint32_t*)counts, kout, vout);
+    switch (bits) {
+#define KM_PASS(B)                                                                                                   \
+  case B:                                                                                                            \
+    hipLaunchKernelGGL((radix_scatter_kernel<B>), dim3((unsigned)g.nblk), dim3(kRadixThreads), 0, stream, kin, vin, \
+                       g.N, g.K, first, shift, g.nblk, (const uint32_t*)counts, kout, vout);                        \
+    break;
+      KM_PASS(1) KM_PASS(2) KM_PASS(3) KM_PASS(4) KM_PASS(5) KM_PASS(6)
+#undef KM_PASS
+      default: return hipErrorInvalidValue;
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     kin = kout;
