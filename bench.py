@@ -30,18 +30,24 @@ PEAK = {  # MI355X published dense peaks
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def _src_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+ASSIGN_SOURCES = [os.path.join(ROOT, "means_clustering_amd", "csrc", f) for f in ("flash_assign.hip", "km_internal.hpp")]
 
 
-def _traffic(kernel_src, workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it is still current."""
+def _src_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_srcs, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if the kernel is unchanged since."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
         r = rec[workload]
-        if r["source_sha"] != _src_hash(kernel_src):
+        if r["source_sha"] != _src_hash(kernel_srcs):
             return None
         return r["bytes_per_launch"]
     except (OSError, KeyError, ValueError):
@@ -185,7 +191,7 @@ def main():
             flops = 2.0 * w.N * w.K * w.D * its / phases["assign"]["launches"]
         achieved = flops / avg_s
         peak = PEAK[w.dtype]
-        traffic = _traffic(os.path.join(ROOT, "means_clustering_amd", "csrc", "flash_assign.hip"), w.name)
+        traffic = _traffic(ASSIGN_SOURCES, w.name)
         roof = {"bound": "mfma", "kernel": "flash_assign", "achieved": round(achieved / 1e12, 2),
                 "peak": round(peak / 1e12, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic, "flops_per_launch": flops, "avg_launch_us": phases["assign"]["avg_us"]}
