@@ -54,22 +54,22 @@ def _traffic(kernel_srcs, workload):
         return None
 
 
-def cpu_baseline(w, C0, budget_s=10.0):
+def cpu_baseline(w, C0, rows_of, budget_s=10.0):
     """The oracle (never tuned) on a bounded sample of the same workload, scaled to the full N.
 
-    A first run on a small sample calibrates the rate; the measured run then
-    takes enough leading rows of X for about `budget_s` seconds.
+    ``rows_of(r)`` returns the first r rows of X as stored.  A first run on a
+    small sample calibrates the rate; the measured run then takes enough
+    leading rows for about ``budget_s`` seconds of one Lloyd iteration.
     """
     import oracle
-    import synth
 
     def timed(rows):
-        Xs = synth.points(w, 0, rows)
+        Xs = rows_of(rows)
         t0 = time.perf_counter()
         oracle.fit(Xs, C0, 1, contract=True, xdtype=w.dtype)
         return time.perf_counter() - t0
 
-    rows = max(256, min(w.N, w.N // 256))
+    rows = max(256, min(w.N, w.N // 256, 1 << 20))
     dt = timed(rows)
     rows = int(min(w.N, max(rows, rows * budget_s / max(dt, 1e-3))))
     dt = timed(rows)
@@ -121,19 +121,22 @@ def main():
     # ---- inputs (synthetic, seeded), resident in HBM before timing ------------
     t0 = time.perf_counter()
     if streamed:
-        Xh = torch.empty((w.N, w.D), dtype=torch_dt, pin_memory=True)
-        step = 1 << 24
-        cent = synth.centers(w)
-        for r0 in range(0, w.N, step):
-            synth.points_into(w, Xh.data_ptr() + r0 * w.D * Xh.element_size(), r0, min(step, w.N - r0), cent=cent)
-            print(f"[bench] generated {min(r0 + step, w.N)} / {w.N} rows", file=sys.stderr, flush=True)
-        C0 = torch.from_numpy(synth.init_centroids(w)).to(dev)
+        def progress(done):
+            if done % (1 << 28) < (1 << 24) or done == w.N:
+                print(f"[bench] generated {done} / {w.N} rows", file=sys.stderr, flush=True)
+
+        # pageable: 10^9 x 64 bf16 is more than the host lets one process pin; uploaded through a staging ring
+        Xh = synth.host_points(w, dev, pinned=False, progress=progress)
+        stage = km.staging_buffer()
+        Xrows = synth.as_numpy_rows(Xh)
+        C0 = torch.from_numpy(synth.init_centroids(w, Xrows)).to(dev)
+        rows_of = lambda r: Xrows[:r]  # noqa: E731
     else:
         Xn = synth.points(w)
         C0 = torch.from_numpy(synth.init_centroids(w, Xn)).to(dev)
         X = (torch.from_numpy(Xn.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16"
              else torch.from_numpy(Xn)).to(dev)
-        del Xn
+        rows_of = lambda r: Xn[:r]  # noqa: E731
     print(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
 
     C = C0.clone()
@@ -146,7 +149,8 @@ def main():
     def one_step():
         C.copy_(C0)
         if streamed:
-            km.fit_streamed(Xh, C, w.iters, w.chunk_rows, copy_stream=copy_stream, want_assign=False, ws=ws)
+            km.fit_streamed(Xh, C, w.iters, w.chunk_rows, copy_stream=copy_stream, want_assign=False, ws=ws,
+                            stage=stage)
         else:
             km.fit(X, C, w.iters, inplace=True, ws=ws, assign_out=a, counts_out=counts)
 
@@ -196,10 +200,18 @@ def main():
                 "peak": round(peak / 1e12, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic, "flops_per_launch": flops, "avg_launch_us": phases["assign"]["avg_us"]}
 
+    stream = None
+    if streamed and "h2d" in phases:
+        es = 2 if w.dtype == "bf16" else 4
+        h2d_bytes = w.N * w.D * es * its
+        stream = {"h2d_bytes_per_iteration": w.N * w.D * es,
+                  "h2d_GBps_while_copying": round(h2d_bytes / (phases["h2d"]["total_ms"] * 1e-3) / 1e9, 2),
+                  "end_to_end_GBps": round(h2d_bytes / elapsed / 1e9, 2)}
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline: timing the oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, C0.cpu().numpy(), budget_s=args.cpu_budget)
+        cpu = cpu_baseline(w, C0.cpu().numpy(), rows_of, budget_s=args.cpu_budget)
 
     line = {
         "metric": "Lloyd iterations/sec and point-centroid distances/sec (fused assign+update)",
@@ -209,7 +221,7 @@ def main():
         "config": {"workload": w.description, "name": w.name, "N": w.N, "D": w.D, "K": w.K,
                    "iters_per_step": w.iters, "chunk_rows": w.chunk_rows or None},
         "distances_per_s": round(value * w.N * w.K, 1),
-        "roofline": roof, "cpu_baseline": cpu, "phases": phases,
+        "roofline": roof, "cpu_baseline": cpu, "phases": phases, "streaming": stream,
         "device": torch.cuda.get_device_name(dev),
     }
     print(json.dumps(line), flush=True)

@@ -146,25 +146,40 @@ km_status kmeans_fit(const void* X, km_dtype dt, int64_t N, int64_t D, int64_t K
                      void* stream);
 
 /*
- * kmeans_fit_streamed -- Lloyd iterations for X that stays in pinned host
- * memory (tech §2.3 "chunked stream overlap"): every iteration copies X to
- * the device in chunks of `chunk_rows` rows on `copy_stream`, two device
- * buffers in rotation, while `compute_stream` assigns the previous chunk and
- * accumulates its per-cluster sums; the means are formed once per iteration.
- *   X_host       pinned host, N x D, type dt                 (read)
+ * kmeans_fit_streamed -- Lloyd iterations for X that stays in host memory
+ * (tech §2.3 "chunked stream overlap"; tech §1 names data larger than device
+ * memory): every iteration copies X to the device in chunks of `chunk_rows`
+ * rows on `copy_stream`, two device buffers in rotation, while
+ * `compute_stream` assigns the previous chunk and accumulates its per-cluster
+ * sums; the means are formed once per iteration.
+ *   X_host       host, N x D, type dt                        (read)
+ *                With stage_host == NULL it must be pinned (hipHostMalloc /
+ *                torch pin_memory) and is read by the DMA engine directly.
+ *                With a staging buffer it may be ordinary pageable memory:
+ *                host threads of the library copy it slot by slot into the
+ *                staging buffer, from which it is uploaded.
  *   C            device K x D fp32: initial centroids in, C^iters out
  *   assign_host  pinned host int32[N] or NULL: assignment of the last
  *                iteration (copied back chunk by chunk)
  *   counts       device int32[K] or NULL
  *   objective    device double[iters] or NULL (as kmeans_fit)
  *   compute_stream, copy_stream: distinct hipStream_t (NULL allowed for
- *                compute_stream only).  On return all work is enqueued;
- *                synchronise compute_stream before reading any output.
+ *                compute_stream only).
+ *   stage_host, stage_bytes: pinned host staging buffer or NULL.  It is split
+ *                into 4 slots of floor(stage_bytes / 4) bytes rounded down to
+ *                whole rows (at least one row each, else
+ *                KM_ERR_INVALID_VALUE); a few tens of MiB per slot keep the
+ *                host link busy.  The number of copying threads is
+ *                min(8, cores - 1) + the caller, or KM_STAGE_THREADS.
+ * On return all work is enqueued (with staging, the call returns once the
+ * last slot has been filled, so it blocks while the upload proceeds).
+ * Synchronise compute_stream before reading any output or reusing X_host or
+ * the staging buffer.  Calls that share a staging buffer must not overlap.
  */
 km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_t D, int64_t K, float* C,
                               int32_t iters, int64_t chunk_rows, int32_t* assign_host, int32_t* counts,
                               double* objective, void* ws, size_t ws_bytes, void* compute_stream,
-                              void* copy_stream);
+                              void* copy_stream, void* stage_host, size_t stage_bytes);
 
 /* Short constant description of a status code. */
 const char* kmeans_status_string(km_status s);

@@ -15,7 +15,7 @@ Entry points (all tensors on one ROCm device unless stated):
   sort_by_cluster(a, K)              stable argsort + boundaries  (tech §2.2 inverse map)
   update(X, a, C_prev)               means, empty keeps previous  (tech §2.2 Sort-Inverse Update)
   fit(X, C0, iters)                  Lloyd iterations, X resident
-  fit_streamed(X_host, C0, iters, chunk_rows)   X in pinned host memory (tech §2.3 chunked overlap)
+  fit_streamed(X_host, C0, iters, chunk_rows)   X in host memory (tech §2.3 chunked overlap)
 """
 from __future__ import annotations
 
@@ -55,7 +55,7 @@ def _bind(lib):
         "kmeans_update": (c_int, [vp, c_int, i64, i64, vp, i64, vp, vp, vp, vp, sz, vp]),
         "kmeans_fit": (c_int, [vp, c_int, i64, i64, i64, vp, ctypes.c_int32, vp, vp, vp, vp, sz, vp]),
         "kmeans_fit_streamed": (c_int, [vp, c_int, i64, i64, i64, vp, ctypes.c_int32, i64, vp, vp, vp, vp, sz, vp,
-                                        vp]),
+                                        vp, vp, sz]),
         "kmeans_status_string": (ctypes.c_char_p, [c_int]),
         "kmeans_last_error": (ctypes.c_char_p, []),
         "kmeans_timing_enable": (c_int, [c_int]),
@@ -214,20 +214,50 @@ def fit(X: torch.Tensor, C0: torch.Tensor, iters: int, objective: bool = False, 
     return C, a, counts, (obj[:iters] if obj is not None else None)
 
 
-def fit_streamed(X_host: torch.Tensor, C0: torch.Tensor, iters: int, chunk_rows: int, copy_stream=None,
-                 want_assign: bool = True, objective: bool = False, ws: Workspace | None = None):
-    """Lloyd iterations with X in pinned host memory, streamed in chunks.
+STAGE_SLOT_BYTES = 64 << 20  # default staging slot for pageable X (4 slots)
 
-    Returns (C, assign_host int32[N] pinned or None, counts, objective-or-None).
-    The call returns once all work is enqueued on the current stream.
+# Host buffers read or written by enqueued copies, held until the work has passed an event:
+# torch's pinned-memory cache may hand a freed block out again while a DMA still uses it.
+_inflight: list = []
+_inflight_lock = threading.Lock()
+
+
+def _hold_until_done(device, *objs):
+    ev = torch.cuda.Event()
+    ev.record(torch.cuda.current_stream(device))
+    with _inflight_lock:
+        _inflight.append((ev, objs))
+        _inflight[:] = [(e, o) for (e, o) in _inflight if not e.query()]
+
+
+def staging_buffer(nbytes: int = 4 * STAGE_SLOT_BYTES) -> torch.Tensor:
+    """A pinned host byte buffer for streaming X that is not pinned itself."""
+    return torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+
+
+def fit_streamed(X_host: torch.Tensor, C0: torch.Tensor, iters: int, chunk_rows: int, copy_stream=None,
+                 want_assign: bool = True, objective: bool = False, ws: Workspace | None = None,
+                 stage: torch.Tensor | None = None):
+    """Lloyd iterations with X in host memory, streamed in chunks.
+
+    X_host may be pinned (uploaded directly) or pageable (uploaded through the
+    pinned ``stage`` buffer, allocated here if not given).  Returns
+    (C, assign_host int32[N] pinned or None, counts, objective-or-None).  The
+    call returns once all work is enqueued on the current stream.
     """
-    if X_host.is_cuda or not X_host.is_pinned():
-        raise ValueError("X_host must be a pinned host tensor")
-    if not C0.is_cuda or C0.dtype != torch.float32 or X_host.dim() != 2 or X_host.shape[1] != C0.shape[1]:
+    if X_host.is_cuda or X_host.dim() != 2 or not X_host.is_contiguous():
+        raise ValueError("X_host must be a contiguous 2-D host tensor")
+    if not C0.is_cuda or C0.dtype != torch.float32 or X_host.shape[1] != C0.shape[1]:
         raise ValueError("C0 must be a K x D float32 device tensor matching X_host")
     N, D = X_host.shape
     K = C0.shape[0]
     dev = C0.device
+    if X_host.is_pinned():
+        stage = None
+    elif stage is None:
+        stage = staging_buffer()
+    elif stage.is_cuda or not stage.is_pinned() or stage.dtype != torch.uint8:
+        raise ValueError("stage must be a pinned uint8 host tensor")
     C = C0.clone()
     a = torch.empty(N, dtype=torch.int32, pin_memory=True) if want_assign else None
     counts = torch.empty(K, dtype=torch.int32, device=dev)
@@ -237,7 +267,9 @@ def fit_streamed(X_host: torch.Tensor, C0: torch.Tensor, iters: int, chunk_rows:
     cs = copy_stream if copy_stream is not None else torch.cuda.Stream(dev)
     _check(lib().kmeans_fit_streamed(_ptr(X_host), _dtype(X_host), N, D, K, _ptr(C), int(iters), int(chunk_rows),
                                      _ptr(a), _ptr(counts), _ptr(obj), _ptr(w), w.numel(),
-                                     ctypes.c_void_p(_stream(dev)), ctypes.c_void_p(cs.cuda_stream)))
+                                     ctypes.c_void_p(_stream(dev)), ctypes.c_void_p(cs.cuda_stream),
+                                     _ptr(stage), 0 if stage is None else stage.numel()))
+    _hold_until_done(dev, X_host, stage, a)
     return C, a, counts, (obj[:iters] if obj is not None else None)
 
 

@@ -6,8 +6,13 @@
 // of its technical summary.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <condition_variable>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 #include <string>
+#include <thread>
 #include <unordered_map>
 #include <utility>
 #include <vector>
@@ -237,6 +242,98 @@ static km_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   return KM_OK;
 }
 
+// ------------------------------------------------ host staging copies ----
+//
+// X in pageable host memory cannot be read by the DMA engine directly: each
+// piece is first copied into a pinned staging slot by a small pool of host
+// threads (the copy is bound by host memory bandwidth, one thread is not
+// enough to keep up with the host link), then uploaded from the slot.
+
+namespace {
+class CopyPool {
+ public:
+  explicit CopyPool(int workers) : nw_(workers) {
+    for (int i = 0; i < nw_; ++i) th_.emplace_back([this, i] { run(i + 1); });
+  }
+  ~CopyPool() {
+    {
+      std::lock_guard<std::mutex> g(mu_);
+      stop_ = true;
+    }
+    cv_.notify_all();
+    for (auto& t : th_) t.join();
+  }
+  // memcpy(dst, src, n) split over the workers and the calling thread; returns when all parts are done.
+  void copy(uint8_t* dst, const uint8_t* src, size_t n) {
+    std::lock_guard<std::mutex> call(call_mu_);
+    const int parts = nw_ + 1;
+    {
+      std::lock_guard<std::mutex> g(mu_);
+      dst_ = dst;
+      src_ = src;
+      n_ = n;
+      left_ = nw_;
+      ++gen_;
+    }
+    cv_.notify_all();
+    part(0, parts, dst, src, n);
+    std::unique_lock<std::mutex> g(mu_);
+    done_.wait(g, [&] { return left_ == 0; });
+  }
+
+ private:
+  static size_t bound(int i, int parts, size_t n) { return i >= parts ? n : (n / parts * i) & ~(size_t)63; }
+  static void part(int i, int parts, uint8_t* d, const uint8_t* s, size_t n) {
+    const size_t a = bound(i, parts, n), b = bound(i + 1, parts, n);
+    if (b > a) std::memcpy(d + a, s + a, b - a);
+  }
+  void run(int idx) {
+    uint64_t seen = 0;
+    for (;;) {
+      uint8_t* d;
+      const uint8_t* s;
+      size_t n;
+      {
+        std::unique_lock<std::mutex> g(mu_);
+        cv_.wait(g, [&] { return stop_ || gen_ != seen; });
+        if (stop_) return;
+        seen = gen_;
+        d = dst_;
+        s = src_;
+        n = n_;
+      }
+      part(idx, nw_ + 1, d, s, n);
+      std::lock_guard<std::mutex> g(mu_);
+      if (--left_ == 0) done_.notify_one();
+    }
+  }
+  int nw_;
+  std::vector<std::thread> th_;
+  std::mutex mu_, call_mu_;
+  std::condition_variable cv_, done_;
+  uint8_t* dst_ = nullptr;
+  const uint8_t* src_ = nullptr;
+  size_t n_ = 0;
+  int left_ = 0;
+  uint64_t gen_ = 0;
+  bool stop_ = false;
+};
+
+CopyPool& copy_pool() {
+  static CopyPool pool([] {
+    if (const char* e = std::getenv("KM_STAGE_THREADS")) {
+      const int v = std::atoi(e);
+      if (v >= 1 && v <= 256) return v - 1;
+    }
+    const int hc = (int)std::thread::hardware_concurrency();
+    return std::max(0, std::min(8, hc - 1));
+  }());
+  return pool;
+}
+}  // namespace
+
+constexpr int kStageSlots = 4;
+
 // ---------------------------------------------------- launch sequences ----
 
 static km_status run_assign(const void* X, km_dtype dt, int64_t N, int64_t D, const float* C, int64_t K,
@@ -394,7 +491,7 @@ km_status kmeans_fit(const void* X, km_dtype dt, int64_t N, int64_t D, int64_t K
 km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_t D, int64_t K, float* C,
                               int32_t iters, int64_t chunk_rows, int32_t* assign_host, int32_t* counts,
                               double* objective, void* ws, size_t ws_bytes, void* compute_stream,
-                              void* copy_stream) {
+                              void* copy_stream, void* stage_host, size_t stage_bytes) {
   km_status st = check_sizes(N, D, K, dt, true);
   if (st != KM_OK) return st;
   if (iters < 0) return fail(KM_ERR_INVALID_VALUE, "iters must be >= 0");
@@ -405,6 +502,14 @@ km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_
   if (!aligned(X_host, dt == KM_F32 ? 4 : 2) || !aligned(C, 4) || !aligned(assign_host, 4) ||
       !aligned(counts, 4) || !aligned(objective, 8))
     return fail(KM_ERR_INVALID_VALUE, "misaligned pointer");
+  const size_t es = (size_t)dtype_size((int)dt);
+  const size_t row_bytes = (size_t)D * es;
+  size_t slot_bytes = 0;
+  if (stage_host) {
+    slot_bytes = stage_bytes / kStageSlots / row_bytes * row_bytes;
+    if (slot_bytes == 0)
+      return fail(KM_ERR_INVALID_VALUE, "stage_bytes must hold at least " + std::to_string(kStageSlots) + " rows");
+  }
   st = check_ws(ws, ws_bytes, workspace_bytes_impl(KM_OP_FIT_STREAMED, N, D, K, dt, chunk_rows));
   if (st != KM_OK) return st;
   if (iters == 0) return KM_OK;
@@ -413,24 +518,42 @@ km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_
   Carve c(ws);
   const StreamBufs b = carve_streamed(c, rows, D, K, dt);
   const int64_t nchunks = N > 0 ? (N + rows - 1) / rows : 0;
-  const size_t es = (size_t)dtype_size((int)dt);
   const AssignGeom g = assign_geom(rows, D, K, dt);
 
-  hipEvent_t ready[2], freed[2];
-  for (int i = 0; i < 2; ++i) {
-    KM_HIP(hipEventCreateWithFlags(&ready[i], hipEventDisableTiming));
-    KM_HIP(hipEventCreateWithFlags(&freed[i], hipEventDisableTiming));
-  }
+  // ready[b]: chunk buffer b is filled; freed[b]: its compute is done; slot_done[s]: staging slot s uploaded
+  std::vector<hipEvent_t> events;
   struct EventGuard {
-    hipEvent_t* r;
-    hipEvent_t* f;
+    std::vector<hipEvent_t>& ev;
     ~EventGuard() {
-      for (int i = 0; i < 2; ++i) {
-        (void)hipEventDestroy(r[i]);
-        (void)hipEventDestroy(f[i]);
-      }
+      for (hipEvent_t e : ev) (void)hipEventDestroy(e);
     }
-  } guard{ready, freed};
+  } guard{events};
+  hipEvent_t ready[2], freed[2], slot_done[kStageSlots];
+  for (hipEvent_t* e : {&ready[0], &ready[1], &freed[0], &freed[1]}) {
+    KM_HIP(hipEventCreateWithFlags(e, hipEventDisableTiming));
+    events.push_back(*e);
+  }
+  if (stage_host)
+    for (int i = 0; i < kStageSlots; ++i) {
+      KM_HIP(hipEventCreateWithFlags(&slot_done[i], hipEventDisableTiming));
+      events.push_back(slot_done[i]);
+    }
+  uint64_t slot_seq = 0;
+  // Upload `bytes` of host X to `dst`: one copy from pinned X, or slot by slot through the staging ring.
+  auto upload = [&](uint8_t* dst, const uint8_t* src, size_t bytes) -> hipError_t {
+    if (!stage_host) return hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, xs);
+    for (size_t off = 0; off < bytes; off += slot_bytes, ++slot_seq) {
+      const size_t n = std::min(slot_bytes, bytes - off);
+      const int sl = (int)(slot_seq % kStageSlots);
+      hipError_t e;
+      if (slot_seq >= (uint64_t)kStageSlots && (e = hipEventSynchronize(slot_done[sl])) != hipSuccess) return e;
+      uint8_t* slot = (uint8_t*)stage_host + (size_t)sl * slot_bytes;
+      copy_pool().copy(slot, src + off, n);
+      if ((e = hipMemcpyAsync(dst + off, slot, n, hipMemcpyHostToDevice, xs)) != hipSuccess) return e;
+      if ((e = hipEventRecord(slot_done[sl], xs)) != hipSuccess) return e;
+    }
+    return hipSuccess;
+  };
 
   int64_t seq = 0;  // global chunk counter: buffer = seq % 2
   for (int32_t t = 0; t < iters; ++t) {
@@ -445,8 +568,8 @@ km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_
       // copy stream: wait until the compute of the chunk that last used this buffer is done
       if (seq >= 2) KM_HIP(hipStreamWaitEvent(xs, freed[buf], 0));
       KM_TIMED("h2d", xs,
-               return hipMemcpyAsync(b.xbuf[buf], (const uint8_t*)X_host + (size_t)r0 * (size_t)D * es,
-                                     (size_t)nr * (size_t)D * es, hipMemcpyHostToDevice, xs));
+               return upload((uint8_t*)b.xbuf[buf], (const uint8_t*)X_host + (size_t)r0 * row_bytes,
+                             (size_t)nr * row_bytes));
       KM_HIP(hipEventRecord(ready[buf], xs));
       // compute stream: assign the chunk, then fold its per-cluster sums into the totals
       KM_HIP(hipStreamWaitEvent(cs, ready[buf], 0));

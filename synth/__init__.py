@@ -32,15 +32,27 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gen.c")
 _LIB_PATH = os.path.join(_HERE, "libsynth.so")
+_GPU_SRC = os.path.join(_HERE, "gen_gpu.hip")
+_GPU_LIB_PATH = os.path.join(_HERE, "libsynth_gpu.so")
 _lock = threading.Lock()
 _lib = None
+_gpu_lib = None
 
 
-def build(out_path: str = _LIB_PATH) -> str:
+def build(out_path: str = _LIB_PATH, gpu_out_path: str = _GPU_LIB_PATH) -> str:
+    """Compile the host generator (gcc) and its device twin (hipcc, gfx950)."""
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=gnu11", "-ffp-contract=off",
            "-o", out_path + ".tmp", _SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(out_path + ".tmp", out_path)
+    hipcc = os.environ.get("HIPCC") or "/opt/rocm/bin/hipcc"
+    cmd = [hipcc, "-O3", "-fPIC", "-shared", "--offload-arch=gfx950", "-ffp-contract=off",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument",
+           "-o", gpu_out_path + ".tmp", _GPU_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for gen_gpu.hip:\n" + r.stderr)
+    os.replace(gpu_out_path + ".tmp", gpu_out_path)
     return out_path
 
 
@@ -70,6 +82,22 @@ def _load():
             lib.synth_num_threads.restype = ctypes.c_int
             _lib = lib
         return _lib
+
+
+def _load_gpu():
+    global _gpu_lib
+    with _lock:
+        if _gpu_lib is None:
+            if not os.path.exists(_GPU_LIB_PATH):
+                raise RuntimeError(f"{_GPU_LIB_PATH} is not built (run synth.build())")
+            lib = ctypes.CDLL(_GPU_LIB_PATH)
+            lib.synth_points_device.argtypes = [ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int,
+                                                ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            lib.synth_points_device.restype = ctypes.c_int
+            _gpu_lib = lib
+        return _gpu_lib
 
 
 def philox4x32_10(ctr, key):
@@ -119,7 +147,7 @@ WORKLOADS = {
                    description="bf16 N=8388608 D=64 K=4096, 10 it, Zipf(1.2) component weights"),
     "c5": Workload("c5", "bf16", 1_000_000_000, 64, 4_096, 3, 4_096, 2.0, 1.0, seed=5,
                    chunk_rows=64 * 2**20,
-                   description="bf16 N=1e9 D=64 K=4096, 3 it, streamed from pinned host memory"),
+                   description="bf16 N=1e9 D=64 K=4096, 3 it, streamed from host memory"),
 }
 
 
@@ -159,6 +187,71 @@ def points(w: Workload, row0: int = 0, nrows: int | None = None, with_components
     comp = np.empty(nrows, dtype=np.int32) if with_components else None
     points_into(w, out.ctypes.data, row0, nrows, comp=comp)
     return (out, comp) if with_components else out
+
+
+class DeviceGenerator:
+    """Rows of a workload generated on a ROCm device (same definition as ``points``).
+
+    ``fill(out, row0)`` writes rows [row0, row0 + len(out)) into the device
+    tensor ``out`` (float32 for "f32", bfloat16 for "bf16") on the current
+    stream of its device.
+    """
+
+    def __init__(self, w: Workload, device):
+        import torch
+        self.w = w
+        self.device = torch.device(device)
+        self.cent = torch.from_numpy(centers(w)).to(self.device)
+        self.cdf = torch.from_numpy(zipf_cdf(w.M, w.zipf_s)).to(self.device) if w.zipf_s > 0 else None
+
+    def fill(self, out, row0: int, comp=None) -> None:
+        import torch
+        w = self.w
+        want = torch.float32 if w.dtype == "f32" else torch.bfloat16
+        if out.device != self.device or out.dtype != want or not out.is_contiguous() or out.shape[-1] != w.D:
+            raise ValueError("out must be a contiguous (rows, D) tensor of the workload's dtype on the device")
+        nrows = out.numel() // w.D
+        if row0 < 0 or row0 + nrows > w.N:
+            raise ValueError("rows out of range")
+        if comp is not None and (comp.dtype != torch.int32 or comp.numel() != nrows or comp.device != self.device):
+            raise ValueError("comp must be an int32 device tensor with one entry per row")
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        rc = _load_gpu().synth_points_device(
+            w.seed, self.cent.data_ptr(), w.M, w.D, w.kind, w.sigma,
+            None if self.cdf is None else self.cdf.data_ptr(), 0 if w.dtype == "f32" else 1,
+            out.data_ptr(), row0, nrows, None if comp is None else comp.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"synth_points_device failed ({rc})")
+
+
+def host_points(w: Workload, device, pinned: bool = False, block_rows: int = 1 << 24, progress=None):
+    """All of X in host memory (torch tensor, pinned or pageable), generated on ``device`` block by block.
+
+    For the out-of-core workload: 10^9 rows are generated in seconds on the GPU
+    and copied down, instead of minutes on the host cores.  ``progress(rows_done)``
+    is called after every block.
+    """
+    import torch
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    Xh = torch.empty((w.N, w.D), dtype=dt, pin_memory=pinned)
+    gen = DeviceGenerator(w, device)
+    buf = torch.empty((min(block_rows, w.N), w.D), dtype=dt, device=gen.device)
+    for r0 in range(0, w.N, block_rows):
+        nr = min(block_rows, w.N - r0)
+        gen.fill(buf[:nr], r0)
+        Xh[r0:r0 + nr].copy_(buf[:nr])
+        if progress is not None:
+            progress(r0 + nr)
+    torch.cuda.synchronize(gen.device)
+    return Xh
+
+
+def as_numpy_rows(Xh) -> np.ndarray:
+    """Stored values of a host torch X as numpy (float32, or uint16 bfloat16 bits), without copying."""
+    import torch
+    if Xh.dtype == torch.bfloat16:
+        return Xh.view(torch.int16).numpy().view(np.uint16)
+    return Xh.numpy()
 
 
 def sample_indices(seed: int, N: int, K: int) -> np.ndarray:

@@ -81,9 +81,10 @@ def test_update_and_fit_validation(L):
     assert f(FAKE, km.KM_F32, 10, 8, 4, FAKE, -1, None, None, None, WS, 1 << 30, None) == 1  # iters < 0
     assert f(FAKE, km.KM_F32, 10, 8, 4, FAKE, 3, None, None, ctypes.c_void_p(0x10004), WS, 1 << 30, None) == 1
     s = L.kmeans_fit_streamed
-    assert s(FAKE, km.KM_BF16, 10, 8, 4, FAKE, 1, 0, None, None, None, WS, 1 << 30, None, FAKE) == 1  # chunk 0
-    assert s(FAKE, km.KM_BF16, 10, 8, 4, FAKE, 1, 4, None, None, None, WS, 1 << 30, None, None) == 1  # no copy stream
-    assert s(FAKE, km.KM_BF16, 10, 8, 4, FAKE, 1, 4, None, None, None, WS, 1 << 30, FAKE, FAKE) == 1  # same streams
+    assert s(FAKE, km.KM_BF16, 10, 8, 4, FAKE, 1, 0, None, None, None, WS, 1 << 30, None, FAKE, None, 0) == 1  # chunk 0
+    assert s(FAKE, km.KM_BF16, 10, 8, 4, FAKE, 1, 4, None, None, None, WS, 1 << 30, None, None, None, 0) == 1  # no copy stream
+    assert s(FAKE, km.KM_BF16, 10, 8, 4, FAKE, 1, 4, None, None, None, WS, 1 << 30, FAKE, FAKE, None, 0) == 1  # same streams
+    assert s(FAKE, km.KM_BF16, 10, 8, 4, FAKE, 1, 4, None, None, None, WS, 1 << 30, None, FAKE, FAKE, 63) == 1  # stage < 4 rows
     srt = L.kmeans_sort_by_cluster
     assert srt(None, 10, 4, FAKE, None, WS, 1 << 30, None) == 1
     assert srt(FAKE, 10, 0, FAKE, None, WS, 1 << 30, None) == 1

@@ -19,7 +19,7 @@ def _workload(name, **kw):
     return w, Xn, C0
 
 
-def _teacher_forced(Xn, xdtype, C0, T, label, streamed_chunk=None):
+def _teacher_forced(Xn, xdtype, C0, T, label, streamed_chunk=None, stage_bytes=None):
     """Run T single iterations on the GPU; check each against the oracle fed the GPU's own state."""
     X = parity.x_from_numpy(Xn, xdtype, DEV)
     C = torch.from_numpy(C0).to(DEV)
@@ -30,8 +30,11 @@ def _teacher_forced(Xn, xdtype, C0, T, label, streamed_chunk=None):
         if streamed_chunk is None:
             C, a, counts, obj = km.fit(X, C, 1, objective=True)
         else:
-            Xh = X.cpu().pin_memory()
-            C, a, counts, obj = km.fit_streamed(Xh, C, 1, streamed_chunk, objective=True)
+            if stage_bytes is None:  # pinned X, direct upload
+                Xh, stage = X.cpu().pin_memory(), None
+            else:  # pageable X through a pinned staging ring
+                Xh, stage = X.cpu(), km.staging_buffer(stage_bytes)
+            C, a, counts, obj = km.fit_streamed(Xh, C, 1, streamed_chunk, objective=True, stage=stage)
         torch.cuda.synchronize()
         an = a.cpu().numpy() if a.is_cuda else a.numpy()
         nm, _ = parity.check_assign(Xn, xdtype, C_prev, an, label=f"{label} it{t}")
@@ -69,6 +72,23 @@ def test_fit_unit_sphere_bf16():
 def test_fit_streamed_matches_oracle(chunk):
     w, Xn, C0 = _workload("c4", N=9000, K=300)
     _teacher_forced(Xn, "bf16", C0, 2, f"streamed chunk={chunk}", streamed_chunk=chunk)
+
+
+@pytest.mark.parametrize("chunk,stage_rows", [(1000, 4 * 37), (4096, 4 * 4096), (100_000, 4 * 333), (7, 4 * 3)])
+def test_fit_streamed_pageable_matches_oracle(chunk, stage_rows):
+    w, Xn, C0 = _workload("c4", N=9000, K=300)
+    _teacher_forced(Xn, "bf16", C0, 2, f"streamed pageable chunk={chunk} stage={stage_rows}",
+                    streamed_chunk=chunk, stage_bytes=stage_rows * w.D * 2 + 5)
+
+
+def test_fit_streamed_pinned_and_pageable_agree():
+    w, Xn, C0 = _workload("c4", N=20000, K=256)
+    X = parity.x_from_numpy(Xn, "bf16", DEV).cpu()
+    C0t = torch.from_numpy(C0).to(DEV)
+    r1 = km.fit_streamed(X.pin_memory(), C0t, 3, 3000)
+    r2 = km.fit_streamed(X, C0t, 3, 3000, stage=km.staging_buffer(4 * 500 * w.D * 2))
+    torch.cuda.synchronize()
+    assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1]) and torch.equal(r1[2], r2[2])
 
 
 def test_fit_resume_and_determinism():
