@@ -171,10 +171,13 @@ km_status kmeans_fit(const void* X, km_dtype dt, int64_t N, int64_t D, int64_t K
  *                KM_ERR_INVALID_VALUE); a few tens of MiB per slot keep the
  *                host link busy.  The number of copying threads is
  *                min(8, cores - 1) + the caller, or KM_STAGE_THREADS.
- * On return all work is enqueued (with staging, the call returns once the
- * last slot has been filled, so it blocks while the upload proceeds).
- * Synchronise compute_stream before reading any output or reusing X_host or
- * the staging buffer.  Calls that share a staging buffer must not overlap.
+ * On return all work is enqueued.  With staging the call blocks while the
+ * upload proceeds and returns once every byte of X has left the staging
+ * buffer, so X_host and the staging buffer are free again on return; without
+ * staging, keep X_host unchanged until compute_stream has been synchronised.
+ * Synchronise compute_stream before reading any output.  Uploads into the
+ * workspace start only after the work enqueued on compute_stream before the
+ * call, so a workspace may be reused in compute-stream order.
  */
 km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_t D, int64_t K, float* C,
                               int32_t iters, int64_t chunk_rows, int32_t* assign_host, int32_t* counts,

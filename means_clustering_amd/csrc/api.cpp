@@ -336,11 +336,13 @@ constexpr int kStageSlots = 4;
 
 // ---------------------------------------------------- launch sequences ----
 
+// perm/prev (optional): the previous iteration's sorted order and sorted keys (warm start).
 static km_status run_assign(const void* X, km_dtype dt, int64_t N, int64_t D, const float* C, int64_t K,
-                            int32_t* assign, float* min_dist, void* frag, hipStream_t s) {
+                            int32_t* assign, float* min_dist, void* frag, hipStream_t s,
+                            const int32_t* perm = nullptr, const int32_t* prev = nullptr) {
   const AssignGeom g = assign_geom(N, D, K, dt);
   KM_TIMED("prep", s, return launch_prep(g, C, frag, s));
-  if (N > 0) KM_TIMED("assign", s, return launch_flash_assign(g, X, N, frag, assign, min_dist, s));
+  if (N > 0) KM_TIMED("assign", s, return launch_flash_assign(g, X, N, frag, assign, min_dist, s, perm, prev));
   return KM_OK;
 }
 
@@ -359,12 +361,17 @@ static km_status run_sort(const int32_t* assign, int64_t N, int64_t K, const Sor
   return KM_OK;
 }
 
+// sorted_keys/sorted_vals (optional out): where the argsort left the sorted
+// assignment and the point order; valid until the workspace is used again.
 static km_status run_update(const void* X, km_dtype dt, int64_t N, int64_t D, const int32_t* assign, int64_t K,
                             const float* C_prev, float* C_new, int32_t* counts, const UpdateBufs& u, int mode,
-                            float* acc_sum, int64_t* acc_cnt, hipStream_t s) {
+                            float* acc_sum, int64_t* acc_cnt, hipStream_t s, const int32_t** sorted_keys = nullptr,
+                            const int32_t** sorted_vals = nullptr) {
   int32_t *keys = nullptr, *vals = nullptr;
   km_status st = run_sort(assign, N, K, u.s, nullptr, &keys, &vals, s);
   if (st != KM_OK) return st;
+  if (sorted_keys) *sorted_keys = keys;
+  if (sorted_vals) *sorted_vals = vals;
   ReduceArgs a;
   a.X = X;
   a.dt = (int)dt;
@@ -474,15 +481,18 @@ km_status kmeans_fit(const void* X, km_dtype dt, int64_t N, int64_t D, int64_t K
   Carve c(ws);
   const FitBufs f = carve_fit(c, N, D, K, dt);
   int32_t* a = assign ? assign : f.assign;
+  // From the second iteration on, the assign visits points in the order of the
+  // previous argsort and starts each from its previous centroid's group.
+  const int32_t *order = nullptr, *prev = nullptr;
   for (int32_t t = 0; t < iters; ++t) {
-    st = run_assign(X, dt, N, D, C, K, a, objective ? f.min_dist : nullptr, f.frag, s);
+    st = run_assign(X, dt, N, D, C, K, a, objective ? f.min_dist : nullptr, f.frag, s, order, prev);
     if (st != KM_OK) return st;
     if (objective) KM_TIMED("objective", s, return launch_objective(f.min_dist, N, f.obj_part, objective + t, 0, s));
     if (N == 0) {
       if (counts) KM_HIP(launch_zero(counts, sizeof(int32_t) * (size_t)K, s));
       continue;
     }
-    st = run_update(X, dt, N, D, a, K, C, C, counts, f.u, MODE_MEAN, nullptr, nullptr, s);
+    st = run_update(X, dt, N, D, a, K, C, C, counts, f.u, MODE_MEAN, nullptr, nullptr, s, &prev, &order);
     if (st != KM_OK) return st;
   }
   return KM_OK;
@@ -528,11 +538,16 @@ km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_
       for (hipEvent_t e : ev) (void)hipEventDestroy(e);
     }
   } guard{events};
-  hipEvent_t ready[2], freed[2], slot_done[kStageSlots];
-  for (hipEvent_t* e : {&ready[0], &ready[1], &freed[0], &freed[1]}) {
+  hipEvent_t ready[2], freed[2], slot_done[kStageSlots], start;
+  for (hipEvent_t* e : {&ready[0], &ready[1], &freed[0], &freed[1], &start}) {
     KM_HIP(hipEventCreateWithFlags(e, hipEventDisableTiming));
     events.push_back(*e);
   }
+  // The chunk buffers live in the workspace, which earlier work on the compute
+  // stream may still be using (a previous call, or memory the caller's
+  // allocator recycled in compute-stream order): uploads start after it.
+  KM_HIP(hipEventRecord(start, cs));
+  KM_HIP(hipStreamWaitEvent(xs, start, 0));
   if (stage_host)
     for (int i = 0; i < kStageSlots; ++i) {
       KM_HIP(hipEventCreateWithFlags(&slot_done[i], hipEventDisableTiming));
@@ -591,6 +606,10 @@ km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_
     }
     KM_TIMED("finalize", cs, return launch_finalize_accum(b.acc_sum, b.acc_cnt, K, D, C, counts, cs));
   }
+  // With staging, return only once the last uploads have left the slots, so
+  // the staging buffer (and pageable X) can be reused as soon as this returns.
+  if (stage_host)
+    for (uint64_t i = 0; i < slot_seq && i < (uint64_t)kStageSlots; ++i) KM_HIP(hipEventSynchronize(slot_done[i]));
   return KM_OK;
 }
 

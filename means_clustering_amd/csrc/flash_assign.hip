@@ -14,7 +14,7 @@
 // matrix cores produce the score directly; only the running max/argmax costs
 // vector ALU work.  The optional distance output adds ||x||^2 back.
 //
-// Precision: 16-bit X runs on v_mfma_f32_16x16x32_{bf16,f16} (fp32
+// Precision: 16-bit X runs on v_mfma_f32_32x32x16_{bf16,f16} (fp32
 // accumulation); the fp32 centroid state is rounded to X's type once per call
 // (round to nearest, ties to even) and ||c||^2 is taken from the rounded
 // values, so every candidate is scored against exactly the centroid the
@@ -28,13 +28,22 @@
 //   * a wavefront owns NB point groups and keeps their operand fragments in
 //     VGPRs for the whole centroid sweep (X is read from HBM exactly once);
 //   * centroids stream through LDS in tiles of CT groups, double-buffered:
-//     tile t+1 is fetched from L2/HBM into registers while tile t feeds the
-//     matrix cores, then stored to the other LDS buffer (one barrier a tile);
+//     tile t+1 is copied from L2/HBM straight into the other LDS buffer
+//     (global_load_lds, no registers) while tile t feeds the matrix cores
+//     (one barrier a tile); fp32 X stages tiles through registers;
 //   * the accumulator of each MFMA chain starts at the centroid's bias, so
 //     the matrix cores deliver the score and the vector ALUs only keep the
 //     running (best score, selector) per lane in registers;
 //   * the lanes that hold the same point merge once at the end (ties go to
-//     the lowest centroid index).
+//     the lowest centroid index);
+//   * warm start: inside a Lloyd loop the previous iteration's argsort says
+//     which centroid each point had.  Points are then taken in that sorted
+//     order, so the 32 points of a block mostly share their previous
+//     centroid; the block first scores the group of 32 centroids holding it
+//     (exact MFMA values), which gives every point a score its final best
+//     must reach, and the sweep then needs only the group maxima, scanning a
+//     group exactly when some lane's maximum beats the lane's running best.
+//     The result is the same argmax as the full scan, bit for bit.
 #include <math.h>
 
 #include "km_internal.hpp"
@@ -207,6 +216,13 @@ __device__ __forceinline__ f32x16_t mma32(u32x4_t a, u32x4_t b, f32x16_t c) {
 // E is an inline constant, so no selector has to be copied into a vector
 // register.  `rel` counts from the base of the group being scanned (callers
 // rebase it by -16 per group).  A NaN score never wins ("not greater than").
+//
+// The compiler's hazard checker does not look inside inline asm, so an asm
+// instruction must never be the first reader of a fresh MFMA result (the
+// hardware does not wait for the matrix core there).  Every accumulator is
+// therefore first read by compiled code (argmax_update_c, fold_first, which
+// the compiler spaces correctly after the MFMA), and every asm read of it
+// depends on that code's result, so it comes later still.
 template <int E>
 __device__ __forceinline__ void argmax_update(float v, float& best, int& rel) {
   asm("v_cmp_ngt_f32 vcc, %2, %0\n\t"
@@ -215,6 +231,14 @@ __device__ __forceinline__ void argmax_update(float v, float& best, int& rel) {
       : "+v"(best), "+v"(rel)
       : "v"(v), "I"(E)
       : "vcc");
+}
+
+// The same update in compiled code (the first read of an accumulator).
+template <int E>
+__device__ __forceinline__ void argmax_update_c(float v, float& best, int& rel) {
+  const bool gt = v > best;
+  best = gt ? v : best;
+  rel = gt ? E : rel;
 }
 
 template <int E, int NB>
@@ -232,6 +256,15 @@ __device__ __forceinline__ void argmax_range(const f32x16_t (&in)[NB], float (&b
   }
 }
 
+// Elements [0, E1) of a group whose scores have not been read yet: the first
+// in compiled code, the rest in asm.
+template <int E1, int NB>
+__device__ __forceinline__ void argmax_range_first(const f32x16_t (&in)[NB], float (&best)[NB], int (&rel)[NB]) {
+#pragma unroll
+  for (int g = 0; g < NB; ++g) argmax_update_c<0>(in[g][0], best[g], rel[g]);
+  argmax_range<1, E1, NB>(in, best, rel);
+}
+
 __device__ __forceinline__ f32x16_t bias_of(const u32x4_t* bp) {
   const u32x4_t b0 = bp[0], b1 = bp[1], b2 = bp[2], b3 = bp[3];
   return f32x16_t{__uint_as_float(b0.x), __uint_as_float(b0.y), __uint_as_float(b0.z), __uint_as_float(b0.w),
@@ -244,6 +277,14 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
+}
+
+// The largest float strictly below v (-inf for -inf and NaN).
+__device__ __forceinline__ float float_below(float v) {
+  if (!(v > -INFINITY)) return -INFINITY;
+  if (v == 0.0f) return -__uint_as_float(1u);
+  const uint32_t u = __float_as_uint(v);
+  return __uint_as_float(v > 0.0f ? u - 1u : u + 1u);
 }
 
 // Lazy running argmax, fast part: fold a share of the previous group's 16
@@ -261,6 +302,14 @@ __device__ __forceinline__ void fold_range(const f32x16_t (&in)[NB], float (&m)[
       fold_range<E0 + 1, E1, NB>(in, m);
     }
   }
+}
+
+// Start of a fold over a group whose scores have not been read yet (compiled
+// code; a NaN score is ignored like v_max3_f32 ignores it).
+template <int NB>
+__device__ __forceinline__ void fold_first(const f32x16_t (&in)[NB], float (&m)[NB]) {
+#pragma unroll
+  for (int g = 0; g < NB; ++g) m[g] = fmaxf(in[g][0], in[g][1]);
 }
 
 // Lazy running argmax, slow part: only when some lane's group maximum beats
@@ -286,10 +335,19 @@ template <int KB, int NB, int KBI, bool LAZY>
 __device__ __forceinline__ void epilogue_share(const f32x16_t (&in)[NB], float (&best)[NB], int (&rel)[NB],
                                                float (&m)[NB]) {
   constexpr int per = (16 + KB - 1) / KB;  // epilogue elements per depth block
-  if constexpr (LAZY)
-    fold_range<KBI * per, (KBI + 1) * per, NB>(in, m);
-  else
-    argmax_range<KBI * per, (KBI + 1) * per, NB>(in, best, rel);
+  if constexpr (LAZY) {
+    if constexpr (KBI == 0) {  // elements 0 and 1 (and the rest of the share) of a fresh group
+      fold_first<NB>(in, m);
+      fold_range<2, per, NB>(in, m);
+    } else {
+      fold_range<(KBI * per > 2 ? KBI * per : 2), (KBI + 1) * per, NB>(in, m);
+    }
+  } else {
+    if constexpr (KBI == 0)
+      argmax_range_first<per, NB>(in, best, rel);
+    else
+      argmax_range<KBI * per, (KBI + 1) * per, NB>(in, best, rel);
+  }
 }
 
 template <int DT, int KB, int NB, bool LAZY, bool epi, int KBI = 0>
@@ -303,10 +361,7 @@ __device__ __forceinline__ void pipeline_steps(const u32x4_t* __restrict__ grp, 
     if constexpr (epi) {
       if constexpr (KBI == 0) {
 #pragma unroll
-        for (int g = 0; g < NB; ++g) {
-          rel[g] -= 16;  // selectors now count from this group's base
-          m[g] = -INFINITY;
-        }
+        for (int g = 0; g < NB; ++g) rel[g] -= 16;  // selectors now count from this group's base
       }
       epilogue_share<KB, NB, KBI, LAZY>(in, best, rel, m);
     }
@@ -339,19 +394,23 @@ template <int NB>
 __device__ __forceinline__ void drain_epilogue(const f32x16_t (&in)[NB], float (&best)[NB], int (&rel)[NB]) {
 #pragma unroll
   for (int g = 0; g < NB; ++g) rel[g] -= 16;
-  argmax_range<0, 16, NB>(in, best, rel);
+  argmax_range_first<16, NB>(in, best, rel);
 }
 
-template <int DT, int KB, bool LAZY>
+// WARM: points are visited in the order perm[0..N) and prev[i] is the
+// previous centroid of point perm[i] (both from the previous iteration's
+// argsort); the sweep starts from a bound taken from that centroid's group.
+template <int DT, int KB, bool LAZY, bool WARM>
 __global__ __launch_bounds__(wide_cfg(KB).W * 64) void flash_assign_wide_kernel(
     const uint8_t* __restrict__ X, int64_t N, int D, bool vec_ok, const u32x4_t* __restrict__ frag, int ntiles,
-    int32_t* __restrict__ assign, float* __restrict__ min_dist) {
+    int32_t* __restrict__ assign, float* __restrict__ min_dist, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ prev, int64_t K) {
   constexpr AssignCfg cfg = wide_cfg(KB);
   constexpr int NB = cfg.NB, CT = cfg.CT, W = cfg.W;
   constexpr int GS = (int)cfg.group_slots();
   constexpr int TS = (int)cfg.tile_slots();
   constexpr int NTHR = W * 64;
-  constexpr int CPT = TS / NTHR;
+  constexpr bool FOLD = LAZY || WARM;
   static_assert(TS % NTHR == 0 && TS >= CT * GS, "tile padding");
   static_assert(CT % 2 == 0, "groups alternate between two accumulator sets");
   __shared__ u32x4_t lds[2][TS];
@@ -362,16 +421,26 @@ __global__ __launch_bounds__(wide_cfg(KB).W * 64) void flash_assign_wide_kernel(
   const int h = lane >> 5;
   const int64_t wbase = ((int64_t)blockIdx.x * W + wave) * (NB * 32);
 
+  // the point each lane scores, per point group (its row of X, or N past the end)
+  int64_t pt[NB];
+#pragma unroll
+  for (int g = 0; g < NB; ++g) {
+    const int64_t slot = wbase + g * 32 + col;
+    if constexpr (WARM)
+      pt[g] = slot < N ? (int64_t)perm[slot] : N;
+    else
+      pt[g] = slot;
+  }
+
   // Point fragments: read once from HBM, kept in VGPRs for the whole sweep.
   u32x4_t xb[NB][KB];
   float xn[NB];
 #pragma unroll
   for (int g = 0; g < NB; ++g) {
-    const int64_t p = wbase + g * 32 + col;
     float s = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      xb[g][kb] = load_point_frag<2>(X, p, N, D, kb * kFragDepth + h * 8, vec_ok);
+      xb[g][kb] = load_point_frag<2>(X, pt[g], N, D, kb * kFragDepth + h * 8, vec_ok);
       s += sumsq16<DT>(xb[g][kb]);
     }
     s += __shfl_xor(s, 32);
@@ -387,6 +456,30 @@ __global__ __launch_bounds__(wide_cfg(KB).W * 64) void flash_assign_wide_kernel(
   for (int g = 0; g < NB; ++g) {
     best[g] = -INFINITY;
     rel[g] = -(1 << 30);
+  }
+
+  if constexpr (WARM) {
+    // Score the block against the group of its first point's previous
+    // centroid.  The best of those 32 exact scores is reached by the final
+    // answer, so the running best starts just below it: a group can then
+    // hold the answer only if its maximum exceeds the running best, and the
+    // group that supplied the bound is itself scanned exactly in its turn.
+#pragma unroll
+    for (int g = 0; g < NB; ++g) {
+      const int64_t s0 = wbase + g * 32 < N ? wbase + g * 32 : N - 1;
+      int64_t k0 = prev[s0];
+      k0 = k0 < 0 ? 0 : (k0 >= K ? K - 1 : k0);
+      const int64_t q0 = k0 >> 5;
+      const u32x4_t* grp = frag + (q0 / CT) * TS + (q0 % CT) * GS;
+      f32x16_t sc = bias_of(grp + KB * 64 + h * 4);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) sc = mma32<DT>(grp[kb * 64 + lane], xb[g][kb], sc);
+      float mx = fmaxf(sc[0], sc[1]);  // compiled code: the compiler waits for the MFMA results
+#pragma unroll
+      for (int e = 2; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      best[g] = float_below(mx);
+    }
   }
 
   // tile 0 into LDS
@@ -409,12 +502,12 @@ __global__ __launch_bounds__(wide_cfg(KB).W * 64) void flash_assign_wide_kernel(
       const u32x4_t a00 = g0[lane];
       const f32x16_t bias0 = bias_of(g0 + KB * 64 + h * 4);
       if (c == 0 && t == 0)
-        pipeline_steps<DT, KB, NB, LAZY, false>(g0, lane, a00, bias0, xb, acc0, acc1, best, rel, m);
+        pipeline_steps<DT, KB, NB, FOLD, false>(g0, lane, a00, bias0, xb, acc0, acc1, best, rel, m);
       else
-        pipeline_steps<DT, KB, NB, LAZY, true>(g0, lane, a00, bias0, xb, acc0, acc1, best, rel, m);
+        pipeline_steps<DT, KB, NB, FOLD, true>(g0, lane, a00, bias0, xb, acc0, acc1, best, rel, m);
       const u32x4_t a10 = g1[lane];
       const f32x16_t bias1 = bias_of(g1 + KB * 64 + h * 4);
-      pipeline_steps<DT, KB, NB, LAZY, true>(g1, lane, a10, bias1, xb, acc1, acc0, best, rel, m);
+      pipeline_steps<DT, KB, NB, FOLD, true>(g1, lane, a10, bias1, xb, acc1, acc0, best, rel, m);
     }
     if (t + 1 < ntiles) {
       __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the next tile has landed
@@ -428,7 +521,8 @@ __global__ __launch_bounds__(wide_cfg(KB).W * 64) void flash_assign_wide_kernel(
   for (int g = 0; g < NB; ++g) {
     float b = best[g];
     const int sg = last_base + rel[g];
-    int k = b == -INFINITY ? INT32_MAX : (sg >> 4) * 32 + ((sg & 15) >> 2) * 8 + h * 4 + (sg & 3);
+    const bool none = b == -INFINITY || rel[g] <= -(1 << 30);  // nothing selected (NaN scores)
+    int k = none ? INT32_MAX : (sg >> 4) * 32 + ((sg & 15) >> 2) * 8 + h * 4 + (sg & 3);
     const float ob = __shfl_xor(b, 32);
     const int ok = __shfl_xor(k, 32);
     if (ob > b || (ob == b && ok < k)) {
@@ -436,7 +530,7 @@ __global__ __launch_bounds__(wide_cfg(KB).W * 64) void flash_assign_wide_kernel(
       k = ok;
     }
     if (k == INT32_MAX) k = 0;  // no finite score (NaN input): index 0
-    const int64_t p = wbase + g * 32 + col;
+    const int64_t p = pt[g];
     if (h == 0 && p < N) {
       assign[p] = k;
       if (min_dist) min_dist[p] = fmaxf(xn[g] - 2.0f * b, 0.0f);
@@ -579,17 +673,23 @@ __global__ __launch_bounds__(narrow_cfg(KB).W * 64) void flash_assign_narrow_ker
 
 template <int DT, int KB>
 static hipError_t launch_wide(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
-                              float* min_dist, hipStream_t s) {
+                              float* min_dist, const int32_t* perm, const int32_t* prev, hipStream_t s) {
   constexpr AssignCfg cfg = wide_cfg(KB);
   const int64_t pts = (int64_t)cfg.W * cfg.NB * 32;
   const bool vec_ok = (((uintptr_t)X) % 16 == 0) && ((g.D * 2) % 16 == 0);
   const dim3 grid((unsigned)((N + pts - 1) / pts)), block(cfg.W * 64);
-  if (g.lazy)
-    hipLaunchKernelGGL((flash_assign_wide_kernel<DT, KB, true>), grid, block, 0, s, (const uint8_t*)X, N, (int)g.D,
-                       vec_ok, (const u32x4_t*)frag, (int)g.ntiles(), assign, min_dist);
+  const uint8_t* x = (const uint8_t*)X;
+  const u32x4_t* f = (const u32x4_t*)frag;
+  const int nt = (int)g.ntiles();
+  if (perm)
+    hipLaunchKernelGGL((flash_assign_wide_kernel<DT, KB, true, true>), grid, block, 0, s, x, N, (int)g.D, vec_ok, f,
+                       nt, assign, min_dist, perm, prev, g.K);
+  else if (g.lazy)
+    hipLaunchKernelGGL((flash_assign_wide_kernel<DT, KB, true, false>), grid, block, 0, s, x, N, (int)g.D, vec_ok, f,
+                       nt, assign, min_dist, perm, prev, g.K);
   else
-    hipLaunchKernelGGL((flash_assign_wide_kernel<DT, KB, false>), grid, block, 0, s, (const uint8_t*)X, N,
-                       (int)g.D, vec_ok, (const u32x4_t*)frag, (int)g.ntiles(), assign, min_dist);
+    hipLaunchKernelGGL((flash_assign_wide_kernel<DT, KB, false, false>), grid, block, 0, s, x, N, (int)g.D, vec_ok,
+                       f, nt, assign, min_dist, perm, prev, g.K);
   return hipGetLastError();
 }
 
@@ -607,10 +707,10 @@ static hipError_t launch_narrow(const AssignGeom& g, const void* X, int64_t N, c
 
 template <int DT>
 static hipError_t dispatch_wide(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
-                                float* min_dist, hipStream_t s) {
+                                float* min_dist, const int32_t* perm, const int32_t* prev, hipStream_t s) {
   switch (g.cfg.KB) {
 #define KM_CASE(n) \
-  case n: return launch_wide<DT, n>(g, X, N, frag, assign, min_dist, s);
+  case n: return launch_wide<DT, n>(g, X, N, frag, assign, min_dist, perm, prev, s);
     KM_CASE(1) KM_CASE(2) KM_CASE(3) KM_CASE(4) KM_CASE(5) KM_CASE(6) KM_CASE(7) KM_CASE(8)
     KM_CASE(10) KM_CASE(12) KM_CASE(14) KM_CASE(16) KM_CASE(20) KM_CASE(24) KM_CASE(28) KM_CASE(32)
 #undef KM_CASE
@@ -619,11 +719,12 @@ static hipError_t dispatch_wide(const AssignGeom& g, const void* X, int64_t N, c
 }
 
 hipError_t launch_flash_assign(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
-                               float* min_dist, hipStream_t stream) {
+                               float* min_dist, hipStream_t stream, const int32_t* perm, const int32_t* prev) {
   if (N == 0) return hipSuccess;
+  if ((perm == nullptr) != (prev == nullptr)) return hipErrorInvalidValue;
   switch (g.dt) {
-    case DT_BF16: return dispatch_wide<DT_BF16>(g, X, N, frag, assign, min_dist, stream);
-    case DT_F16: return dispatch_wide<DT_F16>(g, X, N, frag, assign, min_dist, stream);
+    case DT_BF16: return dispatch_wide<DT_BF16>(g, X, N, frag, assign, min_dist, perm, prev, stream);
+    case DT_F16: return dispatch_wide<DT_F16>(g, X, N, frag, assign, min_dist, perm, prev, stream);
     case DT_F32:
       switch (g.cfg.KB) {
 #define KM_CASE(n) \

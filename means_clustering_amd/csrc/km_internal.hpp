@@ -142,8 +142,13 @@ struct SortGeom {
 // ---------------------------------------------------------------------------
 hipError_t launch_prep(const AssignGeom& g, const float* C, void* frag, hipStream_t stream);
 
+// perm/prev (both or neither): visit points in the order perm[0..N), where
+// prev[i] is the previous centroid of point perm[i]; the result is the same,
+// only faster when the assignment changes little (16-bit X only; ignored for
+// fp32 X).
 hipError_t launch_flash_assign(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
-                               float* min_dist, hipStream_t stream);
+                               float* min_dist, hipStream_t stream, const int32_t* perm = nullptr,
+                               const int32_t* prev = nullptr);
 
 // Radix argsort of cluster ids.  keys_in: the assignment vector.  The passes
 // ping-pong through (key_a, val_a) and (key_b, val_b); the last pass writes
