@@ -538,6 +538,144 @@ __global__ __launch_bounds__(wide_cfg(KB).W * 64) void flash_assign_wide_kernel(
   }
 }
 
+// Single-accumulator variant for long sweeps (D <= 128; layout in wide8_cfg).
+// Per group of 32 centroids a wavefront loads the group's bias straight into
+// its accumulators, runs the KB-step MFMA chain for all of its point groups,
+// then updates the running argmax from those accumulators while the other
+// wavefront on the SIMD keeps the matrix cores busy.
+template <int DT, int KB, bool LAZY, bool WARM>
+__global__ __launch_bounds__(wide8_cfg(KB).W * 64) __attribute__((amdgpu_waves_per_eu(KM_W8_WPE))) void flash_assign_w8_kernel(
+    const uint8_t* __restrict__ X, int64_t N, int D, bool vec_ok, const u32x4_t* __restrict__ frag, int ntiles,
+    int32_t* __restrict__ assign, float* __restrict__ min_dist, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ prev, int64_t K) {
+  constexpr AssignCfg cfg = wide8_cfg(KB);
+  constexpr int NB = cfg.NB, CT = cfg.CT, W = cfg.W;
+  constexpr int GS = (int)cfg.group_slots();
+  constexpr int TS = (int)cfg.tile_slots();
+  constexpr int NTHR = W * 64;
+  constexpr bool FOLD = LAZY || WARM;
+  static_assert(TS % NTHR == 0 && TS >= CT * GS, "tile padding");
+  __shared__ u32x4_t lds[2][TS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 31;
+  const int h = lane >> 5;
+  const int64_t wbase = ((int64_t)blockIdx.x * W + wave) * (NB * 32);
+
+  // the point each lane scores (its row of X, or N past the end); looked up
+  // again at the end rather than kept live through the sweep
+  auto point_of = [&](int g) -> int64_t {
+    const int64_t slot = wbase + g * 32 + col;
+    if constexpr (WARM)
+      return slot < N ? (int64_t)perm[slot] : N;
+    else
+      return slot;
+  };
+
+  u32x4_t xb[NB][KB];
+#pragma unroll
+  for (int g = 0; g < NB; ++g) {
+    const int64_t p = point_of(g);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) xb[g][kb] = load_point_frag<2>(X, p, N, D, kb * kFragDepth + h * 8, vec_ok);
+  }
+
+  float best[NB];
+  int rel[NB];
+#pragma unroll
+  for (int g = 0; g < NB; ++g) {
+    best[g] = -INFINITY;
+    rel[g] = -(1 << 30);
+  }
+
+  if constexpr (WARM) {
+    // bound from the group of the block's first point's previous centroid (see the four-wavefront kernel)
+#pragma unroll
+    for (int g = 0; g < NB; ++g) {
+      const int64_t s0 = wbase + g * 32 < N ? wbase + g * 32 : N - 1;
+      int64_t k0 = prev[s0];
+      k0 = k0 < 0 ? 0 : (k0 >= K ? K - 1 : k0);
+      const int64_t q0 = k0 >> 5;
+      const u32x4_t* grp = frag + (q0 / CT) * TS + (q0 % CT) * GS;
+      f32x16_t sc = bias_of(grp + KB * 64 + h * 4);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) sc = mma32<DT>(grp[kb * 64 + lane], xb[g][kb], sc);
+      float mx = fmaxf(sc[0], sc[1]);
+#pragma unroll
+      for (int e = 2; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      best[g] = float_below(mx);
+    }
+  }
+
+  tile_dma<TS, NTHR>(frag, &lds[0][0], wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  f32x16_t acc[NB];
+  for (int t = 0; t < ntiles; ++t) {
+    const u32x4_t* tile = &lds[t & 1][0];
+    if (t + 1 < ntiles) tile_dma<TS, NTHR>(frag + (size_t)(t + 1) * TS, &lds[(t + 1) & 1][0], wave, lane);
+#pragma unroll 2
+    for (int c = 0; c < CT; ++c) {
+      const u32x4_t* grp = tile + c * GS;
+#pragma unroll
+      for (int g = 0; g < NB; ++g) acc[g] = bias_of(grp + KB * 64 + h * 4);
+      u32x4_t a = grp[lane];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        u32x4_t an;
+        if (kb + 1 < KB) an = grp[(kb + 1) * 64 + lane];
+#pragma unroll
+        for (int g = 0; g < NB; ++g) acc[g] = mma32<DT>(a, xb[g][kb], acc[g]);
+        if (kb + 1 < KB) a = an;
+      }
+#pragma unroll
+      for (int g = 0; g < NB; ++g) rel[g] -= 16;  // selectors now count from this group's base
+      if constexpr (FOLD) {
+        float m[NB];
+        fold_first<NB>(acc, m);
+        fold_range<2, 16, NB>(acc, m);
+        lazy_resolve<NB>(acc, m, best, rel);
+      } else {
+        argmax_range_first<16, NB>(acc, best, rel);
+      }
+    }
+    if (t + 1 < ntiles) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  }
+
+  const int last_base = (ntiles * CT - 1) * 16;
+#pragma unroll
+  for (int g = 0; g < NB; ++g) {
+    float b = best[g];
+    const int sg = last_base + rel[g];
+    const bool none = b == -INFINITY || rel[g] <= -(1 << 30);
+    int k = none ? INT32_MAX : (sg >> 4) * 32 + ((sg & 15) >> 2) * 8 + h * 4 + (sg & 3);
+    const float ob = __shfl_xor(b, 32);
+    const int ok = __shfl_xor(k, 32);
+    if (ob > b || (ob == b && ok < k)) {
+      b = ob;
+      k = ok;
+    }
+    if (k == INT32_MAX) k = 0;
+    float xn = 0.0f;
+    if (min_dist) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) xn += sumsq16<DT>(xb[g][kb]);
+      xn += __shfl_xor(xn, 32);
+    }
+    const int64_t p = point_of(g);
+    if (h == 0 && p < N) {
+      assign[p] = k;
+      if (min_dist) min_dist[p] = fmaxf(xn - 2.0f * b, 0.0f);
+    }
+  }
+}
+
 // --------------------------------------------------- FlashAssign, fp32 X ----
 //
 // MFMA 16x16x4 f32 layout: lane l supplies A row (l % 16) and B column
@@ -671,10 +809,43 @@ __global__ __launch_bounds__(narrow_cfg(KB).W * 64) void flash_assign_narrow_ker
 
 // --------------------------------------------------------------- launch ----
 
+static bool same_cfg(const AssignCfg& a, const AssignCfg& b) {
+  return a.rows == b.rows && a.KB == b.KB && a.NB == b.NB && a.CT == b.CT && a.W == b.W;
+}
+
+template <int DT, int KB>
+static hipError_t launch_wide8(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
+                               float* min_dist, const int32_t* perm, const int32_t* prev, hipStream_t s) {
+  constexpr AssignCfg cfg = wide8_cfg(KB);
+  if (!same_cfg(g.cfg, cfg)) return hipErrorInvalidValue;
+  const int64_t pts = (int64_t)cfg.W * cfg.NB * 32;
+  const bool vec_ok = (((uintptr_t)X) % 16 == 0) && ((g.D * 2) % 16 == 0);
+  const dim3 grid((unsigned)((N + pts - 1) / pts)), block(cfg.W * 64);
+  const uint8_t* x = (const uint8_t*)X;
+  const u32x4_t* f = (const u32x4_t*)frag;
+  const int nt = (int)g.ntiles();
+  if (perm)
+    hipLaunchKernelGGL((flash_assign_w8_kernel<DT, KB, true, true>), grid, block, 0, s, x, N, (int)g.D, vec_ok, f,
+                       nt, assign, min_dist, perm, prev, g.K);
+  else if (g.lazy)
+    hipLaunchKernelGGL((flash_assign_w8_kernel<DT, KB, true, false>), grid, block, 0, s, x, N, (int)g.D, vec_ok, f,
+                       nt, assign, min_dist, perm, prev, g.K);
+  else
+    hipLaunchKernelGGL((flash_assign_w8_kernel<DT, KB, false, false>), grid, block, 0, s, x, N, (int)g.D, vec_ok,
+                       f, nt, assign, min_dist, perm, prev, g.K);
+  return hipGetLastError();
+}
+
 template <int DT, int KB>
 static hipError_t launch_wide(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
                               float* min_dist, const int32_t* perm, const int32_t* prev, hipStream_t s) {
+  if constexpr (KB <= kWide8MaxKB) {
+    if (same_cfg(g.cfg, wide8_cfg(KB))) return launch_wide8<DT, KB>(g, X, N, frag, assign, min_dist, perm, prev, s);
+  }
   constexpr AssignCfg cfg = wide_cfg(KB);
+  // The centroid fragments were laid out with the caller's geometry: it must be
+  // the one this kernel was compiled for (both come from one header).
+  if (!same_cfg(g.cfg, cfg)) return hipErrorInvalidValue;
   const int64_t pts = (int64_t)cfg.W * cfg.NB * 32;
   const bool vec_ok = (((uintptr_t)X) % 16 == 0) && ((g.D * 2) % 16 == 0);
   const dim3 grid((unsigned)((N + pts - 1) / pts)), block(cfg.W * 64);
@@ -697,6 +868,7 @@ template <int KB>
 static hipError_t launch_narrow(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
                                 float* min_dist, hipStream_t s) {
   constexpr AssignCfg cfg = narrow_cfg(KB);
+  if (!same_cfg(g.cfg, cfg)) return hipErrorInvalidValue;
   const int64_t pts = (int64_t)cfg.W * cfg.NB * 16;
   const bool vec_ok = (((uintptr_t)X) % 16 == 0) && ((g.D * 4) % 16 == 0);
   hipLaunchKernelGGL((flash_assign_narrow_kernel<KB>), dim3((unsigned)((N + pts - 1) / pts)), dim3(cfg.W * 64), 0, s,

@@ -64,11 +64,46 @@ constexpr int kWideKB[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16, 20, 24, 28, 3
 #define KM_WIDE_W 4         // wavefronts per workgroup
 #endif
 #ifndef KM_WIDE_CT
-#define KM_WIDE_CT 2        // centroid groups per LDS tile for 64 < D <= 256 (even)
+#define KM_WIDE_CT 2        // centroid groups per LDS tile for 64 < D <= 256 (even, divides 4)
+#endif
+#ifndef KM_WIDE_CT_SMALL
+#define KM_WIDE_CT_SMALL 4  // ... for D <= 64
 #endif
 constexpr AssignCfg wide_cfg(int KB) {
   return AssignCfg{32, KB, KB <= 4 ? KM_WIDE_NB_SMALL : (KB <= 8 ? KM_WIDE_NB_MID : (KB <= 16 ? 2 : 1)),
-                   KB <= 4 ? 4 : (KB <= 16 ? KM_WIDE_CT : 2), KM_WIDE_W};
+                   KB <= 4 ? KM_WIDE_CT_SMALL : (KB <= 16 ? KM_WIDE_CT : 2), KM_WIDE_W};
+}
+// Single-accumulator layout for long centroid sweeps (D <= 128, at least 256
+// groups of 32): four point groups per wavefront (each centroid fragment read
+// from LDS feeds four MFMAs), two wavefronts per SIMD, tiles of 4 (D <= 128)
+// or 8 (D <= 64) groups.  On gfx950 the matrix cores sustain more with fewer
+// wavefronts holding more independent accumulators than with many wavefronts
+// interleaving single chains; for short sweeps the pipelined four-wavefront
+// kernel measured as fast or faster.
+#ifndef KM_WIDE8
+#define KM_WIDE8 1  // 0: always use the four-wavefront layout (for comparisons)
+#endif
+#ifndef KM_W8_NB
+#define KM_W8_NB 4         // point groups per wavefront (64 < D <= 128)
+#endif
+#ifndef KM_W8_NB_SMALL
+#define KM_W8_NB_SMALL 4   // ... (D <= 64)
+#endif
+#ifndef KM_W8_CT
+#define KM_W8_CT 4         // groups per tile (64 < D <= 128)
+#endif
+#ifndef KM_W8_CT_SMALL
+#define KM_W8_CT_SMALL 8   // ... (D <= 64)
+#endif
+#ifndef KM_W8_W
+#define KM_W8_W 4          // wavefronts per workgroup
+#endif
+#ifndef KM_W8_WPE
+#define KM_W8_WPE 2        // wavefronts per SIMD the register budget is sized for
+#endif
+constexpr int kWide8MaxKB = KM_WIDE8 ? 8 : 0;
+constexpr AssignCfg wide8_cfg(int KB) {
+  return AssignCfg{32, KB, KB <= 4 ? KM_W8_NB_SMALL : KM_W8_NB, KB <= 4 ? KM_W8_CT_SMALL : KM_W8_CT, KM_W8_W};
 }
 constexpr AssignCfg narrow_cfg(int KB) {
   return AssignCfg{16, KB, KB <= 4 ? 4 : (KB <= 8 ? 2 : 1), KB <= 2 ? 8 : (KB <= 4 ? 4 : (KB <= 8 ? 2 : 1)), 4};
@@ -85,7 +120,7 @@ inline int64_t pad_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 struct AssignGeom {
   int dt;
   int64_t N, D, K;
-  int64_t Kpad;    // K rounded up to kPadK
+  int64_t Kpad;    // K rounded up to a whole number of tiles (at least kPadK)
   AssignCfg cfg;
   bool lazy;       // argmax by group maxima first (pays off when the centroid sweep is long)
   int64_t groups() const { return Kpad / cfg.rows; }
@@ -100,10 +135,18 @@ inline AssignGeom make_assign_geom(int64_t N, int64_t D, int64_t K, int dt) {
   g.D = D;
   g.K = K;
   g.Kpad = pad_up(K, kPadK);
-  if (dt == DT_F32)
+  if (dt == DT_F32) {
     g.cfg = narrow_cfg((int)((D + kFragDepth - 1) / kFragDepth));
-  else
-    g.cfg = wide_cfg(wide_kb(D));
+  } else {
+    const int kb = wide_kb(D);
+    const AssignCfg c8 = wide8_cfg(kb);
+    if (kb <= kWide8MaxKB && pad_up(K, kPadK) / 32 >= 256 && K >= 2 * (int64_t)c8.rows * c8.CT) {
+      g.cfg = c8;
+      g.Kpad = pad_up(K, (int64_t)c8.rows * c8.CT);
+    } else {
+      g.cfg = wide_cfg(kb);
+    }
+  }
   // A group whose maximum does not beat a lane's running best costs one max3
   // per two scores instead of a full compare-and-select; with many groups such
   // groups dominate (measured on gfx950: better from about 256 groups of 32).

@@ -51,6 +51,19 @@ def test_assign_random(shape, xdtype):
     _run(X, C, f"random {shape} {xdtype}")
 
 
+# long centroid sweeps (>= 256 groups of 32) take the single-accumulator kernel for D <= 128
+LONG_SHAPES = [(1500, 16, 8192), (1100, 40, 8200), (900, 64, 9000), (700, 100, 8300), (600, 128, 8192),
+               (300, 200, 8192)]
+
+
+@pytest.mark.parametrize("xdtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", LONG_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_assign_long_sweep(shape, xdtype):
+    N, D, K = shape
+    X, C = _data(N, D, K, xdtype, seed=N * 17 + D * 3 + K)
+    _run(X, C, f"long sweep {shape} {xdtype}")
+
+
 @pytest.mark.parametrize("xdtype", ["bf16", "f32"])
 def test_assign_exact_ties(xdtype):
     # centroids on a coarse grid, points on a finer grid: many exactly equal distances,

@@ -68,6 +68,19 @@ def test_fit_unit_sphere_bf16():
     _teacher_forced(Xn, "bf16", C0, 3, "c3-like sphere")
 
 
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_fit_long_sweep_warm_start(D):
+    """K = 8192: the warm-started single-accumulator kernel from the second iteration on."""
+    w, Xn, C0 = _workload("c3", N=12000, K=8192, D=D)
+    _teacher_forced(Xn, "bf16", C0, 3, f"long sweep D={D}")
+    X = parity.x_from_numpy(Xn, "bf16", DEV)
+    C3, a3, n3, _ = km.fit(X, torch.from_numpy(C0).to(DEV), 3)
+    C2, _, _, _ = km.fit(X, torch.from_numpy(C0).to(DEV), 2)
+    C1, a1, n1, _ = km.fit(X, C2, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(C3, C1) and torch.equal(a3, a1) and torch.equal(n3, n1)
+
+
 @pytest.mark.parametrize("chunk", [7, 1000, 4096, 100_000])
 def test_fit_streamed_matches_oracle(chunk):
     w, Xn, C0 = _workload("c4", N=9000, K=300)
