@@ -121,7 +121,9 @@ static SortGeom sort_geom(int64_t N, int64_t K) {
   g.npass = (kb + kMaxDigitBits - 1) / kMaxDigitBits;
   const int base = kb / g.npass, rem = kb % g.npass;
   for (int p = 0; p < 6; ++p) g.bits[p] = p < g.npass ? base + (p < rem ? 1 : 0) : 0;
-  g.nblk = (N + kRadixBlock - 1) / kRadixBlock;
+  g.items = radix_items(N);
+  const int64_t blk = (int64_t)kRadixThreads * g.items;
+  g.nblk = (N + blk - 1) / blk;
   int64_t m = 1;
   for (int p = 0; p < g.npass; ++p) {
     const int64_t len = ((int64_t)1 << g.bits[p]) * g.nblk;
@@ -346,9 +348,9 @@ static km_status run_assign(const void* X, km_dtype dt, int64_t N, int64_t D, co
   return KM_OK;
 }
 
-// Argsort + boundaries; returns the sorted keys and values (the inverse map).
+// Argsort (+ cluster offsets when `offsets`); returns the sorted keys and values (the inverse map).
 static km_status run_sort(const int32_t* assign, int64_t N, int64_t K, const SortBufs& b, int32_t* perm_out,
-                          int32_t** keys, int32_t** vals, hipStream_t s) {
+                          int32_t** keys, int32_t** vals, hipStream_t s, bool offsets = true) {
   const SortGeom g = sort_geom(N, K);
   // ping-pong through set a / set b; the last pass may write the caller's perm
   int32_t* kf = (g.npass % 2) ? b.key_a : b.key_b;
@@ -357,7 +359,7 @@ static km_status run_sort(const int32_t* assign, int64_t N, int64_t K, const Sor
                                             b.scan_part, s));
   *keys = kf;
   *vals = vf;
-  KM_TIMED("segments", s, return launch_boundaries(kf, N, K, b.off, s));
+  if (offsets) KM_TIMED("segments", s, return launch_boundaries(kf, N, K, b.off, s));
   return KM_OK;
 }
 
@@ -368,7 +370,8 @@ static km_status run_update(const void* X, km_dtype dt, int64_t N, int64_t D, co
                             float* acc_sum, int64_t* acc_cnt, hipStream_t s, const int32_t** sorted_keys = nullptr,
                             const int32_t** sorted_vals = nullptr) {
   int32_t *keys = nullptr, *vals = nullptr;
-  km_status st = run_sort(assign, N, K, u.s, nullptr, &keys, &vals, s);
+  // the segmented reduction writes the cluster offsets itself (it sees every id change)
+  km_status st = run_sort(assign, N, K, u.s, nullptr, &keys, &vals, s, /*offsets=*/N == 0);
   if (st != KM_OK) return st;
   if (sorted_keys) *sorted_keys = keys;
   if (sorted_vals) *sorted_vals = vals;

@@ -164,8 +164,10 @@ inline AssignGeom make_assign_geom(int64_t N, int64_t D, int64_t K, int dt) {
 #define KM_SEG_U 16       // rows in flight per lane group in the segmented reduction
 #endif
 constexpr int kRadixThreads = 256;
-constexpr int kRadixItems = 32;              // consecutive keys per thread
-constexpr int kRadixBlock = kRadixThreads * kRadixItems;  // keys per block (block positions fit in 16 bits)
+constexpr int kRadixMaxItems = 32;           // consecutive keys per thread: 8, 16 or 32 (block positions fit in 16 bits)
+// Keys per thread for N keys: blocks of 2048..8192 keys, small enough that
+// about a thousand blocks (four per CU) share the work when N allows.
+inline int radix_items(int64_t N) { return N >= 1024 * 8192 ? 32 : (N >= 1024 * 4096 ? 16 : 8); }
 constexpr int kMaxDigitBits = 6;             // digits of at most 64 values per pass
 constexpr int kSegTile = KM_SEG_TILE;
 constexpr uint32_t kInvalidFlag = 0x80000000u;  // marks a point whose cluster id was out of range
@@ -176,7 +178,8 @@ struct SortGeom {
   int kbits;        // bits of the largest valid id (K - 1), at least 1
   int npass;        // radix passes
   int bits[6];      // digit width of each pass
-  int64_t nblk;     // key blocks of kRadixBlock
+  int items;        // keys per thread (radix_items)
+  int64_t nblk;     // key blocks of kRadixThreads * items keys
   int64_t count_len;  // max over passes of (2^bits * nblk)
 };
 
@@ -217,7 +220,7 @@ struct ReduceArgs {
   int64_t N, D, K;
   const int32_t* keys;
   const int32_t* vals;
-  const int32_t* off;
+  int32_t* off;         // K+1 cluster offsets (written by launch_segment_reduce, read by launch_fixup)
   float* carry_sum;     // [ntiles][2][Dc]
   int32_t* carry_cnt;   // [ntiles][2]
   int mode;

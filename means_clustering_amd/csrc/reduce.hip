@@ -88,7 +88,7 @@ struct SegParams {
   bool vec_ok;
   const int32_t* keys;
   const int32_t* vals;
-  const int32_t* off;
+  int32_t* off;  // K+1 cluster offsets, written by the segmented reduction
   float* carry_sum;
   int32_t* carry_cnt;
   int Dc;
@@ -162,6 +162,17 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
   const int32_t before_key = ps > 0 ? P.keys[ps - 1] : -1;   // id just before the tile
   const int32_t after_key = pe < P.N ? P.keys[pe] : -1;      // id just after the tile
 
+  // Cluster offsets: off[k] = first sorted position with id >= k.  Every id
+  // change between positions p-1 and p is seen by exactly one lane group
+  // (the one whose tile holds p), which writes off[(id before, id at p]] = p.
+  auto write_offsets = [&](int64_t a, int64_t b, int64_t p) {
+    if (j != 0) return;
+    a = a < -1 ? -1 : (a >= P.K ? P.K : a);  // sorted ids lie in [0, K); clamping keeps writes in bounds
+    b = b < -1 ? -1 : (b >= P.K ? P.K : b);
+    for (int64_t k = a + 1; k <= b; ++k) P.off[k] = (int32_t)p;
+  };
+  if (before_key != first_key) write_offsets(before_key, first_key, ps);
+
   float acc[CPL][EPL];
 #pragma unroll
   for (int q = 0; q < CPL; ++q)
@@ -196,6 +207,7 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
       for (int u = 0; u < U; ++u) {
         if (in[u]) {
           if (kk[u] != cur) {  // the current segment ends inside the tile
+            write_offsets(cur, kk[u], p0 + b0 + u);
             flush_piece<EPL, CPL, G>(P, tile, first_key, cur, started, acc, cnt, j);
             cur = kk[u];
             cnt = 0;
@@ -218,6 +230,7 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
     }
   }
   flush_piece<EPL, CPL, G>(P, tile, first_key, cur, started && after_key != cur, acc, cnt, j);
+  if (pe == P.N) write_offsets(cur, P.K, P.N);  // ids after the last one start (and end) at N
 }
 
 // Segments cut by tile edges are summed from their carry pieces; empty

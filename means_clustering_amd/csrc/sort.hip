@@ -10,8 +10,8 @@
 // instead of scattering.  Here the sort is an LSD radix sort over the bits of
 // the largest cluster id, at most 6 bits a pass, passes of balanced width.
 // Nothing in it uses an atomic, so a hot cluster (many points with one id)
-// costs no contention.  Ranking inside a block of kRadixBlock keys: every
-// thread owns kRadixItems consecutive keys and a private 16-bit counter per
+// costs no contention.  Ranking inside a block of 256 x IT keys (IT = 8, 16
+// or 32 by N): every thread owns IT consecutive keys and a private 16-bit counter per
 // digit in LDS; counting its own keys in order gives each key its rank among
 // the thread's keys of that digit, and one exclusive scan over the counters in
 // (digit, thread) order turns them into block-wide ranks that keep the input
@@ -67,10 +67,9 @@ __device__ __forceinline__ uint32_t block_scan_excl(uint32_t v, uint32_t& excl, 
 // the thread's i-th key (valid[i] false: not a key).  On return rank[i] is
 // the key's position in the block sorted by digit, and start[dd] (LDS, R+1
 // entries) the first position of digit dd.
-template <int BITS>
-__device__ __forceinline__ void block_rank(const uint32_t (&d)[kRadixItems], const bool (&valid)[kRadixItems],
-                                           uint32_t* ctr, uint32_t* wsum, uint32_t* start,
-                                           uint32_t (&rank)[kRadixItems]) {
+template <int BITS, int IT>
+__device__ __forceinline__ void block_rank(const uint32_t (&d)[IT], const bool (&valid)[IT], uint32_t* ctr,
+                                           uint32_t* wsum, uint32_t* start, uint32_t (&rank)[IT]) {
   constexpr int R = 1 << BITS;
   constexpr int T = kRadixThreads;
   const int t = threadIdx.x;
@@ -79,7 +78,7 @@ __device__ __forceinline__ void block_rank(const uint32_t (&d)[kRadixItems], con
   // count own keys in order: rank among this thread's keys of the same digit
   uint16_t* c16 = reinterpret_cast<uint16_t*>(ctr);
 #pragma unroll
-  for (int i = 0; i < kRadixItems; ++i) {
+  for (int i = 0; i < IT; ++i) {
     if (valid[i]) {
       const int f = (int)d[i] * T + t;
       const int h = ctr_word(f) * 2 + (f & 1);
@@ -112,25 +111,26 @@ __device__ __forceinline__ void block_rank(const uint32_t (&d)[kRadixItems], con
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kRadixItems; ++i)
+  for (int i = 0; i < IT; ++i)
     if (valid[i]) rank[i] += ctr_get(ctr, (int)d[i] * T + t);
   for (int dd = t; dd < R; dd += T) start[dd] = ctr_get(ctr, dd * T);
   if (t == T - 1) start[R] = run;  // the last thread's running sum is the block's key count
   __syncthreads();
 }
 
-// Keys (and values) of this thread: kRadixItems consecutive positions.
+// Keys (and values) of this thread: IT consecutive positions.
 // Pass 0 reads the caller's assignment vector: ids outside [0, K) become K-1
 // with the invalid flag in the value, and the value is the point index itself.
+template <int IT>
 __device__ __forceinline__ void load_block_keys(const int32_t* __restrict__ keys, const int32_t* __restrict__ vals,
                                                 bool first, int64_t N, int64_t K, int64_t base,
-                                                int32_t (&key)[kRadixItems], int32_t (&val)[kRadixItems],
-                                                bool (&valid)[kRadixItems], bool want_vals) {
-  const int64_t p0 = base + (int64_t)threadIdx.x * kRadixItems;
-  if (p0 + kRadixItems <= N && ((reinterpret_cast<uintptr_t>(keys + p0) & 15) == 0)) {
+                                                int32_t (&key)[IT], int32_t (&val)[IT],
+                                                bool (&valid)[IT], bool want_vals) {
+  const int64_t p0 = base + (int64_t)threadIdx.x * IT;
+  if (p0 + IT <= N && ((reinterpret_cast<uintptr_t>(keys + p0) & 15) == 0)) {
     const int4* k4 = reinterpret_cast<const int4*>(keys + p0);
 #pragma unroll
-    for (int i = 0; i < kRadixItems / 4; ++i) {
+    for (int i = 0; i < IT / 4; ++i) {
       const int4 v = k4[i];
       key[4 * i] = v.x;
       key[4 * i + 1] = v.y;
@@ -140,7 +140,7 @@ __device__ __forceinline__ void load_block_keys(const int32_t* __restrict__ keys
     if (want_vals && !first) {
       const int4* v4 = reinterpret_cast<const int4*>(vals + p0);
 #pragma unroll
-      for (int i = 0; i < kRadixItems / 4; ++i) {
+      for (int i = 0; i < IT / 4; ++i) {
         const int4 v = v4[i];
         val[4 * i] = v.x;
         val[4 * i + 1] = v.y;
@@ -149,10 +149,10 @@ __device__ __forceinline__ void load_block_keys(const int32_t* __restrict__ keys
       }
     }
 #pragma unroll
-    for (int i = 0; i < kRadixItems; ++i) valid[i] = true;
+    for (int i = 0; i < IT; ++i) valid[i] = true;
   } else {
 #pragma unroll
-    for (int i = 0; i < kRadixItems; ++i) {
+    for (int i = 0; i < IT; ++i) {
       const int64_t pos = p0 + i;
       valid[i] = pos < N;
       key[i] = valid[i] ? keys[pos] : 0;
@@ -161,7 +161,7 @@ __device__ __forceinline__ void load_block_keys(const int32_t* __restrict__ keys
   }
   if (first) {
 #pragma unroll
-    for (int i = 0; i < kRadixItems; ++i) {
+    for (int i = 0; i < IT; ++i) {
       const int64_t pos = p0 + i;
       val[i] = (int32_t)pos;
       if ((uint32_t)key[i] >= (uint32_t)K) {
@@ -173,7 +173,7 @@ __device__ __forceinline__ void load_block_keys(const int32_t* __restrict__ keys
 }
 
 // Per-block digit counts: counts[d * nblk + b].
-template <int BITS>
+template <int BITS, int IT>
 __global__ __launch_bounds__(kRadixThreads) void radix_count_kernel(const int32_t* __restrict__ keys, int64_t N,
                                                                     int64_t K, int first, int shift, int64_t nblk,
                                                                     uint32_t* __restrict__ counts) {
@@ -182,13 +182,13 @@ __global__ __launch_bounds__(kRadixThreads) void radix_count_kernel(const int32_
   __shared__ uint32_t wsum[kRadixThreads / 64];
   __shared__ uint32_t start[R + 1];
   const int64_t b = blockIdx.x;
-  int32_t key[kRadixItems], val[kRadixItems];
-  bool valid[kRadixItems];
-  load_block_keys(keys, nullptr, first, N, K, b * kRadixBlock, key, val, valid, false);
-  uint32_t d[kRadixItems], rank[kRadixItems];
+  int32_t key[IT], val[IT];
+  bool valid[IT];
+  load_block_keys<IT>(keys, nullptr, first, N, K, b * (kRadixThreads * IT), key, val, valid, false);
+  uint32_t d[IT], rank[IT];
 #pragma unroll
-  for (int i = 0; i < kRadixItems; ++i) d[i] = ((uint32_t)key[i] >> shift) & (uint32_t)(R - 1);
-  block_rank<BITS>(d, valid, ctr, wsum, start, rank);
+  for (int i = 0; i < IT; ++i) d[i] = ((uint32_t)key[i] >> shift) & (uint32_t)(R - 1);
+  block_rank<BITS, IT>(d, valid, ctr, wsum, start, rank);
   for (int dd = threadIdx.x; dd < R; dd += kRadixThreads) counts[(int64_t)dd * nblk + b] = start[dd + 1] - start[dd];
 }
 
@@ -197,8 +197,8 @@ __global__ __launch_bounds__(kRadixThreads) void radix_count_kernel(const int32_
 // LDS in sorted order (reusing the counter space), then written out with
 // consecutive lanes on consecutive block positions, so each digit's run
 // leaves as contiguous stores rather than scattered words.
-static_assert(kRadixPadded >= kRadixBlock, "staging reuses the counter space");
-template <int BITS>
+static_assert(kRadixPadded >= kRadixThreads * kRadixMaxItems, "staging reuses the counter space");
+template <int BITS, int IT>
 __global__ __launch_bounds__(kRadixThreads) void radix_scatter_kernel(const int32_t* __restrict__ keys_in,
                                                                       const int32_t* __restrict__ vals_in, int64_t N,
                                                                       int64_t K, int first, int shift, int64_t nblk,
@@ -212,23 +212,23 @@ __global__ __launch_bounds__(kRadixThreads) void radix_scatter_kernel(const int3
   __shared__ uint32_t gbase[R];
   const int64_t b = blockIdx.x;
   for (int dd = threadIdx.x; dd < R; dd += kRadixThreads) gbase[dd] = offsets[(int64_t)dd * nblk + b];
-  int32_t key[kRadixItems], val[kRadixItems];
-  bool valid[kRadixItems];
-  load_block_keys(keys_in, vals_in, first, N, K, b * kRadixBlock, key, val, valid, true);
-  uint32_t d[kRadixItems], rank[kRadixItems];
+  int32_t key[IT], val[IT];
+  bool valid[IT];
+  load_block_keys<IT>(keys_in, vals_in, first, N, K, b * (kRadixThreads * IT), key, val, valid, true);
+  uint32_t d[IT], rank[IT];
 #pragma unroll
-  for (int i = 0; i < kRadixItems; ++i) d[i] = ((uint32_t)key[i] >> shift) & (uint32_t)(R - 1);
-  block_rank<BITS>(d, valid, ctr, wsum, start, rank);
+  for (int i = 0; i < IT; ++i) d[i] = ((uint32_t)key[i] >> shift) & (uint32_t)(R - 1);
+  block_rank<BITS, IT>(d, valid, ctr, wsum, start, rank);
   const uint32_t nkeys = start[R];
   int32_t* stage = reinterpret_cast<int32_t*>(ctr);
   // keys in sorted order; remember each striped position's destination
 #pragma unroll
-  for (int i = 0; i < kRadixItems; ++i)
+  for (int i = 0; i < IT; ++i)
     if (valid[i]) stage[rank[i]] = key[i];
   __syncthreads();
-  uint32_t dst[kRadixItems];
+  uint32_t dst[IT];
 #pragma unroll
-  for (int i = 0; i < kRadixItems; ++i) {
+  for (int i = 0; i < IT; ++i) {
     const uint32_t p = (uint32_t)(i * kRadixThreads + threadIdx.x);
     dst[i] = 0xffffffffu;
     if (p < nkeys) {
@@ -240,11 +240,11 @@ __global__ __launch_bounds__(kRadixThreads) void radix_scatter_kernel(const int3
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kRadixItems; ++i)
+  for (int i = 0; i < IT; ++i)
     if (valid[i]) stage[rank[i]] = val[i];
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kRadixItems; ++i) {
+  for (int i = 0; i < IT; ++i) {
     const uint32_t p = (uint32_t)(i * kRadixThreads + threadIdx.x);
     if (p < nkeys && dst[i] < (uint64_t)N) vals_out[dst[i]] = stage[p];
   }
@@ -362,6 +362,60 @@ static hipError_t launch_scan(uint32_t* a, int64_t n, uint32_t* part, hipStream_
 
 int64_t scan_part_len(int64_t n) { return (n + kScanTile - 1) / kScanTile + 1; }
 
+template <int B, int IT>
+static void count_pass(const SortGeom& g, const int32_t* kin, int first, int shift, uint32_t* counts, hipStream_t s) {
+  hipLaunchKernelGGL((radix_count_kernel<B, IT>), dim3((unsigned)g.nblk), dim3(kRadixThreads), 0, s, kin, g.N, g.K,
+                     first, shift, g.nblk, counts);
+}
+
+template <int B, int IT>
+static void scatter_pass(const SortGeom& g, const int32_t* kin, const int32_t* vin, int first, int shift,
+                         const uint32_t* counts, int32_t* kout, int32_t* vout, hipStream_t s) {
+  hipLaunchKernelGGL((radix_scatter_kernel<B, IT>), dim3((unsigned)g.nblk), dim3(kRadixThreads), 0, s, kin, vin, g.N,
+                     g.K, first, shift, g.nblk, counts, kout, vout);
+}
+
+#define KM_SORT_DISPATCH(CALL)                                                               \
+  switch (g.items * 16 + bits) {                                                             \
+    case 8 * 16 + 1: CALL(1, 8); break;                                                      \
+    case 8 * 16 + 2: CALL(2, 8); break;                                                      \
+    case 8 * 16 + 3: CALL(3, 8); break;                                                      \
+    case 8 * 16 + 4: CALL(4, 8); break;                                                      \
+    case 8 * 16 + 5: CALL(5, 8); break;                                                      \
+    case 8 * 16 + 6: CALL(6, 8); break;                                                      \
+    case 16 * 16 + 1: CALL(1, 16); break;                                                    \
+    case 16 * 16 + 2: CALL(2, 16); break;                                                    \
+    case 16 * 16 + 3: CALL(3, 16); break;                                                    \
+    case 16 * 16 + 4: CALL(4, 16); break;                                                    \
+    case 16 * 16 + 5: CALL(5, 16); break;                                                    \
+    case 16 * 16 + 6: CALL(6, 16); break;                                                    \
+    case 32 * 16 + 1: CALL(1, 32); break;                                                    \
+    case 32 * 16 + 2: CALL(2, 32); break;                                                    \
+    case 32 * 16 + 3: CALL(3, 32); break;                                                    \
+    case 32 * 16 + 4: CALL(4, 32); break;                                                    \
+    case 32 * 16 + 5: CALL(5, 32); break;                                                    \
+    case 32 * 16 + 6: CALL(6, 32); break;                                                    \
+    default: return hipErrorInvalidValue;                                                    \
+  }
+
+static hipError_t launch_pass_count(const SortGeom& g, int bits, const int32_t* kin, int first, int shift,
+                                    uint32_t* counts, hipStream_t s) {
+#define KM_CALL(B, IT) count_pass<B, IT>(g, kin, first, shift, counts, s)
+  KM_SORT_DISPATCH(KM_CALL)
+#undef KM_CALL
+  return hipGetLastError();
+}
+
+static hipError_t launch_pass_scatter(const SortGeom& g, int bits, const int32_t* kin, const int32_t* vin, int first,
+                                      int shift, const uint32_t* counts, int32_t* kout, int32_t* vout,
+                                      hipStream_t s) {
+#define KM_CALL(B, IT) scatter_pass<B, IT>(g, kin, vin, first, shift, counts, kout, vout, s)
+  KM_SORT_DISPATCH(KM_CALL)
+#undef KM_CALL
+  return hipGetLastError();
+}
+#undef KM_SORT_DISPATCH
+
 hipError_t launch_argsort(const SortGeom& g, const int32_t* keys_in, int32_t* key_a, int32_t* val_a,
                           int32_t* key_b, int32_t* val_b, int32_t* key_final, int32_t* val_final, uint32_t* counts,
                           uint32_t* scan_part, hipStream_t stream) {
@@ -375,28 +429,12 @@ hipError_t launch_argsort(const SortGeom& g, const int32_t* keys_in, int32_t* ke
     const bool last = p == g.npass - 1;
     int32_t* kout = last ? key_final : (p % 2 == 0 ? key_a : key_b);
     int32_t* vout = last ? val_final : (p % 2 == 0 ? val_a : val_b);
-    switch (bits) {
-#define KM_PASS(B)                                                                                                 \
-  case B:                                                                                                          \
-    hipLaunchKernelGGL((radix_count_kernel<B>), dim3((unsigned)g.nblk), dim3(kRadixThreads), 0, stream, kin, g.N, \
-                       g.K, first, shift, g.nblk, counts);                                                        \
-    break;
-      KM_PASS(1) KM_PASS(2) KM_PASS(3) KM_PASS(4) KM_PASS(5) KM_PASS(6)
-#undef KM_PASS
-      default: return hipErrorInvalidValue;
-    }
-    hipError_t e = launch_scan(counts, ((int64_t)1 << bits) * g.nblk, scan_part, stream);
+    hipError_t e = launch_pass_count(g, bits, kin, first, shift, counts, stream);
     if (e != hipSuccess) return e;
-    switch (bits) {
-#define KM_PASS(B)                                                                                                   \
-  case B:                                                                                                            \
-    hipLaunchKernelGGL((radix_scatter_kernel<B>), dim3((unsigned)g.nblk), dim3(kRadixThreads), 0, stream, kin, vin, \
-                       g.N, g.K, first, shift, g.nblk, (const uint32_t*)counts, kout, vout);                        \
-    break;
-      KM_PASS(1) KM_PASS(2) KM_PASS(3) KM_PASS(4) KM_PASS(5) KM_PASS(6)
-#undef KM_PASS
-      default: return hipErrorInvalidValue;
-    }
+    e = launch_scan(counts, ((int64_t)1 << bits) * g.nblk, scan_part, stream);
+    if (e != hipSuccess) return e;
+    e = launch_pass_scatter(g, bits, kin, vin, first, shift, counts, kout, vout, stream);
+    if (e != hipSuccess) return e;
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     kin = kout;

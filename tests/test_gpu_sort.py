@@ -52,6 +52,16 @@ def test_sort_zipf_and_invalid():
     _check(a, K, "zipf + invalid ids")
 
 
+@pytest.mark.parametrize("N", [4 * 2**20 - 1, 4 * 2**20 + 5, 8 * 2**20 + 3])
+def test_sort_block_sizes(N):
+    """Around the sizes where the block switches from 2048 to 4096 to 8192 keys."""
+    rng = np.random.default_rng(N)
+    K = 3000
+    a = rng.integers(0, K, N)
+    a[::1001] = K + 1  # a few invalid ids
+    _check(a, K, "block sizes")
+
+
 def test_sort_empty_input():
     perm, off = km.sort_by_cluster(torch.empty(0, dtype=torch.int32, device=DEV), 5)
     torch.cuda.synchronize()

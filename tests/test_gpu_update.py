@@ -68,6 +68,23 @@ def test_update_zipf_inplace():
     _run(X, a, C_prev, "zipf in place", inplace=True)
 
 
+@pytest.mark.parametrize("cluster", [0, 16])
+def test_update_only_first_or_last_cluster(cluster):
+    """Cluster offsets written by the segmented reduction at both ends of the id range."""
+    X = _x(5000, 40, "bf16", seed=8 + cluster)
+    C_prev = torch.randn(17, 40).to(DEV)
+    _run(X, np.full(5000, cluster), C_prev, f"only cluster {cluster}")
+
+
+def test_update_five_million_points():
+    """Radix blocks of 4096 keys (4 Mi <= N < 8 Mi)."""
+    N = 5 * 2**20 + 7
+    X = _x(N, 16, "bf16", seed=9)
+    rng = np.random.default_rng(10)
+    C_prev = torch.randn(3000, 16).to(DEV)
+    _run(X, rng.integers(0, 3000, N), C_prev, "5 Mi points")
+
+
 def test_update_invalid_ids_are_ignored():
     X = _x(10_000, 32, "f32", seed=6)
     rng = np.random.default_rng(7)
