@@ -151,7 +151,14 @@ __device__ __forceinline__ void flush_piece(const SegParams& P, int64_t tile, in
 template <int ES, int CPL, int G>
 __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
   constexpr int EPL = 16 / ES;
-  constexpr int U = G < KM_SEG_U ? G : KM_SEG_U;  // rows in flight per lane group
+  // The ids and point indices of a whole chunk of the tile (KPL per lane, up
+  // to 16) are read in one round trip; the chunk's rows then go out U at a
+  // time in a fully unrolled walk, so the next rows can be in flight while
+  // the current ones are added.
+  constexpr int KPL = kSegTile / G < 16 ? kSegTile / G : 16;
+  constexpr int BATCH = G * KPL;
+  constexpr int U = G < KM_SEG_U ? G : KM_SEG_U;
+  static_assert(BATCH % U == 0 && kSegTile % BATCH == 0, "rows in flight divide the chunk");
   const int j = threadIdx.x % G;
   const int lgbase = (threadIdx.x & 63) & ~(G - 1);
   const int64_t tile = (int64_t)blockIdx.x * (256 / G) + threadIdx.x / G;
@@ -182,20 +189,26 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
   int32_t cur = first_key;
   bool started = before_key != first_key;  // the current segment began inside this tile
 
-  for (int64_t p0 = ps; p0 < pe; p0 += G) {
-    const int64_t mypos = p0 + j;
-    const int32_t kj = mypos < pe ? P.keys[mypos] : 0;
-    const int32_t vj = mypos < pe ? P.vals[mypos] : (int32_t)kInvalidFlag;
-    for (int b0 = 0; b0 < G; b0 += U) {
+  for (int64_t p0 = ps; p0 < pe; p0 += BATCH) {
+    // lane j holds positions p0 + j + G*m, m < KPL
+    int32_t kj[KPL], vj[KPL];
+#pragma unroll
+    for (int m = 0; m < KPL; ++m) {
+      const int64_t mypos = p0 + j + (int64_t)G * m;
+      kj[m] = mypos < pe ? P.keys[mypos] : 0;
+      vj[m] = mypos < pe ? P.vals[mypos] : (int32_t)kInvalidFlag;
+    }
+#pragma unroll
+    for (int b0 = 0; b0 < BATCH; b0 += U) {
       if (p0 + b0 >= pe) break;
       u32x4_r xr[U][CPL];
       int32_t kk[U];
       bool ok[U], in[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int b = b0 + u;
-        const int32_t v = __shfl(vj, lgbase + b);
-        kk[u] = __shfl(kj, lgbase + b);
+        const int b = b0 + u;  // batch position: lane b % G, slot b / G
+        const int32_t v = __shfl(vj[b / G], lgbase + b % G);
+        kk[u] = __shfl(kj[b / G], lgbase + b % G);
         in[u] = p0 + b < pe;
         const int64_t row = (int64_t)((uint32_t)v & ~kInvalidFlag);
         ok[u] = in[u] && v >= 0 && row < P.N;
