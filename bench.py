@@ -54,6 +54,52 @@ def _traffic(kernel_srcs, workload):
         return None
 
 
+def measured_peaks(dev, dtype):
+    """Same-run peaks: sustained MFMA rate (random operands), device copy, pinned host-to-device copy."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "means_clustering_amd", "libkm_peaks.so"))
+    lib.km_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.POINTER(ctypes.c_double)]
+    lib.km_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                 ctypes.POINTER(ctypes.c_double)]
+    lib.km_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.POINTER(ctypes.c_double)]
+    out = {}
+    blocks = 512  # two workgroups (two wavefronts per SIMD) per CU
+    scratch = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    tf = ctypes.c_double()
+    if dtype in ("bf16", "f16"):
+        rc = lib.km_peak_mfma(1 if dtype == "bf16" else 0, blocks, 20000, ctypes.c_void_p(scratch.data_ptr()),
+                              ctypes.byref(tf))
+        if rc == 0:
+            out["mfma_TFLOPs"] = round(tf.value, 1)
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    gb = ctypes.c_double()
+    if lib.km_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes, 5,
+                        ctypes.byref(gb)) == 0:
+        out["hbm_copy_GBps"] = round(gb.value, 1)
+    rs = torch.empty(256 * 4096, dtype=torch.int32, device=dev)
+    if lib.km_peak_read(ctypes.c_void_p(src.data_ptr()), nbytes, 5, ctypes.c_void_p(rs.data_ptr()),
+                        ctypes.byref(gb)) == 0:
+        out["hbm_read_GBps"] = round(gb.value, 1)
+    del src, dst, rs
+    h = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
+    d = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    d.copy_(h, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(8):
+        d.copy_(h, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    out["h2d_pinned_GBps"] = round(8 * (256 << 20) / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    return out
+
+
 def cpu_baseline(w, C0, rows_of, budget_s=10.0):
     """The oracle (never tuned) on a bounded sample of the same workload, scaled to the full N.
 
@@ -89,6 +135,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-timing", action="store_true", help="no per-kernel events (for profiler runs)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the same-run peak probes")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -159,10 +206,12 @@ def main():
         torch.cuda.synchronize()
         print(f"[bench] warmup step {i} done", file=sys.stderr, flush=True)
 
+    # Timed region: HIP events bracket only the FlashAssign launches (mode 2), so
+    # the measured throughput carries almost none of their cost.
     timing = not args.no_timing
     if timing:
         km.timing_reset()
-        km.timing_enable(True)
+        km.timing_enable(2)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -178,12 +227,26 @@ def main():
     its = args.steps * w.iters
     value = its / elapsed
     phases = {}
-    if timing:
+
+    def read_phases():
+        out = {}
         for ph in km.PHASES:
             ms, n = km.timing_read(ph)
             if n:
-                phases[ph] = {"total_ms": round(ms, 4), "launches": n, "avg_us": round(1e3 * ms / n, 3)}
+                out[ph] = {"total_ms": round(ms, 4), "launches": n, "avg_us": round(1e3 * ms / n, 3)}
         km.timing_reset()
+        return out
+
+    if timing:
+        phases = read_phases()
+        # per-phase breakdown from one more step with every phase timed (not part of `value`)
+        km.timing_enable(1)
+        one_step()
+        torch.cuda.synchronize()
+        km.timing_enable(False)
+        breakdown = read_phases()
+    else:
+        breakdown = {}
 
     # ---- roofline of the dominant kernel (FlashAssign): algorithmic flops per launch
     roof = None
@@ -200,13 +263,25 @@ def main():
                 "peak": round(peak / 1e12, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic, "flops_per_launch": flops, "avg_launch_us": phases["assign"]["avg_us"]}
 
+    peaks = None if args.no_peaks else measured_peaks(dev, w.dtype)
+    if roof is not None and peaks and "mfma_TFLOPs" in peaks:
+        roof["peak_measured"] = peaks["mfma_TFLOPs"]
+        roof["frac_of_measured"] = round(roof["achieved"] / peaks["mfma_TFLOPs"], 4)
+
     stream = None
-    if streamed and "h2d" in phases:
+    if streamed:
         es = 2 if w.dtype == "bf16" else 4
         h2d_bytes = w.N * w.D * es * its
+        e2e = h2d_bytes / elapsed / 1e9
+        copying = None
+        if "h2d" in breakdown:  # the extra step: w.iters iterations, each chunk's upload bracketed
+            copying = round(w.N * w.D * es * w.iters / (breakdown["h2d"]["total_ms"] * 1e-3) / 1e9, 2)
         stream = {"h2d_bytes_per_iteration": w.N * w.D * es,
-                  "h2d_GBps_while_copying": round(h2d_bytes / (phases["h2d"]["total_ms"] * 1e-3) / 1e9, 2),
-                  "end_to_end_GBps": round(h2d_bytes / elapsed / 1e9, 2)}
+                  "h2d_GBps_while_copying": copying,
+                  "end_to_end_GBps": round(e2e, 2),
+                  "frac_of_pcie5_x16": round(e2e / 64.0, 4)}
+        if peaks and "h2d_pinned_GBps" in peaks:
+            stream["frac_of_measured_h2d"] = round(e2e / peaks["h2d_pinned_GBps"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -221,7 +296,8 @@ def main():
         "config": {"workload": w.description, "name": w.name, "N": w.N, "D": w.D, "K": w.K,
                    "iters_per_step": w.iters, "chunk_rows": w.chunk_rows or None},
         "distances_per_s": round(value * w.N * w.K, 1),
-        "roofline": roof, "cpu_baseline": cpu, "phases": phases, "streaming": stream,
+        "roofline": roof, "cpu_baseline": cpu, "phases_timed_region": phases, "phase_breakdown_extra_step": breakdown,
+        "streaming": stream, "peaks_measured": peaks,
         "device": torch.cuda.get_device_name(dev),
     }
     print(json.dumps(line), flush=True)

@@ -273,8 +273,10 @@ def fit_streamed(X_host: torch.Tensor, C0: torch.Tensor, iters: int, chunk_rows:
     return C, a, counts, (obj[:iters] if obj is not None else None)
 
 
-def timing_enable(on: bool = True):
-    _check(lib().kmeans_timing_enable(1 if on else 0))
+def timing_enable(on=True):
+    """on: True / 1 = every kernel phase, 2 = FlashAssign launches only, False / 0 = off."""
+    mode = int(on) if not isinstance(on, bool) else (1 if on else 0)
+    _check(lib().kmeans_timing_enable(mode))
 
 
 def timing_reset():

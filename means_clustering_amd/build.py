@@ -16,6 +16,9 @@ ROOT = os.path.dirname(HERE)
 LIB_NAME = "libkmeans_amd.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["csrc/flash_assign.hip", "csrc/sort.hip", "csrc/reduce.hip", "csrc/api.cpp"]
+# peak probes for the benchmark's roofline denominators (a library of their own)
+PEAKS_SOURCE = "csrc/peaks.hip"
+PEAKS_PATH = os.path.join(HERE, "libkm_peaks.so")
 ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 instructions.
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
@@ -47,7 +50,14 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         return obj
 
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
+        objs = list(ex.map(compile_one, SOURCES + [PEAKS_SOURCE]))
+    peaks_obj = objs.pop()
+    tmp = PEAKS_PATH + ".tmp"
+    r = subprocess.run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, peaks_obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, PEAKS_PATH)
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

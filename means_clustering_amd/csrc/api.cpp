@@ -42,7 +42,7 @@ static km_status fail(km_status s, const std::string& msg) {
 namespace {
 struct TimingRegistry {
   std::mutex mu;
-  bool enabled = false;
+  int mode = 0;  // 0 off, 1 every phase, 2 the "assign" phase only
   std::unordered_map<std::string, std::vector<std::pair<hipEvent_t, hipEvent_t>>> rec;
 };
 TimingRegistry& timing() {
@@ -57,7 +57,7 @@ hipError_t timed(const char* phase, hipStream_t stream, F&& fn) {
   bool on;
   {
     std::lock_guard<std::mutex> g(T.mu);
-    on = T.enabled;
+    on = T.mode == 1 || (T.mode == 2 && std::strcmp(phase, "assign") == 0);
   }
   if (!on) return fn();
   hipEvent_t a, b;
@@ -632,7 +632,8 @@ const char* kmeans_last_error(void) { return g_last_error.c_str(); }
 km_status kmeans_timing_enable(int enable) {
   TimingRegistry& T = timing();
   std::lock_guard<std::mutex> g(T.mu);
-  T.enabled = enable != 0;
+  if (enable < 0 || enable > 2) return fail(KM_ERR_INVALID_VALUE, "timing mode must be 0, 1 or 2");
+  T.mode = enable;
   return KM_OK;
 }
 

@@ -346,8 +346,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_apply_kernel(uint32_t* __re
   scan_tile(a, n, (int64_t)blockIdx.x * kScanTile, part[blockIdx.x], wsum);
 }
 
+// Up to this many entries one block scans tile after tile (a kernel launch
+// costs more than the few extra tiles); beyond it, reduce / scan / apply.
+constexpr int64_t kScanSingleMax = 16 * kScanTile;
+
 static hipError_t launch_scan(uint32_t* a, int64_t n, uint32_t* part, hipStream_t s) {
-  if (n <= kScanTile) {
+  if (n <= kScanSingleMax) {
     hipLaunchKernelGGL(scan_single_kernel, dim3(1), dim3(kScanThreads), 0, s, a, n);
     return hipGetLastError();
   }

@@ -91,6 +91,8 @@ def test_update_and_fit_validation(L):
 
 
 def test_timing_registry_without_gpu(L):
+    assert L.kmeans_timing_enable(3) == 1 and L.kmeans_timing_enable(-1) == 1
+    assert L.kmeans_timing_enable(2) == 0
     assert L.kmeans_timing_enable(1) == 0
     ms, n = ctypes.c_double(), ctypes.c_int64()
     assert L.kmeans_timing_read(b"assign", ctypes.byref(ms), ctypes.byref(n)) == 0 and n.value == 0
