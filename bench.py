@@ -126,6 +126,73 @@ def cpu_baseline(w, C0, rows_of, budget_s=10.0):
             "distances_per_s": round(w.K * w.N / sec_per_iter_full, 1)}
 
 
+def ablation(dev):
+    """The designs Flash-KMeans replaces, timed next to the library's kernels on the same inputs."""
+    import numpy as np
+    import torch
+
+    import means_clustering_amd as km
+    import synth
+    from means_clustering_amd import ablation as abl
+
+    def timeit(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3  # us
+
+    out = {"ablation": "designs replaced by FlashAssign and Sort-Inverse Update, same GPU, same inputs"}
+    for name, rows in (("c2", None), ("c4", 1 << 21)):
+        w = synth.WORKLOADS[name]
+        n = w.N if rows is None else rows
+        Xn = synth.points(w, 0, n)
+        C = torch.from_numpy(synth.init_centroids(w.scaled(N=n), Xn)).to(dev)
+        X = torch.from_numpy(Xn.view(np.int16)).view(torch.bfloat16).to(dev)
+        del Xn
+        print(f"[bench] ablation assign {name} N={n}", file=sys.stderr, flush=True)
+        ws = km.Workspace(dev)
+        a_out = torch.empty(n, dtype=torch.int32, device=dev)
+        scratch = torch.empty(abl.lib().kmeans_abl_materialized_bytes(n, w.D, w.K), dtype=torch.uint8, device=dev)
+        t_fa = timeit(lambda: km.assign(X, C, out=a_out, ws=ws), 5)
+        t_mat = timeit(lambda: abl.assign_materialized(X, C, scratch), 3)
+        same = torch.equal(a_out, abl.assign_materialized(X, C, scratch))
+        out[f"assign_{name}"] = {"N": n, "D": w.D, "K": w.K, "flash_assign_us": round(t_fa, 1),
+                                 "materialized_us": round(t_mat, 1), "speedup": round(t_mat / t_fa, 2),
+                                 "score_matrix_bytes": n * w.K * 4, "same_assignment": bool(same)}
+        del scratch, X
+        torch.cuda.empty_cache()
+    w = synth.WORKLOADS["c4"]
+    Xn = synth.points(w)
+    C = torch.from_numpy(synth.init_centroids(w, Xn)).to(dev)
+    X = torch.from_numpy(Xn.view(np.int16)).view(torch.bfloat16).to(dev)
+    del Xn
+    a_real, _ = km.assign(X, C)
+    rng = np.random.default_rng(11)
+    zw = 1.0 / np.arange(1, w.K + 1) ** 1.2
+    cases = {"c4_assignments": a_real,
+             "zipf_ids": torch.from_numpy(rng.choice(w.K, size=w.N, p=zw / zw.sum()).astype(np.int32)).to(dev),
+             "one_cluster": torch.zeros(w.N, dtype=torch.int32, device=dev)}
+    ws = km.Workspace(dev)
+    C_out = torch.empty_like(C)
+    cnt = torch.empty(w.K, dtype=torch.int32, device=dev)
+    scratch = torch.empty(abl.lib().kmeans_abl_atomic_bytes(w.D, w.K), dtype=torch.uint8, device=dev)
+    bmin = w.N * w.D * 2 + w.N * 4 + w.K * w.D * 4
+    for cname, a in cases.items():
+        print(f"[bench] ablation update {cname}", file=sys.stderr, flush=True)
+        t_si = timeit(lambda: km.update(X, a, C, out=C_out, counts_out=cnt, ws=ws), 5)
+        t_at = timeit(lambda: abl.update_atomic(X, a, C, scratch), 3)
+        out[f"update_{cname}"] = {"N": w.N, "D": w.D, "K": w.K, "sort_inverse_us": round(t_si, 1),
+                                  "atomic_scatter_us": round(t_at, 1), "speedup": round(t_at / t_si, 2),
+                                  "sort_inverse_GBps_Bmin": round(bmin / (t_si * 1e-6) / 1e9, 1),
+                                  "atomic_GBps_Bmin": round(bmin / (t_at * 1e-6) / 1e9, 1)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +203,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-timing", action="store_true", help="no per-kernel events (for profiler runs)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the same-run peak probes")
+    ap.add_argument("--ablation", action="store_true",
+                    help="only time the materialised-distance assignment and the atomic scatter update "
+                         "against FlashAssign and Sort-Inverse Update (one JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -147,6 +217,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "copy", "bytes_read_per_launch": 1 << 30, "bytes_written_per_launch": 1 << 30}))
+        return
+    if args.ablation:
+        import torch
+        ablation(torch.device("cuda:0"))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding of this "

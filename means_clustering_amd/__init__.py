@@ -174,7 +174,7 @@ def sort_by_cluster(a: torch.Tensor, K: int, ws: Workspace | None = None):
 
 
 def update(X: torch.Tensor, a: torch.Tensor, C_prev: torch.Tensor, out: torch.Tensor | None = None,
-           ws: Workspace | None = None):
+           ws: Workspace | None = None, counts_out: torch.Tensor | None = None):
     """Sort-Inverse Update. Returns (C_new fp32[K, D], counts int32[K])."""
     _need(X, C_prev)
     if a.dtype != torch.int32 or a.shape != (X.shape[0],) or not a.is_contiguous():
@@ -182,7 +182,7 @@ def update(X: torch.Tensor, a: torch.Tensor, C_prev: torch.Tensor, out: torch.Te
     N, D = X.shape
     K = C_prev.shape[0]
     C_new = out if out is not None else torch.empty_like(C_prev)
-    counts = torch.empty(K, dtype=torch.int32, device=X.device)
+    counts = counts_out if counts_out is not None else torch.empty(K, dtype=torch.int32, device=X.device)
     nb = workspace_bytes(KM_OP_UPDATE, N, D, K, X.dtype)
     w = _ws(ws, nb, X.device)
     _check(lib().kmeans_update(_ptr(X), _dtype(X), N, D, _ptr(a), K, _ptr(C_prev), _ptr(C_new), _ptr(counts),

@@ -16,9 +16,10 @@ ROOT = os.path.dirname(HERE)
 LIB_NAME = "libkmeans_amd.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["csrc/flash_assign.hip", "csrc/sort.hip", "csrc/reduce.hip", "csrc/api.cpp"]
-# peak probes for the benchmark's roofline denominators (a library of their own)
-PEAKS_SOURCE = "csrc/peaks.hip"
-PEAKS_PATH = os.path.join(HERE, "libkm_peaks.so")
+# peak probes for the benchmark's roofline denominators, and the ablation
+# baselines (libraries of their own, not part of libkmeans_amd.so)
+EXTRA_LIBS = [("csrc/peaks.hip", os.path.join(HERE, "libkm_peaks.so"), []),
+              ("csrc/ablation.hip", os.path.join(HERE, "libkm_ablation.so"), ["-munsafe-fp-atomics"])]
 ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 instructions.
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
@@ -39,9 +40,9 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     bdir = os.path.join(ROOT, "_build")
     os.makedirs(bdir, exist_ok=True)
 
-    def compile_one(src):
+    def compile_one(src, extra=()):
         obj = os.path.join(bdir, os.path.basename(src) + ".o")
-        cmd = [hipcc, *CFLAGS, "-I", os.path.join(ROOT, "include"), "-c", os.path.join(HERE, src), "-o", obj]
+        cmd = [hipcc, *CFLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-c", os.path.join(HERE, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -50,14 +51,17 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         return obj
 
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(compile_one, SOURCES + [PEAKS_SOURCE]))
-    peaks_obj = objs.pop()
-    tmp = PEAKS_PATH + ".tmp"
-    r = subprocess.run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, peaks_obj],
-                       capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, PEAKS_PATH)
+        futs = [ex.submit(compile_one, src) for src in SOURCES]
+        extra = [ex.submit(compile_one, src, flags) for src, _, flags in EXTRA_LIBS]
+        objs = [f.result() for f in futs]
+        extra_objs = [f.result() for f in extra]
+    for (_, path, _), obj in zip(EXTRA_LIBS, extra_objs):
+        tmp = path + ".tmp"
+        r = subprocess.run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, obj],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stderr}")
+        os.replace(tmp, path)
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

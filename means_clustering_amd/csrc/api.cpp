@@ -170,6 +170,8 @@ struct UpdateBufs {
   SortBufs s;
   float* carry_sum;
   int32_t* carry_cnt;
+  float* group_sum;
+  int32_t* group_cnt;
 };
 
 static UpdateBufs carve_update(Carve& c, const SortGeom& g, int64_t D, km_dtype dt) {
@@ -178,6 +180,9 @@ static UpdateBufs carve_update(Carve& c, const SortGeom& g, int64_t D, km_dtype 
   const int64_t ntiles = (g.N + kSegTile - 1) / kSegTile;
   u.carry_sum = c.take<float>((size_t)(ntiles > 0 ? ntiles : 1) * 2 * (size_t)reduce_dc((int)dt, D));
   u.carry_cnt = c.take<int32_t>((size_t)(ntiles > 0 ? ntiles : 1) * 2);
+  const int64_t ngroups = (ntiles + kSegGroup - 1) / kSegGroup;
+  u.group_sum = c.take<float>((size_t)(ngroups > 0 ? ngroups : 1) * (size_t)reduce_dc((int)dt, D));
+  u.group_cnt = c.take<int32_t>((size_t)(ngroups > 0 ? ngroups : 1));
   return u;
 }
 
@@ -386,6 +391,8 @@ static km_status run_update(const void* X, km_dtype dt, int64_t N, int64_t D, co
   a.off = u.s.off;
   a.carry_sum = u.carry_sum;
   a.carry_cnt = u.carry_cnt;
+  a.group_sum = u.group_sum;
+  a.group_cnt = u.group_cnt;
   a.mode = mode;
   a.C_prev = C_prev;
   a.C_new = C_new;

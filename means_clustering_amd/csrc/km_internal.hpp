@@ -170,6 +170,7 @@ constexpr int kRadixMaxItems = 32;           // consecutive keys per thread: 8, 
 inline int radix_items(int64_t N) { return N >= 1024 * 8192 ? 32 : (N >= 1024 * 4096 ? 16 : 8); }
 constexpr int kMaxDigitBits = 6;             // digits of at most 64 values per pass
 constexpr int kSegTile = KM_SEG_TILE;
+constexpr int kSegGroup = 64;  // tiles per carry group (second reduction level for long segments)
 constexpr uint32_t kInvalidFlag = 0x80000000u;  // marks a point whose cluster id was out of range
 
 struct SortGeom {
@@ -223,6 +224,8 @@ struct ReduceArgs {
   int32_t* off;         // K+1 cluster offsets (written by launch_segment_reduce, read by launch_fixup)
   float* carry_sum;     // [ntiles][2][Dc]
   int32_t* carry_cnt;   // [ntiles][2]
+  float* group_sum;     // [ngroups][Dc]: slot-0 carries of a single-id group of kSegGroup tiles, summed
+  int32_t* group_cnt;   // [ngroups]
   int mode;
   const float* C_prev;  // MODE_MEAN
   float* C_new;         // MODE_MEAN

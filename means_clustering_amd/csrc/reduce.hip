@@ -91,6 +91,8 @@ struct SegParams {
   int32_t* off;  // K+1 cluster offsets, written by the segmented reduction
   float* carry_sum;
   int32_t* carry_cnt;
+  float* group_sum;
+  int32_t* group_cnt;
   int Dc;
   int mode;
   const float* C_prev;
@@ -246,12 +248,63 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
   if (pe == P.N) write_offsets(cur, P.K, P.N);  // ids after the last one start (and end) at N
 }
 
-// Segments cut by tile edges are summed from their carry pieces; empty
-// clusters keep their centroid.  One wavefront per cluster, 16 clusters a
-// workgroup.  Lanes split into R rows x (Dc/4) float4 columns; row r adds the
-// pieces of tiles t0+r, t0+r+R, ... and the rows are combined by a fixed
+// Second level for long segments: a group of kSegGroup consecutive tiles
+// whose sorted positions all hold one id lies inside that id's segment, so
+// every tile of it left its piece in slot 0.  One wavefront per group sums
+// those pieces in tile order (rows strided over the tiles, then a fixed
+// shuffle tree); the fix-up then adds whole groups instead of their tiles.
+template <int CPL>
+__global__ __launch_bounds__(256) void carry_group_kernel(SegParams P, int64_t ngroups) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t grp = (int64_t)blockIdx.x * 4 + wave;
+  if (grp >= ngroups) return;
+  const int64_t ntiles = (P.N + kSegTile - 1) / kSegTile;
+  const int64_t tb = grp * kSegGroup;
+  const int64_t te = tb + kSegGroup < ntiles ? tb + kSegGroup : ntiles;
+  const int64_t pe = te * kSegTile < P.N ? te * kSegTile : P.N;
+  if (P.keys[tb * kSegTile] != P.keys[pe - 1]) return;  // more than one id: the fix-up never asks for it
+  const int gc = P.Dc / 4;
+  const int lpr = gc < 64 ? gc : 64;
+  const int R = 64 / lpr;
+  const int r = lane / lpr, c0 = lane % lpr;
+  float a[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  int32_t n = 0;
+  for (int64_t t = tb + r; t < te; t += R) {
+    const float* piece = P.carry_sum + (t * 2) * (int64_t)P.Dc;
+#pragma unroll
+    for (int cl = 0; cl < CPL; ++cl) {
+      const float4 v = *reinterpret_cast<const float4*>(piece + (c0 + cl * lpr) * 4);
+      a[cl][0] += v.x;
+      a[cl][1] += v.y;
+      a[cl][2] += v.z;
+      a[cl][3] += v.w;
+    }
+    n += P.carry_cnt[t * 2];
+  }
+  for (int off = lpr; off < 64; off <<= 1) {
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) a[cl][x] += __shfl_xor(a[cl][x], off);
+    n += __shfl_xor(n, off);
+  }
+  if (r == 0) {
+    float* dst = P.group_sum + grp * (int64_t)P.Dc;
+#pragma unroll
+    for (int cl = 0; cl < CPL; ++cl)
+      *reinterpret_cast<float4*>(dst + (c0 + cl * lpr) * 4) = make_float4(a[cl][0], a[cl][1], a[cl][2], a[cl][3]);
+    if (c0 == 0) P.group_cnt[grp] = n;
+  }
+}
+
+// Segments cut by tile edges are summed from their pieces; empty clusters
+// keep their centroid.  One wavefront per cluster.  The pieces of cluster k,
+// tiles t0..t1, are taken as: the head tiles before the first group boundary
+// after t0, then every whole group up to the group holding t1 (one summed
+// piece each, see carry_group_kernel), then the tail tiles of t1's group.
+// Lanes split into R rows x (Dc/4) float4 columns; row r takes items r,
+// r + R, ... of that list in order and the rows are combined by a fixed
 // shuffle tree, so the order of additions never depends on scheduling.
-constexpr int kFixupPerWave = 1;
 template <int CPL>  // float4 columns per lane: 2 only when a piece has 128 of them
 __global__ __launch_bounds__(256) void fixup_kernel(SegParams P) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -260,78 +313,94 @@ __global__ __launch_bounds__(256) void fixup_kernel(SegParams P) {
   const int R = 64 / lpr;                     // rows
   constexpr int cpl = CPL;
   const int r = lane / lpr, c0 = lane % lpr;
-  for (int i = 0; i < kFixupPerWave; ++i) {
-    const int64_t k = ((int64_t)blockIdx.x * 4 + wave) * kFixupPerWave + i;
-    if (k >= P.K) return;
-    const int64_t s = P.off[k], e = P.off[k + 1];
-    if (s < 0 || e > P.N || s > e) continue;  // boundaries are monotone in [0, N]
-    if (s == e) {
-      if (P.mode == MODE_MEAN) {
-        if (lane == 0 && P.counts) P.counts[k] = 0;
-        if (P.C_new != P.C_prev)
-          for (int c = lane; c < P.D; c += 64) P.C_new[k * P.D + c] = P.C_prev[k * P.D + c];
-      }
-      continue;
+  const int64_t k = (int64_t)blockIdx.x * 4 + wave;
+  if (k >= P.K) return;
+  const int64_t s = P.off[k], e = P.off[k + 1];
+  if (s < 0 || e > P.N || s > e) return;  // offsets are monotone in [0, N]
+  if (s == e) {
+    if (P.mode == MODE_MEAN) {
+      if (lane == 0 && P.counts) P.counts[k] = 0;
+      if (P.C_new != P.C_prev)
+        for (int c = lane; c < P.D; c += 64) P.C_new[k * P.D + c] = P.C_prev[k * P.D + c];
     }
-    const int64_t t0 = s / kSegTile, t1 = (e - 1) / kSegTile;
-    if (t0 == t1) continue;  // finished by segment_reduce_kernel
-    float a[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    int32_t n = 0;
-    constexpr int UNR = 4;  // pieces in flight per lane
-    for (int64_t tb = t0 + r; tb <= t1; tb += (int64_t)R * UNR) {
-      float4 v[UNR][2];
-      int32_t cc[UNR];
+    return;
+  }
+  const int64_t t0 = s / kSegTile, t1 = (e - 1) / kSegTile;
+  if (t0 == t1) return;  // finished by segment_reduce_kernel
+  // item list: head tiles [t0, hb), whole groups [g0, g1), tail tiles [tb, t1]
+  int64_t hb = (t0 / kSegGroup + 1) * kSegGroup;
+  const int64_t tb = (t1 / kSegGroup) * kSegGroup;
+  int64_t g0 = hb / kSegGroup, g1 = tb / kSegGroup;
+  if (hb > tb) {  // t0 and t1 in the same or adjacent groups: tiles only
+    hb = t1 + 1;
+    g0 = g1 = 0;
+  }
+  const int64_t nh = hb - t0, ng = g1 - g0, nt = hb > tb ? 0 : t1 - tb + 1;
+  const int64_t nitems = nh + ng + nt;
+  float a[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  int32_t n = 0;
+  constexpr int UNR = 4;  // items in flight per lane
+  for (int64_t ib = r; ib < nitems; ib += (int64_t)R * UNR) {
+    float4 v[UNR][2];
+    int32_t cc[UNR];
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const int64_t t = tb + (int64_t)u * R;
-        cc[u] = 0;
-        v[u][0] = v[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (t <= t1) {
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t it = ib + (int64_t)u * R;
+      cc[u] = 0;
+      v[u][0] = v[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (it < nitems) {
+        const float* piece;
+        if (it < nh || it >= nh + ng) {
+          const int64_t t = it < nh ? t0 + it : tb + (it - nh - ng);
           const int slot = (t == t0 && s != t0 * kSegTile) ? 1 : 0;
-          const float* piece = P.carry_sum + (t * 2 + slot) * (int64_t)P.Dc;
-#pragma unroll
-          for (int cl = 0; cl < cpl; ++cl) v[u][cl] = *reinterpret_cast<const float4*>(piece + (c0 + cl * lpr) * 4);
+          piece = P.carry_sum + (t * 2 + slot) * (int64_t)P.Dc;
           cc[u] = P.carry_cnt[t * 2 + slot];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {  // ascending tile order within the row
-#pragma unroll
-        for (int cl = 0; cl < 2; ++cl) {
-          a[cl][0] += v[u][cl].x;
-          a[cl][1] += v[u][cl].y;
-          a[cl][2] += v[u][cl].z;
-          a[cl][3] += v[u][cl].w;
-        }
-        n += cc[u];
-      }
-    }
-    for (int off = lpr; off < 64; off <<= 1) {  // fixed tree over the rows
-#pragma unroll
-      for (int cl = 0; cl < 2; ++cl)
-#pragma unroll
-        for (int x = 0; x < 4; ++x) a[cl][x] += __shfl_xor(a[cl][x], off);
-      n += __shfl_xor(n, off);
-    }
-    if (r == 0) {
-#pragma unroll
-      for (int cl = 0; cl < cpl; ++cl)
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int c = (c0 + cl * lpr) * 4 + x;
-          if (c >= P.D) continue;
-          const int64_t o = k * P.D + c;
-          if (P.mode == MODE_MEAN)
-            P.C_new[o] = n > 0 ? a[cl][x] / (float)n : P.C_prev[o];
-          else
-            P.acc_sum[o] += a[cl][x];
-        }
-      if (c0 == 0) {
-        if (P.mode == MODE_MEAN) {
-          if (P.counts) P.counts[k] = n;
         } else {
-          P.acc_cnt[k] += n;
+          const int64_t gi = g0 + (it - nh);
+          piece = P.group_sum + gi * (int64_t)P.Dc;
+          cc[u] = P.group_cnt[gi];
         }
+#pragma unroll
+        for (int cl = 0; cl < cpl; ++cl) v[u][cl] = *reinterpret_cast<const float4*>(piece + (c0 + cl * lpr) * 4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {  // ascending item order within the row
+#pragma unroll
+      for (int cl = 0; cl < 2; ++cl) {
+        a[cl][0] += v[u][cl].x;
+        a[cl][1] += v[u][cl].y;
+        a[cl][2] += v[u][cl].z;
+        a[cl][3] += v[u][cl].w;
+      }
+      n += cc[u];
+    }
+  }
+  for (int off = lpr; off < 64; off <<= 1) {  // fixed tree over the rows
+#pragma unroll
+    for (int cl = 0; cl < 2; ++cl)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) a[cl][x] += __shfl_xor(a[cl][x], off);
+    n += __shfl_xor(n, off);
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int cl = 0; cl < cpl; ++cl)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int c = (c0 + cl * lpr) * 4 + x;
+        if (c >= P.D) continue;
+        const int64_t o = k * P.D + c;
+        if (P.mode == MODE_MEAN)
+          P.C_new[o] = n > 0 ? a[cl][x] / (float)n : P.C_prev[o];
+        else
+          P.acc_sum[o] += a[cl][x];
+      }
+    if (c0 == 0) {
+      if (P.mode == MODE_MEAN) {
+        if (P.counts) P.counts[k] = n;
+      } else {
+        P.acc_cnt[k] += n;
       }
     }
   }
@@ -351,6 +420,8 @@ static SegParams make_params(const ReduceArgs& a) {
   P.off = a.off;
   P.carry_sum = a.carry_sum;
   P.carry_cnt = a.carry_cnt;
+  P.group_sum = a.group_sum;
+  P.group_cnt = a.group_cnt;
   P.Dc = (int)reduce_dc(a.dt, a.D);
   P.mode = a.mode;
   P.C_prev = a.C_prev;
@@ -391,9 +462,18 @@ hipError_t launch_segment_reduce(const ReduceArgs& a, hipStream_t stream) {
 hipError_t launch_fixup(const ReduceArgs& a, hipStream_t stream) {
   if (a.K == 0) return hipSuccess;
   const SegParams P = make_params(a);
-  const int64_t per_block = 4 * kFixupPerWave;
-  const dim3 grid((unsigned)((a.K + per_block - 1) / per_block));
-  if (P.Dc / 4 > 64)
+  const bool wide = P.Dc / 4 > 64;
+  if (a.N > 0) {
+    const int64_t ntiles = (a.N + kSegTile - 1) / kSegTile;
+    const int64_t ngroups = (ntiles + kSegGroup - 1) / kSegGroup;
+    const dim3 gg((unsigned)((ngroups + 3) / 4));
+    if (wide)
+      hipLaunchKernelGGL(carry_group_kernel<2>, gg, dim3(256), 0, stream, P, ngroups);
+    else
+      hipLaunchKernelGGL(carry_group_kernel<1>, gg, dim3(256), 0, stream, P, ngroups);
+  }
+  const dim3 grid((unsigned)((a.K + 3) / 4));
+  if (wide)
     hipLaunchKernelGGL(fixup_kernel<2>, grid, dim3(256), 0, stream, P);
   else
     hipLaunchKernelGGL(fixup_kernel<1>, grid, dim3(256), 0, stream, P);

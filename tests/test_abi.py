@@ -107,3 +107,19 @@ def test_python_binding_rejects_host_tensors():
     C = torch.zeros(2, 8)
     with pytest.raises(ValueError):
         km.assign(X, C)
+
+
+def test_ablation_library_exports_and_validates():
+    from means_clustering_amd import ablation
+    A = ablation.lib()
+    declared = ablation.header_functions()
+    assert len(declared) == 4
+    for name in declared:
+        assert hasattr(A, name), name
+    assert A.kmeans_abl_materialized_bytes(10, 600, 4) == 0  # D > 512
+    assert A.kmeans_abl_materialized_bytes(10, 64, 4) >= 10 * 4 * 4
+    FAKE = ctypes.c_void_p(0x10000)
+    assert A.kmeans_abl_assign_materialized(FAKE, 0, 10, 8, FAKE, 4, FAKE, FAKE, 1 << 30, None) == -1  # fp32 X
+    assert A.kmeans_abl_assign_materialized(FAKE, 1, 10, 8, FAKE, 4, FAKE, FAKE, 8, None) == -1  # scratch too small
+    assert A.kmeans_abl_update_atomic(FAKE, 1, 10, 8, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == -1  # alias
+

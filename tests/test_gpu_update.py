@@ -76,6 +76,20 @@ def test_update_only_first_or_last_cluster(cluster):
     _run(X, np.full(5000, cluster), C_prev, f"only cluster {cluster}")
 
 
+@pytest.mark.parametrize("D,xdtype", [(64, "bf16"), (512, "bf16"), (200, "f32")])
+def test_update_segments_at_group_edges(D, xdtype):
+    """Long segments that start or end on, or one position off, the edges of
+    64-tile (8192-position) carry groups, so that whole groups, head tiles
+    and tail tiles are all summed."""
+    G = 64 * 128
+    sizes = [3 * G, 2 * G + 1, 2 * G - 2, 1, 5 * G + 128, 70 * G - 1, 127, G + 77]
+    a = np.repeat(np.arange(len(sizes) * 2, step=2), sizes)  # every other cluster empty
+    np.random.default_rng(11).shuffle(a)
+    X = _x(a.size, D, xdtype, seed=12 + D)
+    C_prev = torch.randn(len(sizes) * 2, D).to(DEV)
+    _run(X, a, C_prev, f"segments at group edges D={D} {xdtype}")
+
+
 def test_update_five_million_points():
     """Radix blocks of 4096 keys (4 Mi <= N < 8 Mi)."""
     N = 5 * 2**20 + 7
