@@ -7,6 +7,7 @@ HBM.  The default workload is c2 (bf16 N=1,048,576 D=128 K=1,024, 20
 iterations).  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload c1|c2|c3|c4|c5] [--no-cpu-baseline]
+  python bench.py --workload c1 --batch 256      (256 independent c1-shaped problems per call)
 
 --workload c5 runs the host-streamed path (X in pinned host memory).
 """
@@ -193,6 +194,99 @@ def ablation(dev):
     print(json.dumps(out), flush=True)
 
 
+def batched(args, dev):
+    """B independent problems of one workload's shape per call (kmeans_fit_batched); one JSON line.
+
+    Problem b draws its own mixture and points with seed (workload seed + 1000 b), so problem 0 is the
+    workload itself.  ``value`` is Lloyd iterations per second summed over the batch.
+    """
+    import numpy as np
+    import torch
+
+    import means_clustering_amd as km
+    import synth
+
+    base = synth.WORKLOADS[args.workload]
+    if base.chunk_rows:
+        raise SystemExit("--batch applies to device-resident workloads")
+    B = args.batch
+    print(f"[bench] batch of {B} x {base.name}: {base.description}", file=sys.stderr, flush=True)
+    Xs, Cs = [], []
+    for b in range(B):
+        w = base.scaled(seed=base.seed + 1000 * b)
+        Xn = synth.points(w)
+        Cs.append(synth.init_centroids(w, Xn))
+        Xs.append(Xn)
+    Xn = np.stack(Xs)
+    del Xs
+    X = (torch.from_numpy(Xn.view(np.int16)).view(torch.bfloat16) if base.dtype == "bf16"
+         else torch.from_numpy(Xn)).to(dev)
+    C0 = torch.from_numpy(np.stack(Cs)).to(dev)
+    C = C0.clone()
+    a = torch.empty((B, base.N), dtype=torch.int32, device=dev)
+    counts = torch.empty((B, base.K), dtype=torch.int32, device=dev)
+    ws = km.Workspace(dev)
+
+    def one_step():
+        C.copy_(C0)
+        km.fit_batched(X, C, base.iters, inplace=True, ws=ws, assign_out=a, counts_out=counts)
+
+    for i in range(args.warmup):
+        one_step()
+        torch.cuda.synchronize()
+        print(f"[bench] warmup step {i} done", file=sys.stderr, flush=True)
+    timing = not args.no_timing
+    if timing:
+        km.timing_reset()
+        km.timing_enable(2)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    if timing:
+        km.timing_enable(False)
+    value = args.steps * base.iters * B / elapsed
+    roof, breakdown = None, {}
+    if timing:
+        ms, n = km.timing_read("assign")
+        km.timing_reset()
+        if n:
+            flops = 2.0 * B * base.N * base.K * base.D
+            avg_s = ms * 1e-3 / n
+            peak = PEAK[base.dtype]
+            roof = {"bound": "mfma", "kernel": "flash_assign (batched)", "achieved": round(flops / avg_s / 1e12, 2),
+                    "peak": round(peak / 1e12, 1), "unit": "TFLOP/s", "frac": round(flops / avg_s / peak, 4),
+                    "traffic": None, "flops_per_launch": flops, "avg_launch_us": round(avg_s * 1e6, 3)}
+        km.timing_enable(1)
+        one_step()
+        torch.cuda.synchronize()
+        km.timing_enable(False)
+        for ph in km.PHASES:
+            ms, n = km.timing_read(ph)
+            if n:
+                breakdown[ph] = {"total_ms": round(ms, 4), "launches": n, "avg_us": round(1e3 * ms / n, 3)}
+        km.timing_reset()
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline: timing the oracle on problem 0", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(base, Cs[0], lambda r: Xn[0][:r], budget_s=args.cpu_budget)
+        cpu["sample"] += " (one problem of the batch; iterations/s of one problem)"
+    line = {
+        "metric": "Lloyd iterations/sec and point-centroid distances/sec (fused assign+update)",
+        "value": round(value, 3), "unit": "iterations/s (summed over the batch)", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1e3 * elapsed / args.steps, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": base.dtype, "data": "synthetic",
+        "config": {"workload": f"{B} independent problems of {base.description}", "name": base.name, "batch": B,
+                   "N": base.N, "D": base.D, "K": base.K, "iters_per_step": base.iters},
+        "distances_per_s": round(value * base.N * base.K, 1),
+        "roofline": roof, "cpu_baseline": cpu, "phase_breakdown_extra_step": breakdown,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,6 +297,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-timing", action="store_true", help="no per-kernel events (for profiler runs)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the same-run peak probes")
+    ap.add_argument("--batch", type=int, default=1,
+                    help="B > 1: time B independent problems of the workload's shape per call (batched fit)")
     ap.add_argument("--ablation", action="store_true",
                     help="only time the materialised-distance assignment and the atomic scatter update "
                          "against FlashAssign and Sort-Inverse Update (one JSON line)")
@@ -226,6 +322,11 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding of this "
               "path is a design note, not a measured configuration.", file=sys.stderr)
         sys.exit(2)
+
+    if args.batch > 1:
+        import torch
+        batched(args, torch.device("cuda:0"))
+        return
 
     import numpy as np
     import torch

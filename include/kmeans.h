@@ -184,6 +184,41 @@ km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_
                               double* objective, void* ws, size_t ws_bytes, void* compute_stream,
                               void* copy_stream, void* stage_host, size_t stage_bytes);
 
+/*
+ * kmeans_workspace_bytes_batched -- workspace bytes for kmeans_fit_batched
+ * (B problems of N points, D dimensions and K clusters each).  Returns 0 if
+ * the arguments are invalid.
+ */
+size_t kmeans_workspace_bytes_batched(int64_t B, int64_t N, int64_t D, int64_t K, km_dtype dt);
+
+/*
+ * kmeans_fit_batched -- Lloyd iterations of B independent problems of one
+ * shape in the same launches.  The page treats K-Means as an online
+ * primitive called at high frequency inside AI pipelines (tech §1, tech §5);
+ * a single small problem leaves the GPU idle between short kernels, so here
+ * every phase of an iteration covers all B problems at once: one centroid
+ * preparation, one FlashAssign launch (workgroups split over the problems),
+ * and one sort-inverse update over B*N points whose cluster ids are made
+ * distinct per problem (b*K + k), so each problem's clusters get their own
+ * segments.  Each problem follows the same rules as kmeans_fit.
+ *   X          device, B x N x D, type dt (problem b is rows b*N .. b*N+N-1)
+ *   C          device B x K x D fp32: initial centroids in, C^iters out
+ *   assign     device int32[B*N] or NULL: per-problem ids in [0, K) of the
+ *              last iteration
+ *   counts     device int32[B*K] or NULL: counts that formed C^iters
+ *   objective  device double[iters*B] or NULL: objective[t*B + b] = sum of
+ *              squared distances of problem b in iteration t (fp32 terms,
+ *              fp64 sum)
+ *   Limits: as kmeans_fit per problem, and B >= 1, B*N < 2^31, B*K < 2^31.
+ *   iters = 0 leaves every output untouched.  Centroid sums of different
+ *   problems never mix; the summation order inside a problem may differ
+ *   from kmeans_fit on that problem alone (fp32 rounding only), and the
+ *   assignment of a given centroid state is the same bit for bit.
+ */
+km_status kmeans_fit_batched(const void* X, km_dtype dt, int64_t B, int64_t N, int64_t D, int64_t K, float* C,
+                             int32_t iters, int32_t* assign, int32_t* counts, double* objective, void* ws,
+                             size_t ws_bytes, void* stream);
+
 /* Short constant description of a status code. */
 const char* kmeans_status_string(km_status s);
 

@@ -16,6 +16,7 @@ Entry points (all tensors on one ROCm device unless stated):
   update(X, a, C_prev)               means, empty keeps previous  (tech §2.2 Sort-Inverse Update)
   fit(X, C0, iters)                  Lloyd iterations, X resident
   fit_streamed(X_host, C0, iters, chunk_rows)   X in host memory (tech §2.3 chunked overlap)
+  fit_batched(X, C0, iters)          B independent problems per launch (tech §1 online primitive)
 """
 from __future__ import annotations
 
@@ -56,6 +57,8 @@ def _bind(lib):
         "kmeans_fit": (c_int, [vp, c_int, i64, i64, i64, vp, ctypes.c_int32, vp, vp, vp, vp, sz, vp]),
         "kmeans_fit_streamed": (c_int, [vp, c_int, i64, i64, i64, vp, ctypes.c_int32, i64, vp, vp, vp, vp, sz, vp,
                                         vp, vp, sz]),
+        "kmeans_workspace_bytes_batched": (sz, [i64, i64, i64, i64, c_int]),
+        "kmeans_fit_batched": (c_int, [vp, c_int, i64, i64, i64, i64, vp, ctypes.c_int32, vp, vp, vp, vp, sz, vp]),
         "kmeans_status_string": (ctypes.c_char_p, [c_int]),
         "kmeans_last_error": (ctypes.c_char_p, []),
         "kmeans_timing_enable": (c_int, [c_int]),
@@ -211,6 +214,36 @@ def fit(X: torch.Tensor, C0: torch.Tensor, iters: int, objective: bool = False, 
     w = _ws(ws, nb, X.device)
     _check(lib().kmeans_fit(_ptr(X), _dtype(X), N, D, K, _ptr(C), int(iters), _ptr(a), _ptr(counts), _ptr(obj),
                             _ptr(w), w.numel(), ctypes.c_void_p(_stream(X.device))))
+    return C, a, counts, (obj[:iters] if obj is not None else None)
+
+
+def fit_batched(X: torch.Tensor, C0: torch.Tensor, iters: int, objective: bool = False, inplace: bool = False,
+                ws: Workspace | None = None, assign_out: torch.Tensor | None = None,
+                counts_out: torch.Tensor | None = None, objective_out: torch.Tensor | None = None):
+    """Lloyd iterations of B independent problems: X is B x N x D, C0 is B x K x D (fp32).
+
+    Returns (C [B, K, D], assign int32 [B, N], counts int32 [B, K], objective fp64 [iters, B] or None).
+    """
+    if not X.is_cuda or not C0.is_cuda:
+        raise ValueError("X and C0 must be device tensors")
+    if X.dim() != 3 or C0.dim() != 3 or X.shape[0] != C0.shape[0] or X.shape[2] != C0.shape[2]:
+        raise ValueError("X must be B x N x D and C0 B x K x D")
+    if C0.dtype != torch.float32:
+        raise TypeError("centroids must be float32")
+    if not X.is_contiguous() or not C0.is_contiguous():
+        raise ValueError("X and C0 must be contiguous")
+    B, N, D = X.shape
+    K = C0.shape[1]
+    C = C0 if inplace else C0.clone()
+    a = assign_out if assign_out is not None else torch.empty((B, N), dtype=torch.int32, device=X.device)
+    counts = counts_out if counts_out is not None else torch.empty((B, K), dtype=torch.int32, device=X.device)
+    obj = objective_out
+    if objective and obj is None:
+        obj = torch.empty((max(iters, 1), B), dtype=torch.float64, device=X.device)
+    nb = int(lib().kmeans_workspace_bytes_batched(B, N, D, K, _dtype(X)))
+    w = _ws(ws, nb, X.device)
+    _check(lib().kmeans_fit_batched(_ptr(X), _dtype(X), B, N, D, K, _ptr(C), int(iters), _ptr(a), _ptr(counts),
+                                    _ptr(obj), _ptr(w), w.numel(), ctypes.c_void_p(_stream(X.device))))
     return C, a, counts, (obj[:iters] if obj is not None else None)
 
 

@@ -223,6 +223,42 @@ static StreamBufs carve_streamed(Carve& c, int64_t rows, int64_t D, int64_t K, k
   return s;
 }
 
+// Batched fit: B problems of one shape.  The update treats the batch as one
+// problem of B*N points and B*K clusters (composite id b*K + k), so one sort
+// and one segmented reduction serve every problem.
+struct BatchBufs {
+  void* frag;  // B x frag_bytes
+  UpdateBufs u;
+  int32_t* ids;  // B*N composite ids
+  float* min_dist;
+};
+
+static BatchBufs carve_batched(Carve& c, int64_t B, int64_t N, int64_t D, int64_t K, km_dtype dt) {
+  BatchBufs b;
+  b.frag = c.take<uint8_t>((size_t)B * assign_geom(N, D, K, dt).frag_bytes());
+  b.u = carve_update(c, sort_geom(B * N, B * K), D, dt);
+  const size_t n = (size_t)(B * N > 0 ? B * N : 1);
+  b.ids = c.take<int32_t>(n);
+  b.min_dist = c.take<float>(n);
+  return b;
+}
+
+static km_status check_batch(int64_t B, int64_t N, int64_t D, int64_t K, km_dtype dt) {
+  km_status st = check_sizes(N, D, K, dt, true);
+  if (st != KM_OK) return st;
+  if (B < 1 || B >= kMaxN) return fail(KM_ERR_INVALID_VALUE, "B must satisfy 1 <= B < 2^31");
+  if (B * N >= kMaxN) return fail(KM_ERR_UNSUPPORTED, "B*N must be < 2^31");
+  if (B * K >= kMaxN) return fail(KM_ERR_UNSUPPORTED, "B*K must be < 2^31");
+  if (B * K * D >= kMaxN * 64) return fail(KM_ERR_UNSUPPORTED, "B*K*D too large");
+  return KM_OK;
+}
+
+static size_t workspace_bytes_batched_impl(int64_t B, int64_t N, int64_t D, int64_t K, km_dtype dt) {
+  Carve c(nullptr);
+  carve_batched(c, B, N, D, K, dt);
+  return (c.used + 255) / 256 * 256;
+}
+
 static size_t workspace_bytes_impl(km_op op, int64_t N, int64_t D, int64_t K, km_dtype dt, int64_t chunk_rows) {
   Carve c(nullptr);
   switch (op) {
@@ -505,6 +541,47 @@ km_status kmeans_fit(const void* X, km_dtype dt, int64_t N, int64_t D, int64_t K
     st = run_update(X, dt, N, D, a, K, C, C, counts, f.u, MODE_MEAN, nullptr, nullptr, s, &prev, &order);
     if (st != KM_OK) return st;
   }
+  return KM_OK;
+}
+
+size_t kmeans_workspace_bytes_batched(int64_t B, int64_t N, int64_t D, int64_t K, km_dtype dt) {
+  if (check_batch(B, N, D, K, dt) != KM_OK) return 0;
+  return workspace_bytes_batched_impl(B, N, D, K, dt);
+}
+
+km_status kmeans_fit_batched(const void* X, km_dtype dt, int64_t B, int64_t N, int64_t D, int64_t K, float* C,
+                             int32_t iters, int32_t* assign, int32_t* counts, double* objective, void* ws,
+                             size_t ws_bytes, void* stream) {
+  km_status st = check_batch(B, N, D, K, dt);
+  if (st != KM_OK) return st;
+  if (iters < 0) return fail(KM_ERR_INVALID_VALUE, "iters must be >= 0");
+  if (!C || (N > 0 && !X)) return fail(KM_ERR_INVALID_VALUE, "X and C must be non-NULL");
+  if (!aligned(X, dt == KM_F32 ? 4 : 2) || !aligned(C, 4) || !aligned(assign, 4) || !aligned(counts, 4) ||
+      !aligned(objective, 8))
+    return fail(KM_ERR_INVALID_VALUE, "misaligned pointer");
+  st = check_ws(ws, ws_bytes, workspace_bytes_batched_impl(B, N, D, K, dt));
+  if (st != KM_OK) return st;
+  if (iters == 0) return KM_OK;
+  hipStream_t s = (hipStream_t)stream;
+  Carve c(ws);
+  const BatchBufs b = carve_batched(c, B, N, D, K, dt);
+  const AssignGeom g = assign_geom(N, D, K, dt);
+  for (int32_t t = 0; t < iters; ++t) {
+    KM_TIMED("prep", s, return launch_prep(g, C, b.frag, s, B));
+    if (N > 0)
+      KM_TIMED("assign", s,
+               return launch_flash_assign(g, X, N, b.frag, b.ids, objective ? b.min_dist : nullptr, s, nullptr,
+                                          nullptr, B, (int32_t)K));
+    if (objective)
+      KM_TIMED("objective", s, return launch_objective_batched(b.min_dist, B, N, objective + (int64_t)t * B, s));
+    if (N == 0) {
+      if (counts) KM_HIP(launch_zero(counts, sizeof(int32_t) * (size_t)(B * K), s));
+      continue;
+    }
+    st = run_update(X, dt, B * N, D, b.ids, B * K, C, C, counts, b.u, MODE_MEAN, nullptr, nullptr, s);
+    if (st != KM_OK) return st;
+  }
+  if (assign && N > 0) KM_TIMED("finalize", s, return launch_local_ids(b.ids, B, N, K, assign, s));
   return KM_OK;
 }
 

@@ -80,11 +80,16 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
 // squares of the quantised values meet in LDS, and -||Q(c)||^2/2 (fp32) is
 // written in the order the FlashAssign lanes read it.  Padding rows get zero
 // fragments and a bias of -inf, so they can never be selected.
+// Batched: workgroup w prepares group w % groups of problem w / groups, whose
+// centroids start K*D floats and whose fragments start f_stride slots further.
 __global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ C, int64_t K, int D, int dt, AssignCfg cfg,
-                                                   int64_t groups, u32x4_t* __restrict__ frag) {
+                                                   int64_t groups, u32x4_t* __restrict__ frag, int64_t f_stride) {
   __shared__ float part[4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t g = blockIdx.x;
+  const int64_t bz = (int64_t)blockIdx.x / groups;
+  const int64_t g = (int64_t)blockIdx.x - bz * groups;
+  C += bz * K * D;
+  frag += bz * f_stride;
   const bool wide = cfg.rows == 32;
   const int rsel = wide ? (lane & 31) : (lane & 15);
   const int piece = wide ? (lane >> 5) : (lane >> 4);  // which 8 (wide) or 4 (narrow) depth values
@@ -145,10 +150,11 @@ __global__ __launch_bounds__(256) void prep_kernel(const float* __restrict__ C, 
   }
 }
 
-hipError_t launch_prep(const AssignGeom& g, const float* C, void* frag, hipStream_t stream) {
+hipError_t launch_prep(const AssignGeom& g, const float* C, void* frag, hipStream_t stream, int64_t B) {
   const int64_t groups = g.groups();
-  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)groups), dim3(256), 0, stream, C, g.K, (int)g.D, g.dt, g.cfg, groups,
-                     (u32x4_t*)frag);
+  if (B < 1 || groups * B >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(groups * B)), dim3(256), 0, stream, C, g.K, (int)g.D, g.dt, g.cfg,
+                     groups, (u32x4_t*)frag, (int64_t)(g.frag_bytes() / 16));
   return hipGetLastError();
 }
 
@@ -404,7 +410,7 @@ template <int DT, int KB, bool LAZY, bool WARM>
 __global__ __launch_bounds__(wide_cfg(KB).W * 64) void flash_assign_wide_kernel(
     const uint8_t* __restrict__ X, int64_t N, int D, bool vec_ok, const u32x4_t* __restrict__ frag, int ntiles,
     int32_t* __restrict__ assign, float* __restrict__ min_dist, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ prev, int64_t K) {
+    const int32_t* __restrict__ prev, int64_t K, Batch bt) {
   constexpr AssignCfg cfg = wide_cfg(KB);
   constexpr int NB = cfg.NB, CT = cfg.CT, W = cfg.W;
   constexpr int GS = (int)cfg.group_slots();
@@ -419,7 +425,13 @@ __global__ __launch_bounds__(wide_cfg(KB).W * 64) void flash_assign_wide_kernel(
   const int wave = threadIdx.x >> 6;
   const int col = lane & 31;
   const int h = lane >> 5;
-  const int64_t wbase = ((int64_t)blockIdx.x * W + wave) * (NB * 32);
+  const uint32_t bz = blockIdx.x / bt.bpp;  // problem of this workgroup (0 unless batched)
+  const int64_t wbase = ((int64_t)(blockIdx.x - bz * bt.bpp) * W + wave) * (NB * 32);
+  X += (int64_t)bz * bt.x_stride;
+  frag += (int64_t)bz * bt.f_stride;
+  assign += (int64_t)bz * N;
+  if (min_dist) min_dist += (int64_t)bz * N;
+  const int32_t id_base = (int32_t)bz * bt.id_mul;
 
   // the point each lane scores, per point group (its row of X, or N past the end)
   int64_t pt[NB];
@@ -532,7 +544,7 @@ __global__ __launch_bounds__(wide_cfg(KB).W * 64) void flash_assign_wide_kernel(
     if (k == INT32_MAX) k = 0;  // no finite score (NaN input): index 0
     const int64_t p = pt[g];
     if (h == 0 && p < N) {
-      assign[p] = k;
+      assign[p] = k + id_base;
       if (min_dist) min_dist[p] = fmaxf(xn[g] - 2.0f * b, 0.0f);
     }
   }
@@ -547,7 +559,7 @@ template <int DT, int KB, bool LAZY, bool WARM>
 __global__ __launch_bounds__(wide8_cfg(KB).W * 64) __attribute__((amdgpu_waves_per_eu(KM_W8_WPE))) void flash_assign_w8_kernel(
     const uint8_t* __restrict__ X, int64_t N, int D, bool vec_ok, const u32x4_t* __restrict__ frag, int ntiles,
     int32_t* __restrict__ assign, float* __restrict__ min_dist, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ prev, int64_t K) {
+    const int32_t* __restrict__ prev, int64_t K, Batch bt) {
   constexpr AssignCfg cfg = wide8_cfg(KB);
   constexpr int NB = cfg.NB, CT = cfg.CT, W = cfg.W;
   constexpr int GS = (int)cfg.group_slots();
@@ -561,7 +573,13 @@ __global__ __launch_bounds__(wide8_cfg(KB).W * 64) __attribute__((amdgpu_waves_p
   const int wave = threadIdx.x >> 6;
   const int col = lane & 31;
   const int h = lane >> 5;
-  const int64_t wbase = ((int64_t)blockIdx.x * W + wave) * (NB * 32);
+  const uint32_t bz = blockIdx.x / bt.bpp;  // problem of this workgroup (0 unless batched)
+  const int64_t wbase = ((int64_t)(blockIdx.x - bz * bt.bpp) * W + wave) * (NB * 32);
+  X += (int64_t)bz * bt.x_stride;
+  frag += (int64_t)bz * bt.f_stride;
+  assign += (int64_t)bz * N;
+  if (min_dist) min_dist += (int64_t)bz * N;
+  const int32_t id_base = (int32_t)bz * bt.id_mul;
 
   // the point each lane scores (its row of X, or N past the end); looked up
   // again at the end rather than kept live through the sweep
@@ -670,7 +688,7 @@ __global__ __launch_bounds__(wide8_cfg(KB).W * 64) __attribute__((amdgpu_waves_p
     }
     const int64_t p = point_of(g);
     if (h == 0 && p < N) {
-      assign[p] = k;
+      assign[p] = k + id_base;
       if (min_dist) min_dist[p] = fmaxf(xn - 2.0f * b, 0.0f);
     }
   }
@@ -694,7 +712,7 @@ __device__ __forceinline__ f32x4_t mma16_f32(u32x4_t a, u32x4_t b, f32x4_t c) {
 template <int KB>
 __global__ __launch_bounds__(narrow_cfg(KB).W * 64) void flash_assign_narrow_kernel(
     const uint8_t* __restrict__ X, int64_t N, int D, bool vec_ok, const u32x4_t* __restrict__ frag, int ntiles,
-    int32_t* __restrict__ assign, float* __restrict__ min_dist) {
+    int32_t* __restrict__ assign, float* __restrict__ min_dist, Batch bt) {
   constexpr AssignCfg cfg = narrow_cfg(KB);
   constexpr int NB = cfg.NB, CT = cfg.CT, W = cfg.W;
   constexpr int GS = (int)cfg.group_slots();
@@ -708,7 +726,13 @@ __global__ __launch_bounds__(narrow_cfg(KB).W * 64) void flash_assign_narrow_ker
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
   const int quad = lane >> 4;
-  const int64_t wbase = ((int64_t)blockIdx.x * W + wave) * (NB * 16);
+  const uint32_t bz = blockIdx.x / bt.bpp;  // problem of this workgroup (0 unless batched)
+  const int64_t wbase = ((int64_t)(blockIdx.x - bz * bt.bpp) * W + wave) * (NB * 16);
+  X += (int64_t)bz * bt.x_stride;
+  frag += (int64_t)bz * bt.f_stride;
+  assign += (int64_t)bz * N;
+  if (min_dist) min_dist += (int64_t)bz * N;
+  const int32_t id_base = (int32_t)bz * bt.id_mul;
 
   u32x4_t xb[NB][KB];
   float xn[NB];
@@ -801,7 +825,7 @@ __global__ __launch_bounds__(narrow_cfg(KB).W * 64) void flash_assign_narrow_ker
     if (k == INT32_MAX) k = 0;
     const int64_t p = wbase + g * 16 + col;
     if (quad == 0 && p < N) {
-      assign[p] = k;
+      assign[p] = k + id_base;
       if (min_dist) min_dist[p] = fmaxf(xn[g] - 2.0f * b, 0.0f);
     }
   }
@@ -813,76 +837,98 @@ static bool same_cfg(const AssignCfg& a, const AssignCfg& b) {
   return a.rows == b.rows && a.KB == b.KB && a.NB == b.NB && a.CT == b.CT && a.W == b.W;
 }
 
+// Workgroups per problem times problems; the batch strides follow from the shape.
+static Batch make_batch(const AssignGeom& g, int64_t N, int64_t blocks, int32_t id_mul) {
+  Batch b;
+  b.bpp = (uint32_t)blocks;
+  b.id_mul = id_mul;
+  b.x_stride = N * g.D * (int64_t)dtype_size(g.dt);
+  b.f_stride = (int64_t)(g.frag_bytes() / 16);
+  return b;
+}
+
 template <int DT, int KB>
 static hipError_t launch_wide8(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
-                               float* min_dist, const int32_t* perm, const int32_t* prev, hipStream_t s) {
+                               float* min_dist, const int32_t* perm, const int32_t* prev, int64_t B, int32_t id_mul,
+                               hipStream_t s) {
   constexpr AssignCfg cfg = wide8_cfg(KB);
   if (!same_cfg(g.cfg, cfg)) return hipErrorInvalidValue;
   const int64_t pts = (int64_t)cfg.W * cfg.NB * 32;
+  const int64_t blocks = (N + pts - 1) / pts;
+  if (blocks * B >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const bool vec_ok = (((uintptr_t)X) % 16 == 0) && ((g.D * 2) % 16 == 0);
-  const dim3 grid((unsigned)((N + pts - 1) / pts)), block(cfg.W * 64);
+  const dim3 grid((unsigned)(blocks * B)), block(cfg.W * 64);
+  const Batch bt = make_batch(g, N, blocks, id_mul);
   const uint8_t* x = (const uint8_t*)X;
   const u32x4_t* f = (const u32x4_t*)frag;
   const int nt = (int)g.ntiles();
   if (perm)
     hipLaunchKernelGGL((flash_assign_w8_kernel<DT, KB, true, true>), grid, block, 0, s, x, N, (int)g.D, vec_ok, f,
-                       nt, assign, min_dist, perm, prev, g.K);
+                       nt, assign, min_dist, perm, prev, g.K, bt);
   else if (g.lazy)
     hipLaunchKernelGGL((flash_assign_w8_kernel<DT, KB, true, false>), grid, block, 0, s, x, N, (int)g.D, vec_ok, f,
-                       nt, assign, min_dist, perm, prev, g.K);
+                       nt, assign, min_dist, perm, prev, g.K, bt);
   else
     hipLaunchKernelGGL((flash_assign_w8_kernel<DT, KB, false, false>), grid, block, 0, s, x, N, (int)g.D, vec_ok,
-                       f, nt, assign, min_dist, perm, prev, g.K);
+                       f, nt, assign, min_dist, perm, prev, g.K, bt);
   return hipGetLastError();
 }
 
 template <int DT, int KB>
 static hipError_t launch_wide(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
-                              float* min_dist, const int32_t* perm, const int32_t* prev, hipStream_t s) {
+                              float* min_dist, const int32_t* perm, const int32_t* prev, int64_t B, int32_t id_mul,
+                              hipStream_t s) {
   if constexpr (KB <= kWide8MaxKB) {
-    if (same_cfg(g.cfg, wide8_cfg(KB))) return launch_wide8<DT, KB>(g, X, N, frag, assign, min_dist, perm, prev, s);
+    if (same_cfg(g.cfg, wide8_cfg(KB)))
+      return launch_wide8<DT, KB>(g, X, N, frag, assign, min_dist, perm, prev, B, id_mul, s);
   }
   constexpr AssignCfg cfg = wide_cfg(KB);
   // The centroid fragments were laid out with the caller's geometry: it must be
   // the one this kernel was compiled for (both come from one header).
   if (!same_cfg(g.cfg, cfg)) return hipErrorInvalidValue;
   const int64_t pts = (int64_t)cfg.W * cfg.NB * 32;
+  const int64_t blocks = (N + pts - 1) / pts;
+  if (blocks * B >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const bool vec_ok = (((uintptr_t)X) % 16 == 0) && ((g.D * 2) % 16 == 0);
-  const dim3 grid((unsigned)((N + pts - 1) / pts)), block(cfg.W * 64);
+  const dim3 grid((unsigned)(blocks * B)), block(cfg.W * 64);
+  const Batch bt = make_batch(g, N, blocks, id_mul);
   const uint8_t* x = (const uint8_t*)X;
   const u32x4_t* f = (const u32x4_t*)frag;
   const int nt = (int)g.ntiles();
   if (perm)
     hipLaunchKernelGGL((flash_assign_wide_kernel<DT, KB, true, true>), grid, block, 0, s, x, N, (int)g.D, vec_ok, f,
-                       nt, assign, min_dist, perm, prev, g.K);
+                       nt, assign, min_dist, perm, prev, g.K, bt);
   else if (g.lazy)
     hipLaunchKernelGGL((flash_assign_wide_kernel<DT, KB, true, false>), grid, block, 0, s, x, N, (int)g.D, vec_ok, f,
-                       nt, assign, min_dist, perm, prev, g.K);
+                       nt, assign, min_dist, perm, prev, g.K, bt);
   else
     hipLaunchKernelGGL((flash_assign_wide_kernel<DT, KB, false, false>), grid, block, 0, s, x, N, (int)g.D, vec_ok,
-                       f, nt, assign, min_dist, perm, prev, g.K);
+                       f, nt, assign, min_dist, perm, prev, g.K, bt);
   return hipGetLastError();
 }
 
 template <int KB>
 static hipError_t launch_narrow(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
-                                float* min_dist, hipStream_t s) {
+                                float* min_dist, int64_t B, int32_t id_mul, hipStream_t s) {
   constexpr AssignCfg cfg = narrow_cfg(KB);
   if (!same_cfg(g.cfg, cfg)) return hipErrorInvalidValue;
   const int64_t pts = (int64_t)cfg.W * cfg.NB * 16;
+  const int64_t blocks = (N + pts - 1) / pts;
+  if (blocks * B >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const bool vec_ok = (((uintptr_t)X) % 16 == 0) && ((g.D * 4) % 16 == 0);
-  hipLaunchKernelGGL((flash_assign_narrow_kernel<KB>), dim3((unsigned)((N + pts - 1) / pts)), dim3(cfg.W * 64), 0, s,
+  hipLaunchKernelGGL((flash_assign_narrow_kernel<KB>), dim3((unsigned)(blocks * B)), dim3(cfg.W * 64), 0, s,
                      (const uint8_t*)X, N, (int)g.D, vec_ok, (const u32x4_t*)frag, (int)g.ntiles(), assign,
-                     min_dist);
+                     min_dist, make_batch(g, N, blocks, id_mul));
   return hipGetLastError();
 }
 
 template <int DT>
 static hipError_t dispatch_wide(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
-                                float* min_dist, const int32_t* perm, const int32_t* prev, hipStream_t s) {
+                                float* min_dist, const int32_t* perm, const int32_t* prev, int64_t B, int32_t id_mul,
+                                hipStream_t s) {
   switch (g.cfg.KB) {
 #define KM_CASE(n) \
-  case n: return launch_wide<DT, n>(g, X, N, frag, assign, min_dist, perm, prev, s);
+  case n: return launch_wide<DT, n>(g, X, N, frag, assign, min_dist, perm, prev, B, id_mul, s);
     KM_CASE(1) KM_CASE(2) KM_CASE(3) KM_CASE(4) KM_CASE(5) KM_CASE(6) KM_CASE(7) KM_CASE(8)
     KM_CASE(10) KM_CASE(12) KM_CASE(14) KM_CASE(16) KM_CASE(20) KM_CASE(24) KM_CASE(28) KM_CASE(32)
 #undef KM_CASE
@@ -891,16 +937,18 @@ static hipError_t dispatch_wide(const AssignGeom& g, const void* X, int64_t N, c
 }
 
 hipError_t launch_flash_assign(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
-                               float* min_dist, hipStream_t stream, const int32_t* perm, const int32_t* prev) {
+                               float* min_dist, hipStream_t stream, const int32_t* perm, const int32_t* prev,
+                               int64_t B, int32_t id_mul) {
   if (N == 0) return hipSuccess;
   if ((perm == nullptr) != (prev == nullptr)) return hipErrorInvalidValue;
+  if (B < 1 || (perm && B != 1)) return hipErrorInvalidValue;  // the warm order is per problem
   switch (g.dt) {
-    case DT_BF16: return dispatch_wide<DT_BF16>(g, X, N, frag, assign, min_dist, perm, prev, stream);
-    case DT_F16: return dispatch_wide<DT_F16>(g, X, N, frag, assign, min_dist, perm, prev, stream);
+    case DT_BF16: return dispatch_wide<DT_BF16>(g, X, N, frag, assign, min_dist, perm, prev, B, id_mul, stream);
+    case DT_F16: return dispatch_wide<DT_F16>(g, X, N, frag, assign, min_dist, perm, prev, B, id_mul, stream);
     case DT_F32:
       switch (g.cfg.KB) {
 #define KM_CASE(n) \
-  case n: return launch_narrow<n>(g, X, N, frag, assign, min_dist, stream);
+  case n: return launch_narrow<n>(g, X, N, frag, assign, min_dist, B, id_mul, stream);
         KM_CASE(1) KM_CASE(2) KM_CASE(3) KM_CASE(4) KM_CASE(5) KM_CASE(6) KM_CASE(7) KM_CASE(8)
         KM_CASE(9) KM_CASE(10) KM_CASE(11) KM_CASE(12) KM_CASE(13) KM_CASE(14) KM_CASE(15) KM_CASE(16)
 #undef KM_CASE

@@ -184,18 +184,31 @@ struct SortGeom {
   int64_t count_len;  // max over passes of (2^bits * nblk)
 };
 
+// Several independent problems of one shape in one launch.  Workgroup w works
+// on problem b = w / bpp; that problem's X, centroid fragments and outputs
+// start b * x_stride bytes, b * f_stride fragment slots and b * N entries
+// further, and its cluster ids are written as b * id_mul + k.
+struct Batch {
+  uint32_t bpp;      // workgroups per problem
+  int32_t id_mul;
+  int64_t x_stride;
+  int64_t f_stride;
+};
+
 // ---------------------------------------------------------------------------
 // Launchers (all asynchronous on `stream`; they return the launch status).
 // ---------------------------------------------------------------------------
-hipError_t launch_prep(const AssignGeom& g, const float* C, void* frag, hipStream_t stream);
+// B problems: C holds B x K x D floats, frag B x frag_bytes().
+hipError_t launch_prep(const AssignGeom& g, const float* C, void* frag, hipStream_t stream, int64_t B = 1);
 
 // perm/prev (both or neither): visit points in the order perm[0..N), where
 // prev[i] is the previous centroid of point perm[i]; the result is the same,
 // only faster when the assignment changes little (16-bit X only; ignored for
-// fp32 X).
+// fp32 X).  B > 1 (no perm/prev): B problems of N points each, X holding
+// B x N rows and assign/min_dist B x N entries; ids are written as b*id_mul + k.
 hipError_t launch_flash_assign(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
                                float* min_dist, hipStream_t stream, const int32_t* perm = nullptr,
-                               const int32_t* prev = nullptr);
+                               const int32_t* prev = nullptr, int64_t B = 1, int32_t id_mul = 0);
 
 // Radix argsort of cluster ids.  keys_in: the assignment vector.  The passes
 // ping-pong through (key_a, val_a) and (key_b, val_b); the last pass writes
@@ -245,5 +258,9 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 int64_t objective_partials(int64_t n);
 hipError_t launch_objective(const float* v, int64_t n, double* partials, double* out, int accumulate,
                             hipStream_t stream);
+// out[b] = sum of v[b*n .. (b+1)*n) in fp64 with a fixed reduction order, b < B.
+hipError_t launch_objective_batched(const float* v, int64_t B, int64_t n, double* out, hipStream_t stream);
+// out[i] = ids[i] - (i / n) * K for i < B*n: composite ids of a batch back to per-problem ids.
+hipError_t launch_local_ids(const int32_t* ids, int64_t B, int64_t n, int64_t K, int32_t* out, hipStream_t stream);
 
 }  // namespace km

@@ -568,4 +568,41 @@ hipError_t launch_objective(const float* v, int64_t n, double* partials, double*
   return hipGetLastError();
 }
 
+// One workgroup per problem: a strided fp64 sum per thread, then a fixed tree.
+__global__ __launch_bounds__(kObjThreads) void objective_batched_kernel(const float* __restrict__ v, int64_t n,
+                                                                        double* __restrict__ out) {
+  __shared__ double red[kObjThreads];
+  const float* vb = v + (int64_t)blockIdx.x * n;
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += kObjThreads) s += (double)vb[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int st = kObjThreads / 2; st > 0; st >>= 1) {
+    if ((int)threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[blockIdx.x] = red[0];
+}
+
+hipError_t launch_objective_batched(const float* v, int64_t B, int64_t n, double* out, hipStream_t stream) {
+  if (B < 1 || B >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(objective_batched_kernel, dim3((unsigned)B), dim3(kObjThreads), 0, stream, v, n, out);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void local_ids_kernel(const int32_t* __restrict__ ids, int64_t total, int64_t n,
+                                                        int64_t K, int32_t* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256)
+    out[i] = (int32_t)((int64_t)ids[i] - (i / n) * K);
+}
+
+hipError_t launch_local_ids(const int32_t* ids, int64_t B, int64_t n, int64_t K, int32_t* out, hipStream_t stream) {
+  const int64_t total = B * n;
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(local_ids_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, ids, total, n, K, out);
+  return hipGetLastError();
+}
+
 }  // namespace km

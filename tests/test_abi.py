@@ -17,7 +17,7 @@ def test_exports_every_declared_function(L):
     assert "kmeans_assign" in declared and "kmeans_fit_streamed" in declared
     for name in declared:
         assert hasattr(L, name), name
-    assert len(declared) == 11
+    assert len(declared) == 13
 
 
 def test_status_strings(L):
@@ -88,6 +88,25 @@ def test_update_and_fit_validation(L):
     srt = L.kmeans_sort_by_cluster
     assert srt(None, 10, 4, FAKE, None, WS, 1 << 30, None) == 1
     assert srt(FAKE, 10, 0, FAKE, None, WS, 1 << 30, None) == 1
+
+
+def test_batched_fit_validation(L):
+    wb = L.kmeans_workspace_bytes_batched
+    one = wb(1, 16384, 32, 64, km.KM_F32)
+    assert one > 0 and one % 256 == 0
+    assert wb(256, 16384, 32, 64, km.KM_F32) > 200 * one  # grows with the batch
+    assert wb(0, 10, 8, 4, km.KM_F32) == 0
+    assert wb(1 << 20, 1 << 12, 8, 4, km.KM_F32) == 0      # B*N = 2^32
+    assert wb(1 << 16, 10, 8, 1 << 16, km.KM_F32) == 0     # B*K = 2^32
+    assert wb(4, 10, 300, 4, km.KM_F32) == 0               # D > 256 for fp32
+    f = L.kmeans_fit_batched
+    assert f(FAKE, km.KM_F32, 0, 10, 8, 4, FAKE, 1, None, None, None, WS, 1 << 30, None) == 1        # B = 0
+    assert f(FAKE, km.KM_F32, 1 << 20, 1 << 12, 8, 4, FAKE, 1, None, None, None, WS, 1 << 30, None) == 2
+    assert "B*N" in _last(L)
+    assert f(FAKE, km.KM_F32, 2, 10, 8, 4, FAKE, -1, None, None, None, WS, 1 << 30, None) == 1       # iters < 0
+    assert f(FAKE, km.KM_F32, 2, 10, 8, 4, None, 1, None, None, None, WS, 1 << 30, None) == 1        # null C
+    assert f(FAKE, km.KM_F32, 2, 10, 8, 4, FAKE, 1, None, None, None, WS, 64, None) == 3             # small ws
+    assert f(FAKE, km.KM_F32, 2, 10, 8, 4, FAKE, 1, None, None, ctypes.c_void_p(0x10004), WS, 1 << 30, None) == 1
 
 
 def test_timing_registry_without_gpu(L):
