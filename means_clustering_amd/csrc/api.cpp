@@ -180,7 +180,8 @@ static UpdateBufs carve_update(Carve& c, const SortGeom& g, int64_t D, km_dtype 
   const int64_t ntiles = (g.N + kSegTile - 1) / kSegTile;
   u.carry_sum = c.take<float>((size_t)(ntiles > 0 ? ntiles : 1) * 2 * (size_t)reduce_dc((int)dt, D));
   u.carry_cnt = c.take<int32_t>((size_t)(ntiles > 0 ? ntiles : 1) * 2);
-  const int64_t ngroups = (ntiles + kSegGroup - 1) / kSegGroup;
+  const int64_t tpb = reduce_tpb((int)dt, D);
+  const int64_t ngroups = (ntiles + tpb - 1) / tpb;
   u.group_sum = c.take<float>((size_t)(ngroups > 0 ? ngroups : 1) * (size_t)reduce_dc((int)dt, D));
   u.group_cnt = c.take<int32_t>((size_t)(ngroups > 0 ? ngroups : 1));
   return u;

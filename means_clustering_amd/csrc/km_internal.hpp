@@ -170,7 +170,6 @@ constexpr int kRadixMaxItems = 32;           // consecutive keys per thread: 8, 
 inline int radix_items(int64_t N) { return N >= 1024 * 8192 ? 32 : (N >= 1024 * 4096 ? 16 : 8); }
 constexpr int kMaxDigitBits = 6;             // digits of at most 64 values per pass
 constexpr int kSegTile = KM_SEG_TILE;
-constexpr int kSegGroup = 64;  // tiles per carry group (second reduction level for long segments)
 constexpr uint32_t kInvalidFlag = 0x80000000u;  // marks a point whose cluster id was out of range
 
 struct SortGeom {
@@ -237,8 +236,8 @@ struct ReduceArgs {
   int32_t* off;         // K+1 cluster offsets (written by launch_segment_reduce, read by launch_fixup)
   float* carry_sum;     // [ntiles][2][Dc]
   int32_t* carry_cnt;   // [ntiles][2]
-  float* group_sum;     // [ngroups][Dc]: slot-0 carries of a single-id group of kSegGroup tiles, summed
-  int32_t* group_cnt;   // [ngroups]
+  float* group_sum;     // [ceil(ntiles / reduce_tpb)][Dc]: per segment-reduce workgroup whose positions hold one id
+  int32_t* group_cnt;
   int mode;
   const float* C_prev;  // MODE_MEAN
   float* C_new;         // MODE_MEAN
@@ -247,7 +246,8 @@ struct ReduceArgs {
   int64_t* acc_cnt;     // MODE_ACCUM: K running counts
 };
 
-int64_t reduce_dc(int dt, int64_t D);  // padded row length of a carry piece
+int64_t reduce_dc(int dt, int64_t D);   // padded row length of a carry piece
+int64_t reduce_tpb(int dt, int64_t D);  // tiles per segment-reduce workgroup
 hipError_t launch_segment_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_fixup(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_finalize_accum(const float* acc_sum, const int64_t* acc_cnt, int64_t K, int64_t D,

@@ -49,6 +49,16 @@ __device__ __forceinline__ void widen(const u32x4_r& v, int dt, float* out) {
   }
 }
 
+static int64_t reduce_lanes(int dt, int64_t D) {  // G: lanes holding one row (16 bytes each)
+  const int64_t epl = dt == DT_F32 ? 4 : 8;
+  const int64_t nch = (D + epl - 1) / epl;
+  int64_t g = 1;
+  while (g < nch && g < 64) g <<= 1;
+  return g;
+}
+
+int64_t reduce_tpb(int dt, int64_t D) { return 256 / reduce_lanes(dt, D); }
+
 int64_t reduce_dc(int dt, int64_t D) {
   const int64_t epl = dt == DT_F32 ? 4 : 8;
   const int64_t nch = (D + epl - 1) / epl;
@@ -91,8 +101,9 @@ struct SegParams {
   int32_t* off;  // K+1 cluster offsets, written by the segmented reduction
   float* carry_sum;
   int32_t* carry_cnt;
-  float* group_sum;
+  float* group_sum;   // [blocks][Dc]: a segment-reduce workgroup's slot-0 pieces, summed, when its positions hold one id
   int32_t* group_cnt;
+  int tpb;            // tiles per segment-reduce workgroup
   int Dc;
   int mode;
   const float* C_prev;
@@ -152,6 +163,7 @@ __device__ __forceinline__ void flush_piece(const SegParams& P, int64_t tile, in
 
 template <int ES, int CPL, int G>
 __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
+  static_assert(CPL == 1, "a lane holds one 16-byte column chunk");
   constexpr int EPL = 16 / ES;
   // The ids and point indices of a whole chunk of the tile (KPL per lane, up
   // to 16) are read in one round trip; the chunk's rows then go out U at a
@@ -163,145 +175,139 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
   static_assert(BATCH % U == 0 && kSegTile % BATCH == 0, "rows in flight divide the chunk");
   const int j = threadIdx.x % G;
   const int lgbase = (threadIdx.x & 63) & ~(G - 1);
-  const int64_t tile = (int64_t)blockIdx.x * (256 / G) + threadIdx.x / G;
+  constexpr int T = 256 / G;  // tiles per workgroup
+  const int64_t tile = (int64_t)blockIdx.x * T + threadIdx.x / G;
   const int64_t ps = tile * kSegTile;
-  if (ps >= P.N) return;
-  const int64_t pe = ps + kSegTile < P.N ? ps + kSegTile : P.N;
-  const int32_t first_key = P.keys[ps];
-  const int32_t before_key = ps > 0 ? P.keys[ps - 1] : -1;   // id just before the tile
-  const int32_t after_key = pe < P.N ? P.keys[pe] : -1;      // id just after the tile
+  // A workgroup whose positions all hold one id sums its tiles' pieces at the
+  // end (one piece for the fix-up instead of T); it keeps every thread until then.
+  const int64_t bps = (int64_t)blockIdx.x * T * kSegTile;
+  const int64_t bpe = bps + (int64_t)T * kSegTile < P.N ? bps + (int64_t)T * kSegTile : P.N;
+  const bool solid = P.keys[bps] == P.keys[bpe - 1];
+  if (ps >= P.N && !solid) return;
+  if (ps < P.N) {
+    const int64_t pe = ps + kSegTile < P.N ? ps + kSegTile : P.N;
+    const int32_t first_key = P.keys[ps];
+    const int32_t before_key = ps > 0 ? P.keys[ps - 1] : -1;   // id just before the tile
+    const int32_t after_key = pe < P.N ? P.keys[pe] : -1;      // id just after the tile
 
-  // Cluster offsets: off[k] = first sorted position with id >= k.  Every id
-  // change between positions p-1 and p is seen by exactly one lane group
-  // (the one whose tile holds p), which writes off[(id before, id at p]] = p.
-  auto write_offsets = [&](int64_t a, int64_t b, int64_t p) {
-    if (j != 0) return;
-    a = a < -1 ? -1 : (a >= P.K ? P.K : a);  // sorted ids lie in [0, K); clamping keeps writes in bounds
-    b = b < -1 ? -1 : (b >= P.K ? P.K : b);
-    for (int64_t k = a + 1; k <= b; ++k) P.off[k] = (int32_t)p;
-  };
-  if (before_key != first_key) write_offsets(before_key, first_key, ps);
+    // Cluster offsets: off[k] = first sorted position with id >= k.  Every id
+    // change between positions p-1 and p is seen by exactly one lane group
+    // (the one whose tile holds p), which writes off[(id before, id at p]] = p.
+    auto write_offsets = [&](int64_t a, int64_t b, int64_t p) {
+      if (j != 0) return;
+      a = a < -1 ? -1 : (a >= P.K ? P.K : a);  // sorted ids lie in [0, K); clamping keeps writes in bounds
+      b = b < -1 ? -1 : (b >= P.K ? P.K : b);
+      for (int64_t k = a + 1; k <= b; ++k) P.off[k] = (int32_t)p;
+    };
+    if (before_key != first_key) write_offsets(before_key, first_key, ps);
 
-  float acc[CPL][EPL];
-#pragma unroll
-  for (int q = 0; q < CPL; ++q)
-#pragma unroll
-    for (int x = 0; x < EPL; ++x) acc[q][x] = 0.0f;
-  int32_t cnt = 0;
-  int32_t cur = first_key;
-  bool started = before_key != first_key;  // the current segment began inside this tile
+    float acc[CPL][EPL];
+  #pragma unroll
+    for (int q = 0; q < CPL; ++q)
+  #pragma unroll
+      for (int x = 0; x < EPL; ++x) acc[q][x] = 0.0f;
+    int32_t cnt = 0;
+    int32_t cur = first_key;
+    bool started = before_key != first_key;  // the current segment began inside this tile
 
-  for (int64_t p0 = ps; p0 < pe; p0 += BATCH) {
-    // lane j holds positions p0 + j + G*m, m < KPL
-    int32_t kj[KPL], vj[KPL];
-#pragma unroll
-    for (int m = 0; m < KPL; ++m) {
-      const int64_t mypos = p0 + j + (int64_t)G * m;
-      kj[m] = mypos < pe ? P.keys[mypos] : 0;
-      vj[m] = mypos < pe ? P.vals[mypos] : (int32_t)kInvalidFlag;
-    }
-#pragma unroll
-    for (int b0 = 0; b0 < BATCH; b0 += U) {
-      if (p0 + b0 >= pe) break;
-      u32x4_r xr[U][CPL];
-      int32_t kk[U];
-      bool ok[U], in[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int b = b0 + u;  // batch position: lane b % G, slot b / G
-        const int32_t v = __shfl(vj[b / G], lgbase + b % G);
-        kk[u] = __shfl(kj[b / G], lgbase + b % G);
-        in[u] = p0 + b < pe;
-        const int64_t row = (int64_t)((uint32_t)v & ~kInvalidFlag);
-        ok[u] = in[u] && v >= 0 && row < P.N;
-#pragma unroll
-        for (int q = 0; q < CPL; ++q)
-          xr[u][q] = ok[u] ? load_chunk<ES>(P.X, row, P.D, (j + q * G) * EPL, P.vec_ok) : u32x4_r{0u, 0u, 0u, 0u};
+    for (int64_t p0 = ps; p0 < pe; p0 += BATCH) {
+      // lane j holds positions p0 + j + G*m, m < KPL
+      int32_t kj[KPL], vj[KPL];
+  #pragma unroll
+      for (int m = 0; m < KPL; ++m) {
+        const int64_t mypos = p0 + j + (int64_t)G * m;
+        kj[m] = mypos < pe ? P.keys[mypos] : 0;
+        vj[m] = mypos < pe ? P.vals[mypos] : (int32_t)kInvalidFlag;
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (in[u]) {
-          if (kk[u] != cur) {  // the current segment ends inside the tile
-            write_offsets(cur, kk[u], p0 + b0 + u);
-            flush_piece<EPL, CPL, G>(P, tile, first_key, cur, started, acc, cnt, j);
-            cur = kk[u];
-            cnt = 0;
-            started = true;
-#pragma unroll
-            for (int q = 0; q < CPL; ++q)
-#pragma unroll
-              for (int x = 0; x < EPL; ++x) acc[q][x] = 0.0f;
-          }
-          cnt += ok[u] ? 1 : 0;
-#pragma unroll
-          for (int q = 0; q < CPL; ++q) {
-            float f[EPL];
-            widen(xr[u][q], P.dt, f);
-#pragma unroll
-            for (int x = 0; x < EPL; ++x) acc[q][x] += f[x];
+  #pragma unroll
+      for (int b0 = 0; b0 < BATCH; b0 += U) {
+        if (p0 + b0 >= pe) break;
+        u32x4_r xr[U][CPL];
+        int32_t kk[U];
+        bool ok[U], in[U];
+  #pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int b = b0 + u;  // batch position: lane b % G, slot b / G
+          const int32_t v = __shfl(vj[b / G], lgbase + b % G);
+          kk[u] = __shfl(kj[b / G], lgbase + b % G);
+          in[u] = p0 + b < pe;
+          const int64_t row = (int64_t)((uint32_t)v & ~kInvalidFlag);
+          ok[u] = in[u] && v >= 0 && row < P.N;
+  #pragma unroll
+          for (int q = 0; q < CPL; ++q)
+            xr[u][q] = ok[u] ? load_chunk<ES>(P.X, row, P.D, (j + q * G) * EPL, P.vec_ok) : u32x4_r{0u, 0u, 0u, 0u};
+        }
+  #pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (in[u]) {
+            if (kk[u] != cur) {  // the current segment ends inside the tile
+              write_offsets(cur, kk[u], p0 + b0 + u);
+              flush_piece<EPL, CPL, G>(P, tile, first_key, cur, started, acc, cnt, j);
+              cur = kk[u];
+              cnt = 0;
+              started = true;
+  #pragma unroll
+              for (int q = 0; q < CPL; ++q)
+  #pragma unroll
+                for (int x = 0; x < EPL; ++x) acc[q][x] = 0.0f;
+            }
+            cnt += ok[u] ? 1 : 0;
+  #pragma unroll
+            for (int q = 0; q < CPL; ++q) {
+              float f[EPL];
+              widen(xr[u][q], P.dt, f);
+  #pragma unroll
+              for (int x = 0; x < EPL; ++x) acc[q][x] += f[x];
+            }
           }
         }
       }
     }
+    flush_piece<EPL, CPL, G>(P, tile, first_key, cur, started && after_key != cur, acc, cnt, j);
+    if (pe == P.N) write_offsets(cur, P.K, P.N);  // ids after the last one start (and end) at N
   }
-  flush_piece<EPL, CPL, G>(P, tile, first_key, cur, started && after_key != cur, acc, cnt, j);
-  if (pe == P.N) write_offsets(cur, P.K, P.N);  // ids after the last one start (and end) at N
-}
-
-// Second level for long segments: a group of kSegGroup consecutive tiles
-// whose sorted positions all hold one id lies inside that id's segment, so
-// every tile of it left its piece in slot 0.  One wavefront per group sums
-// those pieces in tile order (rows strided over the tiles, then a fixed
-// shuffle tree); the fix-up then adds whole groups instead of their tiles.
-template <int CPL>
-__global__ __launch_bounds__(256) void carry_group_kernel(SegParams P, int64_t ngroups) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t grp = (int64_t)blockIdx.x * 4 + wave;
-  if (grp >= ngroups) return;
-  const int64_t ntiles = (P.N + kSegTile - 1) / kSegTile;
-  const int64_t tb = grp * kSegGroup;
-  const int64_t te = tb + kSegGroup < ntiles ? tb + kSegGroup : ntiles;
-  const int64_t pe = te * kSegTile < P.N ? te * kSegTile : P.N;
-  if (P.keys[tb * kSegTile] != P.keys[pe - 1]) return;  // more than one id: the fix-up never asks for it
-  const int gc = P.Dc / 4;
-  const int lpr = gc < 64 ? gc : 64;
-  const int R = 64 / lpr;
-  const int r = lane / lpr, c0 = lane % lpr;
-  float a[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  int32_t n = 0;
-  for (int64_t t = tb + r; t < te; t += R) {
-    const float* piece = P.carry_sum + (t * 2) * (int64_t)P.Dc;
+  if (!solid) return;
+  __syncthreads();  // the workgroup's pieces are stored
+  if (threadIdx.x >= 64) return;
+  // wavefront 0: rows of G lanes take the tiles r, r + R, ... in order, then a fixed tree
+  constexpr int R = 64 / G;
+  const int r = threadIdx.x / G;
+  const int64_t t_end = (bpe + kSegTile - 1) / kSegTile;
+  float sum[EPL];
 #pragma unroll
-    for (int cl = 0; cl < CPL; ++cl) {
-      const float4 v = *reinterpret_cast<const float4*>(piece + (c0 + cl * lpr) * 4);
-      a[cl][0] += v.x;
-      a[cl][1] += v.y;
-      a[cl][2] += v.z;
-      a[cl][3] += v.w;
+  for (int x = 0; x < EPL; ++x) sum[x] = 0.0f;
+  int32_t n = 0;
+  for (int64_t t = (int64_t)blockIdx.x * T + r; t < t_end; t += R) {
+    const float4* src = reinterpret_cast<const float4*>(P.carry_sum + (t * 2) * (int64_t)P.Dc + j * EPL);
+#pragma unroll
+    for (int x = 0; x < EPL; x += 4) {
+      const float4 w = src[x / 4];
+      sum[x] += w.x;
+      sum[x + 1] += w.y;
+      sum[x + 2] += w.z;
+      sum[x + 3] += w.w;
     }
     n += P.carry_cnt[t * 2];
   }
-  for (int off = lpr; off < 64; off <<= 1) {
+  for (int off = G; off < 64; off <<= 1) {
 #pragma unroll
-    for (int cl = 0; cl < 2; ++cl)
-#pragma unroll
-      for (int x = 0; x < 4; ++x) a[cl][x] += __shfl_xor(a[cl][x], off);
+    for (int x = 0; x < EPL; ++x) sum[x] += __shfl_xor(sum[x], off);
     n += __shfl_xor(n, off);
   }
   if (r == 0) {
-    float* dst = P.group_sum + grp * (int64_t)P.Dc;
+    float4* dst = reinterpret_cast<float4*>(P.group_sum + (int64_t)blockIdx.x * P.Dc + j * EPL);
 #pragma unroll
-    for (int cl = 0; cl < CPL; ++cl)
-      *reinterpret_cast<float4*>(dst + (c0 + cl * lpr) * 4) = make_float4(a[cl][0], a[cl][1], a[cl][2], a[cl][3]);
-    if (c0 == 0) P.group_cnt[grp] = n;
+    for (int x = 0; x < EPL; x += 4) dst[x / 4] = make_float4(sum[x], sum[x + 1], sum[x + 2], sum[x + 3]);
+    if (j == 0) P.group_cnt[blockIdx.x] = n;
   }
 }
 
 // Segments cut by tile edges are summed from their pieces; empty clusters
 // keep their centroid.  One wavefront per cluster.  The pieces of cluster k,
-// tiles t0..t1, are taken as: the head tiles before the first group boundary
-// after t0, then every whole group up to the group holding t1 (one summed
-// piece each, see carry_group_kernel), then the tail tiles of t1's group.
+// tiles t0..t1, are taken as: the head tiles up to the end of t0's
+// segment-reduce workgroup, then every whole workgroup up to the one holding
+// t1 (one piece each, summed by that workgroup since all its positions hold
+// k), then the tail tiles of t1's workgroup.
 // Lanes split into R rows x (Dc/4) float4 columns; row r takes items r,
 // r + R, ... of that list in order and the rows are combined by a fixed
 // shuffle tree, so the order of additions never depends on scheduling.
@@ -328,9 +334,10 @@ __global__ __launch_bounds__(256) void fixup_kernel(SegParams P) {
   const int64_t t0 = s / kSegTile, t1 = (e - 1) / kSegTile;
   if (t0 == t1) return;  // finished by segment_reduce_kernel
   // item list: head tiles [t0, hb), whole groups [g0, g1), tail tiles [tb, t1]
-  int64_t hb = (t0 / kSegGroup + 1) * kSegGroup;
-  const int64_t tb = (t1 / kSegGroup) * kSegGroup;
-  int64_t g0 = hb / kSegGroup, g1 = tb / kSegGroup;
+  const int64_t T = P.tpb;
+  int64_t hb = (t0 / T + 1) * T;
+  const int64_t tb = (t1 / T) * T;
+  int64_t g0 = hb / T, g1 = tb / T;
   if (hb > tb) {  // t0 and t1 in the same or adjacent groups: tiles only
     hb = t1 + 1;
     g0 = g1 = 0;
@@ -422,6 +429,7 @@ static SegParams make_params(const ReduceArgs& a) {
   P.carry_cnt = a.carry_cnt;
   P.group_sum = a.group_sum;
   P.group_cnt = a.group_cnt;
+  P.tpb = (int)reduce_tpb(a.dt, a.D);
   P.Dc = (int)reduce_dc(a.dt, a.D);
   P.mode = a.mode;
   P.C_prev = a.C_prev;
@@ -463,15 +471,6 @@ hipError_t launch_fixup(const ReduceArgs& a, hipStream_t stream) {
   if (a.K == 0) return hipSuccess;
   const SegParams P = make_params(a);
   const bool wide = P.Dc / 4 > 64;
-  if (a.N > 0) {
-    const int64_t ntiles = (a.N + kSegTile - 1) / kSegTile;
-    const int64_t ngroups = (ntiles + kSegGroup - 1) / kSegGroup;
-    const dim3 gg((unsigned)((ngroups + 3) / 4));
-    if (wide)
-      hipLaunchKernelGGL(carry_group_kernel<2>, gg, dim3(256), 0, stream, P, ngroups);
-    else
-      hipLaunchKernelGGL(carry_group_kernel<1>, gg, dim3(256), 0, stream, P, ngroups);
-  }
   const dim3 grid((unsigned)((a.K + 3) / 4));
   if (wide)
     hipLaunchKernelGGL(fixup_kernel<2>, grid, dim3(256), 0, stream, P);

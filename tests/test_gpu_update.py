@@ -76,12 +76,22 @@ def test_update_only_first_or_last_cluster(cluster):
     _run(X, np.full(5000, cluster), C_prev, f"only cluster {cluster}")
 
 
-@pytest.mark.parametrize("D,xdtype", [(64, "bf16"), (512, "bf16"), (200, "f32")])
+def _positions_per_reduce_block(D, xdtype):
+    """Sorted positions one segmented-reduction workgroup covers: 256 / G tiles of 128,
+    G = lanes holding a row in 16-byte pieces (a power of two, at most 64)."""
+    per = 4 if xdtype == "f32" else 8
+    G = 1
+    while G < -(-D // per) and G < 64:
+        G *= 2
+    return (256 // G) * 128
+
+
+@pytest.mark.parametrize("D,xdtype", [(64, "bf16"), (512, "bf16"), (200, "f32"), (8, "bf16")])
 def test_update_segments_at_group_edges(D, xdtype):
-    """Long segments that start or end on, or one position off, the edges of
-    64-tile (8192-position) carry groups, so that whole groups, head tiles
-    and tail tiles are all summed."""
-    G = 64 * 128
+    """Long segments that start or end on, or one position off, the edges of the
+    segmented reduction's workgroups, so that whole workgroup sums, head tiles and
+    tail tiles are all added."""
+    G = _positions_per_reduce_block(D, xdtype)
     sizes = [3 * G, 2 * G + 1, 2 * G - 2, 1, 5 * G + 128, 70 * G - 1, 127, G + 77]
     a = np.repeat(np.arange(len(sizes) * 2, step=2), sizes)  # every other cluster empty
     np.random.default_rng(11).shuffle(a)
