@@ -32,7 +32,7 @@ inline int dtype_size(int dt) { return dt == DT_F32 ? 4 : 2; }
 // is one contiguous, unconditional copy and every LDS read is lane-linear.
 // ---------------------------------------------------------------------------
 constexpr int kFragDepth = 16;     // depth values per fragment block (both layouts)
-constexpr int kPadK = 128;         // K is padded to a multiple of this (>= any tile)
+constexpr int kPadK = 128;         // 16-bit X: K is padded to a multiple of this (>= any tile)
 constexpr int kMaxD16 = 512;       // D limit for 16-bit X
 constexpr int kMaxD32 = 256;       // D limit for fp32 X
 
@@ -105,9 +105,13 @@ constexpr int kWide8MaxKB = KM_WIDE8 ? 8 : 0;
 constexpr AssignCfg wide8_cfg(int KB) {
   return AssignCfg{32, KB, KB <= 4 ? KM_W8_NB_SMALL : KM_W8_NB, KB <= 4 ? KM_W8_CT_SMALL : KM_W8_CT, KM_W8_W};
 }
-constexpr AssignCfg narrow_cfg(int KB) {
-  return AssignCfg{16, KB, KB <= 4 ? 4 : (KB <= 8 ? 2 : 1), KB <= 2 ? 8 : (KB <= 4 ? 4 : (KB <= 8 ? 2 : 1)), 4};
+// fp32 X.  `half`: tiles of half as many groups, so that a small K (e.g. 64)
+// is not padded up to a whole 128-centroid tile.
+constexpr AssignCfg narrow_cfg(int KB, bool half = false) {
+  return AssignCfg{16, KB, KB <= 4 ? 4 : (KB <= 8 ? 2 : 1),
+                   (KB <= 2 ? 8 : (KB <= 4 ? 4 : (KB <= 8 ? 2 : 1))) / (half && KB <= 8 ? 2 : 1), 4};
 }
+constexpr int kNarrowHalfMaxKB = 8;
 
 inline int wide_kb(int64_t D) {
   const int need = (int)((D + kFragDepth - 1) / kFragDepth);
@@ -120,7 +124,7 @@ inline int64_t pad_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 struct AssignGeom {
   int dt;
   int64_t N, D, K;
-  int64_t Kpad;    // K rounded up to a whole number of tiles (at least kPadK)
+  int64_t Kpad;    // K rounded up to a whole number of tiles
   AssignCfg cfg;
   bool lazy;       // argmax by group maxima first (pays off when the centroid sweep is long)
   int64_t groups() const { return Kpad / cfg.rows; }
@@ -136,7 +140,13 @@ inline AssignGeom make_assign_geom(int64_t N, int64_t D, int64_t K, int dt) {
   g.K = K;
   g.Kpad = pad_up(K, kPadK);
   if (dt == DT_F32) {
-    g.cfg = narrow_cfg((int)((D + kFragDepth - 1) / kFragDepth));
+    const int kb = (int)((D + kFragDepth - 1) / kFragDepth);
+    const AssignCfg full = narrow_cfg(kb), half = narrow_cfg(kb, true);
+    const int64_t kp_full = pad_up(K, (int64_t)full.rows * full.CT);
+    const int64_t kp_half = pad_up(K, (int64_t)half.rows * half.CT);
+    const bool use_half = kb <= kNarrowHalfMaxKB && kp_half < kp_full;
+    g.cfg = use_half ? half : full;
+    g.Kpad = use_half ? kp_half : kp_full;
   } else {
     const int kb = wide_kb(D);
     const AssignCfg c8 = wide8_cfg(kb);
