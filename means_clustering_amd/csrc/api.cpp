@@ -172,11 +172,18 @@ struct UpdateBufs {
   int32_t* carry_cnt;
   float* group_sum;
   int32_t* group_cnt;
+  float* small_sum;  // chunk sums of the small-codebook update
+  int32_t* small_cnt;
 };
 
-static UpdateBufs carve_update(Carve& c, const SortGeom& g, int64_t D, km_dtype dt) {
+// g: the whole update (all B problems); B problems of g.N / B points and g.K / B clusters each.
+static UpdateBufs carve_update(Carve& c, const SortGeom& g, int64_t D, km_dtype dt, int64_t B = 1) {
   UpdateBufs u;
   u.s = carve_sort(c, g);
+  const int64_t kper = g.K / B;
+  const int64_t nsmall = kper <= kSmallMaxK ? B * small_chunks(g.N / B) * kper : 1;
+  u.small_sum = c.take<float>((size_t)(nsmall > 0 ? nsmall : 1) * (size_t)reduce_dc((int)dt, D));
+  u.small_cnt = c.take<int32_t>((size_t)(nsmall > 0 ? nsmall : 1));
   const int64_t ntiles = (g.N + kSegTile - 1) / kSegTile;
   u.carry_sum = c.take<float>((size_t)(ntiles > 0 ? ntiles : 1) * 2 * (size_t)reduce_dc((int)dt, D));
   u.carry_cnt = c.take<int32_t>((size_t)(ntiles > 0 ? ntiles : 1) * 2);
@@ -237,7 +244,7 @@ struct BatchBufs {
 static BatchBufs carve_batched(Carve& c, int64_t B, int64_t N, int64_t D, int64_t K, km_dtype dt) {
   BatchBufs b;
   b.frag = c.take<uint8_t>((size_t)B * assign_geom(N, D, K, dt).frag_bytes());
-  b.u = carve_update(c, sort_geom(B * N, B * K), D, dt);
+  b.u = carve_update(c, sort_geom(B * N, B * K), D, dt, B);
   const size_t n = (size_t)(B * N > 0 ? B * N : 1);
   b.ids = c.take<int32_t>(n);
   b.min_dist = c.take<float>(n);
@@ -406,11 +413,33 @@ static km_status run_sort(const int32_t* assign, int64_t N, int64_t K, const Sor
 }
 
 // sorted_keys/sorted_vals (optional out): where the argsort left the sorted
-// assignment and the point order; valid until the workspace is used again.
+// assignment and the point order, valid until the workspace is used again;
+// NULL when the small-codebook path ran (it sorts on chip only).
+// B > 1: N points of B problems (N / B each) with K / B clusters each and ids b*(K/B) + k.
 static km_status run_update(const void* X, km_dtype dt, int64_t N, int64_t D, const int32_t* assign, int64_t K,
                             const float* C_prev, float* C_new, int32_t* counts, const UpdateBufs& u, int mode,
                             float* acc_sum, int64_t* acc_cnt, hipStream_t s, const int32_t** sorted_keys = nullptr,
-                            const int32_t** sorted_vals = nullptr) {
+                            const int32_t** sorted_vals = nullptr, int64_t B = 1) {
+  if (sorted_keys) *sorted_keys = nullptr;
+  if (sorted_vals) *sorted_vals = nullptr;
+  if (mode == MODE_MEAN && K / B <= kSmallMaxK) {
+    SmallArgs a;
+    a.X = X;
+    a.dt = (int)dt;
+    a.B = B;
+    a.N = N / B;
+    a.D = D;
+    a.K = K / B;
+    a.ids = assign;
+    a.id_mul = K / B;
+    a.C_prev = C_prev;
+    a.C_new = C_new;
+    a.counts = counts;
+    a.part_sum = u.small_sum;
+    a.part_cnt = u.small_cnt;
+    KM_TIMED("reduce", s, return launch_small_update(a, s));
+    return KM_OK;
+  }
   int32_t *keys = nullptr, *vals = nullptr;
   // the segmented reduction writes the cluster offsets itself (it sees every id change)
   km_status st = run_sort(assign, N, K, u.s, nullptr, &keys, &vals, s, /*offsets=*/N == 0);
@@ -579,7 +608,8 @@ km_status kmeans_fit_batched(const void* X, km_dtype dt, int64_t B, int64_t N, i
       if (counts) KM_HIP(launch_zero(counts, sizeof(int32_t) * (size_t)(B * K), s));
       continue;
     }
-    st = run_update(X, dt, B * N, D, b.ids, B * K, C, C, counts, b.u, MODE_MEAN, nullptr, nullptr, s);
+    st = run_update(X, dt, B * N, D, b.ids, B * K, C, C, counts, b.u, MODE_MEAN, nullptr, nullptr, s, nullptr,
+                    nullptr, B);
     if (st != KM_OK) return st;
   }
   if (assign && N > 0) KM_TIMED("finalize", s, return launch_local_ids(b.ids, B, N, K, assign, s));

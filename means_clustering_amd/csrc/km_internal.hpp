@@ -260,6 +260,24 @@ int64_t reduce_dc(int dt, int64_t D);   // padded row length of a carry piece
 int64_t reduce_tpb(int dt, int64_t D);  // tiles per segment-reduce workgroup
 hipError_t launch_segment_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_fixup(const ReduceArgs& a, hipStream_t stream);
+// Small codebooks (K <= kSmallMaxK per problem, mean mode): the update of B
+// problems of N points each in one launch (two when a problem spans several
+// 2048-point chunks), sort and reduction on chip.  ids[b*N + i] = b*id_mul + k.
+constexpr int64_t kSmallMaxK = 64;
+struct SmallArgs {
+  const void* X;        // B x N x D
+  int dt;
+  int64_t B, N, D, K;   // per problem
+  const int32_t* ids;
+  int64_t id_mul;
+  const float* C_prev;  // B x K x D
+  float* C_new;         // may alias C_prev
+  int32_t* counts;      // B x K, nullable
+  float* part_sum;      // B * small_chunks(N) * K * reduce_dc(dt, D) floats
+  int32_t* part_cnt;    // B * small_chunks(N) * K
+};
+int64_t small_chunks(int64_t N);  // chunks per problem
+hipError_t launch_small_update(const SmallArgs& a, hipStream_t stream);
 hipError_t launch_finalize_accum(const float* acc_sum, const int64_t* acc_cnt, int64_t K, int64_t D,
                                  float* C, int32_t* counts, hipStream_t stream);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);

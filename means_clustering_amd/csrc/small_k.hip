@@ -1,0 +1,215 @@
+// Sort-Inverse Update for small codebooks (at most 64 clusters per problem),
+// the shape of many small K-Means problems called back to back or batched.
+//
+// Citations name the page "Flash-KMeans: Fast and Memory-Efficient Exact
+// K-Means" (gist.science summary of paper 2603.09229); "tech §n" is a section
+// of its technical summary.
+//
+// Same idea as tech §2.2 (make each cluster's points contiguous, then reduce
+// contiguous runs with no atomics), with the sort kept on chip: with K <= 64
+// the whole cluster id is one 6-bit radix digit, so one workgroup ranks the
+// ids of a 2048-point chunk stably in LDS (the radix sort's block rank), lays
+// the chunk's point indices out in cluster order in LDS, and then lets each
+// lane group walk whole clusters of the chunk in that order, 16 rows in
+// flight.  No global sort, no carries: a cluster's chunk sum is complete in
+// one lane group.  When a problem has one chunk the means are written right
+// away (one launch for the whole update); otherwise the chunk sums are added
+// chunk by chunk in a second launch.  The order of every addition is fixed
+// (chunk, then point index), so results are deterministic.
+#include "block_rank.hpp"
+#include "km_internal.hpp"
+#include "rows.hpp"
+
+namespace km {
+
+// Points per workgroup: 2048 (8 ids a thread).  Measured on c1-shaped problems,
+// 8192-point chunks were slower both alone and in a batch of 256 (the walk
+// after the rank is latency-bound, and fewer workgroups fit a CU).
+constexpr int kSmallIT = 8;
+constexpr int kSmallChunk = kRadixThreads * kSmallIT;
+static_assert(kSmallMaxK <= (1 << kMaxDigitBits), "one radix digit holds every id");
+
+struct SmallParams {
+  const uint8_t* X;     // B x N x D
+  int dt;
+  int64_t N;            // points per problem
+  int D;
+  int64_t K;            // clusters per problem
+  bool vec_ok;
+  const int32_t* ids;   // B x N; problem b's ids are b * id_mul + k
+  int64_t id_mul;
+  int64_t P;            // chunks per problem
+  int Dc;
+  const float* C_prev;  // B x K x D
+  float* C_new;
+  int32_t* counts;      // B x K, nullable
+  float* part_sum;      // (B * P) x K x Dc (P > 1)
+  int32_t* part_cnt;    // (B * P) x K
+};
+
+// Sum of the rows srow[s0 .. s1) (lane j: its 16-byte column chunk).  The
+// U indices of a round are read from LDS first and the row loads are
+// unconditional (the tail repeats the last row and skips its add), so a
+// round's U loads leave back to back.  VEC: rows are whole 16-byte chunks.
+template <int ES, bool VEC, int U>
+__device__ __forceinline__ void walk_rows(const uint8_t* __restrict__ Xb, const int32_t* srow, int s0, int s1, int D,
+                                          int dt, int j, float (&acc)[16 / ES]) {
+  constexpr int EPL = 16 / ES;
+  for (int p = s0; p < s1; p += U) {
+    int32_t r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) r[u] = srow[p + u < s1 ? p + u : s1 - 1];
+    u32x4_r xr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if constexpr (VEC)
+        xr[u] = *reinterpret_cast<const u32x4_r*>(Xb + ((size_t)r[u] * (size_t)D + (size_t)(j * EPL)) * ES);
+      else
+        xr[u] = load_chunk<ES>(Xb, r[u], D, j * EPL, false);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (p + u < s1) {
+        float f[EPL];
+        widen(xr[u], dt, f);
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) acc[x] += f[x];
+      }
+    }
+  }
+}
+
+template <int ES, int G>
+__global__ __launch_bounds__(kRadixThreads) void small_update_kernel(SmallParams S) {
+  constexpr int EPL = 16 / ES;
+  constexpr int NG = kRadixThreads / G;  // lane groups
+  constexpr int U = 16;                  // rows in flight per lane group
+  __shared__ uint32_t ctr[kRadixPadded];
+  __shared__ uint32_t wsum[kRadixThreads / 64];
+  __shared__ uint32_t start[(1 << kMaxDigitBits) + 1];
+  __shared__ int32_t srow[kSmallChunk];
+  const int64_t b = blockIdx.x / S.P, c = blockIdx.x - b * S.P;
+  const int64_t c0 = c * kSmallChunk;
+  const int64_t n = S.N - c0 < kSmallChunk ? S.N - c0 : kSmallChunk;
+  const int32_t* ids = S.ids + b * S.N + c0;
+  const int64_t id0 = b * S.id_mul;
+
+  uint32_t d[kSmallIT], rank[kSmallIT];
+  bool valid[kSmallIT];
+#pragma unroll
+  for (int i = 0; i < kSmallIT; ++i) {
+    const int64_t pos = (int64_t)threadIdx.x * kSmallIT + i;
+    const int64_t k = pos < n ? (int64_t)ids[pos] - id0 : -1;
+    valid[i] = k >= 0 && k < S.K;  // ids outside [0, K) are ignored
+    d[i] = valid[i] ? (uint32_t)k : 0u;
+  }
+  block_rank<kMaxDigitBits, kSmallIT>(d, valid, ctr, wsum, start, rank);
+#pragma unroll
+  for (int i = 0; i < kSmallIT; ++i)
+    if (valid[i]) srow[rank[i]] = (int32_t)(c0 + (int64_t)threadIdx.x * kSmallIT + i);
+  __syncthreads();
+
+  const int g = threadIdx.x / G, j = threadIdx.x % G;
+  const uint8_t* Xb = S.X + (size_t)b * (size_t)S.N * (size_t)S.D * ES;
+  for (int64_t k = g; k < S.K; k += NG) {
+    const int s0 = (int)start[k], s1 = (int)start[k + 1];
+    float acc[EPL];
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) acc[x] = 0.0f;
+    if (S.vec_ok && (j + 1) * EPL <= S.D)
+      walk_rows<ES, true, U>(Xb, srow, s0, s1, S.D, S.dt, j, acc);
+    else if (j * EPL < S.D)
+      walk_rows<ES, false, U>(Xb, srow, s0, s1, S.D, S.dt, j, acc);
+    const int32_t cnt = s1 - s0;
+    if (S.P == 1) {  // the chunk is the whole problem: its means (an empty cluster keeps its centroid)
+      const int64_t row = (b * S.K + k) * S.D;
+#pragma unroll
+      for (int x = 0; x < EPL; ++x) {
+        const int col = j * EPL + x;
+        if (col < S.D) S.C_new[row + col] = cnt > 0 ? acc[x] / (float)cnt : S.C_prev[row + col];
+      }
+      if (j == 0 && S.counts) S.counts[b * S.K + k] = cnt;
+    } else {
+      float4* dst = reinterpret_cast<float4*>(S.part_sum + ((b * S.P + c) * S.K + k) * S.Dc + j * EPL);
+#pragma unroll
+      for (int x = 0; x < EPL; x += 4) dst[x / 4] = make_float4(acc[x], acc[x + 1], acc[x + 2], acc[x + 3]);
+      if (j == 0) S.part_cnt[(b * S.P + c) * S.K + k] = cnt;
+    }
+  }
+}
+
+// One wavefront per (problem, cluster): chunk sums added in chunk order.
+__global__ __launch_bounds__(256) void small_combine_kernel(SmallParams S, int64_t nclusters) {
+  const int lane = threadIdx.x & 63;
+  const int64_t q = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // b * K + k
+  if (q >= nclusters) return;
+  const int64_t b = q / S.K, k = q - b * S.K;
+  constexpr int kMaxCols = 512 / 64;
+  float acc[kMaxCols];
+#pragma unroll
+  for (int x = 0; x < kMaxCols; ++x) acc[x] = 0.0f;
+  int32_t cnt = 0;
+  for (int64_t c = 0; c < S.P; ++c) {
+    const float* src = S.part_sum + ((b * S.P + c) * S.K + k) * S.Dc;
+#pragma unroll
+    for (int x = 0; x < kMaxCols; ++x) {
+      const int col = lane + 64 * x;
+      if (col < S.D) acc[x] += src[col];
+    }
+    cnt += S.part_cnt[(b * S.P + c) * S.K + k];
+  }
+  const int64_t row = q * S.D;
+#pragma unroll
+  for (int x = 0; x < kMaxCols; ++x) {
+    const int col = lane + 64 * x;
+    if (col < S.D) S.C_new[row + col] = cnt > 0 ? acc[x] / (float)cnt : S.C_prev[row + col];
+  }
+  if (lane == 0 && S.counts) S.counts[q] = cnt;
+}
+
+int64_t small_chunks(int64_t N) { return (N + kSmallChunk - 1) / kSmallChunk; }
+
+hipError_t launch_small_update(const SmallArgs& a, hipStream_t stream) {
+  if (a.N == 0 || a.B == 0) return hipSuccess;
+  if (a.K < 1 || a.K > kSmallMaxK || a.D < 1 || a.D > 512) return hipErrorInvalidValue;
+  SmallParams S;
+  S.X = (const uint8_t*)a.X;
+  S.dt = a.dt;
+  S.N = a.N;
+  S.D = (int)a.D;
+  S.K = a.K;
+  const int es = dtype_size(a.dt);
+  S.vec_ok = (((uintptr_t)a.X) % 16 == 0) && ((a.D * es) % 16 == 0);
+  S.ids = a.ids;
+  S.id_mul = a.id_mul;
+  S.P = small_chunks(a.N);
+  S.Dc = (int)reduce_dc(a.dt, a.D);
+  S.C_prev = a.C_prev;
+  S.C_new = a.C_new;
+  S.counts = a.counts;
+  S.part_sum = a.part_sum;
+  S.part_cnt = a.part_cnt;
+  const int64_t grid = a.B * S.P;
+  if (grid >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const int epl = 16 / es;
+  const int64_t nch = (a.D + epl - 1) / epl;
+  int g = 1;
+  while (g < nch && g < 64) g <<= 1;
+  bool launched = false;
+#define KM_SMALL(ES_, G_)                                                                                     \
+  if (!launched && es == ES_ && g == G_) {                                                                    \
+    hipLaunchKernelGGL((small_update_kernel<ES_, G_>), dim3((unsigned)grid), dim3(kRadixThreads), 0, stream, S); \
+    launched = true;                                                                                          \
+  }
+  KM_SMALL(2, 1) KM_SMALL(2, 2) KM_SMALL(2, 4) KM_SMALL(2, 8) KM_SMALL(2, 16) KM_SMALL(2, 32) KM_SMALL(2, 64)
+  KM_SMALL(4, 1) KM_SMALL(4, 2) KM_SMALL(4, 4) KM_SMALL(4, 8) KM_SMALL(4, 16) KM_SMALL(4, 32) KM_SMALL(4, 64)
+#undef KM_SMALL
+  if (!launched) return hipErrorInvalidValue;
+  if (S.P > 1) {
+    const int64_t nq = a.B * a.K;
+    hipLaunchKernelGGL(small_combine_kernel, dim3((unsigned)((nq + 3) / 4)), dim3(256), 0, stream, S, nq);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace km

@@ -93,11 +93,41 @@ def test_update_segments_at_group_edges(D, xdtype):
     tail tiles are all added."""
     G = _positions_per_reduce_block(D, xdtype)
     sizes = [3 * G, 2 * G + 1, 2 * G - 2, 1, 5 * G + 128, 70 * G - 1, 127, G + 77]
-    a = np.repeat(np.arange(len(sizes) * 2, step=2), sizes)  # every other cluster empty
+    # ids 0, 10, 20, ...: the clusters between stay empty, and K = 80 takes the sorted path
+    a = np.repeat(np.arange(len(sizes) * 10, step=10), sizes)
     np.random.default_rng(11).shuffle(a)
     X = _x(a.size, D, xdtype, seed=12 + D)
-    C_prev = torch.randn(len(sizes) * 2, D).to(DEV)
+    C_prev = torch.randn(len(sizes) * 10, D).to(DEV)
     _run(X, a, C_prev, f"segments at group edges D={D} {xdtype}")
+
+
+@pytest.mark.parametrize("xdtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("shape", [(2048, 32, 64), (2049, 32, 64), (50000, 64, 64), (20000, 17, 33), (9000, 1, 2),
+                                   (6000, 512, 5), (4100, 100, 1), (2_100_000, 16, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_update_small_codebook(shape, xdtype):
+    """K <= 64: the on-chip path (one chunk of 2048 points per workgroup, chunk sums added in order)."""
+    N, D, K = shape
+    if xdtype == "f32" and D > 256:
+        pytest.skip("fp32 supports D <= 256")
+    X = _x(N, D, xdtype, seed=N + 7 * D + K)
+    rng = np.random.default_rng(N + K)
+    w = rng.random(K) ** 3  # uneven cluster sizes, some clusters empty
+    a = rng.choice(K, size=N, p=w / w.sum())
+    if K > 3:
+        a[a == K // 2] = K - 1  # one empty cluster for sure
+    C_prev = torch.randn(K, D, generator=torch.Generator().manual_seed(K + D)).to(DEV)
+    _run(X, a, C_prev, f"small codebook {shape} {xdtype}")
+
+
+def test_update_small_codebook_hot_cluster_and_invalid_ids():
+    X = _x(120_000, 32, "f32", seed=21)
+    rng = np.random.default_rng(22)
+    a = np.where(rng.random(120_000) < 0.9, 3, rng.integers(0, 40, 120_000))
+    a[::97] = -5
+    a[1::89] = 40
+    C_prev = torch.randn(40, 32).to(DEV)
+    _run(X, a, C_prev, "small codebook, 90% in one cluster, invalid ids", inplace=True)
 
 
 def test_update_five_million_points():
