@@ -116,7 +116,8 @@ __device__ __forceinline__ void flush_piece(const SegParams& P, int64_t tile, in
   }
 }
 
-template <int ES, int CPL, int G>
+// VEC: X rows are whole, 16-byte aligned chunks (vector loads without a per-row fallback).
+template <int ES, int CPL, int G, bool VEC>
 __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
   static_assert(CPL == 1, "a lane holds one 16-byte column chunk");
   constexpr int EPL = 16 / ES;
@@ -157,9 +158,9 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
     if (before_key != first_key) write_offsets(before_key, first_key, ps);
 
     float acc[CPL][EPL];
-  #pragma unroll
+#pragma unroll
     for (int q = 0; q < CPL; ++q)
-  #pragma unroll
+#pragma unroll
       for (int x = 0; x < EPL; ++x) acc[q][x] = 0.0f;
     int32_t cnt = 0;
     int32_t cur = first_key;
@@ -168,19 +169,19 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
     for (int64_t p0 = ps; p0 < pe; p0 += BATCH) {
       // lane j holds positions p0 + j + G*m, m < KPL
       int32_t kj[KPL], vj[KPL];
-  #pragma unroll
+#pragma unroll
       for (int m = 0; m < KPL; ++m) {
         const int64_t mypos = p0 + j + (int64_t)G * m;
         kj[m] = mypos < pe ? P.keys[mypos] : 0;
         vj[m] = mypos < pe ? P.vals[mypos] : (int32_t)kInvalidFlag;
       }
-  #pragma unroll
+#pragma unroll
       for (int b0 = 0; b0 < BATCH; b0 += U) {
         if (p0 + b0 >= pe) break;
         u32x4_r xr[U][CPL];
         int32_t kk[U];
         bool ok[U], in[U];
-  #pragma unroll
+#pragma unroll
         for (int u = 0; u < U; ++u) {
           const int b = b0 + u;  // batch position: lane b % G, slot b / G
           const int32_t v = __shfl(vj[b / G], lgbase + b % G);
@@ -188,11 +189,20 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
           in[u] = p0 + b < pe;
           const int64_t row = (int64_t)((uint32_t)v & ~kInvalidFlag);
           ok[u] = in[u] && v >= 0 && row < P.N;
-  #pragma unroll
-          for (int q = 0; q < CPL; ++q)
-            xr[u][q] = ok[u] ? load_chunk<ES>(P.X, row, P.D, (j + q * G) * EPL, P.vec_ok) : u32x4_r{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int q = 0; q < CPL; ++q) {
+            const int c0 = (j + q * G) * EPL;
+            if constexpr (VEC) {  // whole 16-byte chunks: one unconditional load, masked after
+              const int64_t rr = ok[u] ? row : 0;
+              const int cc = c0 < P.D ? c0 : 0;
+              const u32x4_r w = *reinterpret_cast<const u32x4_r*>(P.X + ((size_t)rr * (size_t)P.D + (size_t)cc) * ES);
+              xr[u][q] = (ok[u] && c0 < P.D) ? w : u32x4_r{0u, 0u, 0u, 0u};
+            } else {
+              xr[u][q] = ok[u] ? load_chunk<ES>(P.X, row, P.D, c0, false) : u32x4_r{0u, 0u, 0u, 0u};
+            }
+          }
         }
-  #pragma unroll
+#pragma unroll
         for (int u = 0; u < U; ++u) {
           if (in[u]) {
             if (kk[u] != cur) {  // the current segment ends inside the tile
@@ -201,17 +211,17 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
               cur = kk[u];
               cnt = 0;
               started = true;
-  #pragma unroll
+#pragma unroll
               for (int q = 0; q < CPL; ++q)
-  #pragma unroll
+#pragma unroll
                 for (int x = 0; x < EPL; ++x) acc[q][x] = 0.0f;
             }
             cnt += ok[u] ? 1 : 0;
-  #pragma unroll
+#pragma unroll
             for (int q = 0; q < CPL; ++q) {
               float f[EPL];
               widen(xr[u][q], P.dt, f);
-  #pragma unroll
+#pragma unroll
               for (int x = 0; x < EPL; ++x) acc[q][x] += f[x];
             }
           }
@@ -399,8 +409,11 @@ template <int ES, int CPL, int G>
 static void launch_seg(const SegParams& P, hipStream_t s) {
   const int64_t ntiles = (P.N + kSegTile - 1) / kSegTile;
   const int64_t per_block = 256 / G;
-  hipLaunchKernelGGL((segment_reduce_kernel<ES, CPL, G>), dim3((unsigned)((ntiles + per_block - 1) / per_block)),
-                     dim3(256), 0, s, P);
+  const dim3 grid((unsigned)((ntiles + per_block - 1) / per_block));
+  if (P.vec_ok)
+    hipLaunchKernelGGL((segment_reduce_kernel<ES, CPL, G, true>), grid, dim3(256), 0, s, P);
+  else
+    hipLaunchKernelGGL((segment_reduce_kernel<ES, CPL, G, false>), grid, dim3(256), 0, s, P);
 }
 
 hipError_t launch_segment_reduce(const ReduceArgs& a, hipStream_t stream) {
