@@ -262,7 +262,7 @@ hipError_t launch_segment_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_fixup(const ReduceArgs& a, hipStream_t stream);
 // Small codebooks (K <= kSmallMaxK per problem, mean mode): the update of B
 // problems of N points each in one launch (two when a problem spans several
-// 2048-point chunks), sort and reduction on chip.  ids[b*N + i] = b*id_mul + k.
+// chunks of 512 or 2048 points), sort and reduction on chip.  ids[b*N + i] = b*id_mul + k.
 constexpr int64_t kSmallMaxK = 64;
 struct SmallArgs {
   const void* X;        // B x N x D
@@ -276,7 +276,7 @@ struct SmallArgs {
   float* part_sum;      // B * small_chunks(N) * K * reduce_dc(dt, D) floats
   int32_t* part_cnt;    // B * small_chunks(N) * K
 };
-int64_t small_chunks(int64_t N);  // chunks per problem
+int64_t small_chunks(int64_t N);  // chunks per problem, at most
 hipError_t launch_small_update(const SmallArgs& a, hipStream_t stream);
 hipError_t launch_finalize_accum(const float* acc_sum, const int64_t* acc_cnt, int64_t K, int64_t D,
                                  float* C, int32_t* counts, hipStream_t stream);

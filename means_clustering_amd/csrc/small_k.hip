@@ -8,7 +8,7 @@
 // Same idea as tech §2.2 (make each cluster's points contiguous, then reduce
 // contiguous runs with no atomics), with the sort kept on chip: with K <= 64
 // the whole cluster id is one 6-bit radix digit, so one workgroup ranks the
-// ids of a 2048-point chunk stably in LDS (the radix sort's block rank), lays
+// ids of a chunk (2048 points, 512 for small calls) stably in LDS (the radix sort's block rank), lays
 // the chunk's point indices out in cluster order in LDS, and then lets each
 // lane group walk whole clusters of the chunk in that order, 16 rows in
 // flight.  No global sort, no carries: a cluster's chunk sum is complete in
@@ -22,12 +22,18 @@
 
 namespace km {
 
-// Points per workgroup: 2048 (8 ids a thread).  Measured on c1-shaped problems,
-// 8192-point chunks were slower both alone and in a batch of 256 (the walk
-// after the rank is latency-bound, and fewer workgroups fit a CU).
-constexpr int kSmallIT = 8;
-constexpr int kSmallChunk = kRadixThreads * kSmallIT;
+// Points per workgroup: 2048 (8 ids a thread), or 512 (2 a thread) when that
+// many chunks would leave most CUs idle: the walk after the rank is
+// latency-bound, so a lone small problem finishes sooner spread thinner.
+// (8192-point chunks were slower on c1-shaped problems, alone and batched.)
+constexpr int kSmallChunk = kRadixThreads * 8;
+constexpr int kSmallChunkThin = kRadixThreads * 2;
+constexpr int64_t kSmallThinBelow = 256;  // 2048-point chunks in the call
 static_assert(kSmallMaxK <= (1 << kMaxDigitBits), "one radix digit holds every id");
+
+static int small_it(int64_t B, int64_t N) {
+  return B * ((N + kSmallChunk - 1) / kSmallChunk) < kSmallThinBelow ? 2 : 8;
+}
 
 struct SmallParams {
   const uint8_t* X;     // B x N x D
@@ -79,18 +85,20 @@ __device__ __forceinline__ void walk_rows(const uint8_t* __restrict__ Xb, const 
   }
 }
 
-template <int ES, int G>
+template <int ES, int G, int IT>
 __global__ __launch_bounds__(kRadixThreads) void small_update_kernel(SmallParams S) {
+  constexpr int kSmallIT = IT;
+  constexpr int kChunk = kRadixThreads * IT;
   constexpr int EPL = 16 / ES;
   constexpr int NG = kRadixThreads / G;  // lane groups
   constexpr int U = 16;                  // rows in flight per lane group
   __shared__ uint32_t ctr[kRadixPadded];
   __shared__ uint32_t wsum[kRadixThreads / 64];
   __shared__ uint32_t start[(1 << kMaxDigitBits) + 1];
-  __shared__ int32_t srow[kSmallChunk];
+  __shared__ int32_t srow[kChunk];
   const int64_t b = blockIdx.x / S.P, c = blockIdx.x - b * S.P;
-  const int64_t c0 = c * kSmallChunk;
-  const int64_t n = S.N - c0 < kSmallChunk ? S.N - c0 : kSmallChunk;
+  const int64_t c0 = c * kChunk;
+  const int64_t n = S.N - c0 < kChunk ? S.N - c0 : kChunk;
   const int32_t* ids = S.ids + b * S.N + c0;
   const int64_t id0 = b * S.id_mul;
 
@@ -138,36 +146,62 @@ __global__ __launch_bounds__(kRadixThreads) void small_update_kernel(SmallParams
   }
 }
 
-// One wavefront per (problem, cluster): chunk sums added in chunk order.
-__global__ __launch_bounds__(256) void small_combine_kernel(SmallParams S, int64_t nclusters) {
+// One wavefront per (problem, cluster): the chunk sums of a cluster, added in
+// a fixed order.  Lanes form R rows of DL lanes (DL = D rounded up to a power
+// of two, at most 64); row r takes chunks r, r + R, ... in ascending order,
+// 8 in flight, and the rows then meet in a fixed shuffle tree.
+__global__ __launch_bounds__(256) void small_combine_kernel(SmallParams S, int64_t nclusters, int DL) {
   const int lane = threadIdx.x & 63;
   const int64_t q = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // b * K + k
   if (q >= nclusters) return;
   const int64_t b = q / S.K, k = q - b * S.K;
-  constexpr int kMaxCols = 512 / 64;
+  constexpr int kMaxCols = 512 / 64;  // columns per lane at most (D <= 512 with DL = 64)
+  const int R = 64 / DL, r = lane / DL, cl = lane % DL;
   float acc[kMaxCols];
 #pragma unroll
   for (int x = 0; x < kMaxCols; ++x) acc[x] = 0.0f;
   int32_t cnt = 0;
-  for (int64_t c = 0; c < S.P; ++c) {
-    const float* src = S.part_sum + ((b * S.P + c) * S.K + k) * S.Dc;
+  constexpr int UNR = 8;  // chunks in flight per row
+  for (int64_t c0 = r; c0 < S.P; c0 += (int64_t)R * UNR) {
+    float v[UNR][kMaxCols];
+    int32_t n[UNR];
 #pragma unroll
-    for (int x = 0; x < kMaxCols; ++x) {
-      const int col = lane + 64 * x;
-      if (col < S.D) acc[x] += src[col];
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t cu = c0 + (int64_t)u * R;
+      const int64_t c = cu < S.P ? cu : S.P - 1;  // the tail reloads the last chunk, not added
+      const float* src = S.part_sum + ((b * S.P + c) * S.K + k) * S.Dc;
+#pragma unroll
+      for (int x = 0; x < kMaxCols; ++x) {
+        const int col = cl + DL * x;
+        v[u][x] = col < S.D ? src[col] : 0.0f;
+      }
+      n[u] = S.part_cnt[(b * S.P + c) * S.K + k];
     }
-    cnt += S.part_cnt[(b * S.P + c) * S.K + k];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      if (c0 + (int64_t)u * R < S.P) {
+#pragma unroll
+        for (int x = 0; x < kMaxCols; ++x) acc[x] += v[u][x];
+        cnt += n[u];
+      }
+    }
   }
+  for (int off = DL; off < 64; off <<= 1) {
+#pragma unroll
+    for (int x = 0; x < kMaxCols; ++x) acc[x] += __shfl_xor(acc[x], off);
+    cnt += __shfl_xor(cnt, off);
+  }
+  if (r != 0) return;
   const int64_t row = q * S.D;
 #pragma unroll
   for (int x = 0; x < kMaxCols; ++x) {
-    const int col = lane + 64 * x;
+    const int col = cl + DL * x;
     if (col < S.D) S.C_new[row + col] = cnt > 0 ? acc[x] / (float)cnt : S.C_prev[row + col];
   }
-  if (lane == 0 && S.counts) S.counts[q] = cnt;
+  if (cl == 0 && S.counts) S.counts[q] = cnt;
 }
 
-int64_t small_chunks(int64_t N) { return (N + kSmallChunk - 1) / kSmallChunk; }
+int64_t small_chunks(int64_t N) { return (N + kSmallChunkThin - 1) / kSmallChunkThin; }  // at most
 
 hipError_t launch_small_update(const SmallArgs& a, hipStream_t stream) {
   if (a.N == 0 || a.B == 0) return hipSuccess;
@@ -182,7 +216,8 @@ hipError_t launch_small_update(const SmallArgs& a, hipStream_t stream) {
   S.vec_ok = (((uintptr_t)a.X) % 16 == 0) && ((a.D * es) % 16 == 0);
   S.ids = a.ids;
   S.id_mul = a.id_mul;
-  S.P = small_chunks(a.N);
+  const int it = small_it(a.B, a.N);
+  S.P = (a.N + kRadixThreads * it - 1) / (kRadixThreads * it);
   S.Dc = (int)reduce_dc(a.dt, a.D);
   S.C_prev = a.C_prev;
   S.C_new = a.C_new;
@@ -198,7 +233,12 @@ hipError_t launch_small_update(const SmallArgs& a, hipStream_t stream) {
   bool launched = false;
 #define KM_SMALL(ES_, G_)                                                                                     \
   if (!launched && es == ES_ && g == G_) {                                                                    \
-    hipLaunchKernelGGL((small_update_kernel<ES_, G_>), dim3((unsigned)grid), dim3(kRadixThreads), 0, stream, S); \
+    if (it == 2)                                                                                              \
+      hipLaunchKernelGGL((small_update_kernel<ES_, G_, 2>), dim3((unsigned)grid), dim3(kRadixThreads), 0,      \
+                         stream, S);                                                                          \
+    else                                                                                                      \
+      hipLaunchKernelGGL((small_update_kernel<ES_, G_, 8>), dim3((unsigned)grid), dim3(kRadixThreads), 0,      \
+                         stream, S);                                                                          \
     launched = true;                                                                                          \
   }
   KM_SMALL(2, 1) KM_SMALL(2, 2) KM_SMALL(2, 4) KM_SMALL(2, 8) KM_SMALL(2, 16) KM_SMALL(2, 32) KM_SMALL(2, 64)
@@ -207,7 +247,9 @@ hipError_t launch_small_update(const SmallArgs& a, hipStream_t stream) {
   if (!launched) return hipErrorInvalidValue;
   if (S.P > 1) {
     const int64_t nq = a.B * a.K;
-    hipLaunchKernelGGL(small_combine_kernel, dim3((unsigned)((nq + 3) / 4)), dim3(256), 0, stream, S, nq);
+    int dl = 1;
+    while (dl < a.D && dl < 64) dl <<= 1;
+    hipLaunchKernelGGL(small_combine_kernel, dim3((unsigned)((nq + 3) / 4)), dim3(256), 0, stream, S, nq, dl);
   }
   return hipGetLastError();
 }

@@ -102,11 +102,11 @@ def test_update_segments_at_group_edges(D, xdtype):
 
 
 @pytest.mark.parametrize("xdtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("shape", [(2048, 32, 64), (2049, 32, 64), (50000, 64, 64), (20000, 17, 33), (9000, 1, 2),
-                                   (6000, 512, 5), (4100, 100, 1), (2_100_000, 16, 64)],
+@pytest.mark.parametrize("shape", [(512, 32, 64), (513, 32, 64), (2048, 32, 64), (2049, 32, 64), (50000, 64, 64), (20000, 17, 33), (9000, 1, 2),
+                                   (6000, 512, 5), (4100, 100, 1), (600_000, 16, 64)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_update_small_codebook(shape, xdtype):
-    """K <= 64: the on-chip path (one chunk of 2048 points per workgroup, chunk sums added in order)."""
+    """K <= 64: the on-chip path (one chunk of 512 or 2048 points per workgroup, chunk sums added in order)."""
     N, D, K = shape
     if xdtype == "f32" and D > 256:
         pytest.skip("fp32 supports D <= 256")
