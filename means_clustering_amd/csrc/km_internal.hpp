@@ -171,7 +171,7 @@ inline AssignGeom make_assign_geom(int64_t N, int64_t D, int64_t K, int dt) {
 #define KM_SEG_TILE 128   // sorted positions per segment tile
 #endif
 #ifndef KM_SEG_U
-#define KM_SEG_U 16       // rows in flight per lane group in the segmented reduction
+#define KM_SEG_U 16       // most rows in flight per lane group in the segmented reduction
 #endif
 constexpr int kRadixThreads = 256;
 constexpr int kRadixMaxItems = 32;           // consecutive keys per thread: 8, 16 or 32 (block positions fit in 16 bits)

@@ -127,7 +127,9 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
   // the current ones are added.
   constexpr int KPL = kSegTile / G < 16 ? kSegTile / G : 16;
   constexpr int BATCH = G * KPL;
-  constexpr int U = G < KM_SEG_U ? G : KM_SEG_U;
+  // rows in flight per lane group: half the lane group's width (measured on gfx950:
+  // more rows cost occupancy, c2 G=16 best at 8, c4 G=8 at 4), at least 2
+  constexpr int U = G / 2 < 2 ? 2 : (G / 2 > KM_SEG_U ? KM_SEG_U : G / 2);
   static_assert(BATCH % U == 0 && kSegTile % BATCH == 0, "rows in flight divide the chunk");
   const int j = threadIdx.x % G;
   const int lgbase = (threadIdx.x & 63) & ~(G - 1);
