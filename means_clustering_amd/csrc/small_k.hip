@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kRadixThreads) void small_update_kernel(SmallParams
   constexpr int kChunk = kRadixThreads * IT;
   constexpr int EPL = 16 / ES;
   constexpr int NG = kRadixThreads / G;  // lane groups
-  constexpr int U = 16;                  // rows in flight per lane group
+  constexpr int U = IT == 2 ? 8 : 16;    // rows in flight per lane group (measured: 8 for a lone problem, 16 batched)
   __shared__ uint32_t ctr[kRadixPadded];
   __shared__ uint32_t wsum[kRadixThreads / 64];
   __shared__ uint32_t start[(1 << kMaxDigitBits) + 1];
