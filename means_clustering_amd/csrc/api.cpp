@@ -106,8 +106,8 @@ static km_status check_sizes(int64_t N, int64_t D, int64_t K, km_dtype dt, bool 
 
 // ----------------------------------------------------------- geometry -----
 
-static AssignGeom assign_geom(int64_t N, int64_t D, int64_t K, km_dtype dt) {
-  return make_assign_geom(N, D, K, (int)dt);
+static AssignGeom assign_geom(int64_t N, int64_t D, int64_t K, km_dtype dt, int64_t B = 1) {
+  return make_assign_geom(N, D, K, (int)dt, B);
 }
 
 static SortGeom sort_geom(int64_t N, int64_t K) {
@@ -243,7 +243,7 @@ struct BatchBufs {
 
 static BatchBufs carve_batched(Carve& c, int64_t B, int64_t N, int64_t D, int64_t K, km_dtype dt) {
   BatchBufs b;
-  b.frag = c.take<uint8_t>((size_t)B * assign_geom(N, D, K, dt).frag_bytes());
+  b.frag = c.take<uint8_t>((size_t)B * assign_geom(N, D, K, dt, B).frag_bytes());
   b.u = carve_update(c, sort_geom(B * N, B * K), D, dt, B);
   const size_t n = (size_t)(B * N > 0 ? B * N : 1);
   b.ids = c.take<int32_t>(n);
@@ -595,7 +595,7 @@ km_status kmeans_fit_batched(const void* X, km_dtype dt, int64_t B, int64_t N, i
   hipStream_t s = (hipStream_t)stream;
   Carve c(ws);
   const BatchBufs b = carve_batched(c, B, N, D, K, dt);
-  const AssignGeom g = assign_geom(N, D, K, dt);
+  const AssignGeom g = assign_geom(N, D, K, dt, B);
   for (int32_t t = 0; t < iters; ++t) {
     KM_TIMED("prep", s, return launch_prep(g, C, b.frag, s, B));
     if (N > 0)

@@ -709,11 +709,11 @@ __device__ __forceinline__ f32x4_t mma16_f32(u32x4_t a, u32x4_t b, f32x4_t c) {
   return c;
 }
 
-template <int KB, bool HALF>
-__global__ __launch_bounds__(narrow_cfg(KB, HALF).W * 64) void flash_assign_narrow_kernel(
+template <int KB, bool HALF, bool THIN>
+__global__ __launch_bounds__(narrow_cfg(KB, HALF, THIN).W * 64) void flash_assign_narrow_kernel(
     const uint8_t* __restrict__ X, int64_t N, int D, bool vec_ok, const u32x4_t* __restrict__ frag, int ntiles,
     int32_t* __restrict__ assign, float* __restrict__ min_dist, Batch bt) {
-  constexpr AssignCfg cfg = narrow_cfg(KB, HALF);
+  constexpr AssignCfg cfg = narrow_cfg(KB, HALF, THIN);
   constexpr int NB = cfg.NB, CT = cfg.CT, W = cfg.W;
   constexpr int GS = (int)cfg.group_slots();
   constexpr int TS = (int)cfg.tile_slots();
@@ -911,15 +911,21 @@ template <int KB>
 static hipError_t launch_narrow(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
                                 float* min_dist, int64_t B, int32_t id_mul, hipStream_t s) {
   if constexpr (KB <= kNarrowHalfMaxKB) {
-    if (same_cfg(g.cfg, narrow_cfg(KB, true))) {
-      constexpr AssignCfg cfg = narrow_cfg(KB, true);
+    const bool thin = same_cfg(g.cfg, narrow_cfg(KB, true, true));
+    if (thin || same_cfg(g.cfg, narrow_cfg(KB, true))) {
+      const AssignCfg cfg = g.cfg;
       const int64_t pts = (int64_t)cfg.W * cfg.NB * 16;
       const int64_t blocks = (N + pts - 1) / pts;
       if (blocks * B >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
       const bool vec_ok = (((uintptr_t)X) % 16 == 0) && ((g.D * 4) % 16 == 0);
-      hipLaunchKernelGGL((flash_assign_narrow_kernel<KB, true>), dim3((unsigned)(blocks * B)), dim3(cfg.W * 64), 0,
-                         s, (const uint8_t*)X, N, (int)g.D, vec_ok, (const u32x4_t*)frag, (int)g.ntiles(), assign,
-                         min_dist, make_batch(g, N, blocks, id_mul));
+      if (thin)
+        hipLaunchKernelGGL((flash_assign_narrow_kernel<KB, true, true>), dim3((unsigned)(blocks * B)),
+                           dim3(cfg.W * 64), 0, s, (const uint8_t*)X, N, (int)g.D, vec_ok, (const u32x4_t*)frag,
+                           (int)g.ntiles(), assign, min_dist, make_batch(g, N, blocks, id_mul));
+      else
+        hipLaunchKernelGGL((flash_assign_narrow_kernel<KB, true, false>), dim3((unsigned)(blocks * B)),
+                           dim3(cfg.W * 64), 0, s, (const uint8_t*)X, N, (int)g.D, vec_ok, (const u32x4_t*)frag,
+                           (int)g.ntiles(), assign, min_dist, make_batch(g, N, blocks, id_mul));
       return hipGetLastError();
     }
   }
@@ -929,8 +935,8 @@ static hipError_t launch_narrow(const AssignGeom& g, const void* X, int64_t N, c
   const int64_t blocks = (N + pts - 1) / pts;
   if (blocks * B >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const bool vec_ok = (((uintptr_t)X) % 16 == 0) && ((g.D * 4) % 16 == 0);
-  hipLaunchKernelGGL((flash_assign_narrow_kernel<KB, false>), dim3((unsigned)(blocks * B)), dim3(cfg.W * 64), 0, s,
-                     (const uint8_t*)X, N, (int)g.D, vec_ok, (const u32x4_t*)frag, (int)g.ntiles(), assign,
+  hipLaunchKernelGGL((flash_assign_narrow_kernel<KB, false, false>), dim3((unsigned)(blocks * B)), dim3(cfg.W * 64),
+                     0, s, (const uint8_t*)X, N, (int)g.D, vec_ok, (const u32x4_t*)frag, (int)g.ntiles(), assign,
                      min_dist, make_batch(g, N, blocks, id_mul));
   return hipGetLastError();
 }

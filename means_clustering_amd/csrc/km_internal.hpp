@@ -106,12 +106,14 @@ constexpr AssignCfg wide8_cfg(int KB) {
   return AssignCfg{32, KB, KB <= 4 ? KM_W8_NB_SMALL : KM_W8_NB, KB <= 4 ? KM_W8_CT_SMALL : KM_W8_CT, KM_W8_W};
 }
 // fp32 X.  `half`: tiles of half as many groups, so that a small K (e.g. 64)
-// is not padded up to a whole 128-centroid tile.
-constexpr AssignCfg narrow_cfg(int KB, bool half = false) {
-  return AssignCfg{16, KB, KB <= 4 ? 4 : (KB <= 8 ? 2 : 1),
+// is not padded up to a whole 128-centroid tile.  `thin`: one point group per
+// wavefront, for calls too small to fill the GPU otherwise (with half tiles).
+constexpr AssignCfg narrow_cfg(int KB, bool half = false, bool thin = false) {
+  return AssignCfg{16, KB, thin ? 1 : (KB <= 4 ? 4 : (KB <= 8 ? 2 : 1)),
                    (KB <= 2 ? 8 : (KB <= 4 ? 4 : (KB <= 8 ? 2 : 1))) / (half && KB <= 8 ? 2 : 1), 4};
 }
 constexpr int kNarrowHalfMaxKB = 8;
+constexpr int64_t kNarrowThinBelow = 256;  // workgroups of the call at the usual point groups per wavefront
 
 inline int wide_kb(int64_t D) {
   const int need = (int)((D + kFragDepth - 1) / kFragDepth);
@@ -132,7 +134,8 @@ struct AssignGeom {
   size_t frag_bytes() const { return (size_t)ntiles() * (size_t)cfg.tile_slots() * 16; }
 };
 
-inline AssignGeom make_assign_geom(int64_t N, int64_t D, int64_t K, int dt) {
+// B: problems launched together (batched calls), for the choice of a thin layout.
+inline AssignGeom make_assign_geom(int64_t N, int64_t D, int64_t K, int dt, int64_t B = 1) {
   AssignGeom g;
   g.dt = dt;
   g.N = N;
@@ -147,6 +150,8 @@ inline AssignGeom make_assign_geom(int64_t N, int64_t D, int64_t K, int dt) {
     const bool use_half = kb <= kNarrowHalfMaxKB && kp_half < kp_full;
     g.cfg = use_half ? half : full;
     g.Kpad = use_half ? kp_half : kp_full;
+    const int64_t pts = (int64_t)half.W * half.NB * 16;
+    if (use_half && B * ((N + pts - 1) / pts) < kNarrowThinBelow) g.cfg = narrow_cfg(kb, true, true);
   } else {
     const int kb = wide_kb(D);
     const AssignCfg c8 = wide8_cfg(kb);
