@@ -407,7 +407,7 @@ __device__ __forceinline__ void drain_epilogue(const f32x16_t (&in)[NB], float (
 // previous centroid of point perm[i] (both from the previous iteration's
 // argsort); the sweep starts from a bound taken from that centroid's group.
 template <int DT, int KB, bool LAZY, bool WARM>
-__global__ __launch_bounds__(wide_cfg(KB).W * 64) void flash_assign_wide_kernel(
+__global__ __launch_bounds__(wide_cfg(KB).W * 64) __attribute__((amdgpu_waves_per_eu(wide_wpe(KB)))) void flash_assign_wide_kernel(
     const uint8_t* __restrict__ X, int64_t N, int D, bool vec_ok, const u32x4_t* __restrict__ frag, int ntiles,
     int32_t* __restrict__ assign, float* __restrict__ min_dist, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ prev, int64_t K, Batch bt) {
