@@ -58,6 +58,12 @@ def test_fit_small_mixture_bf16():
     _teacher_forced(Xn, "bf16", C0, 5, "c2-like bf16")
 
 
+def test_fit_small_mixture_fp16():
+    w, Xn, C0 = _workload("c2", N=15000, K=200, D=72)
+    X16 = synth.bf16_bits_to_f32(Xn).astype(np.float16)  # the same points stored as fp16
+    _teacher_forced(X16, "f16", C0.astype(np.float16).astype(np.float32), 4, "c2-like fp16, D=72")
+
+
 def test_fit_skewed_bf16():
     w, Xn, C0 = _workload("c4", N=60000, K=512)
     _teacher_forced(Xn, "bf16", C0, 4, "c4-like zipf")

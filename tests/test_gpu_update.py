@@ -120,6 +120,20 @@ def test_update_small_codebook(shape, xdtype):
     _run(X, a, C_prev, f"small codebook {shape} {xdtype}")
 
 
+@pytest.mark.parametrize("shape,xdtype", [((7001, 37, 300), "bf16"), ((5000, 3, 129), "f32"), ((9000, 100, 200), "f16"),
+                                          ((4000, 257, 70), "bf16")],
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else v)
+def test_update_rows_not_whole_16_byte_pieces(shape, xdtype):
+    """Sorted path (K > 64) with rows whose byte length is not a multiple of 16 (element-wise row loads)."""
+    N, D, K = shape
+    X = _x(N, D, xdtype, seed=N + D)
+    rng = np.random.default_rng(K + 5)
+    a = rng.integers(0, K, N)
+    a[: N // 3] = K // 2  # one long segment across many tiles
+    C_prev = torch.randn(K, D, generator=torch.Generator().manual_seed(D)).to(DEV)
+    _run(X, a, C_prev, f"unaligned rows {shape} {xdtype}")
+
+
 def test_update_small_codebook_hot_cluster_and_invalid_ids():
     X = _x(120_000, 32, "f32", seed=21)
     rng = np.random.default_rng(22)
