@@ -388,11 +388,12 @@ constexpr int kStageSlots = 4;
 // ---------------------------------------------------- launch sequences ----
 
 // perm/prev (optional): the previous iteration's sorted order and sorted keys (warm start).
+// prepped: the fragments of C are already in `frag` (written by the last update).
 static km_status run_assign(const void* X, km_dtype dt, int64_t N, int64_t D, const float* C, int64_t K,
                             int32_t* assign, float* min_dist, void* frag, hipStream_t s,
-                            const int32_t* perm = nullptr, const int32_t* prev = nullptr) {
+                            const int32_t* perm = nullptr, const int32_t* prev = nullptr, bool prepped = false) {
   const AssignGeom g = assign_geom(N, D, K, dt);
-  KM_TIMED("prep", s, return launch_prep(g, C, frag, s));
+  if (!prepped) KM_TIMED("prep", s, return launch_prep(g, C, frag, s));
   if (N > 0) KM_TIMED("assign", s, return launch_flash_assign(g, X, N, frag, assign, min_dist, s, perm, prev));
   return KM_OK;
 }
@@ -416,12 +417,17 @@ static km_status run_sort(const int32_t* assign, int64_t N, int64_t K, const Sor
 // assignment and the point order, valid until the workspace is used again;
 // NULL when the small-codebook path ran (it sorts on chip only).
 // B > 1: N points of B problems (N / B each) with K / B clusters each and ids b*(K/B) + k.
+// frag/geom/prepped (optional): FlashAssign's fragment buffer and geometry for
+// the next assignment; *prepped tells whether this update already wrote the
+// fragments of C_new (then the next assignment skips its centroid preparation).
 static km_status run_update(const void* X, km_dtype dt, int64_t N, int64_t D, const int32_t* assign, int64_t K,
                             const float* C_prev, float* C_new, int32_t* counts, const UpdateBufs& u, int mode,
                             float* acc_sum, int64_t* acc_cnt, hipStream_t s, const int32_t** sorted_keys = nullptr,
-                            const int32_t** sorted_vals = nullptr, int64_t B = 1) {
+                            const int32_t** sorted_vals = nullptr, int64_t B = 1, void* frag = nullptr,
+                            const AssignGeom* geom = nullptr, bool* prepped = nullptr) {
   if (sorted_keys) *sorted_keys = nullptr;
   if (sorted_vals) *sorted_vals = nullptr;
+  if (prepped) *prepped = false;
   if (mode == MODE_MEAN && K / B <= kSmallMaxK) {
     SmallArgs a;
     a.X = X;
@@ -437,6 +443,10 @@ static km_status run_update(const void* X, km_dtype dt, int64_t N, int64_t D, co
     a.counts = counts;
     a.part_sum = u.small_sum;
     a.part_cnt = u.small_cnt;
+    a.frag = (frag && geom && prepped) ? frag : nullptr;
+    a.f_stride = geom ? (int64_t)(geom->frag_bytes() / 16) : 0;
+    if (geom) a.cfg = geom->cfg;
+    a.emitted = prepped;
     KM_TIMED("reduce", s, return launch_small_update(a, s));
     return KM_OK;
   }
@@ -560,15 +570,18 @@ km_status kmeans_fit(const void* X, km_dtype dt, int64_t N, int64_t D, int64_t K
   // From the second iteration on, the assign visits points in the order of the
   // previous argsort and starts each from its previous centroid's group.
   const int32_t *order = nullptr, *prev = nullptr;
+  const AssignGeom geom = assign_geom(N, D, K, dt);
+  bool prepped = false;  // the last update already wrote the centroid fragments
   for (int32_t t = 0; t < iters; ++t) {
-    st = run_assign(X, dt, N, D, C, K, a, objective ? f.min_dist : nullptr, f.frag, s, order, prev);
+    st = run_assign(X, dt, N, D, C, K, a, objective ? f.min_dist : nullptr, f.frag, s, order, prev, prepped);
     if (st != KM_OK) return st;
     if (objective) KM_TIMED("objective", s, return launch_objective(f.min_dist, N, f.obj_part, objective + t, 0, s));
     if (N == 0) {
       if (counts) KM_HIP(launch_zero(counts, sizeof(int32_t) * (size_t)K, s));
       continue;
     }
-    st = run_update(X, dt, N, D, a, K, C, C, counts, f.u, MODE_MEAN, nullptr, nullptr, s, &prev, &order);
+    st = run_update(X, dt, N, D, a, K, C, C, counts, f.u, MODE_MEAN, nullptr, nullptr, s, &prev, &order, 1, f.frag,
+                    &geom, &prepped);
     if (st != KM_OK) return st;
   }
   return KM_OK;
@@ -596,8 +609,9 @@ km_status kmeans_fit_batched(const void* X, km_dtype dt, int64_t B, int64_t N, i
   Carve c(ws);
   const BatchBufs b = carve_batched(c, B, N, D, K, dt);
   const AssignGeom g = assign_geom(N, D, K, dt, B);
+  bool prepped = false;  // the last update already wrote the centroid fragments
   for (int32_t t = 0; t < iters; ++t) {
-    KM_TIMED("prep", s, return launch_prep(g, C, b.frag, s, B));
+    if (!prepped) KM_TIMED("prep", s, return launch_prep(g, C, b.frag, s, B));
     if (N > 0)
       KM_TIMED("assign", s,
                return launch_flash_assign(g, X, N, b.frag, b.ids, objective ? b.min_dist : nullptr, s, nullptr,
@@ -609,7 +623,7 @@ km_status kmeans_fit_batched(const void* X, km_dtype dt, int64_t B, int64_t N, i
       continue;
     }
     st = run_update(X, dt, B * N, D, b.ids, B * K, C, C, counts, b.u, MODE_MEAN, nullptr, nullptr, s, nullptr,
-                    nullptr, B);
+                    nullptr, B, b.frag, &g, &prepped);
     if (st != KM_OK) return st;
   }
   if (assign && N > 0) KM_TIMED("finalize", s, return launch_local_ids(b.ids, B, N, K, assign, s));

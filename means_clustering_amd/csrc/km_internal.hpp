@@ -286,6 +286,13 @@ struct SmallArgs {
   int32_t* counts;      // B x K, nullable
   float* part_sum;      // B * small_chunks(N) * K * reduce_dc(dt, D) floats
   int32_t* part_cnt;    // B * small_chunks(N) * K
+  // optional (fp32 X): FlashAssign's centroid fragments for the next
+  // assignment, written along with the means when that step runs as a
+  // separate chunk-sum pass (*emitted says whether it did)
+  void* frag;           // B x frag_bytes of geometry cfg (NULL: none)
+  int64_t f_stride;     // 16-byte slots per problem
+  AssignCfg cfg;
+  bool* emitted;
 };
 int64_t small_chunks(int64_t N);  // chunks per problem, at most
 hipError_t launch_small_update(const SmallArgs& a, hipStream_t stream);

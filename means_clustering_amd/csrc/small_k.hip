@@ -51,6 +51,11 @@ struct SmallParams {
   int32_t* counts;      // B x K, nullable
   float* part_sum;      // (B * P) x K x Dc (P > 1)
   int32_t* part_cnt;    // (B * P) x K
+  // fp32 X, P > 1: the chunk-sum step also writes each new centroid's MFMA
+  // fragment and bias for the next assignment (frag == NULL: it does not)
+  uint32_t* frag;       // 16-byte slots, problem b at b * f_stride
+  int64_t f_stride;
+  AssignCfg cfg;
 };
 
 // Sum of the rows srow[s0 .. s1) (lane j: its 16-byte column chunk).  The
@@ -150,11 +155,57 @@ __global__ __launch_bounds__(kRadixThreads) void small_update_kernel(SmallParams
 // a fixed order.  Lanes form R rows of DL lanes (DL = D rounded up to a power
 // of two, at most 64); row r takes chunks r, r + R, ... in ascending order,
 // 8 in flight, and the rows then meet in a fixed shuffle tree.
-__global__ __launch_bounds__(256) void small_combine_kernel(SmallParams S, int64_t nclusters, int DL) {
+// Fragment and bias of centroid k of problem b from its final fp32 row (in
+// LDS), exactly as the centroid preparation of FlashAssign lays them out for
+// fp32 X: per group of 16 centroids, depth block kb, lane quad p holds depth
+// values 16 kb + 4 p .. + 3; the bias -||c||^2 / 2 is summed in the same
+// order (fmaf chains over the depth blocks kb = w, w + 4, ... for w = 0..3
+// and p = 0..3, then the four w, then the quads in pairs), so the result is
+// the same bit for bit.  One wavefront.
+__device__ void emit_fragment_f32(const SmallParams& S, int64_t b, int64_t k, const float* row) {
   const int lane = threadIdx.x & 63;
-  const int64_t q = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // b * K + k
-  if (q >= nclusters) return;
-  const int64_t b = q / S.K, k = q - b * S.K;
+  const AssignCfg& cfg = S.cfg;
+  const int KB = cfg.KB;
+  const int64_t g = k / 16;
+  const int rsel = (int)(k % 16);
+  uint32_t* gdst = S.frag + 4 * (b * S.f_stride + (g / cfg.CT) * cfg.tile_slots() + (g % cfg.CT) * cfg.group_slots());
+  if (lane < 4 * KB) {
+    const int kb = lane >> 2, p = lane & 3;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int d = kb * kFragDepth + p * 4 + e;
+      w[e] = __float_as_uint(d < S.D ? row[d] : 0.0f);
+    }
+    *reinterpret_cast<u32x4_r*>(gdst + 4 * (kb * 64 + p * 16 + rsel)) = u32x4_r{w[0], w[1], w[2], w[3]};
+  }
+  float ss = 0.0f;  // lane 4 w + p: the chain of (w, p)
+  if (lane < 16) {
+    const int w = lane >> 2, p = lane & 3;
+    for (int kb = w; kb < KB; kb += 4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = kb * kFragDepth + p * 4 + e;
+        const float c = d < S.D ? row[d] : 0.0f;
+        ss = fmaf(c, c, ss);
+      }
+  }
+  const int p = lane & 3;
+  const float t = ((__shfl(ss, p) + __shfl(ss, 4 + p)) + __shfl(ss, 8 + p)) + __shfl(ss, 12 + p);  // lane p: T_p
+  const float t01 = __shfl(t, 0) + __shfl(t, 1), t23 = __shfl(t, 2) + __shfl(t, 3);
+  if (lane == 0) reinterpret_cast<float*>(gdst + 4 * (KB * 64))[rsel] = -0.5f * (t01 + t23);
+}
+
+// One wavefront per (problem, cluster): the chunk sums of a cluster, added in
+// a fixed order.  Lanes form R rows of DL lanes (DL = D rounded up to a power
+// of two, at most 64); row r takes chunks r, r + R, ... in ascending order,
+// 8 in flight, and the rows then meet in a fixed shuffle tree.
+__global__ __launch_bounds__(256) void small_combine_kernel(SmallParams S, int64_t nclusters, int DL) {
+  __shared__ float rows[4][kMaxD32];  // fp32 rows for the fragments
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t q = (int64_t)blockIdx.x * 4 + wv;  // b * K + k
+  const bool active = q < nclusters;                 // (every wavefront reaches the barrier below)
+  const int64_t b = active ? q / S.K : 0, k = active ? q - b * S.K : 0;
   constexpr int kMaxCols = 512 / 64;  // columns per lane at most (D <= 512 with DL = 64)
   const int R = 64 / DL, r = lane / DL, cl = lane % DL;
   float acc[kMaxCols];
@@ -162,7 +213,7 @@ __global__ __launch_bounds__(256) void small_combine_kernel(SmallParams S, int64
   for (int x = 0; x < kMaxCols; ++x) acc[x] = 0.0f;
   int32_t cnt = 0;
   constexpr int UNR = 8;  // chunks in flight per row
-  for (int64_t c0 = r; c0 < S.P; c0 += (int64_t)R * UNR) {
+  for (int64_t c0 = r; active && c0 < S.P; c0 += (int64_t)R * UNR) {
     float v[UNR][kMaxCols];
     int32_t n[UNR];
 #pragma unroll
@@ -191,14 +242,22 @@ __global__ __launch_bounds__(256) void small_combine_kernel(SmallParams S, int64
     for (int x = 0; x < kMaxCols; ++x) acc[x] += __shfl_xor(acc[x], off);
     cnt += __shfl_xor(cnt, off);
   }
-  if (r != 0) return;
   const int64_t row = q * S.D;
+  if (active && r == 0) {
 #pragma unroll
-  for (int x = 0; x < kMaxCols; ++x) {
-    const int col = cl + DL * x;
-    if (col < S.D) S.C_new[row + col] = cnt > 0 ? acc[x] / (float)cnt : S.C_prev[row + col];
+    for (int x = 0; x < kMaxCols; ++x) {
+      const int col = cl + DL * x;
+      if (col < S.D) {
+        const float c = cnt > 0 ? acc[x] / (float)cnt : S.C_prev[row + col];
+        S.C_new[row + col] = c;
+        if (S.frag) rows[wv][col] = c;
+      }
+    }
+    if (cl == 0 && S.counts) S.counts[q] = cnt;
   }
-  if (cl == 0 && S.counts) S.counts[q] = cnt;
+  if (!S.frag) return;  // (uniform)
+  __syncthreads();
+  if (active) emit_fragment_f32(S, b, k, rows[wv]);
 }
 
 int64_t small_chunks(int64_t N) { return (N + kSmallChunkThin - 1) / kSmallChunkThin; }  // at most
@@ -224,6 +283,9 @@ hipError_t launch_small_update(const SmallArgs& a, hipStream_t stream) {
   S.counts = a.counts;
   S.part_sum = a.part_sum;
   S.part_cnt = a.part_cnt;
+  S.frag = nullptr;
+  S.f_stride = 0;
+  S.cfg = a.cfg;
   const int64_t grid = a.B * S.P;
   if (grid >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const int epl = 16 / es;
@@ -245,7 +307,13 @@ hipError_t launch_small_update(const SmallArgs& a, hipStream_t stream) {
   KM_SMALL(4, 1) KM_SMALL(4, 2) KM_SMALL(4, 4) KM_SMALL(4, 8) KM_SMALL(4, 16) KM_SMALL(4, 32) KM_SMALL(4, 64)
 #undef KM_SMALL
   if (!launched) return hipErrorInvalidValue;
+  if (a.emitted) *a.emitted = false;
   if (S.P > 1) {
+    if (a.frag && a.dt == DT_F32 && a.cfg.rows == 16 && a.D <= kMaxD32) {
+      S.frag = (uint32_t*)a.frag;
+      S.f_stride = a.f_stride;
+      if (a.emitted) *a.emitted = true;
+    }
     const int64_t nq = a.B * a.K;
     int dl = 1;
     while (dl < a.D && dl < 64) dl <<= 1;

@@ -127,6 +127,25 @@ def test_fit_resume_and_determinism():
     assert torch.equal(obj6, torch.cat(objs))
 
 
+@pytest.mark.parametrize("shape", [(16384, 32, 64), (3000, 100, 40), (70000, 7, 20)], ids=lambda s: "x".join(map(str, s)))
+def test_fit_small_codebook_many_iterations_equal_single_steps(shape):
+    """fp32, K <= 64: from the second iteration of a call on, FlashAssign uses the centroid fragments that the
+    update wrote; T iterations in one call must equal T calls of one iteration (which prepare them afresh)."""
+    N, D, K = shape
+    w = synth.WORKLOADS["c1"].scaled(N=N, D=D, K=K)
+    Xn = synth.points(w)
+    X = torch.from_numpy(Xn).to(DEV)
+    C0 = torch.from_numpy(synth.init_centroids(w, Xn)).to(DEV)
+    Ca, aa, na, oa = km.fit(X, C0, 8, objective=True)
+    Cs, objs = C0, []
+    for _ in range(8):
+        Cs, a1, n1, o1 = km.fit(X, Cs, 1, objective=True)
+        objs.append(o1)
+    torch.cuda.synchronize()
+    assert torch.equal(Ca, Cs) and torch.equal(aa, a1) and torch.equal(na, n1)
+    assert torch.equal(oa, torch.cat(objs))
+
+
 def test_fit_zero_iterations_and_fixed_point():
     g = torch.Generator().manual_seed(1)
     cen = torch.tensor([[0.0, 0.0], [10.0, 0.0], [0.0, 10.0]])
