@@ -475,8 +475,15 @@ static km_status run_update(const void* X, km_dtype dt, int64_t N, int64_t D, co
   a.counts = counts;
   a.acc_sum = acc_sum;
   a.acc_cnt = acc_cnt;
+  if (mode == MODE_MEAN && frag && geom && prepped) {  // the fix-up writes the next assignment's operands
+    a.frag = frag;
+    a.f_stride = (int64_t)(geom->frag_bytes() / 16);
+    a.kper = K / B;
+    a.cfg = geom->cfg;
+  }
   KM_TIMED("reduce", s, return launch_segment_reduce(a, s));
   KM_TIMED("finalize", s, return launch_fixup(a, s));
+  if (a.frag) *prepped = true;
   return KM_OK;
 }
 

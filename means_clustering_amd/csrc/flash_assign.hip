@@ -46,6 +46,7 @@
 //     The result is the same argmax as the full scan, bit for bit.
 #include <math.h>
 
+#include "frag_emit.hpp"
 #include "km_internal.hpp"
 
 namespace km {
@@ -55,23 +56,6 @@ typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // keep NaN quiet
-  u += 0x7fffu + ((u >> 16) & 1u);                                // round to nearest, ties to even
-  return u >> 16;
-}
-
-__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
-  _Float16 h = (_Float16)f;  // IEEE conversion, round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, h);
-}
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
-__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-}
 
 // ---------------------------------------------------------------- prep ----
 

@@ -265,6 +265,12 @@ struct ReduceArgs {
   int32_t* counts;      // MODE_MEAN, nullable
   float* acc_sum;       // MODE_ACCUM: K x D running sums
   int64_t* acc_cnt;     // MODE_ACCUM: K running counts
+  // MODE_MEAN, optional: the fix-up also writes FlashAssign's operand
+  // fragments of C_new (cluster k = centroid k % kper of problem k / kper,
+  // problem fragments f_stride 16-byte slots apart, geometry cfg)
+  void* frag = nullptr;
+  int64_t f_stride = 0, kper = 0;
+  AssignCfg cfg{};
 };
 
 int64_t reduce_dc(int dt, int64_t D);   // padded row length of a carry piece

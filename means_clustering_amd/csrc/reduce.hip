@@ -20,6 +20,7 @@
 //     carry pieces in a fixed order (strided per thread row, then a fixed
 //     tree), so results do not depend on scheduling.
 // Atomic count: zero, against the page's O((K + N/B_N) d) boundary atomics.
+#include "frag_emit.hpp"
 #include "km_internal.hpp"
 #include "rows.hpp"
 
@@ -59,6 +60,12 @@ struct SegParams {
   float* group_sum;   // [blocks][Dc]: a segment-reduce workgroup's slot-0 pieces, summed, when its positions hold one id
   int32_t* group_cnt;
   int tpb;            // tiles per segment-reduce workgroup
+  // mean mode, optional: FlashAssign's operand fragments of the new centroids
+  // (cluster k is centroid k % kper of problem k / kper, whose fragments start
+  // f_stride 16-byte slots further), written by the fix-up
+  uint32_t* frag;
+  int64_t f_stride, kper;
+  AssignCfg cfg;
   int Dc;
   int mode;
   const float* C_prev;
@@ -280,6 +287,7 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
 // shuffle tree, so the order of additions never depends on scheduling.
 template <int CPL>  // float4 columns per lane: 2 only when a piece has 128 of them
 __global__ __launch_bounds__(256) void fixup_kernel(SegParams P) {
+  __shared__ float rows[4][kMaxD16];  // each wavefront's final row, for the operand fragments
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gc = P.Dc / 4;                    // float4 columns of a carry piece (power of two, <= 128)
   const int lpr = gc < 64 ? gc : 64;          // lanes per row
@@ -287,96 +295,112 @@ __global__ __launch_bounds__(256) void fixup_kernel(SegParams P) {
   constexpr int cpl = CPL;
   const int r = lane / lpr, c0 = lane % lpr;
   const int64_t k = (int64_t)blockIdx.x * 4 + wave;
-  if (k >= P.K) return;
-  const int64_t s = P.off[k], e = P.off[k + 1];
-  if (s < 0 || e > P.N || s > e) return;  // offsets are monotone in [0, N]
-  if (s == e) {
-    if (P.mode == MODE_MEAN) {
-      if (lane == 0 && P.counts) P.counts[k] = 0;
-      if (P.C_new != P.C_prev)
-        for (int c = lane; c < P.D; c += 64) P.C_new[k * P.D + c] = P.C_prev[k * P.D + c];
+  // (no early return: with fragments to write every wavefront meets the barrier below)
+  const bool active = k < P.K;
+  const int64_t s = active ? P.off[k] : 0, e = active ? P.off[k + 1] : 0;
+  const bool valid = active && s >= 0 && e <= P.N && s <= e;  // offsets are monotone in [0, N]
+  const int64_t t0 = s / kSegTile, t1 = e > s ? (e - 1) / kSegTile : t0;
+  const bool cut = valid && s < e && t0 != t1;  // otherwise empty, or finished by segment_reduce_kernel
+  if (valid && s == e && P.mode == MODE_MEAN) {  // empty: keeps its centroid
+    if (lane == 0 && P.counts) P.counts[k] = 0;
+    if (P.C_new != P.C_prev)
+      for (int c = lane; c < P.D; c += 64) P.C_new[k * P.D + c] = P.C_prev[k * P.D + c];
+  }
+  float* row = rows[wave];
+  if (cut) {
+    // item list: head tiles [t0, hb), whole groups [g0, g1), tail tiles [tb, t1]
+    const int64_t T = P.tpb;
+    int64_t hb = (t0 / T + 1) * T;
+    const int64_t tb = (t1 / T) * T;
+    int64_t g0 = hb / T, g1 = tb / T;
+    if (hb > tb) {  // t0 and t1 in the same or adjacent groups: tiles only
+      hb = t1 + 1;
+      g0 = g1 = 0;
     }
-    return;
-  }
-  const int64_t t0 = s / kSegTile, t1 = (e - 1) / kSegTile;
-  if (t0 == t1) return;  // finished by segment_reduce_kernel
-  // item list: head tiles [t0, hb), whole groups [g0, g1), tail tiles [tb, t1]
-  const int64_t T = P.tpb;
-  int64_t hb = (t0 / T + 1) * T;
-  const int64_t tb = (t1 / T) * T;
-  int64_t g0 = hb / T, g1 = tb / T;
-  if (hb > tb) {  // t0 and t1 in the same or adjacent groups: tiles only
-    hb = t1 + 1;
-    g0 = g1 = 0;
-  }
-  const int64_t nh = hb - t0, ng = g1 - g0, nt = hb > tb ? 0 : t1 - tb + 1;
-  const int64_t nitems = nh + ng + nt;
-  float a[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  int32_t n = 0;
-  constexpr int UNR = 4;  // items in flight per lane
-  for (int64_t ib = r; ib < nitems; ib += (int64_t)R * UNR) {
-    float4 v[UNR][2];
-    int32_t cc[UNR];
+    const int64_t nh = hb - t0, ng = g1 - g0, nt = hb > tb ? 0 : t1 - tb + 1;
+    const int64_t nitems = nh + ng + nt;
+    float a[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    int32_t n = 0;
+    constexpr int UNR = 4;  // items in flight per lane
+    for (int64_t ib = r; ib < nitems; ib += (int64_t)R * UNR) {
+      float4 v[UNR][2];
+      int32_t cc[UNR];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int64_t it = ib + (int64_t)u * R;
-      cc[u] = 0;
-      v[u][0] = v[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (it < nitems) {
-        const float* piece;
-        if (it < nh || it >= nh + ng) {
-          const int64_t t = it < nh ? t0 + it : tb + (it - nh - ng);
-          const int slot = (t == t0 && s != t0 * kSegTile) ? 1 : 0;
-          piece = P.carry_sum + (t * 2 + slot) * (int64_t)P.Dc;
-          cc[u] = P.carry_cnt[t * 2 + slot];
-        } else {
-          const int64_t gi = g0 + (it - nh);
-          piece = P.group_sum + gi * (int64_t)P.Dc;
-          cc[u] = P.group_cnt[gi];
+      for (int u = 0; u < UNR; ++u) {
+        const int64_t it = ib + (int64_t)u * R;
+        cc[u] = 0;
+        v[u][0] = v[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (it < nitems) {
+          const float* piece;
+          if (it < nh || it >= nh + ng) {
+            const int64_t t = it < nh ? t0 + it : tb + (it - nh - ng);
+            const int slot = (t == t0 && s != t0 * kSegTile) ? 1 : 0;
+            piece = P.carry_sum + (t * 2 + slot) * (int64_t)P.Dc;
+            cc[u] = P.carry_cnt[t * 2 + slot];
+          } else {
+            const int64_t gi = g0 + (it - nh);
+            piece = P.group_sum + gi * (int64_t)P.Dc;
+            cc[u] = P.group_cnt[gi];
+          }
+#pragma unroll
+          for (int cl = 0; cl < cpl; ++cl) v[u][cl] = *reinterpret_cast<const float4*>(piece + (c0 + cl * lpr) * 4);
         }
+      }
 #pragma unroll
-        for (int cl = 0; cl < cpl; ++cl) v[u][cl] = *reinterpret_cast<const float4*>(piece + (c0 + cl * lpr) * 4);
+      for (int u = 0; u < UNR; ++u) {  // ascending item order within the row
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl) {
+          a[cl][0] += v[u][cl].x;
+          a[cl][1] += v[u][cl].y;
+          a[cl][2] += v[u][cl].z;
+          a[cl][3] += v[u][cl].w;
+        }
+        n += cc[u];
       }
     }
+    for (int off = lpr; off < 64; off <<= 1) {  // fixed tree over the rows
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {  // ascending item order within the row
+      for (int cl = 0; cl < 2; ++cl)
 #pragma unroll
-      for (int cl = 0; cl < 2; ++cl) {
-        a[cl][0] += v[u][cl].x;
-        a[cl][1] += v[u][cl].y;
-        a[cl][2] += v[u][cl].z;
-        a[cl][3] += v[u][cl].w;
+        for (int x = 0; x < 4; ++x) a[cl][x] += __shfl_xor(a[cl][x], off);
+      n += __shfl_xor(n, off);
+    }
+    if (r == 0) {
+#pragma unroll
+      for (int cl = 0; cl < cpl; ++cl)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int c = (c0 + cl * lpr) * 4 + x;
+          if (c >= P.D) continue;
+          const int64_t o = k * P.D + c;
+          if (P.mode == MODE_MEAN) {
+            const float m = n > 0 ? a[cl][x] / (float)n : P.C_prev[o];
+            P.C_new[o] = m;
+            if (P.frag) row[c] = m;
+          } else {
+            P.acc_sum[o] += a[cl][x];
+          }
+        }
+      if (c0 == 0) {
+        if (P.mode == MODE_MEAN) {
+          if (P.counts) P.counts[k] = n;
+        } else {
+          P.acc_cnt[k] += n;
+        }
       }
-      n += cc[u];
     }
   }
-  for (int off = lpr; off < 64; off <<= 1) {  // fixed tree over the rows
-#pragma unroll
-    for (int cl = 0; cl < 2; ++cl)
-#pragma unroll
-      for (int x = 0; x < 4; ++x) a[cl][x] += __shfl_xor(a[cl][x], off);
-    n += __shfl_xor(n, off);
+  if (!P.frag) return;  // (uniform: mean mode with a fragment buffer)
+  // The new centroid's row: from the sums above, else as the segmented
+  // reduction (finished clusters) or the empty rule (C_prev) left it.
+  if (valid && !cut) {
+    const float* src = s == e ? P.C_prev : P.C_new;
+    for (int c = lane; c < P.D; c += 64) row[c] = src[k * P.D + c];
   }
-  if (r == 0) {
-#pragma unroll
-    for (int cl = 0; cl < cpl; ++cl)
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int c = (c0 + cl * lpr) * 4 + x;
-        if (c >= P.D) continue;
-        const int64_t o = k * P.D + c;
-        if (P.mode == MODE_MEAN)
-          P.C_new[o] = n > 0 ? a[cl][x] / (float)n : P.C_prev[o];
-        else
-          P.acc_sum[o] += a[cl][x];
-      }
-    if (c0 == 0) {
-      if (P.mode == MODE_MEAN) {
-        if (P.counts) P.counts[k] = n;
-      } else {
-        P.acc_cnt[k] += n;
-      }
-    }
+  __syncthreads();
+  if (valid) {
+    const int64_t b = k / P.kper;
+    emit_fragment_row(row, P.D, P.dt, P.cfg, P.frag + 4 * b * P.f_stride, k - b * P.kper);
   }
 }
 
@@ -397,6 +421,10 @@ static SegParams make_params(const ReduceArgs& a) {
   P.group_sum = a.group_sum;
   P.group_cnt = a.group_cnt;
   P.tpb = (int)reduce_tpb(a.dt, a.D);
+  P.frag = a.mode == MODE_MEAN ? (uint32_t*)a.frag : nullptr;
+  P.f_stride = a.f_stride;
+  P.kper = a.kper > 0 ? a.kper : a.K;
+  P.cfg = a.cfg;
   P.Dc = (int)reduce_dc(a.dt, a.D);
   P.mode = a.mode;
   P.C_prev = a.C_prev;

@@ -17,6 +17,7 @@
 // chunk by chunk in a second launch.  The order of every addition is fixed
 // (chunk, then point index), so results are deterministic.
 #include "block_rank.hpp"
+#include "frag_emit.hpp"
 #include "km_internal.hpp"
 #include "rows.hpp"
 
@@ -155,51 +156,6 @@ __global__ __launch_bounds__(kRadixThreads) void small_update_kernel(SmallParams
 // a fixed order.  Lanes form R rows of DL lanes (DL = D rounded up to a power
 // of two, at most 64); row r takes chunks r, r + R, ... in ascending order,
 // 8 in flight, and the rows then meet in a fixed shuffle tree.
-// Fragment and bias of centroid k of problem b from its final fp32 row (in
-// LDS), exactly as the centroid preparation of FlashAssign lays them out for
-// fp32 X: per group of 16 centroids, depth block kb, lane quad p holds depth
-// values 16 kb + 4 p .. + 3; the bias -||c||^2 / 2 is summed in the same
-// order (fmaf chains over the depth blocks kb = w, w + 4, ... for w = 0..3
-// and p = 0..3, then the four w, then the quads in pairs), so the result is
-// the same bit for bit.  One wavefront.
-__device__ void emit_fragment_f32(const SmallParams& S, int64_t b, int64_t k, const float* row) {
-  const int lane = threadIdx.x & 63;
-  const AssignCfg& cfg = S.cfg;
-  const int KB = cfg.KB;
-  const int64_t g = k / 16;
-  const int rsel = (int)(k % 16);
-  uint32_t* gdst = S.frag + 4 * (b * S.f_stride + (g / cfg.CT) * cfg.tile_slots() + (g % cfg.CT) * cfg.group_slots());
-  if (lane < 4 * KB) {
-    const int kb = lane >> 2, p = lane & 3;
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int d = kb * kFragDepth + p * 4 + e;
-      w[e] = __float_as_uint(d < S.D ? row[d] : 0.0f);
-    }
-    *reinterpret_cast<u32x4_r*>(gdst + 4 * (kb * 64 + p * 16 + rsel)) = u32x4_r{w[0], w[1], w[2], w[3]};
-  }
-  float ss = 0.0f;  // lane 4 w + p: the chain of (w, p)
-  if (lane < 16) {
-    const int w = lane >> 2, p = lane & 3;
-    for (int kb = w; kb < KB; kb += 4)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = kb * kFragDepth + p * 4 + e;
-        const float c = d < S.D ? row[d] : 0.0f;
-        ss = fmaf(c, c, ss);
-      }
-  }
-  const int p = lane & 3;
-  const float t = ((__shfl(ss, p) + __shfl(ss, 4 + p)) + __shfl(ss, 8 + p)) + __shfl(ss, 12 + p);  // lane p: T_p
-  const float t01 = __shfl(t, 0) + __shfl(t, 1), t23 = __shfl(t, 2) + __shfl(t, 3);
-  if (lane == 0) reinterpret_cast<float*>(gdst + 4 * (KB * 64))[rsel] = -0.5f * (t01 + t23);
-}
-
-// One wavefront per (problem, cluster): the chunk sums of a cluster, added in
-// a fixed order.  Lanes form R rows of DL lanes (DL = D rounded up to a power
-// of two, at most 64); row r takes chunks r, r + R, ... in ascending order,
-// 8 in flight, and the rows then meet in a fixed shuffle tree.
 __global__ __launch_bounds__(256) void small_combine_kernel(SmallParams S, int64_t nclusters, int DL) {
   __shared__ float rows[4][kMaxD32];  // fp32 rows for the fragments
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -257,7 +213,7 @@ __global__ __launch_bounds__(256) void small_combine_kernel(SmallParams S, int64
   }
   if (!S.frag) return;  // (uniform)
   __syncthreads();
-  if (active) emit_fragment_f32(S, b, k, rows[wv]);
+  if (active) emit_fragment_row(rows[wv], S.D, S.dt, S.cfg, S.frag + 4 * b * S.f_stride, k);
 }
 
 int64_t small_chunks(int64_t N) { return (N + kSmallChunkThin - 1) / kSmallChunkThin; }  // at most

@@ -127,14 +127,19 @@ def test_fit_resume_and_determinism():
     assert torch.equal(obj6, torch.cat(objs))
 
 
-@pytest.mark.parametrize("shape", [(16384, 32, 64), (3000, 100, 40), (70000, 7, 20)], ids=lambda s: "x".join(map(str, s)))
-def test_fit_small_codebook_many_iterations_equal_single_steps(shape):
-    """fp32, K <= 64: from the second iteration of a call on, FlashAssign uses the centroid fragments that the
-    update wrote; T iterations in one call must equal T calls of one iteration (which prepare them afresh)."""
+@pytest.mark.parametrize("shape,xdtype", [((16384, 32, 64), "f32"), ((3000, 100, 40), "f32"), ((70000, 7, 20), "f32"),
+                                          ((6000, 32, 100), "f32"), ((20000, 72, 300), "bf16"),
+                                          ((9000, 200, 130), "f16"), ((5000, 512, 70), "bf16")],
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else v)
+def test_fit_many_iterations_equal_single_steps(shape, xdtype):
+    """From the second iteration of a call on, FlashAssign uses the operand fragments that the update wrote
+    (the small-codebook path for fp32 K <= 64, the fix-up otherwise); T iterations in one call must equal T
+    calls of one iteration (which prepare them afresh), bit for bit."""
     N, D, K = shape
     w = synth.WORKLOADS["c1"].scaled(N=N, D=D, K=K)
     Xn = synth.points(w)
-    X = torch.from_numpy(Xn).to(DEV)
+    Xf = torch.from_numpy(Xn)
+    X = (Xf if xdtype == "f32" else Xf.to(torch.bfloat16 if xdtype == "bf16" else torch.float16)).to(DEV)
     C0 = torch.from_numpy(synth.init_centroids(w, Xn)).to(DEV)
     Ca, aa, na, oa = km.fit(X, C0, 8, objective=True)
     Cs, objs = C0, []
