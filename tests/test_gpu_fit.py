@@ -129,7 +129,8 @@ def test_fit_resume_and_determinism():
 
 @pytest.mark.parametrize("shape,xdtype", [((16384, 32, 64), "f32"), ((3000, 100, 40), "f32"), ((70000, 7, 20), "f32"),
                                           ((6000, 32, 100), "f32"), ((20000, 72, 300), "bf16"),
-                                          ((9000, 200, 130), "f16"), ((5000, 512, 70), "bf16")],
+                                          ((9000, 200, 130), "f16"), ((5000, 512, 70), "bf16"),
+                                          ((30000, 24, 8192), "f32"), ((40000, 16, 9000), "bf16")],
                          ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else v)
 def test_fit_many_iterations_equal_single_steps(shape, xdtype):
     """From the second iteration of a call on, FlashAssign uses the operand fragments that the update wrote
