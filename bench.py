@@ -200,6 +200,18 @@ def ablation(dev):
     print(json.dumps(out), flush=True)
 
 
+# Timed steps by default: enough that the timed region is tens of milliseconds.
+DEFAULT_STEPS = {"c1": 200, "c2": 10}
+
+
+def timed_step(i: int, steps: int) -> bool:
+    """Whether timed step i carries the FlashAssign events.  A timing event costs a
+    marker packet and a few microseconds of host time per launch, which is ~12%
+    of a c1 iteration, so with many steps only every s-th step is bracketed
+    (s = ceil(steps / 8)); the launches of those steps give the average."""
+    return i % -(-steps // 8) == 0
+
+
 def batched(args, dev):
     """B independent problems of one workload's shape per call (kmeans_fit_batched); one JSON line.
 
@@ -244,10 +256,11 @@ def batched(args, dev):
     timing = not args.no_timing
     if timing:
         km.timing_reset()
-        km.timing_enable(2)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        if timing:
+            km.timing_enable(2 if timed_step(i, args.steps) else 0)
         one_step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -264,7 +277,8 @@ def batched(args, dev):
             peak = PEAK[base.dtype]
             roof = {"bound": "mfma", "kernel": "flash_assign (batched)", "achieved": round(flops / avg_s / 1e12, 2),
                     "peak": round(peak / 1e12, 1), "unit": "TFLOP/s", "frac": round(flops / avg_s / peak, 4),
-                    "traffic": None, "flops_per_launch": flops, "avg_launch_us": round(avg_s * 1e6, 3)}
+                    "traffic": None, "flops_per_launch": flops, "avg_launch_us": round(avg_s * 1e6, 3),
+                    "timed_launches": n, "timed_steps": sum(timed_step(i, args.steps) for i in range(args.steps))}
         km.timing_enable(1)
         one_step()
         torch.cuda.synchronize()
@@ -296,7 +310,8 @@ def batched(args, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 200 for c1, 10 for c2, 5 otherwise)")
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -311,6 +326,8 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = DEFAULT_STEPS.get(args.workload, 5)
     if args.calibrate_copy:
         import torch
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB
@@ -387,15 +404,16 @@ def main():
         torch.cuda.synchronize()
         print(f"[bench] warmup step {i} done", file=sys.stderr, flush=True)
 
-    # Timed region: HIP events bracket only the FlashAssign launches (mode 2), so
-    # the measured throughput carries almost none of their cost.
+    # Timed region: HIP events bracket only the FlashAssign launches (mode 2) of a
+    # sample of the steps, so the measured throughput carries almost none of their cost.
     timing = not args.no_timing
     if timing:
         km.timing_reset()
-        km.timing_enable(2)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if timing:
+            km.timing_enable(2 if timed_step(i, args.steps) else 0)
         one_step()
         if streamed:
             torch.cuda.synchronize()
@@ -442,7 +460,9 @@ def main():
         traffic = _traffic(ASSIGN_SOURCES, w.name)
         roof = {"bound": "mfma", "kernel": "flash_assign", "achieved": round(achieved / 1e12, 2),
                 "peak": round(peak / 1e12, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": traffic, "flops_per_launch": flops, "avg_launch_us": phases["assign"]["avg_us"]}
+                "traffic": traffic, "flops_per_launch": flops, "avg_launch_us": phases["assign"]["avg_us"],
+                "timed_launches": phases["assign"]["launches"],
+                "timed_steps": sum(timed_step(i, args.steps) for i in range(args.steps))}
 
     peaks = None if args.no_peaks else measured_peaks(dev, w.dtype)
     if roof is not None and peaks and "mfma_TFLOPs" in peaks:

@@ -50,6 +50,13 @@ TimingRegistry& timing() {
   return r;
 }
 
+// Timing events carry no system-scope fence: they only take timestamps, and the
+// fence (a cache writeback and invalidate per record) would slow the work it
+// brackets.  Readers synchronise the device before reading them.
+#ifndef KM_TIMING_EVENT_FLAGS
+#define KM_TIMING_EVENT_FLAGS hipEventDisableSystemFence
+#endif
+
 // Brackets the launches made by `fn` with events on `stream` when timing is on.
 template <class F>
 hipError_t timed(const char* phase, hipStream_t stream, F&& fn) {
@@ -61,9 +68,9 @@ hipError_t timed(const char* phase, hipStream_t stream, F&& fn) {
   }
   if (!on) return fn();
   hipEvent_t a, b;
-  hipError_t e = hipEventCreate(&a);
+  hipError_t e = hipEventCreateWithFlags(&a, KM_TIMING_EVENT_FLAGS);
   if (e != hipSuccess) return e;
-  e = hipEventCreate(&b);
+  e = hipEventCreateWithFlags(&b, KM_TIMING_EVENT_FLAGS);
   if (e != hipSuccess) return e;
   e = hipEventRecord(a, stream);
   if (e != hipSuccess) return e;
