@@ -66,3 +66,11 @@ def test_sort_empty_input():
     perm, off = km.sort_by_cluster(torch.empty(0, dtype=torch.int32, device=DEV), 5)
     torch.cuda.synchronize()
     assert perm.numel() == 0 and off.cpu().tolist() == [0] * 6
+
+
+@pytest.mark.parametrize("N", [2**20, 2**20 + 1])
+def test_sort_scan_paths(N):
+    """K = 4096 (two 6-bit passes) in blocks of 2048 keys: 64 x 512 digit counts (8 scan tiles, scanned by one
+    workgroup) against 64 x 513 (9 tiles, scanned in three launches)."""
+    rng = np.random.default_rng(N)
+    _check(rng.integers(0, 4096, N), 4096, "scan paths")
