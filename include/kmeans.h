@@ -229,9 +229,11 @@ const char* kmeans_last_error(void);
  * Kernel timing (for measurement, off by default).  kmeans_timing_enable(1):
  * every kernel phase a call enqueues is bracketed by HIP events on the stream
  * it runs on; kmeans_timing_enable(2): only the FlashAssign launches ("assign"
- * phase), so the events barely perturb the rest; 0: off.  Event records
- * between kernels cost a little time each, so throughput is measured with 2
- * or 0.  kmeans_timing_read() waits for the recorded events and returns the
+ * phase), so the events barely perturb the rest; 0: off.  The events carry
+ * no system-scope fence (they only take timestamps), but each record still
+ * costs a marker packet and some host time, so throughput is measured with 2
+ * or 0.  The mode can change between calls.  kmeans_timing_read() waits for
+ * the recorded events and returns the
  * summed milliseconds and the number of timed launches of one phase:
  * "prep", "assign", "sort", "segments", "reduce", "finalize", "objective",
  * "h2d", "d2h".  kmeans_timing_reset() forgets all records.

@@ -9,16 +9,17 @@
 // cluster become contiguous; the update then reduces contiguous segments
 // instead of scattering.  Here the sort is an LSD radix sort over the bits of
 // the largest cluster id, at most 6 bits a pass, passes of balanced width.
-// Nothing in it uses an atomic, so a hot cluster (many points with one id)
-// costs no contention.  Ranking inside a block of 256 x IT keys (IT = 8, 16
-// or 32 by N): every thread owns IT consecutive keys and a private 16-bit counter per
+// No global atomic anywhere, so a hot cluster (many points with one id) costs
+// no contention in memory.  Per pass: a count of each block's digits (an LDS
+// histogram per wavefront), the exclusive scan of those counts over (digit,
+// block) (small tables: summed by every scatter workgroup itself), and the
+// scatter.  Ranking inside a block of 256 x IT keys (IT = 8, 16 or 32 by N):
+// every thread owns IT consecutive keys and a private 16-bit counter per
 // digit in LDS; counting its own keys in order gives each key its rank among
 // the thread's keys of that digit, and one exclusive scan over the counters in
 // (digit, thread) order turns them into block-wide ranks that keep the input
-// order of equal digits (stable).  Per-block digit counts then become global
-// destinations through a device-wide exclusive scan.  Every step is a
-// deterministic function of the input, which fixes the summation order of
-// the update.
+// order of equal digits (stable).  Every step is a deterministic function of
+// the input, which fixes the summation order of the update.
 #include "block_rank.hpp"
 #include "km_internal.hpp"
 
