@@ -41,8 +41,11 @@ def x_from_numpy(Xn: np.ndarray, xdtype: str, device) -> torch.Tensor:
     return torch.from_numpy(Xn).to(device)
 
 
-def check_assign(Xn, xdtype, C_state, a_gpu, rows=None, label=""):
-    """Assignment of rows `rows` (all if None) against the oracle on the same centroid state."""
+def check_assign(Xn, xdtype, C_state, a_gpu, rows=None, label="", min_near_ties=0):
+    """Assignment of rows `rows` (all if None) against the oracle on the same centroid state.
+
+    min_near_ties: near-tie mismatches always allowed, whatever 0.01% of the points comes to (small problems,
+    where 0.01% is less than one point; the gap bound on every mismatch still holds)."""
     Xs = Xn if rows is None else Xn[rows]
     a_ref, d1, d2 = oracle.assign(Xs, np.asarray(C_state, dtype=np.float64), xdtype)
     a_gpu = np.asarray(a_gpu if rows is None else a_gpu[rows])
@@ -53,7 +56,7 @@ def check_assign(Xn, xdtype, C_state, a_gpu, rows=None, label=""):
     assert allowed.all(), (f"{label}: {int((~allowed).sum())} mismatches beyond the near-tie gap, e.g. rows "
                            f"{mism[~allowed][:5].tolist()} gpu {a_gpu[mism[~allowed][:5]].tolist()} "
                            f"oracle {a_ref[mism[~allowed][:5]].tolist()} gap {gap[mism[~allowed][:5]].tolist()}")
-    assert len(mism) <= MAX_NEAR_TIE_FRAC * len(Xs) + 1e-9 or len(mism) == 0, \
+    assert len(mism) <= max(MAX_NEAR_TIE_FRAC * len(Xs), min_near_ties) + 1e-9 or len(mism) == 0, \
         f"{label}: {len(mism)} near-tie mismatches of {len(Xs)} points"
     return len(mism), a_ref
 

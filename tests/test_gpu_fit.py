@@ -19,7 +19,7 @@ def _workload(name, **kw):
     return w, Xn, C0
 
 
-def _teacher_forced(Xn, xdtype, C0, T, label, streamed_chunk=None, stage_bytes=None):
+def _teacher_forced(Xn, xdtype, C0, T, label, streamed_chunk=None, stage_bytes=None, min_near_ties=0):
     """Run T single iterations on the GPU; check each against the oracle fed the GPU's own state."""
     X = parity.x_from_numpy(Xn, xdtype, DEV)
     C = torch.from_numpy(C0).to(DEV)
@@ -37,7 +37,7 @@ def _teacher_forced(Xn, xdtype, C0, T, label, streamed_chunk=None, stage_bytes=N
             C, a, counts, obj = km.fit_streamed(Xh, C, 1, streamed_chunk, objective=True, stage=stage)
         torch.cuda.synchronize()
         an = a.cpu().numpy() if a.is_cuda else a.numpy()
-        nm, _ = parity.check_assign(Xn, xdtype, C_prev, an, label=f"{label} it{t}")
+        nm, _ = parity.check_assign(Xn, xdtype, C_prev, an, label=f"{label} it{t}", min_near_ties=min_near_ties)
         flips += nm
         max_err = max(max_err, parity.check_update(Xn, xdtype, an, C_prev, C.cpu().numpy(),
                                                    counts.cpu().numpy(), label=f"{label} it{t}"))
