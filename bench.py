@@ -469,6 +469,25 @@ def main():
         roof["peak_measured"] = peaks["mfma_TFLOPs"]
         roof["frac_of_measured"] = round(roof["achieved"] / peaks["mfma_TFLOPs"], 4)
 
+    # ---- the update's bandwidth: the reduction kernel(s) of the per-phase step against HBM.  Algorithmic
+    # bytes per launch: the rows of X it reads once (gathered in cluster order) plus the sorted keys and
+    # point indices (8 B a point; the small-codebook path reads the 4-byte ids instead).
+    upd = None
+    if "reduce" in breakdown:
+        es = 2 if w.dtype in ("bf16", "f16") else 4
+        rows = w.chunk_rows if streamed else w.N
+        small = w.K <= 64
+        per_launch = rows * (w.D * es + (4 if small else 8))
+        if streamed:  # ragged last chunk: use the total
+            per_launch = w.N * (w.D * es + (4 if small else 8)) * w.iters / breakdown["reduce"]["launches"]
+        gbps = per_launch / (breakdown["reduce"]["avg_us"] * 1e-6) / 1e9
+        upd = {"bound": "hbm", "kernel": "small_update + small_combine" if small else "segment_reduce",
+               "achieved": round(gbps, 1), "peak": 8000.0, "unit": "GB/s", "frac": round(gbps / 8000.0, 4),
+               "bytes_per_launch": round(per_launch), "avg_launch_us": breakdown["reduce"]["avg_us"]}
+        if peaks and "hbm_read_GBps" in peaks:
+            upd["peak_measured_read"] = peaks["hbm_read_GBps"]
+            upd["frac_of_measured_read"] = round(gbps / peaks["hbm_read_GBps"], 4)
+
     stream = None
     if streamed:
         es = 2 if w.dtype == "bf16" else 4
@@ -497,7 +516,8 @@ def main():
         "config": {"workload": w.description, "name": w.name, "N": w.N, "D": w.D, "K": w.K,
                    "iters_per_step": w.iters, "chunk_rows": w.chunk_rows or None},
         "distances_per_s": round(value * w.N * w.K, 1),
-        "roofline": roof, "cpu_baseline": cpu, "phases_timed_region": phases, "phase_breakdown_extra_step": breakdown,
+        "roofline": roof, "update_roofline": upd, "cpu_baseline": cpu, "phases_timed_region": phases,
+        "phase_breakdown_extra_step": breakdown,
         "streaming": stream, "peaks_measured": peaks,
         "device": torch.cuda.get_device_name(dev),
     }
