@@ -74,3 +74,28 @@ def test_fit_at_max_n():
     C2b, a2b, n2b, _ = km.fit(X, C1, 1)  # the same iteration from a cold start
     torch.cuda.synchronize()
     assert torch.equal(C2b, C2) and torch.equal(n2b, n2) and torch.equal(a2b, a2)
+
+
+def test_fit_large_codebook():
+    """K = 2^21 + 3 clusters (65,537 groups of 32 on the single-accumulator kernel, a four-pass argsort, a
+    fix-up over two million clusters), N = 2^22, D = 8 bf16; sampled rows against the oracle, counts against
+    a histogram, three clusters against the oracle's means, warm against cold bit for bit."""
+    N, D, K = 2**22, 8, 2**21 + 3
+    print(f"[limits] N={N} D={D} K={K}", flush=True)
+    w = synth.WORKLOADS["c3"].scaled(N=N, D=D, K=K, M=4096, seed=37)
+    X = torch.empty((N, D), dtype=torch.bfloat16, device=DEV)
+    synth.DeviceGenerator(w, DEV).fill(X, 0)
+    rng = np.random.default_rng(37)
+    C0 = X[torch.from_numpy(rng.choice(N, K, replace=False)).to(DEV)].float().contiguous()
+    rows = torch.from_numpy(rng.choice(N, 1024, replace=False)).to(DEV)
+    xs, name = parity.x_to_numpy(X[rows])
+
+    C1, a1, n1, _ = km.fit(X, C0, 1)
+    C2, a2, n2, _ = km.fit(X, C0, 2)
+    C2b, a2b, n2b, _ = km.fit(X, C1, 1)
+    torch.cuda.synchronize()
+    parity.check_assign(xs, name, C0.cpu().numpy(), a1[rows].cpu().numpy(), label="it0", min_near_ties=1)
+    parity.check_assign(xs, name, C1.cpu().numpy(), a2[rows].cpu().numpy(), label="it1", min_near_ties=1)
+    _check_clusters(X, a1, C0.cpu().numpy(), C1.cpu().numpy(), n1, "it0")
+    _check_clusters(X, a2, C1.cpu().numpy(), C2.cpu().numpy(), n2, "it1")
+    assert torch.equal(C2b, C2) and torch.equal(n2b, n2) and torch.equal(a2b, a2)
