@@ -3,8 +3,9 @@ the tile, block and path boundaries, K above N (empty clusters), one to three it
 the GPU's own state, and a fit of T iterations must equal T fits of one iteration, bit for bit.
 
 The problems here are small, so 0.01% of their points is often less than one point: one near-tie mismatch
-per problem and iteration is allowed (every mismatch must still lie within the near-tie gap).  The full-size
-workloads keep the plain 0.01% bar."""
+per problem and iteration is allowed, and mismatches whose oracle gap is within the fp32 error of the kernel's
+own score (ties at the kernel's precision, frequent for D = 1 with dense centroids) are not counted.  Every
+mismatch must still lie within the near-tie gap.  The full-size workloads keep the plain 0.01% bar."""
 import numpy as np
 import pytest
 import torch
@@ -57,7 +58,7 @@ def test_random_fit(case):
         C, a, counts, _ = km.fit(X, C, 1)
         torch.cuda.synchronize()
         an = a.cpu().numpy()
-        parity.check_assign(Xs, name, C_prev, an, label=f"it{t}", min_near_ties=1)
+        parity.check_assign(Xs, name, C_prev, an, label=f"it{t}", min_near_ties=1, precision_ties=True)
         parity.check_update(Xs, name, an, C_prev, C.cpu().numpy(), counts.cpu().numpy(), label=f"it{t}")
     CT, aT, nT, _ = km.fit(X, C0, T)
     torch.cuda.synchronize()
@@ -104,7 +105,8 @@ def test_random_batched(case):
         for b in range(B):
             xs, name = parity.x_to_numpy(X[b])
             an = a[b].cpu().numpy()
-            parity.check_assign(xs, name, C_prev[b], an, label=f"problem {b} it{t}", min_near_ties=1)
+            parity.check_assign(xs, name, C_prev[b], an, label=f"problem {b} it{t}", min_near_ties=1,
+                                precision_ties=True)
             parity.check_update(xs, name, an, C_prev[b], C[b].cpu().numpy(), counts[b].cpu().numpy(),
                                 label=f"problem {b} it{t}")
     CT, aT, nT, _ = km.fit_batched(X, C0, T)
@@ -118,7 +120,7 @@ def _streamed_cases(n=16, seed=99):
     while len(out) < n:
         dt = str(rng.choice(["f32", "bf16", "f16"]))
         N = int(rng.choice([1, 1000, 4097, 30011]))
-        D = int(rng.choice([1, 16, 33, 64, 128] + ([256] if dt != "f32" else [512])))
+        D = int(rng.choice([1, 16, 33, 64, 128] + ([512] if dt != "f32" else [256])))
         K = int(rng.choice([1, 7, 64, 65, 300]))
         chunk = int(rng.choice([1, 7, 1000, max(N - 1, 1), N, N + 5]))
         stage = int(rng.choice([0, 4096 * 4, 1 << 20]))  # 0: pinned X
@@ -142,4 +144,4 @@ def test_random_streamed(case):
     C0 = synth.init_centroids(w, Xn)
     xs, name = parity.x_to_numpy(torch.from_numpy(Xn).to(TORCH_DT[dt]))
     _teacher_forced(xs, name, C0, T, f"random streamed {case}", streamed_chunk=chunk,
-                    stage_bytes=stage if stage else None, min_near_ties=1)
+                    stage_bytes=stage if stage else None, min_near_ties=1, precision_ties=True)
