@@ -8,7 +8,8 @@
 // Same idea as tech §2.2 (make each cluster's points contiguous, then reduce
 // contiguous runs with no atomics), with the sort kept on chip: with K <= 64
 // the whole cluster id is one 6-bit radix digit, so one workgroup ranks the
-// ids of a chunk (2048 points, 512 for small calls) stably in LDS (the radix sort's block rank), lays
+// ids of a chunk (2048 points, 512 for small calls) stably (512: wavefront
+// ballots and LDS histograms; 2048: the radix sort's block rank), lays
 // the chunk's point indices out in cluster order in LDS, and then lets each
 // lane group walk whole clusters of the chunk in that order, 16 rows in
 // flight.  No global sort, no carries: a cluster's chunk sum is complete in
@@ -91,6 +92,67 @@ __device__ __forceinline__ void walk_rows(const uint8_t* __restrict__ Xb, const 
   }
 }
 
+// Stable rank of a chunk's ids (all below 64): rank = ids smaller than this one
+// anywhere in the chunk + equal ids at earlier positions (position = thread *
+// IT + i), the same order as the radix sort's block rank.  Equal ids earlier in
+// the wavefront come from six bit-sliced ballots per key slot; the wavefronts'
+// id counts (LDS histograms, integer atomics) give the rest.  start[0..64] is
+// left holding each id's first position.
+template <int IT>
+__device__ __forceinline__ void small_rank(const uint32_t (&d)[IT], const bool (&valid)[IT], uint32_t* hist,
+                                           uint32_t* start, uint32_t (&rank)[IT]) {
+  constexpr int NW = kRadixThreads / 64;
+  constexpr int R = 1 << kMaxDigitBits;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < NW * R; i += kRadixThreads) hist[i] = 0u;
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint32_t inwave[IT];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) inwave[i] = 0;
+#pragma unroll
+  for (int j = 0; j < IT; ++j) {  // key slot j of every lane: the lanes whose key there equals each own key
+    const uint64_t vm = __builtin_amdgcn_ballot_w64(valid[j]);
+    uint64_t bal[kMaxDigitBits];
+#pragma unroll
+    for (int b = 0; b < kMaxDigitBits; ++b) bal[b] = __builtin_amdgcn_ballot_w64(valid[j] && ((d[j] >> b) & 1u));
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      uint64_t m = vm;
+#pragma unroll
+      for (int b = 0; b < kMaxDigitBits; ++b) m &= ((d[i] >> b) & 1u) ? bal[b] : ~bal[b];
+      inwave[i] += (uint32_t)__popcll(m & below) + ((j < i && valid[j] && d[j] == d[i]) ? 1u : 0u);
+    }
+  }
+  __syncthreads();  // histograms cleared
+#pragma unroll
+  for (int i = 0; i < IT; ++i)
+    if (valid[i]) atomicAdd(&hist[wave * R + d[i]], 1u);
+  __syncthreads();
+  if (threadIdx.x < R) {  // per id: counts of earlier wavefronts, and the chunk total
+    uint32_t s = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t h = hist[w * R + threadIdx.x];
+      hist[w * R + threadIdx.x] = s;
+      s += h;
+    }
+    start[threadIdx.x + 1] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {  // exclusive scan of the totals over ids
+    uint32_t run = 0;
+    start[0] = 0;
+    for (int k = 0; k < R; ++k) {
+      run += start[k + 1];
+      start[k + 1] = run;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < IT; ++i)
+    if (valid[i]) rank[i] = start[d[i]] + hist[wave * R + d[i]] + inwave[i];
+}
+
 template <int ES, int G, int IT>
 __global__ __launch_bounds__(kRadixThreads) void small_update_kernel(SmallParams S) {
   constexpr int kSmallIT = IT;
@@ -98,8 +160,6 @@ __global__ __launch_bounds__(kRadixThreads) void small_update_kernel(SmallParams
   constexpr int EPL = 16 / ES;
   constexpr int NG = kRadixThreads / G;  // lane groups
   constexpr int U = IT == 2 ? 8 : 16;    // rows in flight per lane group (measured: 8 for a lone problem, 16 batched)
-  __shared__ uint32_t ctr[kRadixPadded];
-  __shared__ uint32_t wsum[kRadixThreads / 64];
   __shared__ uint32_t start[(1 << kMaxDigitBits) + 1];
   __shared__ int32_t srow[kChunk];
   const int64_t b = blockIdx.x / S.P, c = blockIdx.x - b * S.P;
@@ -117,7 +177,14 @@ __global__ __launch_bounds__(kRadixThreads) void small_update_kernel(SmallParams
     valid[i] = k >= 0 && k < S.K;  // ids outside [0, K) are ignored
     d[i] = valid[i] ? (uint32_t)k : 0u;
   }
-  block_rank<kMaxDigitBits, kSmallIT>(d, valid, ctr, wsum, start, rank);
+  if constexpr (IT <= 2) {  // 512 ids: ballots (the general block rank clears and scans 16K counters)
+    __shared__ uint32_t hist[(kRadixThreads / 64) << kMaxDigitBits];
+    small_rank<IT>(d, valid, hist, start, rank);
+  } else {  // more ids a thread: the ballots would outgrow the scalar registers
+    __shared__ uint32_t ctr[kRadixPadded];
+    __shared__ uint32_t wsum[kRadixThreads / 64];
+    block_rank<kMaxDigitBits, IT>(d, valid, ctr, wsum, start, rank);
+  }
 #pragma unroll
   for (int i = 0; i < kSmallIT; ++i)
     if (valid[i]) srow[rank[i]] = (int32_t)(c0 + (int64_t)threadIdx.x * kSmallIT + i);
