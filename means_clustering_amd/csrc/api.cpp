@@ -437,7 +437,7 @@ static km_status run_update(const void* X, km_dtype dt, int64_t N, int64_t D, co
   if (sorted_keys) *sorted_keys = nullptr;
   if (sorted_vals) *sorted_vals = nullptr;
   if (prepped) *prepped = false;
-  if (mode == MODE_MEAN && K / B <= kSmallMaxK) {
+  if (mode == MODE_MEAN && (K / B <= kSmallMaxK || small_owner_fits(B, N / B, K / B))) {
     SmallArgs a;
     a.X = X;
     a.dt = (int)dt;

@@ -277,7 +277,7 @@ int64_t reduce_dc(int dt, int64_t D);   // padded row length of a carry piece
 int64_t reduce_tpb(int dt, int64_t D);  // tiles per segment-reduce workgroup
 hipError_t launch_segment_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_fixup(const ReduceArgs& a, hipStream_t stream);
-// Small codebooks (K <= kSmallMaxK per problem, mean mode): the update of B
+// Small codebooks (K <= kSmallMaxK per problem, or small_owner_fits; mean mode): the update of B
 // problems of N points each in one launch (two when a problem spans several
 // chunks of 512 or 2048 points), sort and reduction on chip.  ids[b*N + i] = b*id_mul + k.
 constexpr int64_t kSmallMaxK = 64;
@@ -292,15 +292,18 @@ struct SmallArgs {
   int32_t* counts;      // B x K, nullable
   float* part_sum;      // B * small_chunks(N) * K * reduce_dc(dt, D) floats
   int32_t* part_cnt;    // B * small_chunks(N) * K
-  // optional (fp32 X): FlashAssign's centroid fragments for the next
-  // assignment, written along with the means when that step runs as a
-  // separate chunk-sum pass (*emitted says whether it did)
+  // optional: FlashAssign's centroid fragments for the next assignment,
+  // written along with the means by the one-launch layout (any X) and by the
+  // chunk-sum combine pass (fp32 X); *emitted says whether they were
   void* frag;           // B x frag_bytes of geometry cfg (NULL: none)
   int64_t f_stride;     // 16-byte slots per problem
   AssignCfg cfg;
   bool* emitted;
 };
 int64_t small_chunks(int64_t N);  // chunks per problem, at most
+// Whether B problems of N points and K clusters each take the one-launch
+// layout of one workgroup per cluster (then also for K above kSmallMaxK).
+bool small_owner_fits(int64_t B, int64_t N, int64_t K);
 hipError_t launch_small_update(const SmallArgs& a, hipStream_t stream);
 hipError_t launch_finalize_accum(const float* acc_sum, const int64_t* acc_cnt, int64_t K, int64_t D,
                                  float* C, int32_t* counts, hipStream_t stream);

@@ -285,13 +285,13 @@ __global__ __launch_bounds__(256) void small_combine_kernel(SmallParams S, int64
   if (active) emit_fragment_row(rows[wv], S.D, S.dt, S.cfg, S.frag + 4 * b * S.f_stride, k);
 }
 
-// A few small problems (at most kOwnerMaxGroups clusters in all, N <= 16384):
-// one workgroup per (problem, cluster).  It reads all of the problem's ids at
+// A few small problems (at most kOwnerMaxGroups clusters in all, N <= 16384,
+// any K up to that): one workgroup per (problem, cluster).  It reads all of the problem's ids at
 // once, lists its cluster's points in ascending index order in LDS (per-thread
 // match counts, one block scan), lets each lane group sum one contiguous block
 // of that list, adds the lane groups' sums in order and writes the mean (an
-// empty cluster keeps its centroid), the count and, for fp32 X when asked, the
-// centroid's operand fragment for the next assignment.  One launch and no
+// empty cluster keeps its centroid), the count and, when asked, the centroid's
+// operand fragment for the next assignment.  One launch and no
 // chunk sums; every addition in a fixed order.
 constexpr int kOwnerMaxN = 16384;
 constexpr int kOwnerIPT = kOwnerMaxN / kRadixThreads;  // ids per thread
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(kRadixThreads) void small_owner_kernel(SmallParams 
   __shared__ int32_t list[kOwnerMaxN];
   __shared__ uint32_t wsum[kRadixThreads / 64];
   __shared__ float part[NG * GE];
-  __shared__ float row[kMaxD32];
+  __shared__ float row[kMaxD16];
   const int64_t q = blockIdx.x, b = q / S.K, k = q - b * S.K;
   const int32_t want = (int32_t)(b * S.id_mul + k);
   const int32_t* ids = S.ids + b * S.N;
@@ -360,7 +360,7 @@ __global__ __launch_bounds__(kRadixThreads) void small_owner_kernel(SmallParams 
     for (int gg = 0; gg < NG; ++gg) sum += part[gg * GE + c];
     const float mean = total > 0 ? sum / (float)total : S.C_prev[base + c];
     S.C_new[base + c] = mean;
-    if (c < kMaxD32) row[c] = mean;
+    if (c < kMaxD16) row[c] = mean;
   }
   if (threadIdx.x == 0 && S.counts) S.counts[q] = (int32_t)total;
   if (!S.frag) return;  // (uniform)
@@ -370,9 +370,14 @@ __global__ __launch_bounds__(kRadixThreads) void small_owner_kernel(SmallParams 
 
 int64_t small_chunks(int64_t N) { return (N + kSmallChunkThin - 1) / kSmallChunkThin; }  // at most
 
+bool small_owner_fits(int64_t B, int64_t N, int64_t K) {
+  return B >= 1 && K >= 1 && N <= kOwnerMaxN && B * K <= kOwnerMaxGroups;
+}
+
 hipError_t launch_small_update(const SmallArgs& a, hipStream_t stream) {
   if (a.N == 0 || a.B == 0) return hipSuccess;
-  if (a.K < 1 || a.K > kSmallMaxK || a.D < 1 || a.D > 512) return hipErrorInvalidValue;
+  const bool owner = small_owner_fits(a.B, a.N, a.K);
+  if (a.K < 1 || (a.K > kSmallMaxK && !owner) || a.D < 1 || a.D > kMaxD16) return hipErrorInvalidValue;
   SmallParams S;
   S.X = (const uint8_t*)a.X;
   S.dt = a.dt;
@@ -394,8 +399,8 @@ hipError_t launch_small_update(const SmallArgs& a, hipStream_t stream) {
   S.frag = nullptr;
   S.f_stride = 0;
   S.cfg = a.cfg;
-  if (a.N <= kOwnerMaxN && a.B * a.K <= kOwnerMaxGroups) {  // one workgroup per cluster, one launch
-    const bool emit = a.frag && a.dt == DT_F32 && a.cfg.rows == 16 && a.D <= kMaxD32;
+  if (owner) {  // one workgroup per cluster, one launch
+    const bool emit = a.frag != nullptr;
     if (emit) {
       S.frag = (uint32_t*)a.frag;
       S.f_stride = a.f_stride;

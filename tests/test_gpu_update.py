@@ -106,7 +106,8 @@ def test_update_segments_at_group_edges(D, xdtype):
                                    (6000, 512, 5), (4100, 100, 1), (600_000, 16, 64)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_update_small_codebook(shape, xdtype):
-    """K <= 64: the on-chip path (one chunk of 512 or 2048 points per workgroup, chunk sums added in order)."""
+    """K <= 64: the on-chip path (one workgroup per cluster for N <= 16384, else one chunk of 512 or 2048
+    points per workgroup with the chunk sums added in order)."""
     N, D, K = shape
     if xdtype == "f32" and D > 256:
         pytest.skip("fp32 supports D <= 256")
@@ -118,6 +119,25 @@ def test_update_small_codebook(shape, xdtype):
         a[a == K // 2] = K - 1  # one empty cluster for sure
     C_prev = torch.randn(K, D, generator=torch.Generator().manual_seed(K + D)).to(DEV)
     _run(X, a, C_prev, f"small codebook {shape} {xdtype}")
+
+
+@pytest.mark.parametrize("xdtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("shape", [(1, 8, 65), (1000, 32, 512), (16384, 128, 512), (16384, 512, 100), (7777, 3, 257),
+                                   (16385, 32, 100), (1000, 32, 513)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_update_one_workgroup_per_cluster(shape, xdtype):
+    """N <= 16384 and 64 < K <= 512: one workgroup per cluster lists its points and sums them (no sort); one
+    point more or one cluster more than that takes the sorted path."""
+    N, D, K = shape
+    if xdtype == "f32" and D > 256:
+        pytest.skip("fp32 supports D <= 256")
+    X = _x(N, D, xdtype, seed=N + 3 * D + K)
+    rng = np.random.default_rng(N + 2 * K)
+    w = rng.random(K) ** 4  # uneven cluster sizes, many clusters empty
+    a = rng.choice(K, size=N, p=w / w.sum())
+    a[a == K - 1] = 0  # the last cluster empty for sure
+    C_prev = torch.randn(K, D, generator=torch.Generator().manual_seed(K + D)).to(DEV)
+    _run(X, a, C_prev, f"one workgroup per cluster {shape} {xdtype}")
 
 
 @pytest.mark.parametrize("shape,xdtype", [((7001, 37, 300), "bf16"), ((5000, 3, 129), "f32"), ((9000, 100, 200), "f16"),
