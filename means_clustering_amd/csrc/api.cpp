@@ -191,7 +191,7 @@ static UpdateBufs carve_update(Carve& c, const SortGeom& g, int64_t D, km_dtype 
   const int64_t nsmall = kper <= kSmallMaxK ? B * small_chunks(g.N / B) * kper : 1;
   u.small_sum = c.take<float>((size_t)(nsmall > 0 ? nsmall : 1) * (size_t)reduce_dc((int)dt, D));
   u.small_cnt = c.take<int32_t>((size_t)(nsmall > 0 ? nsmall : 1));
-  const int64_t ntiles = (g.N + kSegTile - 1) / kSegTile;
+  const int64_t ntiles = reduce_carry_tiles((int)dt, D, g.N);  // (a streamed chunk may hold fewer points)
   u.carry_sum = c.take<float>((size_t)(ntiles > 0 ? ntiles : 1) * 2 * (size_t)reduce_dc((int)dt, D));
   u.carry_cnt = c.take<int32_t>((size_t)(ntiles > 0 ? ntiles : 1) * 2);
   const int64_t tpb = reduce_tpb((int)dt, D);

@@ -184,6 +184,12 @@ inline AssignGeom make_assign_geom(int64_t N, int64_t D, int64_t K, int dt, int6
 #ifndef KM_SEG_U
 #define KM_SEG_U 16       // most rows in flight per lane group in the segmented reduction
 #endif
+#ifndef KM_SEG_FINE_MAX_BYTES
+#define KM_SEG_FINE_MAX_BYTES (1LL << 27)  // short segment tiles while N rows of G 16-byte pieces fit in this
+#endif
+#ifndef KM_SEG_FINE_U
+#define KM_SEG_FINE_U 16  // rows in flight per lane with short segment tiles
+#endif
 constexpr int kRadixThreads = 256;
 constexpr int kRadixMaxItems = 32;           // consecutive keys per thread: 8, 16 or 32 (block positions fit in 16 bits)
 // Keys per thread for N keys: blocks of 2048..8192 keys, small enough that
@@ -191,6 +197,14 @@ constexpr int kRadixMaxItems = 32;           // consecutive keys per thread: 8, 
 inline int radix_items(int64_t N) { return N >= 1024 * 8192 ? 32 : (N >= 1024 * 4096 ? 16 : 8); }
 constexpr int kMaxDigitBits = 6;             // digits of at most 64 values per pass
 constexpr int kSegTile = KM_SEG_TILE;
+// Short segment tiles, for rows of G < 16 lanes (16 bytes each) when N rows
+// take at most KM_SEG_FINE_MAX_BYTES (about half the last-level cache):
+// 8 G positions (8 to kSegTile), so that the walk, bound by memory latency
+// there, spreads over many workgroups and each lane group reaches the end of
+// its tile in a few rounds of loads.  Otherwise, and for wider rows, tiles of
+// kSegTile positions (fewer carry pieces; measured on gfx950, short tiles
+// gain 1.1-10x below that size and lose up to 20% above it or at G = 16).
+constexpr int seg_tile_fine(int G) { return 8 * G < 8 ? 8 : (8 * G > kSegTile ? kSegTile : 8 * G); }
 constexpr uint32_t kInvalidFlag = 0x80000000u;  // marks a point whose cluster id was out of range
 
 struct SortGeom {
@@ -275,6 +289,8 @@ struct ReduceArgs {
 
 int64_t reduce_dc(int dt, int64_t D);   // padded row length of a carry piece
 int64_t reduce_tpb(int dt, int64_t D);  // tiles per segment-reduce workgroup
+int64_t reduce_tile(int dt, int64_t D, int64_t N);         // sorted positions per segment tile for N positions
+int64_t reduce_carry_tiles(int dt, int64_t D, int64_t N);  // most segment tiles of any N' <= N positions
 hipError_t launch_segment_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_fixup(const ReduceArgs& a, hipStream_t stream);
 // Small codebooks (K <= kSmallMaxK per problem, or small_owner_fits; mean mode): the update of B

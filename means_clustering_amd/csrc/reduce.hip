@@ -9,9 +9,10 @@
 // sorted order, so each worker reduces contiguous same-cluster segments on
 // chip and touches global memory only at segment boundaries.  Re-designed for
 // CDNA4 with no atomics at all:
-//   * the sorted order is cut into tiles of kSegTile positions; one "lane
-//     group" (G lanes, 16 bytes of a row each) walks a tile in order,
-//     gathering X[perm[i]] rows and accumulating in fp32 registers;
+//   * the sorted order is cut into tiles (kSegTile positions, fewer for a
+//     small N); one "lane group" (G lanes, 16 bytes of a row each) walks a
+//     tile in order, gathering X[perm[i]] rows and accumulating in fp32
+//     registers;
 //   * a segment that starts and ends inside the tile is finished right there
 //     (mean written, or added to the running totals when streaming);
 //   * a segment cut by a tile edge leaves a partial sum in one of the tile's
@@ -35,6 +36,23 @@ static int64_t reduce_lanes(int dt, int64_t D) {  // G: lanes holding one row (1
 }
 
 int64_t reduce_tpb(int dt, int64_t D) { return 256 / reduce_lanes(dt, D); }
+
+static bool seg_fine(int G, int64_t N) { return G < 16 && N * G * 16 <= (int64_t)KM_SEG_FINE_MAX_BYTES; }
+
+int64_t reduce_tile(int dt, int64_t D, int64_t N) {
+  const int G = (int)reduce_lanes(dt, D);
+  return seg_fine(G, N) ? seg_tile_fine(G) : kSegTile;
+}
+
+int64_t reduce_carry_tiles(int dt, int64_t D, int64_t N) {
+  const int G = (int)reduce_lanes(dt, D);
+  const int64_t fine = seg_tile_fine(G);
+  if (seg_fine(G, N)) return (N + fine - 1) / fine;
+  const int64_t coarse = (N + kSegTile - 1) / kSegTile;
+  const int64_t most_fine_n = G < 16 ? (int64_t)KM_SEG_FINE_MAX_BYTES / (16 * G) : 0;  // largest short-tile N
+  const int64_t most_fine = (most_fine_n + fine - 1) / fine;
+  return coarse > most_fine ? coarse : most_fine;
+}
 
 int64_t reduce_dc(int dt, int64_t D) {
   const int64_t epl = dt == DT_F32 ? 4 : 8;
@@ -60,6 +78,7 @@ struct SegParams {
   float* group_sum;   // [blocks][Dc]: a segment-reduce workgroup's slot-0 pieces, summed, when its positions hold one id
   int32_t* group_cnt;
   int tpb;            // tiles per segment-reduce workgroup
+  int tile;           // sorted positions per tile (reduce_tile)
   // mean mode, optional: FlashAssign's operand fragments of the new centroids
   // (cluster k is centroid k % kper of problem k / kper, whose fragments start
   // f_stride 16-byte slots further), written by the fix-up
@@ -124,7 +143,8 @@ __device__ __forceinline__ void flush_piece(const SegParams& P, int64_t tile, in
 }
 
 // VEC: X rows are whole, 16-byte aligned chunks (vector loads without a per-row fallback).
-template <int ES, int CPL, int G, bool VEC>
+// FINE: short tiles (seg_tile_fine) with more rows in flight, for small N.
+template <int ES, int CPL, int G, bool VEC, bool FINE>
 __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
   static_assert(CPL == 1, "a lane holds one 16-byte column chunk");
   constexpr int EPL = 16 / ES;
@@ -132,25 +152,30 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
   // to 16) are read in one round trip; the chunk's rows then go out U at a
   // time in a fully unrolled walk, so the next rows can be in flight while
   // the current ones are added.
-  constexpr int KPL = kSegTile / G < 16 ? kSegTile / G : 16;
+  constexpr int TILE = FINE ? seg_tile_fine(G) : kSegTile;
+  constexpr int KPL = TILE / G < 16 ? TILE / G : 16;
   constexpr int BATCH = G * KPL;
-  // rows in flight per lane group: half the lane group's width (measured on gfx950:
-  // more rows cost occupancy, c2 G=16 best at 8, c4 G=8 at 4), at least 2
-  constexpr int U = G / 2 < 2 ? 2 : (G / 2 > KM_SEG_U ? KM_SEG_U : G / 2);
-  static_assert(BATCH % U == 0 && kSegTile % BATCH == 0, "rows in flight divide the chunk");
+  // rows in flight per lane group: with kSegTile-long tiles, half the lane
+  // group's width, at least 2 (measured on gfx950: more rows cost occupancy
+  // at large N, c2 G=16 best at 8, c4 G=8 at 4); with short tiles (small N,
+  // occupancy to spare) up to KM_SEG_FINE_U, so a lane group needs few rounds
+  constexpr int UC = G / 2 < 2 ? 2 : (G / 2 > KM_SEG_U ? KM_SEG_U : G / 2);
+  constexpr int UF = KM_SEG_FINE_U < BATCH ? KM_SEG_FINE_U : BATCH;
+  constexpr int U = FINE ? UF : UC;
+  static_assert(U >= 1 && BATCH % U == 0 && TILE % BATCH == 0, "rows in flight divide the chunk");
   const int j = threadIdx.x % G;
   const int lgbase = (threadIdx.x & 63) & ~(G - 1);
   constexpr int T = 256 / G;  // tiles per workgroup
   const int64_t tile = (int64_t)blockIdx.x * T + threadIdx.x / G;
-  const int64_t ps = tile * kSegTile;
+  const int64_t ps = tile * TILE;
   // A workgroup whose positions all hold one id sums its tiles' pieces at the
   // end (one piece for the fix-up instead of T); it keeps every thread until then.
-  const int64_t bps = (int64_t)blockIdx.x * T * kSegTile;
-  const int64_t bpe = bps + (int64_t)T * kSegTile < P.N ? bps + (int64_t)T * kSegTile : P.N;
+  const int64_t bps = (int64_t)blockIdx.x * T * TILE;
+  const int64_t bpe = bps + (int64_t)T * TILE < P.N ? bps + (int64_t)T * TILE : P.N;
   const bool solid = P.keys[bps] == P.keys[bpe - 1];
   if (ps >= P.N && !solid) return;
   if (ps < P.N) {
-    const int64_t pe = ps + kSegTile < P.N ? ps + kSegTile : P.N;
+    const int64_t pe = ps + TILE < P.N ? ps + TILE : P.N;
     const int32_t first_key = P.keys[ps];
     const int32_t before_key = ps > 0 ? P.keys[ps - 1] : -1;   // id just before the tile
     const int32_t after_key = pe < P.N ? P.keys[pe] : -1;      // id just after the tile
@@ -246,7 +271,7 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
   // wavefront 0: rows of G lanes take the tiles r, r + R, ... in order, then a fixed tree
   constexpr int R = 64 / G;
   const int r = threadIdx.x / G;
-  const int64_t t_end = (bpe + kSegTile - 1) / kSegTile;
+  const int64_t t_end = (bpe + TILE - 1) / TILE;
   float sum[EPL];
 #pragma unroll
   for (int x = 0; x < EPL; ++x) sum[x] = 0.0f;
@@ -299,7 +324,7 @@ __global__ __launch_bounds__(256) void fixup_kernel(SegParams P) {
   const bool active = k < P.K;
   const int64_t s = active ? P.off[k] : 0, e = active ? P.off[k + 1] : 0;
   const bool valid = active && s >= 0 && e <= P.N && s <= e;  // offsets are monotone in [0, N]
-  const int64_t t0 = s / kSegTile, t1 = e > s ? (e - 1) / kSegTile : t0;
+  const int64_t t0 = s / P.tile, t1 = e > s ? (e - 1) / P.tile : t0;
   const bool cut = valid && s < e && t0 != t1;  // otherwise empty, or finished by segment_reduce_kernel
   if (valid && s == e && P.mode == MODE_MEAN) {  // empty: keeps its centroid
     if (lane == 0 && P.counts) P.counts[k] = 0;
@@ -334,7 +359,7 @@ __global__ __launch_bounds__(256) void fixup_kernel(SegParams P) {
           const float* piece;
           if (it < nh || it >= nh + ng) {
             const int64_t t = it < nh ? t0 + it : tb + (it - nh - ng);
-            const int slot = (t == t0 && s != t0 * kSegTile) ? 1 : 0;
+            const int slot = (t == t0 && s != t0 * P.tile) ? 1 : 0;
             piece = P.carry_sum + (t * 2 + slot) * (int64_t)P.Dc;
             cc[u] = P.carry_cnt[t * 2 + slot];
           } else {
@@ -421,6 +446,7 @@ static SegParams make_params(const ReduceArgs& a) {
   P.group_sum = a.group_sum;
   P.group_cnt = a.group_cnt;
   P.tpb = (int)reduce_tpb(a.dt, a.D);
+  P.tile = (int)reduce_tile(a.dt, a.D, a.N);
   P.frag = a.mode == MODE_MEAN ? (uint32_t*)a.frag : nullptr;
   P.f_stride = a.f_stride;
   P.kper = a.kper > 0 ? a.kper : a.K;
@@ -437,13 +463,18 @@ static SegParams make_params(const ReduceArgs& a) {
 
 template <int ES, int CPL, int G>
 static void launch_seg(const SegParams& P, hipStream_t s) {
-  const int64_t ntiles = (P.N + kSegTile - 1) / kSegTile;
+  const int64_t ntiles = (P.N + P.tile - 1) / P.tile;
   const int64_t per_block = 256 / G;
   const dim3 grid((unsigned)((ntiles + per_block - 1) / per_block));
-  if (P.vec_ok)
-    hipLaunchKernelGGL((segment_reduce_kernel<ES, CPL, G, true>), grid, dim3(256), 0, s, P);
+  const bool fine = seg_fine(G, P.N);  // (P.tile is reduce_tile of the same N)
+  if (P.vec_ok && fine)
+    hipLaunchKernelGGL((segment_reduce_kernel<ES, CPL, G, true, true>), grid, dim3(256), 0, s, P);
+  else if (P.vec_ok)
+    hipLaunchKernelGGL((segment_reduce_kernel<ES, CPL, G, true, false>), grid, dim3(256), 0, s, P);
+  else if (fine)
+    hipLaunchKernelGGL((segment_reduce_kernel<ES, CPL, G, false, true>), grid, dim3(256), 0, s, P);
   else
-    hipLaunchKernelGGL((segment_reduce_kernel<ES, CPL, G, false>), grid, dim3(256), 0, s, P);
+    hipLaunchKernelGGL((segment_reduce_kernel<ES, CPL, G, false, false>), grid, dim3(256), 0, s, P);
 }
 
 hipError_t launch_segment_reduce(const ReduceArgs& a, hipStream_t stream) {

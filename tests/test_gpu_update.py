@@ -76,24 +76,33 @@ def test_update_only_first_or_last_cluster(cluster):
     _run(X, np.full(5000, cluster), C_prev, f"only cluster {cluster}")
 
 
-def _positions_per_reduce_block(D, xdtype):
-    """Sorted positions one segmented-reduction workgroup covers: 256 / G tiles of 128,
-    G = lanes holding a row in 16-byte pieces (a power of two, at most 64)."""
+def _reduce_geometry(D, xdtype, fine):
+    """(sorted positions one segmented-reduction workgroup covers, positions per tile, largest N with short
+    tiles): 256 / G tiles of 128 positions, or, for G < 16 and N * G * 16 <= 2^27, of 8 G positions (8 to
+    128); G = lanes holding a row in 16-byte pieces (a power of two, at most 64)."""
     per = 4 if xdtype == "f32" else 8
     G = 1
     while G < -(-D // per) and G < 64:
         G *= 2
-    return (256 // G) * 128
+    tile = min(max(8 * G, 8), 128) if fine else 128
+    return (256 // G) * tile, tile, (2**27 // (16 * G) if G < 16 else 0)
 
 
-@pytest.mark.parametrize("D,xdtype", [(64, "bf16"), (512, "bf16"), (200, "f32"), (8, "bf16")])
-def test_update_segments_at_group_edges(D, xdtype):
+@pytest.mark.parametrize("D,xdtype,fine", [(64, "bf16", True), (512, "bf16", False), (200, "f32", False),
+                                           (128, "bf16", False), (8, "bf16", True), (16, "bf16", True),
+                                           (32, "bf16", True), (4, "f32", True), (12, "f32", True),
+                                           (64, "bf16", False), (32, "bf16", False), (12, "f32", False),
+                                           (8, "bf16", False)])
+def test_update_segments_at_group_edges(D, xdtype, fine):
     """Long segments that start or end on, or one position off, the edges of the
     segmented reduction's workgroups, so that whole workgroup sums, head tiles and
-    tail tiles are all added."""
-    G = _positions_per_reduce_block(D, xdtype)
-    sizes = [3 * G, 2 * G + 1, 2 * G - 2, 1, 5 * G + 128, 70 * G - 1, 127, G + 77]
-    # ids 0, 10, 20, ...: the clusters between stay empty, and K = 80 takes the sorted path
+    tail tiles are all added; with short tiles (small N) and long ones."""
+    B, tile, fine_max_n = _reduce_geometry(D, xdtype, fine)
+    sizes = [3 * B, 2 * B + 1, 2 * B - 2, 1, 5 * B + tile, 70 * B - 1, tile - 1, B + 77]
+    if not fine:  # a last long segment takes N up to the long-tile range
+        sizes.append(max(B, fine_max_n + 1 - sum(sizes)))
+    assert (sum(sizes) <= fine_max_n) == fine
+    # ids 0, 10, 20, ...: the clusters between stay empty, and K >= 80 takes the sorted path
     a = np.repeat(np.arange(len(sizes) * 10, step=10), sizes)
     np.random.default_rng(11).shuffle(a)
     X = _x(a.size, D, xdtype, seed=12 + D)
