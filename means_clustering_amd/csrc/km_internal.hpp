@@ -197,14 +197,15 @@ constexpr int kRadixMaxItems = 32;           // consecutive keys per thread: 8, 
 inline int radix_items(int64_t N) { return N >= 1024 * 8192 ? 32 : (N >= 1024 * 4096 ? 16 : 8); }
 constexpr int kMaxDigitBits = 6;             // digits of at most 64 values per pass
 constexpr int kSegTile = KM_SEG_TILE;
-// Short segment tiles, for rows of G < 16 lanes (16 bytes each) when N rows
-// take at most KM_SEG_FINE_MAX_BYTES (about half the last-level cache):
-// 8 G positions (8 to kSegTile), so that the walk, bound by memory latency
-// there, spreads over many workgroups and each lane group reaches the end of
-// its tile in a few rounds of loads.  Otherwise, and for wider rows, tiles of
-// kSegTile positions (fewer carry pieces; measured on gfx950, short tiles
-// gain 1.1-10x below that size and lose up to 20% above it or at G = 16).
-constexpr int seg_tile_fine(int G) { return 8 * G < 8 ? 8 : (8 * G > kSegTile ? kSegTile : 8 * G); }
+// Short segment tiles, used while N rows of G lanes (16 bytes each) take at
+// most KM_SEG_FINE_MAX_BYTES (about half the last-level cache), where the
+// walk is bound by memory latency: 16 positions (8 for rows of one lane, G
+// for rows of more than 16), so that the positions spread over many
+// workgroups and each lane group has its whole tile in flight at once.  A
+// larger N keeps kSegTile positions per tile, with fewer carry pieces for
+// the fix-up (measured on gfx950: short tiles gain 1.1-10x below that size
+// and lose up to 10% above it).
+constexpr int seg_tile_fine(int G) { return G == 1 ? 8 : (G > 16 ? G : 16); }
 constexpr uint32_t kInvalidFlag = 0x80000000u;  // marks a point whose cluster id was out of range
 
 struct SortGeom {

@@ -37,7 +37,7 @@ static int64_t reduce_lanes(int dt, int64_t D) {  // G: lanes holding one row (1
 
 int64_t reduce_tpb(int dt, int64_t D) { return 256 / reduce_lanes(dt, D); }
 
-static bool seg_fine(int G, int64_t N) { return G < 16 && N * G * 16 <= (int64_t)KM_SEG_FINE_MAX_BYTES; }
+static bool seg_fine(int G, int64_t N) { return N * G * 16 <= (int64_t)KM_SEG_FINE_MAX_BYTES; }
 
 int64_t reduce_tile(int dt, int64_t D, int64_t N) {
   const int G = (int)reduce_lanes(dt, D);
@@ -49,7 +49,7 @@ int64_t reduce_carry_tiles(int dt, int64_t D, int64_t N) {
   const int64_t fine = seg_tile_fine(G);
   if (seg_fine(G, N)) return (N + fine - 1) / fine;
   const int64_t coarse = (N + kSegTile - 1) / kSegTile;
-  const int64_t most_fine_n = G < 16 ? (int64_t)KM_SEG_FINE_MAX_BYTES / (16 * G) : 0;  // largest short-tile N
+  const int64_t most_fine_n = (int64_t)KM_SEG_FINE_MAX_BYTES / (16 * G);  // largest short-tile N
   const int64_t most_fine = (most_fine_n + fine - 1) / fine;
   return coarse > most_fine ? coarse : most_fine;
 }

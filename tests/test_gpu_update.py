@@ -78,19 +78,20 @@ def test_update_only_first_or_last_cluster(cluster):
 
 def _reduce_geometry(D, xdtype, fine):
     """(sorted positions one segmented-reduction workgroup covers, positions per tile, largest N with short
-    tiles): 256 / G tiles of 128 positions, or, for G < 16 and N * G * 16 <= 2^27, of 8 G positions (8 to
-    128); G = lanes holding a row in 16-byte pieces (a power of two, at most 64)."""
+    tiles): 256 / G tiles of 128 positions, or, for N * G * 16 <= 2^27, of 16 positions (8 for G = 1, G for
+    G > 16); G = lanes holding a row in 16-byte pieces (a power of two, at most 64)."""
     per = 4 if xdtype == "f32" else 8
     G = 1
     while G < -(-D // per) and G < 64:
         G *= 2
-    tile = min(max(8 * G, 8), 128) if fine else 128
-    return (256 // G) * tile, tile, (2**27 // (16 * G) if G < 16 else 0)
+    tile = (8 if G == 1 else max(G, 16)) if fine else 128
+    return (256 // G) * tile, tile, 2**27 // (16 * G)
 
 
-@pytest.mark.parametrize("D,xdtype,fine", [(64, "bf16", True), (512, "bf16", False), (200, "f32", False),
-                                           (128, "bf16", False), (8, "bf16", True), (16, "bf16", True),
+@pytest.mark.parametrize("D,xdtype,fine", [(64, "bf16", True), (512, "bf16", True), (200, "f32", True),
+                                           (128, "bf16", True), (8, "bf16", True), (16, "bf16", True),
                                            (32, "bf16", True), (4, "f32", True), (12, "f32", True),
+                                           (512, "bf16", False), (200, "f32", False), (128, "bf16", False),
                                            (64, "bf16", False), (32, "bf16", False), (12, "f32", False),
                                            (8, "bf16", False)])
 def test_update_segments_at_group_edges(D, xdtype, fine):
