@@ -95,6 +95,9 @@ size_t kmeans_workspace_bytes(km_op op, int64_t N, int64_t D, int64_t K, km_dtyp
  *   assign   device int32[N]: index of the nearest centroid (written)
  *   min_dist device fp32[N] or NULL: squared distance to that centroid,
  *            computed as ||x||^2 - 2 x.c + ||c||^2 in fp32, clamped at 0
+ * When N is small against the GPU and K is large, the centroid sweep is split
+ * over several workgroups and merged in index order (workspace: a score and an
+ * index per point and range); the result is bit for bit the unsplit one.
  */
 km_status kmeans_assign(const void* X, km_dtype dt, int64_t N, int64_t D, const float* C, int64_t K,
                         int32_t* assign, float* min_dist, void* ws, size_t ws_bytes, void* stream);

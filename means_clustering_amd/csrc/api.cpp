@@ -203,15 +203,21 @@ static UpdateBufs carve_update(Carve& c, const SortGeom& g, int64_t D, km_dtype 
 
 struct FitBufs {
   void* frag;
+  void* split;  // scratch of a split FlashAssign sweep (NULL: none)
   UpdateBufs u;
   int32_t* assign;
   float* min_dist;
   double* obj_part;
 };
 
-static FitBufs carve_fit(Carve& c, int64_t N, int64_t D, int64_t K, km_dtype dt) {
+// split: room for a split FlashAssign sweep (the streamed fit sizes its buffers for its largest chunk and
+// does not split)
+static FitBufs carve_fit(Carve& c, int64_t N, int64_t D, int64_t K, km_dtype dt, bool split = true) {
   FitBufs f;
-  f.frag = c.take<uint8_t>(assign_geom(N, D, K, dt).frag_bytes());
+  const AssignGeom g = assign_geom(N, D, K, dt);
+  f.frag = c.take<uint8_t>(g.frag_bytes());
+  const size_t sb = split ? assign_split_bytes(g, N, 1) : 0;
+  f.split = sb ? c.take<uint8_t>(sb) : nullptr;
   f.u = carve_update(c, sort_geom(N, K), D, dt);
   const size_t n = (size_t)(N > 0 ? N : 1);
   f.assign = c.take<int32_t>(n);
@@ -229,7 +235,7 @@ struct StreamBufs {
 
 static StreamBufs carve_streamed(Carve& c, int64_t rows, int64_t D, int64_t K, km_dtype dt) {
   StreamBufs s;
-  s.f = carve_fit(c, rows, D, K, dt);
+  s.f = carve_fit(c, rows, D, K, dt, /*split=*/false);
   const size_t xb = (size_t)rows * (size_t)D * (size_t)dtype_size((int)dt);
   s.xbuf[0] = c.take<uint8_t>(xb);
   s.xbuf[1] = c.take<uint8_t>(xb);
@@ -243,6 +249,7 @@ static StreamBufs carve_streamed(Carve& c, int64_t rows, int64_t D, int64_t K, k
 // and one segmented reduction serve every problem.
 struct BatchBufs {
   void* frag;  // B x frag_bytes
+  void* split;  // scratch of a split FlashAssign sweep (NULL: none)
   UpdateBufs u;
   int32_t* ids;  // B*N composite ids
   float* min_dist;
@@ -250,7 +257,10 @@ struct BatchBufs {
 
 static BatchBufs carve_batched(Carve& c, int64_t B, int64_t N, int64_t D, int64_t K, km_dtype dt) {
   BatchBufs b;
-  b.frag = c.take<uint8_t>((size_t)B * assign_geom(N, D, K, dt, B).frag_bytes());
+  const AssignGeom g = assign_geom(N, D, K, dt, B);
+  b.frag = c.take<uint8_t>((size_t)B * g.frag_bytes());
+  const size_t sb = assign_split_bytes(g, N, B);
+  b.split = sb ? c.take<uint8_t>(sb) : nullptr;
   b.u = carve_update(c, sort_geom(B * N, B * K), D, dt, B);
   const size_t n = (size_t)(B * N > 0 ? B * N : 1);
   b.ids = c.take<int32_t>(n);
@@ -277,7 +287,12 @@ static size_t workspace_bytes_batched_impl(int64_t B, int64_t N, int64_t D, int6
 static size_t workspace_bytes_impl(km_op op, int64_t N, int64_t D, int64_t K, km_dtype dt, int64_t chunk_rows) {
   Carve c(nullptr);
   switch (op) {
-    case KM_OP_ASSIGN: c.take<uint8_t>(assign_geom(N, D, K, dt).frag_bytes()); break;
+    case KM_OP_ASSIGN: {
+      const AssignGeom g = assign_geom(N, D, K, dt);
+      c.take<uint8_t>(g.frag_bytes());
+      c.take<uint8_t>(assign_split_bytes(g, N, 1));
+      break;
+    }
     case KM_OP_SORT: carve_sort(c, sort_geom(N, K)); break;
     case KM_OP_UPDATE: carve_update(c, sort_geom(N, K), D, dt); break;
     case KM_OP_FIT: carve_fit(c, N, D, K, dt); break;
@@ -396,12 +411,15 @@ constexpr int kStageSlots = 4;
 
 // perm/prev (optional): the previous iteration's sorted order and sorted keys (warm start).
 // prepped: the fragments of C are already in `frag` (written by the last update).
+// split: scratch for a split sweep (assign_split_bytes; NULL: never split).
 static km_status run_assign(const void* X, km_dtype dt, int64_t N, int64_t D, const float* C, int64_t K,
                             int32_t* assign, float* min_dist, void* frag, hipStream_t s,
-                            const int32_t* perm = nullptr, const int32_t* prev = nullptr, bool prepped = false) {
+                            const int32_t* perm = nullptr, const int32_t* prev = nullptr, bool prepped = false,
+                            void* split = nullptr) {
   const AssignGeom g = assign_geom(N, D, K, dt);
   if (!prepped) KM_TIMED("prep", s, return launch_prep(g, C, frag, s));
-  if (N > 0) KM_TIMED("assign", s, return launch_flash_assign(g, X, N, frag, assign, min_dist, s, perm, prev));
+  if (N > 0)
+    KM_TIMED("assign", s, return launch_flash_assign(g, X, N, frag, assign, min_dist, s, perm, prev, 1, 0, split));
   return KM_OK;
 }
 
@@ -520,8 +538,11 @@ km_status kmeans_assign(const void* X, km_dtype dt, int64_t N, int64_t D, const 
   st = check_ws(ws, ws_bytes, workspace_bytes_impl(KM_OP_ASSIGN, N, D, K, dt, 0));
   if (st != KM_OK) return st;
   Carve c(ws);
-  void* frag = c.take<uint8_t>(assign_geom(N, D, K, dt).frag_bytes());
-  return run_assign(X, dt, N, D, C, K, assign, min_dist, frag, (hipStream_t)stream);
+  const AssignGeom g = assign_geom(N, D, K, dt);
+  void* frag = c.take<uint8_t>(g.frag_bytes());
+  const size_t sb = assign_split_bytes(g, N, 1);
+  void* split = sb ? c.take<uint8_t>(sb) : nullptr;
+  return run_assign(X, dt, N, D, C, K, assign, min_dist, frag, (hipStream_t)stream, nullptr, nullptr, false, split);
 }
 
 km_status kmeans_sort_by_cluster(const int32_t* assign, int64_t N, int64_t K, int32_t* perm, int32_t* offsets,
@@ -592,7 +613,8 @@ km_status kmeans_fit(const void* X, km_dtype dt, int64_t N, int64_t D, int64_t K
   const AssignGeom geom = assign_geom(N, D, K, dt);
   bool prepped = false;  // the last update already wrote the centroid fragments
   for (int32_t t = 0; t < iters; ++t) {
-    st = run_assign(X, dt, N, D, C, K, a, objective ? f.min_dist : nullptr, f.frag, s, order, prev, prepped);
+    st = run_assign(X, dt, N, D, C, K, a, objective ? f.min_dist : nullptr, f.frag, s, order, prev, prepped,
+                    f.split);
     if (st != KM_OK) return st;
     if (objective) KM_TIMED("objective", s, return launch_objective(f.min_dist, N, f.obj_part, objective + t, 0, s));
     if (N == 0) {
@@ -634,7 +656,7 @@ km_status kmeans_fit_batched(const void* X, km_dtype dt, int64_t B, int64_t N, i
     if (N > 0)
       KM_TIMED("assign", s,
                return launch_flash_assign(g, X, N, b.frag, b.ids, objective ? b.min_dist : nullptr, s, nullptr,
-                                          nullptr, B, (int32_t)K));
+                                          nullptr, B, (int32_t)K, b.split));
     if (objective)
       KM_TIMED("objective", s, return launch_objective_batched(b.min_dist, B, N, objective + (int64_t)t * B, s));
     if (N == 0) {

@@ -390,7 +390,7 @@ __device__ __forceinline__ void drain_epilogue(const f32x16_t (&in)[NB], float (
 // WARM: points are visited in the order perm[0..N) and prev[i] is the
 // previous centroid of point perm[i] (both from the previous iteration's
 // argsort); the sweep starts from a bound taken from that centroid's group.
-template <int DT, int KB, bool LAZY, bool WARM>
+template <int DT, int KB, bool LAZY, bool WARM, bool SPLIT>
 __global__ __launch_bounds__(wide_cfg(KB).W * 64) __attribute__((amdgpu_waves_per_eu(wide_wpe(KB)))) void flash_assign_wide_kernel(
     const uint8_t* __restrict__ X, int64_t N, int D, bool vec_ok, const u32x4_t* __restrict__ frag, int ntiles,
     int32_t* __restrict__ assign, float* __restrict__ min_dist, const int32_t* __restrict__ perm,
@@ -416,6 +416,11 @@ __global__ __launch_bounds__(wide_cfg(KB).W * 64) __attribute__((amdgpu_waves_pe
   assign += (int64_t)bz * N;
   if (min_dist) min_dist += (int64_t)bz * N;
   const int32_t id_base = (int32_t)bz * bt.id_mul;
+  const int sp = SPLIT ? (int)blockIdx.y : 0;  // centroid range of a split sweep
+  if constexpr (SPLIT) {
+    frag += (int64_t)sp * bt.split_tiles * TS;
+    ntiles = ntiles - sp * bt.split_tiles < bt.split_tiles ? ntiles - sp * bt.split_tiles : bt.split_tiles;
+  }
 
   // the point each lane scores, per point group (its row of X, or N past the end)
   int64_t pt[NB];
@@ -525,8 +530,17 @@ __global__ __launch_bounds__(wide_cfg(KB).W * 64) __attribute__((amdgpu_waves_pe
       b = ob;
       k = ok;
     }
-    if (k == INT32_MAX) k = 0;  // no finite score (NaN input): index 0
     const int64_t p = pt[g];
+    if constexpr (SPLIT) {  // one range of a split sweep: its best, in problem indices
+      if (h == 0 && p < N) {
+        const int64_t o = (int64_t)bz * N + p;
+        bt.part_s[sp * bt.part_stride + o] = b;
+        bt.part_k[sp * bt.part_stride + o] = k == INT32_MAX ? INT32_MAX : k + sp * bt.split_tiles * CT * 32;
+        if (sp == 0 && bt.part_xn) bt.part_xn[o] = xn[g];
+      }
+      continue;
+    }
+    if (k == INT32_MAX) k = 0;  // no finite score (NaN input): index 0
     if (h == 0 && p < N) {
       assign[p] = k + id_base;
       if (min_dist) min_dist[p] = fmaxf(xn[g] - 2.0f * b, 0.0f);
@@ -539,7 +553,7 @@ __global__ __launch_bounds__(wide_cfg(KB).W * 64) __attribute__((amdgpu_waves_pe
 // its accumulators, runs the KB-step MFMA chain for all of its point groups,
 // then updates the running argmax from those accumulators while the other
 // wavefront on the SIMD keeps the matrix cores busy.
-template <int DT, int KB, bool LAZY, bool WARM>
+template <int DT, int KB, bool LAZY, bool WARM, bool SPLIT>
 __global__ __launch_bounds__(wide8_cfg(KB).W * 64) __attribute__((amdgpu_waves_per_eu(KM_W8_WPE))) void flash_assign_w8_kernel(
     const uint8_t* __restrict__ X, int64_t N, int D, bool vec_ok, const u32x4_t* __restrict__ frag, int ntiles,
     int32_t* __restrict__ assign, float* __restrict__ min_dist, const int32_t* __restrict__ perm,
@@ -564,6 +578,11 @@ __global__ __launch_bounds__(wide8_cfg(KB).W * 64) __attribute__((amdgpu_waves_p
   assign += (int64_t)bz * N;
   if (min_dist) min_dist += (int64_t)bz * N;
   const int32_t id_base = (int32_t)bz * bt.id_mul;
+  const int sp = SPLIT ? (int)blockIdx.y : 0;  // centroid range of a split sweep
+  if constexpr (SPLIT) {
+    frag += (int64_t)sp * bt.split_tiles * TS;
+    ntiles = ntiles - sp * bt.split_tiles < bt.split_tiles ? ntiles - sp * bt.split_tiles : bt.split_tiles;
+  }
 
   // the point each lane scores (its row of X, or N past the end); looked up
   // again at the end rather than kept live through the sweep
@@ -663,14 +682,23 @@ __global__ __launch_bounds__(wide8_cfg(KB).W * 64) __attribute__((amdgpu_waves_p
       b = ob;
       k = ok;
     }
-    if (k == INT32_MAX) k = 0;
     float xn = 0.0f;
-    if (min_dist) {
+    if (min_dist || (SPLIT && bt.part_xn)) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) xn += sumsq16<DT>(xb[g][kb]);
       xn += __shfl_xor(xn, 32);
     }
     const int64_t p = point_of(g);
+    if constexpr (SPLIT) {  // one range of a split sweep: its best, in problem indices
+      if (h == 0 && p < N) {
+        const int64_t o = (int64_t)bz * N + p;
+        bt.part_s[sp * bt.part_stride + o] = b;
+        bt.part_k[sp * bt.part_stride + o] = k == INT32_MAX ? INT32_MAX : k + sp * bt.split_tiles * CT * 32;
+        if (sp == 0 && bt.part_xn) bt.part_xn[o] = xn;
+      }
+      continue;
+    }
+    if (k == INT32_MAX) k = 0;
     if (h == 0 && p < N) {
       assign[p] = k + id_base;
       if (min_dist) min_dist[p] = fmaxf(xn - 2.0f * b, 0.0f);
@@ -693,7 +721,7 @@ __device__ __forceinline__ f32x4_t mma16_f32(u32x4_t a, u32x4_t b, f32x4_t c) {
   return c;
 }
 
-template <int KB, bool HALF, bool THIN>
+template <int KB, bool HALF, bool THIN, bool SPLIT>
 __global__ __launch_bounds__(narrow_cfg(KB, HALF, THIN).W * 64) void flash_assign_narrow_kernel(
     const uint8_t* __restrict__ X, int64_t N, int D, bool vec_ok, const u32x4_t* __restrict__ frag, int ntiles,
     int32_t* __restrict__ assign, float* __restrict__ min_dist, Batch bt) {
@@ -717,6 +745,11 @@ __global__ __launch_bounds__(narrow_cfg(KB, HALF, THIN).W * 64) void flash_assig
   assign += (int64_t)bz * N;
   if (min_dist) min_dist += (int64_t)bz * N;
   const int32_t id_base = (int32_t)bz * bt.id_mul;
+  const int sp = SPLIT ? (int)blockIdx.y : 0;  // centroid range of a split sweep
+  if constexpr (SPLIT) {
+    frag += (int64_t)sp * bt.split_tiles * TS;
+    ntiles = ntiles - sp * bt.split_tiles < bt.split_tiles ? ntiles - sp * bt.split_tiles : bt.split_tiles;
+  }
 
   u32x4_t xb[NB][KB];
   float xn[NB];
@@ -806,8 +839,17 @@ __global__ __launch_bounds__(narrow_cfg(KB, HALF, THIN).W * 64) void flash_assig
         k = ok;
       }
     }
-    if (k == INT32_MAX) k = 0;
     const int64_t p = wbase + g * 16 + col;
+    if constexpr (SPLIT) {  // one range of a split sweep: its best, in problem indices
+      if (quad == 0 && p < N) {
+        const int64_t o = (int64_t)bz * N + p;
+        bt.part_s[sp * bt.part_stride + o] = b;
+        bt.part_k[sp * bt.part_stride + o] = k == INT32_MAX ? INT32_MAX : k + sp * bt.split_tiles * CT * 16;
+        if (sp == 0 && bt.part_xn) bt.part_xn[o] = xn[g];
+      }
+      continue;
+    }
+    if (k == INT32_MAX) k = 0;
     if (quad == 0 && p < N) {
       assign[p] = k + id_base;
       if (min_dist) min_dist[p] = fmaxf(xn[g] - 2.0f * b, 0.0f);
@@ -821,39 +863,85 @@ static bool same_cfg(const AssignCfg& a, const AssignCfg& b) {
   return a.rows == b.rows && a.KB == b.KB && a.NB == b.NB && a.CT == b.CT && a.W == b.W;
 }
 
+// How a sweep is split over centroid ranges (S == 1: not split).
+struct SplitPlan {
+  int64_t S = 1;
+  int32_t tiles = 0;
+  float* s = nullptr;
+  int32_t* k = nullptr;
+  float* xn = nullptr;
+  int64_t stride = 0;
+};
+
 // Workgroups per problem times problems; the batch strides follow from the shape.
-static Batch make_batch(const AssignGeom& g, int64_t N, int64_t blocks, int32_t id_mul) {
+static Batch make_batch(const AssignGeom& g, int64_t N, int64_t blocks, int32_t id_mul, const SplitPlan& sp) {
   Batch b;
   b.bpp = (uint32_t)blocks;
   b.id_mul = id_mul;
   b.x_stride = N * g.D * (int64_t)dtype_size(g.dt);
   b.f_stride = (int64_t)(g.frag_bytes() / 16);
+  b.split_tiles = sp.S > 1 ? sp.tiles : 0;
+  b.part_s = sp.S > 1 ? sp.s : nullptr;
+  b.part_k = sp.k;
+  b.part_xn = sp.xn;
+  b.part_stride = sp.stride;
   return b;
+}
+
+// The best of a split sweep's ranges per point, taken in range order with
+// the kernels' own rule (a higher score wins; on equal scores the lower
+// index), so the result is the unsplit sweep's.
+__global__ __launch_bounds__(256) void assign_merge_kernel(const float* __restrict__ part_s,
+                                                           const int32_t* __restrict__ part_k,
+                                                           const float* __restrict__ part_xn, int64_t total, int64_t N,
+                                                           int S, int32_t id_mul, int32_t* __restrict__ assign,
+                                                           float* __restrict__ min_dist) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  float b = -INFINITY;
+  int32_t k = INT32_MAX;
+  for (int r = 0; r < S; ++r) {
+    const float v = part_s[r * total + i];
+    const int32_t kk = part_k[r * total + i];
+    if (v > b || (v == b && kk < k)) {
+      b = v;
+      k = kk;
+    }
+  }
+  if (k == INT32_MAX) k = 0;  // no finite score (NaN input): index 0
+  assign[i] = k + (int32_t)(i / N) * id_mul;
+  if (min_dist) min_dist[i] = fmaxf(part_xn[i] - 2.0f * b, 0.0f);
 }
 
 template <int DT, int KB>
 static hipError_t launch_wide8(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
                                float* min_dist, const int32_t* perm, const int32_t* prev, int64_t B, int32_t id_mul,
-                               hipStream_t s) {
+                               const SplitPlan& sp, hipStream_t s) {
   constexpr AssignCfg cfg = wide8_cfg(KB);
   if (!same_cfg(g.cfg, cfg)) return hipErrorInvalidValue;
   const int64_t pts = (int64_t)cfg.W * cfg.NB * 32;
   const int64_t blocks = (N + pts - 1) / pts;
   if (blocks * B >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const bool vec_ok = (((uintptr_t)X) % 16 == 0) && ((g.D * 2) % 16 == 0);
-  const dim3 grid((unsigned)(blocks * B)), block(cfg.W * 64);
-  const Batch bt = make_batch(g, N, blocks, id_mul);
+  const dim3 grid((unsigned)(blocks * B), (unsigned)sp.S), block(cfg.W * 64);
+  const Batch bt = make_batch(g, N, blocks, id_mul, sp);
   const uint8_t* x = (const uint8_t*)X;
   const u32x4_t* f = (const u32x4_t*)frag;
   const int nt = (int)g.ntiles();
-  if (perm)
-    hipLaunchKernelGGL((flash_assign_w8_kernel<DT, KB, true, true>), grid, block, 0, s, x, N, (int)g.D, vec_ok, f,
+  if (sp.S > 1 && g.lazy)  // (split sweeps are cold)
+    hipLaunchKernelGGL((flash_assign_w8_kernel<DT, KB, true, false, true>), grid, block, 0, s, x, N, (int)g.D, vec_ok, f,
+                       nt, assign, min_dist, nullptr, nullptr, g.K, bt);
+  else if (sp.S > 1)
+    hipLaunchKernelGGL((flash_assign_w8_kernel<DT, KB, false, false, true>), grid, block, 0, s, x, N, (int)g.D, vec_ok,
+                       f, nt, assign, min_dist, nullptr, nullptr, g.K, bt);
+  else if (perm)
+    hipLaunchKernelGGL((flash_assign_w8_kernel<DT, KB, true, true, false>), grid, block, 0, s, x, N, (int)g.D, vec_ok, f,
                        nt, assign, min_dist, perm, prev, g.K, bt);
   else if (g.lazy)
-    hipLaunchKernelGGL((flash_assign_w8_kernel<DT, KB, true, false>), grid, block, 0, s, x, N, (int)g.D, vec_ok, f,
+    hipLaunchKernelGGL((flash_assign_w8_kernel<DT, KB, true, false, false>), grid, block, 0, s, x, N, (int)g.D, vec_ok, f,
                        nt, assign, min_dist, perm, prev, g.K, bt);
   else
-    hipLaunchKernelGGL((flash_assign_w8_kernel<DT, KB, false, false>), grid, block, 0, s, x, N, (int)g.D, vec_ok,
+    hipLaunchKernelGGL((flash_assign_w8_kernel<DT, KB, false, false, false>), grid, block, 0, s, x, N, (int)g.D, vec_ok,
                        f, nt, assign, min_dist, perm, prev, g.K, bt);
   return hipGetLastError();
 }
@@ -861,10 +949,10 @@ static hipError_t launch_wide8(const AssignGeom& g, const void* X, int64_t N, co
 template <int DT, int KB>
 static hipError_t launch_wide(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
                               float* min_dist, const int32_t* perm, const int32_t* prev, int64_t B, int32_t id_mul,
-                              hipStream_t s) {
+                              const SplitPlan& sp, hipStream_t s) {
   if constexpr (KB <= kWide8MaxKB) {
     if (same_cfg(g.cfg, wide8_cfg(KB)))
-      return launch_wide8<DT, KB>(g, X, N, frag, assign, min_dist, perm, prev, B, id_mul, s);
+      return launch_wide8<DT, KB>(g, X, N, frag, assign, min_dist, perm, prev, B, id_mul, sp, s);
   }
   constexpr AssignCfg cfg = wide_cfg(KB);
   // The centroid fragments were laid out with the caller's geometry: it must be
@@ -874,26 +962,32 @@ static hipError_t launch_wide(const AssignGeom& g, const void* X, int64_t N, con
   const int64_t blocks = (N + pts - 1) / pts;
   if (blocks * B >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const bool vec_ok = (((uintptr_t)X) % 16 == 0) && ((g.D * 2) % 16 == 0);
-  const dim3 grid((unsigned)(blocks * B)), block(cfg.W * 64);
-  const Batch bt = make_batch(g, N, blocks, id_mul);
+  const dim3 grid((unsigned)(blocks * B), (unsigned)sp.S), block(cfg.W * 64);
+  const Batch bt = make_batch(g, N, blocks, id_mul, sp);
   const uint8_t* x = (const uint8_t*)X;
   const u32x4_t* f = (const u32x4_t*)frag;
   const int nt = (int)g.ntiles();
-  if (perm)
-    hipLaunchKernelGGL((flash_assign_wide_kernel<DT, KB, true, true>), grid, block, 0, s, x, N, (int)g.D, vec_ok, f,
+  if (sp.S > 1 && g.lazy)  // (split sweeps are cold)
+    hipLaunchKernelGGL((flash_assign_wide_kernel<DT, KB, true, false, true>), grid, block, 0, s, x, N, (int)g.D, vec_ok, f,
+                       nt, assign, min_dist, nullptr, nullptr, g.K, bt);
+  else if (sp.S > 1)
+    hipLaunchKernelGGL((flash_assign_wide_kernel<DT, KB, false, false, true>), grid, block, 0, s, x, N, (int)g.D, vec_ok,
+                       f, nt, assign, min_dist, nullptr, nullptr, g.K, bt);
+  else if (perm)
+    hipLaunchKernelGGL((flash_assign_wide_kernel<DT, KB, true, true, false>), grid, block, 0, s, x, N, (int)g.D, vec_ok, f,
                        nt, assign, min_dist, perm, prev, g.K, bt);
   else if (g.lazy)
-    hipLaunchKernelGGL((flash_assign_wide_kernel<DT, KB, true, false>), grid, block, 0, s, x, N, (int)g.D, vec_ok, f,
+    hipLaunchKernelGGL((flash_assign_wide_kernel<DT, KB, true, false, false>), grid, block, 0, s, x, N, (int)g.D, vec_ok, f,
                        nt, assign, min_dist, perm, prev, g.K, bt);
   else
-    hipLaunchKernelGGL((flash_assign_wide_kernel<DT, KB, false, false>), grid, block, 0, s, x, N, (int)g.D, vec_ok,
+    hipLaunchKernelGGL((flash_assign_wide_kernel<DT, KB, false, false, false>), grid, block, 0, s, x, N, (int)g.D, vec_ok,
                        f, nt, assign, min_dist, perm, prev, g.K, bt);
   return hipGetLastError();
 }
 
 template <int KB>
 static hipError_t launch_narrow(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
-                                float* min_dist, int64_t B, int32_t id_mul, hipStream_t s) {
+                                float* min_dist, int64_t B, int32_t id_mul, const SplitPlan& sp, hipStream_t s) {
   if constexpr (KB <= kNarrowHalfMaxKB) {
     const bool thin = same_cfg(g.cfg, narrow_cfg(KB, true, true));
     if (thin || same_cfg(g.cfg, narrow_cfg(KB, true))) {
@@ -902,14 +996,23 @@ static hipError_t launch_narrow(const AssignGeom& g, const void* X, int64_t N, c
       const int64_t blocks = (N + pts - 1) / pts;
       if (blocks * B >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
       const bool vec_ok = (((uintptr_t)X) % 16 == 0) && ((g.D * 4) % 16 == 0);
-      if (thin)
-        hipLaunchKernelGGL((flash_assign_narrow_kernel<KB, true, true>), dim3((unsigned)(blocks * B)),
-                           dim3(cfg.W * 64), 0, s, (const uint8_t*)X, N, (int)g.D, vec_ok, (const u32x4_t*)frag,
-                           (int)g.ntiles(), assign, min_dist, make_batch(g, N, blocks, id_mul));
+      const dim3 grid((unsigned)(blocks * B), (unsigned)sp.S), block(cfg.W * 64);
+      const Batch bt = make_batch(g, N, blocks, id_mul, sp);
+      const uint8_t* x = (const uint8_t*)X;
+      const u32x4_t* f = (const u32x4_t*)frag;
+      const int nt = (int)g.ntiles();
+      if (thin && sp.S > 1)
+        hipLaunchKernelGGL((flash_assign_narrow_kernel<KB, true, true, true>), grid, block, 0, s, x, N, (int)g.D,
+                           vec_ok, f, nt, assign, min_dist, bt);
+      else if (thin)
+        hipLaunchKernelGGL((flash_assign_narrow_kernel<KB, true, true, false>), grid, block, 0, s, x, N, (int)g.D,
+                           vec_ok, f, nt, assign, min_dist, bt);
+      else if (sp.S > 1)
+        hipLaunchKernelGGL((flash_assign_narrow_kernel<KB, true, false, true>), grid, block, 0, s, x, N, (int)g.D,
+                           vec_ok, f, nt, assign, min_dist, bt);
       else
-        hipLaunchKernelGGL((flash_assign_narrow_kernel<KB, true, false>), dim3((unsigned)(blocks * B)),
-                           dim3(cfg.W * 64), 0, s, (const uint8_t*)X, N, (int)g.D, vec_ok, (const u32x4_t*)frag,
-                           (int)g.ntiles(), assign, min_dist, make_batch(g, N, blocks, id_mul));
+        hipLaunchKernelGGL((flash_assign_narrow_kernel<KB, true, false, false>), grid, block, 0, s, x, N, (int)g.D,
+                           vec_ok, f, nt, assign, min_dist, bt);
       return hipGetLastError();
     }
   }
@@ -919,19 +1022,24 @@ static hipError_t launch_narrow(const AssignGeom& g, const void* X, int64_t N, c
   const int64_t blocks = (N + pts - 1) / pts;
   if (blocks * B >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const bool vec_ok = (((uintptr_t)X) % 16 == 0) && ((g.D * 4) % 16 == 0);
-  hipLaunchKernelGGL((flash_assign_narrow_kernel<KB, false, false>), dim3((unsigned)(blocks * B)), dim3(cfg.W * 64),
-                     0, s, (const uint8_t*)X, N, (int)g.D, vec_ok, (const u32x4_t*)frag, (int)g.ntiles(), assign,
-                     min_dist, make_batch(g, N, blocks, id_mul));
+  const dim3 grid((unsigned)(blocks * B), (unsigned)sp.S), block(cfg.W * 64);
+  const Batch bt = make_batch(g, N, blocks, id_mul, sp);
+  if (sp.S > 1)
+    hipLaunchKernelGGL((flash_assign_narrow_kernel<KB, false, false, true>), grid, block, 0, s, (const uint8_t*)X, N,
+                       (int)g.D, vec_ok, (const u32x4_t*)frag, (int)g.ntiles(), assign, min_dist, bt);
+  else
+    hipLaunchKernelGGL((flash_assign_narrow_kernel<KB, false, false, false>), grid, block, 0, s, (const uint8_t*)X, N,
+                       (int)g.D, vec_ok, (const u32x4_t*)frag, (int)g.ntiles(), assign, min_dist, bt);
   return hipGetLastError();
 }
 
 template <int DT>
 static hipError_t dispatch_wide(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
                                 float* min_dist, const int32_t* perm, const int32_t* prev, int64_t B, int32_t id_mul,
-                                hipStream_t s) {
+                                const SplitPlan& sp, hipStream_t s) {
   switch (g.cfg.KB) {
 #define KM_CASE(n) \
-  case n: return launch_wide<DT, n>(g, X, N, frag, assign, min_dist, perm, prev, B, id_mul, s);
+  case n: return launch_wide<DT, n>(g, X, N, frag, assign, min_dist, perm, prev, B, id_mul, sp, s);
     KM_CASE(1) KM_CASE(2) KM_CASE(3) KM_CASE(4) KM_CASE(5) KM_CASE(6) KM_CASE(7) KM_CASE(8)
     KM_CASE(10) KM_CASE(12) KM_CASE(14) KM_CASE(16) KM_CASE(20) KM_CASE(24) KM_CASE(28) KM_CASE(32)
 #undef KM_CASE
@@ -939,19 +1047,16 @@ static hipError_t dispatch_wide(const AssignGeom& g, const void* X, int64_t N, c
   }
 }
 
-hipError_t launch_flash_assign(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
+static hipError_t launch_sweep(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
                                float* min_dist, hipStream_t stream, const int32_t* perm, const int32_t* prev,
-                               int64_t B, int32_t id_mul) {
-  if (N == 0) return hipSuccess;
-  if ((perm == nullptr) != (prev == nullptr)) return hipErrorInvalidValue;
-  if (B < 1 || (perm && B != 1)) return hipErrorInvalidValue;  // the warm order is per problem
+                               int64_t B, int32_t id_mul, const SplitPlan& sp) {
   switch (g.dt) {
-    case DT_BF16: return dispatch_wide<DT_BF16>(g, X, N, frag, assign, min_dist, perm, prev, B, id_mul, stream);
-    case DT_F16: return dispatch_wide<DT_F16>(g, X, N, frag, assign, min_dist, perm, prev, B, id_mul, stream);
+    case DT_BF16: return dispatch_wide<DT_BF16>(g, X, N, frag, assign, min_dist, perm, prev, B, id_mul, sp, stream);
+    case DT_F16: return dispatch_wide<DT_F16>(g, X, N, frag, assign, min_dist, perm, prev, B, id_mul, sp, stream);
     case DT_F32:
       switch (g.cfg.KB) {
 #define KM_CASE(n) \
-  case n: return launch_narrow<n>(g, X, N, frag, assign, min_dist, B, id_mul, stream);
+  case n: return launch_narrow<n>(g, X, N, frag, assign, min_dist, B, id_mul, sp, stream);
         KM_CASE(1) KM_CASE(2) KM_CASE(3) KM_CASE(4) KM_CASE(5) KM_CASE(6) KM_CASE(7) KM_CASE(8)
         KM_CASE(9) KM_CASE(10) KM_CASE(11) KM_CASE(12) KM_CASE(13) KM_CASE(14) KM_CASE(15) KM_CASE(16)
 #undef KM_CASE
@@ -959,6 +1064,33 @@ hipError_t launch_flash_assign(const AssignGeom& g, const void* X, int64_t N, co
       }
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_flash_assign(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
+                               float* min_dist, hipStream_t stream, const int32_t* perm, const int32_t* prev,
+                               int64_t B, int32_t id_mul, void* split_ws) {
+  if (N == 0) return hipSuccess;
+  if ((perm == nullptr) != (prev == nullptr)) return hipErrorInvalidValue;
+  if (B < 1 || (perm && B != 1)) return hipErrorInvalidValue;  // the warm order is per problem
+  SplitPlan sp;
+  const int64_t st = split_ws ? assign_split_tiles(g, N, B) : 0;
+  if (st == 0) return launch_sweep(g, X, N, frag, assign, min_dist, stream, perm, prev, B, id_mul, sp);
+  // Split sweep: every range of every row block writes its best to the
+  // scratch, then one pass merges the ranges.  (The warm start only reorders
+  // the work; it is not used here.)
+  if ((uintptr_t)split_ws % 16 != 0) return hipErrorInvalidValue;
+  const int64_t total = B * N;
+  sp.S = (g.ntiles() + st - 1) / st;
+  sp.tiles = (int32_t)st;
+  sp.stride = total;
+  sp.s = (float*)split_ws;
+  sp.k = (int32_t*)(sp.s + sp.S * total);
+  sp.xn = min_dist ? (float*)(sp.k + sp.S * total) : nullptr;
+  hipError_t e = launch_sweep(g, X, N, frag, assign, nullptr, stream, nullptr, nullptr, B, id_mul, sp);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(assign_merge_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, sp.s, sp.k,
+                     sp.xn, total, N, (int)sp.S, id_mul, assign, min_dist);
+  return hipGetLastError();
 }
 
 }  // namespace km

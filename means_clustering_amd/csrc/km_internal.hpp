@@ -228,7 +228,55 @@ struct Batch {
   int32_t id_mul;
   int64_t x_stride;
   int64_t f_stride;
+  // Centroid-range split (split_tiles == 0: none).  Workgroup row y =
+  // blockIdx.y sweeps tiles [y * split_tiles, (y + 1) * split_tiles) and
+  // writes, per point o = b * N + p, its best score to part_s[y * part_stride
+  // + o] and that centroid's index in the problem to part_k[...] (INT32_MAX:
+  // none); row 0 also writes ||x||^2 to part_xn[o] when part_xn is set.
+  int32_t split_tiles;
+  float* part_s;
+  int32_t* part_k;
+  float* part_xn;
+  int64_t part_stride;
 };
+
+// FlashAssign splits the centroid sweep over several workgroups per row block
+// when the row blocks alone (B problems of N points, fewer than
+// KM_SPLIT_MAX_BLOCKS workgroups) would leave most of the GPU idle: up to
+// KM_SPLIT_TARGET_BLOCKS workgroups in all, each sweeping at least
+// KM_SPLIT_MIN_TILES tiles, at most 64 ranges; a merge pass then takes the best
+// of the ranges in index order (the result is unchanged).  Measured on gfx950:
+// 2-19x faster sweeps for N up to 65,536 with 4,096 to 65,536 centroids; 4,096
+// workgroups and 4 tiles beat 1,024 / 2,048 workgroups and 8 tiles in most shapes.
+#ifndef KM_SPLIT_MAX_BLOCKS
+#define KM_SPLIT_MAX_BLOCKS 512
+#endif
+#ifndef KM_SPLIT_TARGET_BLOCKS
+#define KM_SPLIT_TARGET_BLOCKS 4096
+#endif
+#ifndef KM_SPLIT_MIN_TILES
+#define KM_SPLIT_MIN_TILES 4
+#endif
+// tiles per range, 0 when the sweep is not split
+inline int64_t assign_split_tiles(const AssignGeom& g, int64_t N, int64_t B) {
+  const int64_t pts = (int64_t)g.cfg.W * g.cfg.NB * g.cfg.rows;
+  const int64_t blocks = B * ((N + pts - 1) / pts);
+  if (N <= 0 || blocks >= KM_SPLIT_MAX_BLOCKS) return 0;
+  const int64_t nt = g.ntiles();
+  int64_t S = (KM_SPLIT_TARGET_BLOCKS + blocks - 1) / blocks;
+  if (S > nt / KM_SPLIT_MIN_TILES) S = nt / KM_SPLIT_MIN_TILES;
+  if (S > 64) S = 64;
+  return S < 2 ? 0 : (nt + S - 1) / S;
+}
+inline int64_t assign_splits(const AssignGeom& g, int64_t N, int64_t B) {
+  const int64_t st = assign_split_tiles(g, N, B);
+  return st ? (g.ntiles() + st - 1) / st : 1;
+}
+// scratch of a split sweep: scores and indices per range and point, ||x||^2 per point
+inline size_t assign_split_bytes(const AssignGeom& g, int64_t N, int64_t B) {
+  const int64_t S = assign_splits(g, N, B);
+  return S > 1 ? (size_t)(B * N) * (size_t)(8 * S + 4) + 256 : 0;
+}
 
 // ---------------------------------------------------------------------------
 // Launchers (all asynchronous on `stream`; they return the launch status).
@@ -241,9 +289,13 @@ hipError_t launch_prep(const AssignGeom& g, const float* C, void* frag, hipStrea
 // only faster when the assignment changes little (16-bit X only; ignored for
 // fp32 X).  B > 1 (no perm/prev): B problems of N points each, X holding
 // B x N rows and assign/min_dist B x N entries; ids are written as b*id_mul + k.
+// split_ws (optional, assign_split_bytes(g, N, B) bytes, 16-byte aligned):
+// scratch that lets a short sweep over many centroids split its centroid range
+// (then perm/prev are not used).
 hipError_t launch_flash_assign(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
                                float* min_dist, hipStream_t stream, const int32_t* perm = nullptr,
-                               const int32_t* prev = nullptr, int64_t B = 1, int32_t id_mul = 0);
+                               const int32_t* prev = nullptr, int64_t B = 1, int32_t id_mul = 0,
+                               void* split_ws = nullptr);
 
 // Radix argsort of cluster ids.  keys_in: the assignment vector.  The passes
 // ping-pong through (key_a, val_a) and (key_b, val_b); the last pass writes

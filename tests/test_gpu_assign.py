@@ -112,3 +112,29 @@ def test_assign_deterministic():
     a2, d2 = km.assign(X, C, min_dist=True)
     torch.cuda.synchronize()
     assert torch.equal(a1, a2) and torch.equal(d1, d2)
+
+
+@pytest.mark.parametrize("xdtype,D,K", [("bf16", 64, 4000), ("bf16", 32, 9000), ("f16", 300, 2000), ("f32", 32, 3000),
+                                        ("f32", 5, 20000), ("bf16", 128, 70000), ("bf16", 512, 3000)],
+                         ids=lambda v: str(v))
+def test_assign_split_sweep_equals_unsplit(xdtype, D, K):
+    """A small N with a long centroid sweep splits the sweep over several workgroups per row block and merges
+    the ranges' best scores in index order.  The same rows inside a large N (one workgroup per row block sweeps
+    every centroid) must get the same centroid and distance bit for bit, a row of NaN index 0, and the small
+    call must match the oracle."""
+    n = 3001
+    # the small call takes the split sweep's scratch, the large one none
+    assert km.workspace_bytes(km.KM_OP_ASSIGN, n, D, K, TORCH_DT[xdtype]) > \
+        km.workspace_bytes(km.KM_OP_ASSIGN, 600_000, D, K, TORCH_DT[xdtype])
+    X, C = _data(600_000, D, K, xdtype, seed=K + D)
+    X[7] = float("nan")
+    print(f"[assign split] {xdtype} D={D} K={K}", flush=True)
+    a_big, d_big = km.assign(X, C, min_dist=True)
+    a_s, d_s = km.assign(X[:n].contiguous(), C, min_dist=True)
+    torch.cuda.synchronize()
+    assert int(a_s[7]) == 0
+    assert torch.equal(a_s, a_big[:n])
+    assert torch.equal(d_s.view(torch.int32), d_big[:n].view(torch.int32))
+    keep = np.arange(n) != 7
+    Xn, xdt = parity.x_to_numpy(X[:n])
+    parity.check_assign(Xn[keep], xdt, C.cpu().numpy(), a_s.cpu().numpy()[keep], label="split sweep")

@@ -57,8 +57,10 @@ def test_batched_bf16_ragged():
     _teacher_forced(Xn, "bf16", C0, 3, "bf16 ragged x5")
 
 
-def test_batched_assignment_is_the_single_problem_assignment():
-    w, Xn, C0 = _batch("c4", 4, 300, N=5000, K=300)
+@pytest.mark.parametrize("K", [300, 5000])
+def test_batched_assignment_is_the_single_problem_assignment(K):
+    """K = 5000: both calls split the centroid sweep, into different numbers of ranges."""
+    w, Xn, C0 = _batch("c4", 4, 300, N=5000, K=K)
     X = _to_dev(Xn, "bf16")
     C0t = torch.from_numpy(C0).to(DEV)
     _, a, _, _ = km.fit_batched(X, C0t, 1)
