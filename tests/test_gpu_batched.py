@@ -57,6 +57,24 @@ def test_batched_bf16_ragged():
     _teacher_forced(Xn, "bf16", C0, 3, "bf16 ragged x5")
 
 
+@pytest.mark.parametrize("xdtype,D", [("bf16", 64), ("f32", 24)])
+def test_batched_split_sweep(xdtype, D):
+    """Three problems of 3,000 points and 2,000 centroids: the centroid sweep is split over several workgroups
+    per row block and merged; assignments, updates and the objective (from the merged distances) of every
+    problem and iteration against the oracle, and T iterations in one call against T calls."""
+    w, Xn, C0 = _batch("c2", 3, 500, N=3000, K=2000, D=D, dtype=xdtype)
+    # one such problem splits its sweep (its assignment takes the split scratch); three have 3x the row
+    # blocks, still far below the 512 where the split stops
+    tdt = torch.bfloat16 if xdtype == "bf16" else torch.float32
+    assert km.workspace_bytes(km.KM_OP_ASSIGN, 3 * 3000, D, 2000, tdt) > \
+        km.workspace_bytes(km.KM_OP_ASSIGN, 600_000, D, 2000, tdt)
+    C = _teacher_forced(Xn, xdtype, C0, 2, f"split sweep {xdtype} x3")
+    X = _to_dev(Xn, xdtype)
+    C2, a2, n2, _ = km.fit_batched(X, torch.from_numpy(C0).to(DEV), 2)
+    torch.cuda.synchronize()
+    assert torch.equal(C2, C)
+
+
 @pytest.mark.parametrize("K", [300, 5000])
 def test_batched_assignment_is_the_single_problem_assignment(K):
     """K = 5000: both calls split the centroid sweep, into different numbers of ranges."""
