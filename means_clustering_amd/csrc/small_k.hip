@@ -1,20 +1,21 @@
-// Sort-Inverse Update for small codebooks (at most 64 clusters per problem),
-// the shape of many small K-Means problems called back to back or batched.
+// Sort-Inverse Update for small problems: codebooks of at most 64 clusters
+// per problem, and a few problems of at most 16384 points with at most 512
+// clusters in all -- the shape of many small K-Means problems called back to
+// back or batched.
 //
 // Citations name the page "Flash-KMeans: Fast and Memory-Efficient Exact
 // K-Means" (gist.science summary of paper 2603.09229); "tech §n" is a section
 // of its technical summary.
 //
 // Same idea as tech §2.2 (make each cluster's points contiguous, then reduce
-// contiguous runs with no atomics), with the sort kept on chip: with K <= 64
-// the whole cluster id is one 6-bit radix digit.  A few problems of at most
-// 16384 points take one workgroup per cluster (small_owner_kernel, below).
-// Otherwise one workgroup ranks the
-// ids of a chunk (2048 points, 512 for small calls) stably (512: wavefront
-// ballots and LDS histograms; 2048: the radix sort's block rank), lays
-// the chunk's point indices out in cluster order in LDS, and then lets each
-// lane group walk whole clusters of the chunk in that order, 16 rows in
-// flight.  No global sort, no carries: a cluster's chunk sum is complete in
+// contiguous runs with no atomics), kept on chip.  A few problems of at most
+// 16384 points take one workgroup per cluster, which lists its own points in
+// index order (small_owner_kernel, below; any K up to 512).  Otherwise, with
+// K <= 64 the whole cluster id is one 6-bit radix digit: one workgroup ranks
+// the ids of a chunk (2048 points, 512 for small calls) stably (512: wavefront
+// ballots and LDS histograms; 2048: the radix sort's block rank), lays the
+// chunk's point indices out in cluster order in LDS, and then lets each lane
+// group walk whole clusters of the chunk in that order, 16 rows in flight.  No global sort, no carries: a cluster's chunk sum is complete in
 // one lane group.  When a problem has one chunk the means are written right
 // away (one launch for the whole update); otherwise the chunk sums are added
 // chunk by chunk in a second launch.  The order of every addition is fixed
