@@ -310,6 +310,7 @@ __global__ __launch_bounds__(kRadixThreads) void small_owner_kernel(SmallParams 
   __shared__ int32_t list[kOwnerMaxN];
   __shared__ uint32_t wsum[kRadixThreads / 64];
   __shared__ float part[NG * GE];
+  __shared__ float part2[kRadixThreads];  // stage-one sums, TPC x GE (below)
   __shared__ float row[kMaxD16];
   const int64_t q = blockIdx.x, b = q / S.K, k = q - b * S.K;
   const int32_t want = (int32_t)(b * S.id_mul + k);
@@ -355,10 +356,29 @@ __global__ __launch_bounds__(kRadixThreads) void small_owner_kernel(SmallParams 
 #pragma unroll
   for (int x = 0; x < EPL; ++x) part[g * GE + j * EPL + x] = acc[x];
   __syncthreads();
+  // The lane groups' sums of a column, in two fixed stages when the workgroup
+  // has threads to spare: TPC threads per column each add every TPC-th lane
+  // group, then one thread adds those TPC partial sums in order.
+  constexpr int TPC0 = kRadixThreads / GE;
+  constexpr int TPC = TPC0 < 2 ? 1 : (TPC0 > NG ? NG : TPC0);
+  if constexpr (TPC > 1) {
+    const int c = threadIdx.x % GE, r = threadIdx.x / GE;
+    if (r < TPC) {
+      float v = 0.0f;
+      for (int gg = r; gg < NG; gg += TPC) v += part[gg * GE + c];
+      part2[r * GE + c] = v;
+    }
+    __syncthreads();
+  }
   const int64_t base = q * S.D;
   for (int c = threadIdx.x; c < S.D; c += kRadixThreads) {
     float sum = 0.0f;
-    for (int gg = 0; gg < NG; ++gg) sum += part[gg * GE + c];
+    if constexpr (TPC > 1) {
+#pragma unroll
+      for (int r = 0; r < TPC; ++r) sum += part2[r * GE + c];
+    } else {
+      for (int gg = 0; gg < NG; ++gg) sum += part[gg * GE + c];
+    }
     const float mean = total > 0 ? sum / (float)total : S.C_prev[base + c];
     S.C_new[base + c] = mean;
     if (c < kMaxD16) row[c] = mean;
