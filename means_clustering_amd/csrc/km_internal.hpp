@@ -371,7 +371,8 @@ struct SmallArgs {
 };
 int64_t small_chunks(int64_t N);  // chunks per problem, at most
 // Whether B problems of N points and K clusters each take the one-launch
-// layout of one workgroup per cluster (then also for K above kSmallMaxK).
+// layout of one workgroup per 1, 2 or 4 clusters (then also for K above
+// kSmallMaxK): N <= 16384 and at most 512 such workgroups.
 bool small_owner_fits(int64_t B, int64_t N, int64_t K);
 hipError_t launch_small_update(const SmallArgs& a, hipStream_t stream);
 hipError_t launch_finalize_accum(const float* acc_sum, const int64_t* acc_cnt, int64_t K, int64_t D,

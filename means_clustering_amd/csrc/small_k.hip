@@ -1,5 +1,5 @@
 // Sort-Inverse Update for small problems: codebooks of at most 64 clusters
-// per problem, and a few problems of at most 16384 points with at most 512
+// per problem, and a few problems of at most 16384 points with at most 2048
 // clusters in all -- the shape of many small K-Means problems called back to
 // back or batched.
 //
@@ -9,16 +9,18 @@
 //
 // Same idea as tech §2.2 (make each cluster's points contiguous, then reduce
 // contiguous runs with no atomics), kept on chip.  A few problems of at most
-// 16384 points take one workgroup per cluster, which lists its own points in
-// index order (small_owner_kernel, below; any K up to 512).  Otherwise, with
-// K <= 64 the whole cluster id is one 6-bit radix digit: one workgroup ranks
+// 16384 points take one workgroup per cluster (or per 2 or 4 clusters),
+// which lists its own points in index order (small_owner_kernel, below).
+// Otherwise, with K <= 64 the whole cluster id is one 6-bit radix digit: one
+// workgroup ranks
 // the ids of a chunk (2048 points, 512 for small calls) stably (512: wavefront
 // ballots and LDS histograms; 2048: the radix sort's block rank), lays the
 // chunk's point indices out in cluster order in LDS, and then lets each lane
-// group walk whole clusters of the chunk in that order, 16 rows in flight.  No global sort, no carries: a cluster's chunk sum is complete in
-// one lane group.  When a problem has one chunk the means are written right
-// away (one launch for the whole update); otherwise the chunk sums are added
-// chunk by chunk in a second launch.  The order of every addition is fixed
+// group walk whole clusters of the chunk in that order, 16 rows in flight.
+// No global sort, no carries: a cluster's chunk sum is complete in one lane
+// group.  When a problem has one chunk the means are written right away (one
+// launch for the whole update); otherwise the chunk sums are added chunk by
+// chunk in a second launch.  The order of every addition is fixed
 // (chunk, then point index), so results are deterministic.
 #include "block_rank.hpp"
 #include "frag_emit.hpp"
@@ -286,14 +288,16 @@ __global__ __launch_bounds__(256) void small_combine_kernel(SmallParams S, int64
   if (active) emit_fragment_row(rows[wv], S.D, S.dt, S.cfg, S.frag + 4 * b * S.f_stride, k);
 }
 
-// A few small problems (at most kOwnerMaxGroups clusters in all, N <= 16384,
-// any K up to that): one workgroup per (problem, cluster).  It reads all of the problem's ids at
-// once, lists its cluster's points in ascending index order in LDS (per-thread
-// match counts, one block scan), lets each lane group sum one contiguous block
-// of that list, adds the lane groups' sums in order and writes the mean (an
-// empty cluster keeps its centroid), the count and, when asked, the centroid's
-// operand fragment for the next assignment.  One launch and no
-// chunk sums; every addition in a fixed order.
+// A few small problems (N <= 16384, at most kOwnerMaxGroups workgroups of R
+// consecutive clusters, R = 1, 2 or 4): one workgroup per (problem, R
+// clusters).  It reads all of the problem's ids at once, lists each of its
+// clusters' points in ascending index order in LDS (per-thread match counts,
+// one block scan per cluster), and then, cluster after cluster, lets each lane
+// group sum one contiguous block of that cluster's list, adds the lane
+// groups' sums in order and writes the mean (an empty cluster keeps its
+// centroid), the count and, when asked, the centroid's operand fragment for
+// the next assignment.  One launch and no chunk sums; every addition in a
+// fixed order, the same for every R.
 constexpr int kOwnerMaxN = 16384;
 constexpr int kOwnerIPT = kOwnerMaxN / kRadixThreads;  // ids per thread
 #ifndef KM_OWNER_MAX_GROUPS
@@ -301,8 +305,20 @@ constexpr int kOwnerIPT = kOwnerMaxN / kRadixThreads;  // ids per thread
                                  //  for 1 to 4 problems, 1.25x for 8; 0.93x for 16, 0.72x for 256)
 #endif
 constexpr int64_t kOwnerMaxGroups = KM_OWNER_MAX_GROUPS;
+#ifndef KM_OWNER_MAX_R
+#define KM_OWNER_MAX_R 4  // (measured on gfx950, single problems of 600 to 2,048 clusters: 1.1-2.2x faster than
+                          //  the sorted path with 2 or 4 clusters a workgroup, 0.87-1.0x with 8)
+#endif
+constexpr int kOwnerMaxR = KM_OWNER_MAX_R;  // clusters per workgroup, at most (1, 2, 4 or 8)
 
-template <int ES, int G>
+// clusters per workgroup for B problems of K clusters (0: the layout does not apply)
+static int owner_r(int64_t B, int64_t K) {
+  for (int r = 1; r <= kOwnerMaxR; r *= 2)
+    if (B * ((K + r - 1) / r) <= kOwnerMaxGroups) return r;
+  return 0;
+}
+
+template <int ES, int G, int R>
 __global__ __launch_bounds__(kRadixThreads) void small_owner_kernel(SmallParams S) {
   constexpr int EPL = 16 / ES;
   constexpr int NG = kRadixThreads / G;  // lane groups
@@ -312,8 +328,9 @@ __global__ __launch_bounds__(kRadixThreads) void small_owner_kernel(SmallParams 
   __shared__ float part[NG * GE];
   __shared__ float part2[kRadixThreads];  // stage-one sums, TPC x GE (below)
   __shared__ float row[kMaxD16];
-  const int64_t q = blockIdx.x, b = q / S.K, k = q - b * S.K;
-  const int32_t want = (int32_t)(b * S.id_mul + k);
+  const int64_t nq = (S.K + R - 1) / R;  // workgroups per problem
+  const int64_t b = blockIdx.x / nq, k0 = (blockIdx.x - b * nq) * R;
+  const int32_t want0 = (int32_t)(b * S.id_mul + k0);  // id of cluster k0 + r: want0 + r
   const int32_t* ids = S.ids + b * S.N;
   const int64_t p0 = (int64_t)threadIdx.x * kOwnerIPT;
   int32_t v[kOwnerIPT];
@@ -329,70 +346,98 @@ __global__ __launch_bounds__(kRadixThreads) void small_owner_kernel(SmallParams 
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < kOwnerIPT; ++i) v[i] = p0 + i < S.N ? ids[p0 + i] : want + 1;  // want + 1: no match
+    for (int i = 0; i < kOwnerIPT; ++i) v[i] = p0 + i < S.N ? ids[p0 + i] : want0 + R;  // want0 + R: no match
   }
-  uint32_t m = 0;
+  uint32_t m[R];
 #pragma unroll
-  for (int i = 0; i < kOwnerIPT; ++i) m += v[i] == want ? 1u : 0u;
-  uint32_t off;
-  const uint32_t total = block_scan_excl(m, off, wsum);
+  for (int r = 0; r < R; ++r) m[r] = 0;
 #pragma unroll
-  for (int i = 0; i < kOwnerIPT; ++i)
-    if (v[i] == want) list[off++] = (int32_t)(p0 + i);
+  for (int i = 0; i < kOwnerIPT; ++i) {
+    const uint32_t rel = (uint32_t)v[i] - (uint32_t)want0;  // (modular: any id outside the R is >= R)
+#pragma unroll
+    for (int r = 0; r < R; ++r) m[r] += rel == (uint32_t)r ? 1u : 0u;
+  }
+  // cluster r's list: [lb[r], lb[r] + tot[r]) of `list`, in point order
+  uint32_t off[R], tot[R], lb[R];
+  uint32_t at = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    tot[r] = block_scan_excl(m[r], off[r], wsum);
+    lb[r] = at;
+    off[r] += at;
+    at += tot[r];
+  }
+#pragma unroll
+  for (int i = 0; i < kOwnerIPT; ++i) {
+    const uint32_t rel = (uint32_t)v[i] - (uint32_t)want0;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (rel == (uint32_t)r) list[off[r]++] = (int32_t)(p0 + i);
+  }
   __syncthreads();
 
   const int g = threadIdx.x / G, j = threadIdx.x % G;
-  const int per = (int)((total + NG - 1) / NG);
-  const int s0 = g * per < (int)total ? g * per : (int)total;
-  const int s1 = s0 + per < (int)total ? s0 + per : (int)total;
-  float acc[EPL];
-#pragma unroll
-  for (int x = 0; x < EPL; ++x) acc[x] = 0.0f;
   const uint8_t* Xb = S.X + (size_t)b * (size_t)S.N * (size_t)S.D * ES;
-  if (S.vec_ok && (j + 1) * EPL <= S.D)
-    walk_rows<ES, true, 8>(Xb, list, s0, s1, S.D, S.dt, j, acc);
-  else if (j * EPL < S.D)
-    walk_rows<ES, false, 8>(Xb, list, s0, s1, S.D, S.dt, j, acc);
+#pragma unroll 1
+  for (int r = 0; r < R; ++r) {
+    const int64_t k = k0 + r;
+    if (k >= S.K) break;  // (uniform)
+    const uint32_t total = tot[r];
+    const int32_t* cl = list + lb[r];
+    const int per = (int)((total + NG - 1) / NG);
+    const int s0 = g * per < (int)total ? g * per : (int)total;
+    const int s1 = s0 + per < (int)total ? s0 + per : (int)total;
+    float acc[EPL];
 #pragma unroll
-  for (int x = 0; x < EPL; ++x) part[g * GE + j * EPL + x] = acc[x];
-  __syncthreads();
-  // The lane groups' sums of a column, in two fixed stages when the workgroup
-  // has threads to spare: TPC threads per column each add every TPC-th lane
-  // group, then one thread adds those TPC partial sums in order.
-  constexpr int TPC0 = kRadixThreads / GE;
-  constexpr int TPC = TPC0 < 2 ? 1 : (TPC0 > NG ? NG : TPC0);
-  if constexpr (TPC > 1) {
-    const int c = threadIdx.x % GE, r = threadIdx.x / GE;
-    if (r < TPC) {
-      float v = 0.0f;
-      for (int gg = r; gg < NG; gg += TPC) v += part[gg * GE + c];
-      part2[r * GE + c] = v;
-    }
+    for (int x = 0; x < EPL; ++x) acc[x] = 0.0f;
+    if (S.vec_ok && (j + 1) * EPL <= S.D)
+      walk_rows<ES, true, 8>(Xb, cl, s0, s1, S.D, S.dt, j, acc);
+    else if (j * EPL < S.D)
+      walk_rows<ES, false, 8>(Xb, cl, s0, s1, S.D, S.dt, j, acc);
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) part[g * GE + j * EPL + x] = acc[x];
     __syncthreads();
-  }
-  const int64_t base = q * S.D;
-  for (int c = threadIdx.x; c < S.D; c += kRadixThreads) {
-    float sum = 0.0f;
+    // The lane groups' sums of a column, in two fixed stages when the
+    // workgroup has threads to spare: TPC threads per column each add every
+    // TPC-th lane group, then one thread adds those TPC partial sums in order.
+    constexpr int TPC0 = kRadixThreads / GE;
+    constexpr int TPC = TPC0 < 2 ? 1 : (TPC0 > NG ? NG : TPC0);
     if constexpr (TPC > 1) {
-#pragma unroll
-      for (int r = 0; r < TPC; ++r) sum += part2[r * GE + c];
-    } else {
-      for (int gg = 0; gg < NG; ++gg) sum += part[gg * GE + c];
+      const int c = threadIdx.x % GE, t = threadIdx.x / GE;
+      if (t < TPC) {
+        float u = 0.0f;
+        for (int gg = t; gg < NG; gg += TPC) u += part[gg * GE + c];
+        part2[t * GE + c] = u;
+      }
+      __syncthreads();
     }
-    const float mean = total > 0 ? sum / (float)total : S.C_prev[base + c];
-    S.C_new[base + c] = mean;
-    if (c < kMaxD16) row[c] = mean;
+    const int64_t q = b * S.K + k;
+    const int64_t base = q * S.D;
+    for (int c = threadIdx.x; c < S.D; c += kRadixThreads) {
+      float sum = 0.0f;
+      if constexpr (TPC > 1) {
+#pragma unroll
+        for (int t = 0; t < TPC; ++t) sum += part2[t * GE + c];
+      } else {
+        for (int gg = 0; gg < NG; ++gg) sum += part[gg * GE + c];
+      }
+      const float mean = total > 0 ? sum / (float)total : S.C_prev[base + c];
+      S.C_new[base + c] = mean;
+      if (c < kMaxD16) row[c] = mean;
+    }
+    if (threadIdx.x == 0 && S.counts) S.counts[q] = (int32_t)total;
+    __syncthreads();  // row complete; part and part2 free for the next cluster
+    if (S.frag) {     // (uniform)
+      if (threadIdx.x < 64) emit_fragment_row(row, S.D, S.dt, S.cfg, S.frag + 4 * b * S.f_stride, k);
+      __syncthreads();  // row read before the next cluster writes it
+    }
   }
-  if (threadIdx.x == 0 && S.counts) S.counts[q] = (int32_t)total;
-  if (!S.frag) return;  // (uniform)
-  __syncthreads();
-  if (threadIdx.x < 64) emit_fragment_row(row, S.D, S.dt, S.cfg, S.frag + 4 * b * S.f_stride, k);
 }
 
 int64_t small_chunks(int64_t N) { return (N + kSmallChunkThin - 1) / kSmallChunkThin; }  // at most
 
 bool small_owner_fits(int64_t B, int64_t N, int64_t K) {
-  return B >= 1 && K >= 1 && N <= kOwnerMaxN && B * K <= kOwnerMaxGroups;
+  return B >= 1 && K >= 1 && N <= kOwnerMaxN && owner_r(B, K) > 0;
 }
 
 hipError_t launch_small_update(const SmallArgs& a, hipStream_t stream) {
@@ -431,13 +476,19 @@ hipError_t launch_small_update(const SmallArgs& a, hipStream_t stream) {
     const int64_t nch_ = (a.D + 16 / es_ - 1) / (16 / es_);
     int g_ = 1;
     while (g_ < nch_ && g_ < 64) g_ <<= 1;
-    const dim3 og((unsigned)(a.B * a.K)), ob(kRadixThreads);
+    const int r_ = owner_r(a.B, a.K);
+    const dim3 og((unsigned)(a.B * ((a.K + r_ - 1) / r_))), ob(kRadixThreads);
     bool done = false;
-#define KM_OWNER(ES_, G_) \
-  if (!done && es_ == ES_ && g_ == G_) { hipLaunchKernelGGL((small_owner_kernel<ES_, G_>), og, ob, 0, stream, S); done = true; }
+#define KM_OWNER_R(ES_, G_, R_)                                                                \
+  if (!done && es_ == ES_ && g_ == G_ && r_ == R_) {                                           \
+    hipLaunchKernelGGL((small_owner_kernel<ES_, G_, R_>), og, ob, 0, stream, S);               \
+    done = true;                                                                               \
+  }
+#define KM_OWNER(ES_, G_) KM_OWNER_R(ES_, G_, 1) KM_OWNER_R(ES_, G_, 2) KM_OWNER_R(ES_, G_, 4) KM_OWNER_R(ES_, G_, 8)
     KM_OWNER(2, 1) KM_OWNER(2, 2) KM_OWNER(2, 4) KM_OWNER(2, 8) KM_OWNER(2, 16) KM_OWNER(2, 32) KM_OWNER(2, 64)
     KM_OWNER(4, 1) KM_OWNER(4, 2) KM_OWNER(4, 4) KM_OWNER(4, 8) KM_OWNER(4, 16) KM_OWNER(4, 32) KM_OWNER(4, 64)
 #undef KM_OWNER
+#undef KM_OWNER_R
     return done ? hipGetLastError() : hipErrorInvalidValue;
   }
   const int64_t grid = a.B * S.P;

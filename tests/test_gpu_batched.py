@@ -57,6 +57,14 @@ def test_batched_bf16_ragged():
     _teacher_forced(Xn, "bf16", C0, 3, "bf16 ragged x5")
 
 
+@pytest.mark.parametrize("B,K", [(3, 600), (2, 400), (3, 170)])
+def test_batched_one_launch_update(B, K):
+    """A few problems whose clusters take one workgroup per 4, 2 or 1 clusters (at most 512 workgroups): every
+    problem and iteration against the oracle."""
+    w, Xn, C0 = _batch("c1", B, 900, N=2000, K=K)
+    _teacher_forced(Xn, "f32", C0, 2, f"one-launch update B={B} K={K}")
+
+
 @pytest.mark.parametrize("xdtype,D", [("bf16", 64), ("f32", 24)])
 def test_batched_split_sweep(xdtype, D):
     """Three problems of 3,000 points and 2,000 centroids: the centroid sweep is split over several workgroups

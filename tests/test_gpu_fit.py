@@ -132,11 +132,12 @@ def test_fit_resume_and_determinism():
                                           ((30000, 24, 8192), "f32"), ((40000, 16, 9000), "bf16"),
                                           ((16384, 128, 512), "bf16"), ((3000, 64, 40), "bf16"),
                                           ((12000, 300, 100), "f16"), ((16384, 512, 64), "bf16"),
-                                          ((16385, 64, 200), "bf16"), ((8000, 33, 513), "f32")],
+                                          ((16385, 64, 200), "bf16"), ((8000, 33, 513), "f32"),
+                                          ((12000, 48, 2000), "bf16"), ((16384, 24, 2049), "f32")],
                          ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else v)
 def test_fit_many_iterations_equal_single_steps(shape, xdtype):
     """From the second iteration of a call on, FlashAssign uses the operand fragments that the update wrote
-    (the one-workgroup-per-cluster update for N <= 16384 and K <= 512, the chunk-sum combine for fp32 K <= 64,
+    (the one-launch update for N <= 16384 and K <= 2048, the chunk-sum combine for fp32 K <= 64,
     the fix-up otherwise); T iterations in one call must equal T calls of one iteration (which prepare them
     afresh), bit for bit."""
     N, D, K = shape

@@ -133,11 +133,13 @@ def test_update_small_codebook(shape, xdtype):
 
 @pytest.mark.parametrize("xdtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("shape", [(1, 8, 65), (1000, 32, 512), (16384, 128, 512), (16384, 512, 100), (7777, 3, 257),
-                                   (16385, 32, 100), (1000, 32, 513)],
+                                   (16385, 32, 100), (1000, 32, 513), (5000, 64, 1000), (3000, 16, 2047),
+                                   (16384, 32, 2048), (9000, 200, 1999), (16384, 32, 2049)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_update_one_workgroup_per_cluster(shape, xdtype):
-    """N <= 16384 and 64 < K <= 512: one workgroup per cluster lists its points and sums them (no sort); one
-    point more or one cluster more than that takes the sorted path."""
+    """N <= 16384 and 64 < K <= 2048: one workgroup per 1, 2 or 4 clusters (at most 512 workgroups) lists
+    each cluster's points and sums them (no sort); one point more (N = 16385) or one cluster more (K = 2049)
+    than that takes the sorted path."""
     N, D, K = shape
     if xdtype == "f32" and D > 256:
         pytest.skip("fp32 supports D <= 256")
