@@ -1,15 +1,20 @@
 """Benchmark: exact Lloyd K-Means iterations on one MI355X.
 
-One step = one kmeans_fit call running the workload's full iteration count
-(every iteration: centroid prep, FlashAssign, radix argsort, boundaries,
-segmented reduction, fix-up/finalise) on synthetic data already resident in
-HBM.  The default workload is c2 (bf16 N=1,048,576 D=128 K=1,024, 20
-iterations).  Prints one JSON line.
+Default run (what `python bench.py --gpus 1 --steps K --warmup W` prints): the
+largest workload, c5 (bf16, N = 10^9 rows, D = 64, K = 4,096, 3 Lloyd
+iterations per fit; X in host memory, streamed in 64 Mi-row chunks).  A step
+is one Lloyd iteration over all 10^9 rows (every chunk uploaded, assigned and
+reduced, then the means formed): the W warm-up and K timed iterations run as
+consecutive fits of the workload's 3 iterations, each starting again from
+C^0, so every iteration of the workload is timed in its proportion.  After
+the headline, the device-resident workloads c2, c3 and c4 are timed the same
+way (a step = one kmeans_fit of all their iterations on X already in HBM) and
+reported under "extra_configs", each with its own FlashAssign roofline,
+whole-update roofline and CPU baseline.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload c1|c2|c3|c4|c5] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload c1..c5] [--extra c2,c3,c4|none] [--no-cpu-baseline]
   python bench.py --workload c1 --batch 256      (256 independent c1-shaped problems per call)
-
---workload c5 runs the host-streamed path (X in pinned host memory).
+  python bench.py --ablation                     (the designs FlashAssign and Sort-Inverse Update replace)
 """
 from __future__ import annotations
 
@@ -200,8 +205,11 @@ def ablation(dev):
     print(json.dumps(out), flush=True)
 
 
-# Timed steps by default: enough that the timed region is tens of milliseconds.
-DEFAULT_STEPS = {"c1": 200, "c2": 10}
+
+# Timed steps when --steps is not given (the driver always gives them).
+DEFAULT_STEPS = {"c1": 200, "c2": 10, "c5": 6}
+EXTRA_DEFAULT = "c2,c3,c4"
+UPDATE_PHASES = ("sort", "segments", "reduce", "finalize")
 
 
 def timed_step(i: int, steps: int) -> bool:
@@ -210,6 +218,213 @@ def timed_step(i: int, steps: int) -> bool:
     of a c1 iteration, so with many steps only every s-th step is bracketed
     (s = ceil(steps / 8)); the launches of those steps give the average."""
     return i % -(-steps // 8) == 0
+
+
+def read_phases(km):
+    out = {}
+    for ph in km.PHASES:
+        ms, n = km.timing_read(ph)
+        if n:
+            out[ph] = {"total_ms": round(ms, 4), "launches": n, "avg_us": round(1e3 * ms / n, 3)}
+    km.timing_reset()
+    return out
+
+
+def assign_roofline(w, phases, total_iters, peaks):
+    """FlashAssign: algorithmic flops 2*N*K*D per iteration over the launches' average duration."""
+    if "assign" not in phases:
+        return None
+    n = phases["assign"]["launches"]
+    flops = 2.0 * w.N * w.K * w.D * total_iters / n  # per launch (streamed: chunks differ, ragged last one)
+    avg_s = phases["assign"]["avg_us"] * 1e-6
+    achieved = flops / avg_s
+    peak = PEAK[w.dtype]
+    roof = {"bound": "mfma", "kernel": "flash_assign", "achieved": round(achieved / 1e12, 2),
+            "peak": round(peak / 1e12, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+            "traffic": _traffic(ASSIGN_SOURCES, w.name), "flops_per_launch": flops,
+            "avg_launch_us": phases["assign"]["avg_us"], "timed_launches": n}
+    if peaks and "mfma_TFLOPs" in peaks and w.dtype != "f32":
+        roof["peak_measured"] = peaks["mfma_TFLOPs"]
+        roof["frac_of_measured"] = round(roof["achieved"] / peaks["mfma_TFLOPs"], 4)
+    return roof
+
+
+def update_roofline(w, breakdown, iters, peaks):
+    """The whole Sort-Inverse Update (argsort + boundaries + segmented reduction + fix-up/finalise) of one
+    iteration against HBM, on the algorithmic minimum B_min = N*D*s + 4N + 4KD (read X and the assignment
+    once, write the centroids), from the per-phase step; the segmented-reduction kernel alone is given
+    separately (its own bytes: the gathered rows plus 8 B of sorted key and index per point)."""
+    if not any(p in breakdown for p in UPDATE_PHASES):
+        return None
+    es = 4 if w.dtype == "f32" else 2
+    bmin = w.N * w.D * es + 4 * w.N + 4 * w.K * w.D
+    t_iter = sum(breakdown[p]["total_ms"] for p in UPDATE_PHASES if p in breakdown) * 1e-3 / iters
+    gbps = bmin / t_iter / 1e9
+    out = {"bound": "hbm", "kernel": "whole update: " + " + ".join(p for p in UPDATE_PHASES if p in breakdown),
+           "achieved": round(gbps, 1), "peak": 8000.0, "unit": "GB/s", "frac": round(gbps / 8000.0, 4),
+           "bytes_min_per_iteration": bmin, "us_per_iteration": round(t_iter * 1e6, 2),
+           "phase_us_per_iteration": {p: round(breakdown[p]["total_ms"] * 1e3 / iters, 2)
+                                      for p in UPDATE_PHASES if p in breakdown}}
+    if peaks and "hbm_read_GBps" in peaks:
+        out["peak_measured_read"] = peaks["hbm_read_GBps"]
+        out["frac_of_measured_read"] = round(gbps / peaks["hbm_read_GBps"], 4)
+    if "reduce" in breakdown:
+        small = w.K <= 64
+        per_point = w.D * es + (4 if small else 8)
+        per_launch = w.N * per_point * iters / breakdown["reduce"]["launches"]
+        kg = per_launch / (breakdown["reduce"]["avg_us"] * 1e-6) / 1e9
+        out["reduce_kernel"] = {"kernel": "small_update" if small else "segment_reduce",
+                                "bytes_per_launch": round(per_launch), "avg_launch_us": breakdown["reduce"]["avg_us"],
+                                "achieved": round(kg, 1), "frac": round(kg / 8000.0, 4)}
+    return out
+
+
+def run_resident(w, args, dev, peaks, steps, warmup, tag):
+    """One workload with X resident in HBM: a step is one kmeans_fit of all its iterations."""
+    import numpy as np
+    import torch
+
+    import means_clustering_amd as km
+    import synth
+
+    print(f"[bench] {tag} {w.name}: {w.description}", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    Xn = synth.points(w)
+    C0 = torch.from_numpy(synth.init_centroids(w, Xn)).to(dev)
+    X = (torch.from_numpy(Xn.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16"
+         else torch.from_numpy(Xn)).to(dev)
+    print(f"[bench] {w.name}: inputs in HBM after {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    C = C0.clone()
+    a = torch.empty(w.N, dtype=torch.int32, device=dev)
+    counts = torch.empty(w.K, dtype=torch.int32, device=dev)
+    ws = km.Workspace(dev)
+
+    def one_step():
+        C.copy_(C0)
+        km.fit(X, C, w.iters, inplace=True, ws=ws, assign_out=a, counts_out=counts)
+
+    for _ in range(warmup):
+        one_step()
+    torch.cuda.synchronize()
+    timing = not args.no_timing
+    if timing:
+        km.timing_reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if timing:
+            km.timing_enable(2 if timed_step(i, steps) else 0)
+        one_step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    phases, breakdown = {}, {}
+    if timing:
+        km.timing_enable(False)
+        phases = read_phases(km)
+        # per-phase breakdown from one more step with every phase timed (not part of `value`)
+        km.timing_enable(1)
+        one_step()
+        torch.cuda.synchronize()
+        km.timing_enable(False)
+        breakdown = read_phases(km)
+    timed_steps = sum(timed_step(i, steps) for i in range(steps))
+    roof = assign_roofline(w, phases, timed_steps * w.iters, peaks)
+    if roof is not None:
+        roof["timed_steps"] = timed_steps
+    res = {"value": round(steps * w.iters / elapsed, 3), "unit": "iterations/s", "steps": steps, "warmup": warmup,
+           "step": f"one kmeans_fit of all {w.iters} iterations from C^0, X resident in HBM",
+           "ms_per_step": round(1e3 * elapsed / steps, 3), "dtype": w.dtype,
+           "config": {"workload": w.description, "name": w.name, "N": w.N, "D": w.D, "K": w.K,
+                      "iters_per_step": w.iters},
+           "distances_per_s": round(steps * w.iters / elapsed * w.N * w.K, 1),
+           "roofline": roof, "update_roofline": update_roofline(w, breakdown, w.iters, peaks),
+           "phases_timed_region": phases, "phase_breakdown_extra_step": breakdown}
+    del X
+    torch.cuda.empty_cache()
+    res["cpu_baseline"] = None
+    if not args.no_cpu_baseline:
+        print(f"[bench] {w.name}: cpu baseline (the oracle on a sample)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, C0.cpu().numpy(), lambda r: Xn[:r], budget_s=args.cpu_budget)
+    return res
+
+
+def run_streamed(w, args, dev, peaks, steps, warmup):
+    """The out-of-core workload: X in host memory, a step is one Lloyd iteration over every chunk."""
+    import torch
+
+    import means_clustering_amd as km
+    import synth
+
+    print(f"[bench] workload {w.name}: {w.description}", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+
+    def progress(done):
+        if done % (1 << 28) < (1 << 24) or done == w.N:
+            print(f"[bench] generated {done} / {w.N} rows", file=sys.stderr, flush=True)
+
+    # pageable: 10^9 x 64 bf16 is more than the host lets one process pin; uploaded through a staging ring
+    Xh = synth.host_points(w, dev, pinned=False, progress=progress)
+    stage = km.staging_buffer()
+    Xrows = synth.as_numpy_rows(Xh)
+    C0 = torch.from_numpy(synth.init_centroids(w, Xrows)).to(dev)
+    print(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    ws = km.Workspace(dev)
+    copy_stream = torch.cuda.Stream(dev)
+
+    def run_iterations(n, label):
+        """n Lloyd iterations as consecutive fits of the workload's iteration count, each from C^0."""
+        done = 0
+        while done < n:
+            it = min(w.iters, n - done)
+            km.fit_streamed(Xh, C0, it, w.chunk_rows, copy_stream=copy_stream, want_assign=False, ws=ws, stage=stage)
+            torch.cuda.synchronize()
+            done += it
+            print(f"[bench] {label}: {done} / {n} iterations", file=sys.stderr, flush=True)
+
+    run_iterations(warmup, "warm-up")
+    timing = not args.no_timing
+    if timing:
+        km.timing_reset()
+        km.timing_enable(2)  # FlashAssign launches only: two events per 64 Mi-row chunk
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_iterations(steps, "timed")
+    elapsed = time.perf_counter() - t0
+    phases, breakdown = {}, {}
+    if timing:
+        km.timing_enable(False)
+        phases = read_phases(km)
+        km.timing_enable(1)
+        run_iterations(w.iters, "per-phase step")
+        km.timing_enable(False)
+        breakdown = read_phases(km)
+    es = 2 if w.dtype == "bf16" else 4
+    e2e = w.N * w.D * es * steps / elapsed / 1e9
+    stream = {"h2d_bytes_per_iteration": w.N * w.D * es, "end_to_end_GBps": round(e2e, 2),
+              "peak": 64.0, "unit": "GB/s", "frac_of_pcie5_x16": round(e2e / 64.0, 4)}
+    if "h2d" in breakdown:  # each chunk's upload bracketed on the copy stream
+        stream["h2d_GBps_while_copying"] = round(w.N * w.D * es * w.iters / (breakdown["h2d"]["total_ms"] * 1e-3) / 1e9,
+                                                 2)
+    if peaks and "h2d_pinned_GBps" in peaks:
+        stream["peak_measured_h2d"] = peaks["h2d_pinned_GBps"]
+        stream["frac_of_measured_h2d"] = round(e2e / peaks["h2d_pinned_GBps"], 4)
+    res = {"value": round(steps / elapsed, 4), "unit": "iterations/s", "steps": steps, "warmup": warmup,
+           "step": (f"one Lloyd iteration over all {w.N} rows (upload, FlashAssign, Sort-Inverse Update of every "
+                    f"{w.chunk_rows}-row chunk, then the means); steps run as consecutive {w.iters}-iteration fits "
+                    "from C^0"),
+           "ms_per_step": round(1e3 * elapsed / steps, 3), "dtype": w.dtype,
+           "config": {"workload": w.description, "name": w.name, "N": w.N, "D": w.D, "K": w.K,
+                      "iters_per_fit": w.iters, "chunk_rows": w.chunk_rows},
+           "distances_per_s": round(steps / elapsed * w.N * w.K, 1),
+           "roofline": assign_roofline(w, phases, steps, peaks),
+           "update_roofline": update_roofline(w, breakdown, w.iters, peaks), "streaming": stream,
+           "phases_timed_region": phases, "phase_breakdown_extra_step": breakdown}
+    res["cpu_baseline"] = None
+    if not args.no_cpu_baseline:
+        print(f"[bench] {w.name}: cpu baseline (the oracle on a sample)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, C0.cpu().numpy(), lambda r: Xrows[:r], budget_s=args.cpu_budget)
+    del Xh, Xrows, stage
+    return res
 
 
 def batched(args, dev):
@@ -311,11 +526,14 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default: 200 for c1, 10 for c2, 5 otherwise)")
+                    help="timed steps (default: 6 for c5, 200 for c1, 10 for c2, 5 otherwise)")
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--workload", default="c5", help="headline workload (default c5, the largest)")
+    ap.add_argument("--extra", default=None,
+                    help="comma-separated resident workloads timed after the headline (default c2,c3,c4 when the "
+                         "headline is c5; 'none' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for each CPU baseline")
     ap.add_argument("--no-timing", action="store_true", help="no per-kernel events (for profiler runs)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the same-run peak probes")
     ap.add_argument("--batch", type=int, default=1,
@@ -326,7 +544,12 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
-    if args.steps is None:
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding of this "
+              "path is a design note, not a measured configuration.", file=sys.stderr)
+        sys.exit(2)
+    steps_given = args.steps is not None
+    if not steps_given:
         args.steps = DEFAULT_STEPS.get(args.workload, 5)
     if args.calibrate_copy:
         import torch
@@ -341,185 +564,45 @@ def main():
         import torch
         ablation(torch.device("cuda:0"))
         return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding of this "
-              "path is a design note, not a measured configuration.", file=sys.stderr)
-        sys.exit(2)
-
     if args.batch > 1:
         import torch
         batched(args, torch.device("cuda:0"))
         return
 
-    import numpy as np
     import torch
 
-    import means_clustering_amd as km
     import synth
 
-    w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    print(f"[bench] workload {w.name}: {w.description}", file=sys.stderr, flush=True)
-    torch_dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
-    streamed = w.chunk_rows > 0
-
-    # ---- inputs (synthetic, seeded), resident in HBM before timing ------------
-    t0 = time.perf_counter()
-    if streamed:
-        def progress(done):
-            if done % (1 << 28) < (1 << 24) or done == w.N:
-                print(f"[bench] generated {done} / {w.N} rows", file=sys.stderr, flush=True)
-
-        # pageable: 10^9 x 64 bf16 is more than the host lets one process pin; uploaded through a staging ring
-        Xh = synth.host_points(w, dev, pinned=False, progress=progress)
-        stage = km.staging_buffer()
-        Xrows = synth.as_numpy_rows(Xh)
-        C0 = torch.from_numpy(synth.init_centroids(w, Xrows)).to(dev)
-        rows_of = lambda r: Xrows[:r]  # noqa: E731
-    else:
-        Xn = synth.points(w)
-        C0 = torch.from_numpy(synth.init_centroids(w, Xn)).to(dev)
-        X = (torch.from_numpy(Xn.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16"
-             else torch.from_numpy(Xn)).to(dev)
-        rows_of = lambda r: Xn[:r]  # noqa: E731
-    print(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
-
-    C = C0.clone()
-    a = torch.empty(w.N, dtype=torch.int32, device=dev) if not streamed else None
-    counts = torch.empty(w.K, dtype=torch.int32, device=dev)
-    ws = km.Workspace(dev)
-    if streamed:
-        copy_stream = torch.cuda.Stream(dev)
-
-    def one_step():
-        C.copy_(C0)
-        if streamed:
-            km.fit_streamed(Xh, C, w.iters, w.chunk_rows, copy_stream=copy_stream, want_assign=False, ws=ws,
-                            stage=stage)
-        else:
-            km.fit(X, C, w.iters, inplace=True, ws=ws, assign_out=a, counts_out=counts)
-
-    for i in range(args.warmup):
-        one_step()
-        torch.cuda.synchronize()
-        print(f"[bench] warmup step {i} done", file=sys.stderr, flush=True)
-
-    # Timed region: HIP events bracket only the FlashAssign launches (mode 2) of a
-    # sample of the steps, so the measured throughput carries almost none of their cost.
-    timing = not args.no_timing
-    if timing:
-        km.timing_reset()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if timing:
-            km.timing_enable(2 if timed_step(i, args.steps) else 0)
-        one_step()
-        if streamed:
-            torch.cuda.synchronize()
-            print(f"[bench] step {i} done", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    if timing:
-        km.timing_enable(False)
-
-    its = args.steps * w.iters
-    value = its / elapsed
-    phases = {}
-
-    def read_phases():
-        out = {}
-        for ph in km.PHASES:
-            ms, n = km.timing_read(ph)
-            if n:
-                out[ph] = {"total_ms": round(ms, 4), "launches": n, "avg_us": round(1e3 * ms / n, 3)}
-        km.timing_reset()
-        return out
-
-    if timing:
-        phases = read_phases()
-        # per-phase breakdown from one more step with every phase timed (not part of `value`)
-        km.timing_enable(1)
-        one_step()
-        torch.cuda.synchronize()
-        km.timing_enable(False)
-        breakdown = read_phases()
-    else:
-        breakdown = {}
-
-    # ---- roofline of the dominant kernel (FlashAssign): algorithmic flops per launch
-    roof = None
-    if "assign" in phases:
-        rows_per_launch = w.chunk_rows if streamed else w.N
-        flops = 2.0 * rows_per_launch * w.K * w.D
-        avg_s = phases["assign"]["avg_us"] * 1e-6
-        if streamed:  # launches differ in size (ragged last chunk): use the total
-            flops = 2.0 * w.N * w.K * w.D * its / phases["assign"]["launches"]
-        achieved = flops / avg_s
-        peak = PEAK[w.dtype]
-        traffic = _traffic(ASSIGN_SOURCES, w.name)
-        roof = {"bound": "mfma", "kernel": "flash_assign", "achieved": round(achieved / 1e12, 2),
-                "peak": round(peak / 1e12, 1), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": traffic, "flops_per_launch": flops, "avg_launch_us": phases["assign"]["avg_us"],
-                "timed_launches": phases["assign"]["launches"],
-                "timed_steps": sum(timed_step(i, args.steps) for i in range(args.steps))}
-
+    w = synth.WORKLOADS[args.workload]
+    extra = args.extra if args.extra is not None else (EXTRA_DEFAULT if w.chunk_rows else "none")
+    extra = [] if extra in ("", "none") else [e.strip() for e in extra.split(",")]
+    for e in extra:
+        if e not in synth.WORKLOADS or synth.WORKLOADS[e].chunk_rows:
+            raise SystemExit(f"--extra takes device-resident workloads, not {e!r}")
     peaks = None if args.no_peaks else measured_peaks(dev, w.dtype)
-    if roof is not None and peaks and "mfma_TFLOPs" in peaks:
-        roof["peak_measured"] = peaks["mfma_TFLOPs"]
-        roof["frac_of_measured"] = round(roof["achieved"] / peaks["mfma_TFLOPs"], 4)
-
-    # ---- the update's bandwidth: the reduction kernel(s) of the per-phase step against HBM.  Algorithmic
-    # bytes per launch: the rows of X it reads once (gathered in cluster order) plus the sorted keys and
-    # point indices (8 B a point; the small-codebook path reads the 4-byte ids instead).
-    upd = None
-    if "reduce" in breakdown:
-        es = 2 if w.dtype in ("bf16", "f16") else 4
-        rows = w.chunk_rows if streamed else w.N
-        small = w.K <= 64
-        per_launch = rows * (w.D * es + (4 if small else 8))
-        if streamed:  # ragged last chunk: use the total
-            per_launch = w.N * (w.D * es + (4 if small else 8)) * w.iters / breakdown["reduce"]["launches"]
-        gbps = per_launch / (breakdown["reduce"]["avg_us"] * 1e-6) / 1e9
-        upd = {"bound": "hbm", "kernel": "small_update + small_combine" if small else "segment_reduce",
-               "achieved": round(gbps, 1), "peak": 8000.0, "unit": "GB/s", "frac": round(gbps / 8000.0, 4),
-               "bytes_per_launch": round(per_launch), "avg_launch_us": breakdown["reduce"]["avg_us"]}
-        if peaks and "hbm_read_GBps" in peaks:
-            upd["peak_measured_read"] = peaks["hbm_read_GBps"]
-            upd["frac_of_measured_read"] = round(gbps / peaks["hbm_read_GBps"], 4)
-
-    stream = None
-    if streamed:
-        es = 2 if w.dtype == "bf16" else 4
-        h2d_bytes = w.N * w.D * es * its
-        e2e = h2d_bytes / elapsed / 1e9
-        copying = None
-        if "h2d" in breakdown:  # the extra step: w.iters iterations, each chunk's upload bracketed
-            copying = round(w.N * w.D * es * w.iters / (breakdown["h2d"]["total_ms"] * 1e-3) / 1e9, 2)
-        stream = {"h2d_bytes_per_iteration": w.N * w.D * es,
-                  "h2d_GBps_while_copying": copying,
-                  "end_to_end_GBps": round(e2e, 2),
-                  "frac_of_pcie5_x16": round(e2e / 64.0, 4)}
-        if peaks and "h2d_pinned_GBps" in peaks:
-            stream["frac_of_measured_h2d"] = round(e2e / peaks["h2d_pinned_GBps"], 4)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline: timing the oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, C0.cpu().numpy(), rows_of, budget_s=args.cpu_budget)
-
+    if w.chunk_rows:
+        res = run_streamed(w, args, dev, peaks, args.steps, args.warmup)
+    else:
+        res = run_resident(w, args, dev, peaks, args.steps, args.warmup, "workload")
+    extras = {}
+    for e in extra:
+        we = synth.WORKLOADS[e]
+        # the extras are short (milliseconds a step): the given counts, or enough steps for tens of milliseconds
+        st = args.steps if steps_given else DEFAULT_STEPS.get(e, 5)
+        extras[e] = run_resident(we, args, dev, peaks, st, max(args.warmup, 1), "extra workload")
+        extras[e]["vs_baseline"] = None
     line = {
         "metric": "Lloyd iterations/sec and point-centroid distances/sec (fused assign+update)",
-        "value": round(value, 3), "unit": "iterations/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(1e3 * elapsed / args.steps, 3), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.description, "name": w.name, "N": w.N, "D": w.D, "K": w.K,
-                   "iters_per_step": w.iters, "chunk_rows": w.chunk_rows or None},
-        "distances_per_s": round(value * w.N * w.K, 1),
-        "roofline": roof, "update_roofline": upd, "cpu_baseline": cpu, "phases_timed_region": phases,
-        "phase_breakdown_extra_step": breakdown,
-        "streaming": stream, "peaks_measured": peaks,
-        "device": torch.cuda.get_device_name(dev),
+        "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": res["steps"], "warmup": res["warmup"],
+        "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": res["dtype"], "data": "synthetic (seeded Gaussian mixtures of the workload's shape)",
+        "config": res["config"], "step": res["step"], "distances_per_s": res["distances_per_s"],
+        "roofline": res["roofline"], "update_roofline": res["update_roofline"],
+        "streaming": res.get("streaming"), "cpu_baseline": res["cpu_baseline"],
+        "phases_timed_region": res["phases_timed_region"],
+        "phase_breakdown_extra_step": res["phase_breakdown_extra_step"],
+        "extra_configs": extras, "peaks_measured": peaks, "device": torch.cuda.get_device_name(dev),
     }
     print(json.dumps(line), flush=True)
 

@@ -311,9 +311,13 @@ constexpr int64_t kOwnerMaxGroups = KM_OWNER_MAX_GROUPS;
 #endif
 constexpr int kOwnerMaxR = KM_OWNER_MAX_R;  // clusters per workgroup, at most (1, 2, 4 or 8)
 
-// clusters per workgroup for B problems of K clusters (0: the layout does not apply)
+// clusters per workgroup for B problems of K clusters (0: the layout does not apply).  Several clusters a
+// workgroup only above kSmallMaxK clusters a problem: at most kSmallMaxK the chunk-sum layout takes over
+// beyond kOwnerMaxGroups one-cluster workgroups (where it measured faster, 16 or more c1-shaped problems),
+// and the 2- and 4-cluster workgroups were measured against the sorted path only.
 static int owner_r(int64_t B, int64_t K) {
-  for (int r = 1; r <= kOwnerMaxR; r *= 2)
+  const int rmax = K > kSmallMaxK ? kOwnerMaxR : 1;
+  for (int r = 1; r <= rmax; r *= 2)
     if (B * ((K + r - 1) / r) <= kOwnerMaxGroups) return r;
   return 0;
 }
