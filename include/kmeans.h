@@ -38,10 +38,14 @@
  *     work is enqueued asynchronously on it; results are ready once the
  *     stream is synchronised.  The library never synchronises the host
  *     (kmeans_fit_streamed returns once its last chunk is enqueued).
- *   - Limits: 1 <= N < 2^31, 1 <= K < 2^31, 1 <= D <= 512 for 16-bit X and
- *     1 <= D <= 256 for fp32 X (other D: KM_ERR_UNSUPPORTED).  K > N is
- *     allowed (the extra clusters stay empty).  N = 0 is accepted and does
- *     nothing except the documented output of an empty update.
+ *   - Limits: 1 <= N < 2^31, 1 <= K < 2^31, 1 <= D <= 2^24 and K*D < 2^37
+ *     (beyond: KM_ERR_UNSUPPORTED).  The page has N, K and D change from call
+ *     to call (tech §1); every D is served: rows of up to 512 16-bit / 256
+ *     fp32 values are held whole in registers, longer rows are walked in
+ *     depth chunks by the assignment and in column strips by the update
+ *     (same results, same rules).  K > N is allowed (the extra clusters stay
+ *     empty).  N = 0 is accepted and does nothing except the documented
+ *     output of an empty update.
  *   - Errors: arguments, dtype and workspace size are checked synchronously
  *     before any HIP call, so a failed check enqueues nothing.  A failed
  *     launch returns KM_ERR_HIP.  Faults inside kernels surface at the
@@ -66,7 +70,7 @@ typedef enum km_dtype { KM_F32 = 0, KM_BF16 = 1, KM_F16 = 2 } km_dtype;
 typedef enum km_status {
   KM_OK = 0,
   KM_ERR_INVALID_VALUE = 1, /* null pointer, size out of range, misalignment, bad dtype */
-  KM_ERR_UNSUPPORTED = 2,   /* valid but not supported here (D too large) */
+  KM_ERR_UNSUPPORTED = 2,   /* valid but beyond a size limit (D > 2^24, K*D, B*N; no-alloc scratch) */
   KM_ERR_WORKSPACE = 3,     /* ws is NULL or ws_bytes smaller than required */
   KM_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
 } km_status;
@@ -134,9 +138,12 @@ km_status kmeans_update(const void* X, km_dtype dt, int64_t N, int64_t D, const 
                         void* stream);
 
 /*
- * kmeans_fit -- `iters` Lloyd iterations with X resident in device memory;
- * each iteration is kmeans_assign followed by kmeans_update, all enqueued on
- * `stream` with no host synchronisation.
+ * kmeans_fit -- `iters` Lloyd iterations with X resident in device memory
+ * (the page's end-to-end K-Means: the assignment step of tech §2.1 followed
+ * by the centroid step of tech §2.2, repeated; tech §1 states the two steps
+ * and tech §4 times them end to end); each iteration is kmeans_assign
+ * followed by kmeans_update, all enqueued on `stream` with no host
+ * synchronisation.
  *   C          device K x D fp32: initial centroids in, C^iters out
  *   assign     device int32[N] or NULL: assignment of the last iteration
  *   counts     device int32[K] or NULL: counts that formed C^iters

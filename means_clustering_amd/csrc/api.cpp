@@ -102,10 +102,9 @@ static km_status check_sizes(int64_t N, int64_t D, int64_t K, km_dtype dt, bool 
   if (K < 1 || K >= kMaxN) return fail(KM_ERR_INVALID_VALUE, "K must satisfy 1 <= K < 2^31");
   if (need_d) {
     if (D < 1) return fail(KM_ERR_INVALID_VALUE, "D must be >= 1");
-    const int64_t dmax = dt == KM_F32 ? kMaxD32 : kMaxD16;
-    if (D > dmax)
+    if (D > kMaxD)
       return fail(KM_ERR_UNSUPPORTED, "D=" + std::to_string(D) + " exceeds the supported maximum " +
-                                          std::to_string(dmax) + " for this dtype");
+                                          std::to_string(kMaxD));
     if (K * D >= kMaxN * 64) return fail(KM_ERR_UNSUPPORTED, "K*D too large");
   }
   return KM_OK;
@@ -455,7 +454,8 @@ static km_status run_update(const void* X, km_dtype dt, int64_t N, int64_t D, co
   if (sorted_keys) *sorted_keys = nullptr;
   if (sorted_vals) *sorted_vals = nullptr;
   if (prepped) *prepped = false;
-  if (mode == MODE_MEAN && (K / B <= kSmallMaxK || small_owner_fits(B, N / B, K / B))) {
+  const bool deep = deep_rows((int)dt, D);  // rows beyond one lane group: no small-codebook path, column strips
+  if (mode == MODE_MEAN && !deep && (K / B <= kSmallMaxK || small_owner_fits(B, N / B, K / B))) {
     SmallArgs a;
     a.X = X;
     a.dt = (int)dt;
@@ -505,14 +505,18 @@ static km_status run_update(const void* X, km_dtype dt, int64_t N, int64_t D, co
   // The fix-up writes the next assignment's operands when it is cheaper than a separate preparation: one
   // wavefront per cluster against one workgroup per 32 centroids (measured on gfx950: a gain up to K = 4096,
   // a loss at K = 65536, where most clusters would keep a wavefront only for this).
-  if (mode == MODE_MEAN && frag && geom && prepped && K / B <= kFuseFragMaxK) {
+  if (mode == MODE_MEAN && frag && geom && prepped && K / B <= kFuseFragMaxK && !deep) {
     a.frag = frag;
     a.f_stride = (int64_t)(geom->frag_bytes() / 16);
     a.kper = K / B;
     a.cfg = geom->cfg;
   }
-  KM_TIMED("reduce", s, return launch_segment_reduce(a, s));
-  KM_TIMED("finalize", s, return launch_fixup(a, s));
+  const int64_t nstrips = reduce_strips((int)dt, D);  // 1 unless the rows are deep
+  for (int64_t strip = 0; strip < nstrips; ++strip) {
+    a.strip = strip;
+    KM_TIMED("reduce", s, return launch_segment_reduce(a, s));
+    KM_TIMED("finalize", s, return launch_fixup(a, s));
+  }
   if (a.frag) *prepped = true;
   return KM_OK;
 }

@@ -888,6 +888,248 @@ static Batch make_batch(const AssignGeom& g, int64_t N, int64_t blocks, int32_t 
   return b;
 }
 
+// ------------------------------------------------- FlashAssign, deep rows ----
+//
+// Rows too long to keep a point's whole operand in registers (16-bit X beyond
+// kMaxD16 values, fp32 X beyond kMaxD32): the same fused distance + argmin,
+// with the depth walked in chunks.  A workgroup (four wavefronts, two point
+// groups each) sweeps tiles of kDeepCT centroid groups; for each tile the
+// depth is taken kDeepKC fragment blocks (64 values) at a time: the tile's
+// centroid fragments of that chunk are copied into LDS (double-buffered,
+// global_load_lds), the points' fragments of that chunk are loaded into
+// registers one step ahead, and the MFMAs accumulate every (point, centroid)
+// score of the tile over the whole depth in registers.  When a tile's last
+// chunk is done its scores (bias-seeded, as in the other kernels) update the
+// running best per lane, ascending centroid order, strict comparison; the
+// lanes holding one point merge at the end with the lower index winning ties.
+// No N x K array exists anywhere: a tile's scores live in registers only.
+// The points' operands are re-read once per tile (from L2 / the last-level
+// cache), the price of rows that do not fit in registers.
+template <int DT>
+struct DeepOps;
+template <>
+struct DeepOps<DT_BF16> {
+  using acc_t = f32x16_t;
+  static constexpr int kRows = 32, kE = 16, kES = 2;
+  static __device__ __forceinline__ acc_t mma(u32x4_t a, u32x4_t b, acc_t c) { return mma32<DT_BF16>(a, b, c); }
+  static __device__ __forceinline__ acc_t bias(const u32x4_t* grp_bias, int piece) { return bias_of(grp_bias + piece * 4); }
+  static __device__ __forceinline__ float sumsq(u32x4_t v) { return sumsq16<DT_BF16>(v); }
+  static __device__ __forceinline__ int row_of(int e, int piece) { return (e >> 2) * 8 + piece * 4 + (e & 3); }
+};
+template <>
+struct DeepOps<DT_F16> {
+  using acc_t = f32x16_t;
+  static constexpr int kRows = 32, kE = 16, kES = 2;
+  static __device__ __forceinline__ acc_t mma(u32x4_t a, u32x4_t b, acc_t c) { return mma32<DT_F16>(a, b, c); }
+  static __device__ __forceinline__ acc_t bias(const u32x4_t* grp_bias, int piece) { return bias_of(grp_bias + piece * 4); }
+  static __device__ __forceinline__ float sumsq(u32x4_t v) { return sumsq16<DT_F16>(v); }
+  static __device__ __forceinline__ int row_of(int e, int piece) { return (e >> 2) * 8 + piece * 4 + (e & 3); }
+};
+template <>
+struct DeepOps<DT_F32> {
+  using acc_t = f32x4_t;
+  static constexpr int kRows = 16, kE = 4, kES = 4;
+  static __device__ __forceinline__ acc_t mma(u32x4_t a, u32x4_t b, acc_t c) { return mma16_f32(a, b, c); }
+  static __device__ __forceinline__ acc_t bias(const u32x4_t* grp_bias, int piece) {
+    return __builtin_bit_cast(f32x4_t, grp_bias[piece]);
+  }
+  static __device__ __forceinline__ float sumsq(u32x4_t v) {
+    float s = 0.0f;
+    s = fmaf(__uint_as_float(v.x), __uint_as_float(v.x), s);
+    s = fmaf(__uint_as_float(v.y), __uint_as_float(v.y), s);
+    s = fmaf(__uint_as_float(v.z), __uint_as_float(v.z), s);
+    s = fmaf(__uint_as_float(v.w), __uint_as_float(v.w), s);
+    return s;
+  }
+  static __device__ __forceinline__ int row_of(int e, int piece) { return piece * 4 + e; }
+};
+
+template <int DT, bool SPLIT>
+__global__ __launch_bounds__(kDeepW * 64) void flash_assign_deep_kernel(
+    const uint8_t* __restrict__ X, int64_t N, int D, bool vec_ok, const u32x4_t* __restrict__ frag, int ntiles, int KB,
+    int32_t* __restrict__ assign, float* __restrict__ min_dist, Batch bt) {
+  using Ops = DeepOps<DT>;
+  using acc_t = typename Ops::acc_t;
+  constexpr int ROWS = Ops::kRows, E = Ops::kE, ES = Ops::kES;
+  constexpr int NB = kDeepNB, CT = kDeepCT, W = kDeepW, KC = kDeepKC;
+  constexpr int PIECE_LANES = ROWS;              // lanes l and l + ROWS (.. ) hold one point
+  constexpr int PIECE_VALS = ROWS / 4;           // depth values per lane per block: 8 or 4
+  const AssignCfg cfg = deep_cfg(DT, KB);
+  const int64_t GS = cfg.group_slots();
+  const int64_t TS = cfg.tile_slots();
+  const int NC = (KB + KC - 1) / KC;  // depth chunks
+  __shared__ u32x4_t lds[2][CT * KC][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane % PIECE_LANES;
+  const int piece = lane / PIECE_LANES;
+  const uint32_t bz = blockIdx.x / bt.bpp;
+  const int64_t wbase = ((int64_t)(blockIdx.x - bz * bt.bpp) * W + wave) * (NB * ROWS);
+  X += (int64_t)bz * bt.x_stride;
+  frag += (int64_t)bz * bt.f_stride;
+  assign += (int64_t)bz * N;
+  if (min_dist) min_dist += (int64_t)bz * N;
+  const int32_t id_base = (int32_t)bz * bt.id_mul;
+  const int sp = SPLIT ? (int)blockIdx.y : 0;
+  if constexpr (SPLIT) {
+    frag += (int64_t)sp * bt.split_tiles * TS;
+    ntiles = ntiles - sp * bt.split_tiles < bt.split_tiles ? ntiles - sp * bt.split_tiles : bt.split_tiles;
+  }
+  int64_t pt[NB];
+#pragma unroll
+  for (int g = 0; g < NB; ++g) pt[g] = wbase + g * ROWS + col;
+
+  // centroid fragments of step s (tile s / NC, depth chunk s % NC) into LDS buffer `buf`: each wavefront
+  // copies whole fragment blocks (64 slots), wave-uniform destinations
+  auto stage_centroids = [&](int s, int buf) {
+    const int t = s / NC, kb0 = (s % NC) * KC;
+#pragma unroll
+    for (int j = 0; j < CT * KC / W; ++j) {
+      const int i = j * W + wave;  // (group, block) pair
+      const int g = i / KC, kk = i % KC;
+      if (kb0 + kk < KB)
+        __builtin_amdgcn_global_load_lds((const void*)(frag + (int64_t)t * TS + g * GS + (int64_t)(kb0 + kk) * 64 + lane),
+                                         (__attribute__((address_space(3))) void*)&lds[buf][i][0], 16, 0, 0);
+    }
+  };
+  // point fragments of depth chunk c into registers (zero beyond D and N)
+  auto load_points = [&](int c, u32x4_t (&xb)[NB][KC]) {
+    const int kb0 = c * KC;
+#pragma unroll
+    for (int g = 0; g < NB; ++g)
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk)
+        xb[g][kk] = load_point_frag<ES>(X, pt[g], N, D, (kb0 + kk) * kFragDepth + piece * PIECE_VALS, vec_ok);
+  };
+
+  float best[NB], xn[NB];
+  int32_t bidx[NB];
+#pragma unroll
+  for (int g = 0; g < NB; ++g) {
+    best[g] = -INFINITY;
+    bidx[g] = INT32_MAX;
+    xn[g] = 0.0f;
+  }
+  const int steps = ntiles * NC;
+  u32x4_t xb[NB][KC], xnx[NB][KC];
+  acc_t acc[NB][CT];
+  if (steps > 0) {
+    stage_centroids(0, 0);
+    load_points(0, xb);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  for (int s = 0; s < steps; ++s) {
+    const int buf = s & 1;
+    const int t = s / NC, c = s % NC;
+    if (s + 1 < steps) {  // the next step's operands stream in while this one computes
+      stage_centroids(s + 1, buf ^ 1);
+      load_points((s + 1) % NC, xnx);
+    }
+    if (c == 0) {
+#pragma unroll
+      for (int g = 0; g < CT; ++g) {
+        const acc_t b = Ops::bias(frag + (int64_t)t * TS + g * GS + (int64_t)KB * 64, piece);
+#pragma unroll
+        for (int q = 0; q < NB; ++q) acc[q][g] = b;
+      }
+    }
+    if (t == 0) {  // ||x||^2 from the first tile's pass over the depth
+#pragma unroll
+      for (int q = 0; q < NB; ++q)
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) xn[q] += Ops::sumsq(xb[q][kk]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) {
+      if (c * KC + kk < KB) {
+#pragma unroll
+        for (int g = 0; g < CT; ++g) {
+          const u32x4_t a = lds[buf][g * KC + kk][lane];
+#pragma unroll
+          for (int q = 0; q < NB; ++q) acc[q][g] = Ops::mma(a, xb[q][kk], acc[q][g]);
+        }
+      }
+    }
+    if (c == NC - 1) {  // the tile's scores are complete: running best, ascending centroid order
+#pragma unroll
+      for (int q = 0; q < NB; ++q)
+#pragma unroll
+        for (int g = 0; g < CT; ++g)
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float v = acc[q][g][e];
+            if (v > best[q]) {
+              best[q] = v;
+              bidx[q] = (t * CT + g) * ROWS + Ops::row_of(e, piece);
+            }
+          }
+    }
+    if (s + 1 < steps) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next step have landed
+      __syncthreads();                // ... and everyone's; this buffer is no longer read
+#pragma unroll
+      for (int q = 0; q < NB; ++q)
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) xb[q][kk] = xnx[q][kk];
+    }
+  }
+
+#pragma unroll
+  for (int q = 0; q < NB; ++q) {
+    float b = best[q], x2 = xn[q];
+    int32_t k = bidx[q];
+#pragma unroll
+    for (int off = PIECE_LANES; off < 64; off <<= 1) {
+      const float ob = __shfl_xor(b, off);
+      const int32_t ok = __shfl_xor(k, off);
+      if (ob > b || (ob == b && ok < k)) {
+        b = ob;
+        k = ok;
+      }
+      x2 += __shfl_xor(x2, off);
+    }
+    const int64_t p = pt[q];
+    if constexpr (SPLIT) {
+      if (piece == 0 && p < N) {
+        const int64_t o = (int64_t)bz * N + p;
+        bt.part_s[sp * bt.part_stride + o] = b;
+        bt.part_k[sp * bt.part_stride + o] = k == INT32_MAX ? INT32_MAX : k + sp * bt.split_tiles * CT * ROWS;
+        if (sp == 0 && bt.part_xn) bt.part_xn[o] = x2;
+      }
+      continue;
+    }
+    if (k == INT32_MAX) k = 0;  // no finite score (NaN input): index 0
+    if (piece == 0 && p < N) {
+      assign[p] = k + id_base;
+      if (min_dist) min_dist[p] = fmaxf(x2 - 2.0f * b, 0.0f);
+    }
+  }
+}
+
+template <int DT>
+static hipError_t launch_deep(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
+                              float* min_dist, int64_t B, int32_t id_mul, const SplitPlan& sp, hipStream_t s) {
+  const AssignCfg cfg = deep_cfg(DT, g.cfg.KB);
+  if (!same_cfg(g.cfg, cfg)) return hipErrorInvalidValue;
+  const int64_t pts = (int64_t)cfg.W * cfg.NB * cfg.rows;
+  const int64_t blocks = (N + pts - 1) / pts;
+  const int64_t nsteps = g.ntiles() * ((cfg.KB + kDeepKC - 1) / kDeepKC);  // (tile, depth chunk) steps
+  if (blocks * B >= ((int64_t)1 << 31) || nsteps >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const int es = dtype_size(g.dt);
+  const bool vec_ok = (((uintptr_t)X) % 16 == 0) && ((g.D * es) % 16 == 0);
+  const dim3 grid((unsigned)(blocks * B), (unsigned)sp.S), block(cfg.W * 64);
+  const Batch bt = make_batch(g, N, blocks, id_mul, sp);
+  if (sp.S > 1)
+    hipLaunchKernelGGL((flash_assign_deep_kernel<DT, true>), grid, block, 0, s, (const uint8_t*)X, N, (int)g.D, vec_ok,
+                       (const u32x4_t*)frag, (int)g.ntiles(), cfg.KB, assign, min_dist, bt);
+  else
+    hipLaunchKernelGGL((flash_assign_deep_kernel<DT, false>), grid, block, 0, s, (const uint8_t*)X, N, (int)g.D, vec_ok,
+                       (const u32x4_t*)frag, (int)g.ntiles(), cfg.KB, assign, min_dist, bt);
+  return hipGetLastError();
+}
+
 // The best of a split sweep's ranges per point, taken in range order with
 // the kernels' own rule (a higher score wins; on equal scores the lower
 // index), so the result is the unsplit sweep's.
@@ -1050,6 +1292,14 @@ static hipError_t dispatch_wide(const AssignGeom& g, const void* X, int64_t N, c
 static hipError_t launch_sweep(const AssignGeom& g, const void* X, int64_t N, const void* frag, int32_t* assign,
                                float* min_dist, hipStream_t stream, const int32_t* perm, const int32_t* prev,
                                int64_t B, int32_t id_mul, const SplitPlan& sp) {
+  if (is_deep_cfg(g.dt, g.cfg)) {  // (cold order: the warm start only reorders work)
+    switch (g.dt) {
+      case DT_BF16: return launch_deep<DT_BF16>(g, X, N, frag, assign, min_dist, B, id_mul, sp, stream);
+      case DT_F16: return launch_deep<DT_F16>(g, X, N, frag, assign, min_dist, B, id_mul, sp, stream);
+      case DT_F32: return launch_deep<DT_F32>(g, X, N, frag, assign, min_dist, B, id_mul, sp, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (g.dt) {
     case DT_BF16: return dispatch_wide<DT_BF16>(g, X, N, frag, assign, min_dist, perm, prev, B, id_mul, sp, stream);
     case DT_F16: return dispatch_wide<DT_F16>(g, X, N, frag, assign, min_dist, perm, prev, B, id_mul, sp, stream);

@@ -33,8 +33,13 @@ inline int dtype_size(int dt) { return dt == DT_F32 ? 4 : 2; }
 // ---------------------------------------------------------------------------
 constexpr int kFragDepth = 16;     // depth values per fragment block (both layouts)
 constexpr int kPadK = 128;         // 16-bit X: K is padded to a multiple of this (>= any tile)
-constexpr int kMaxD16 = 512;       // D limit for 16-bit X
-constexpr int kMaxD32 = 256;       // D limit for fp32 X
+constexpr int kMaxD16 = 512;       // longest 16-bit rows kept whole in registers / one lane group
+constexpr int kMaxD32 = 256;       // ... fp32 rows
+constexpr int64_t kMaxD = (int64_t)1 << 24;  // longest rows accepted at all (32-bit index arithmetic)
+// Rows longer than the register-resident limit take the depth-tiled FlashAssign
+// (both operands staged per depth chunk) and a segmented reduction in column
+// strips of kMaxD16 / kMaxD32 values.
+inline bool deep_rows(int dt, int64_t D) { return D > (dt == DT_F32 ? kMaxD32 : kMaxD16); }
 
 // Launch shape of one FlashAssign instantiation.
 struct AssignCfg {
@@ -111,6 +116,14 @@ constexpr int kWide8MaxKB = KM_WIDE8 ? 8 : 0;
 constexpr AssignCfg wide8_cfg(int KB) {
   return AssignCfg{32, KB, KB <= 4 ? KM_W8_NB_SMALL : KM_W8_NB, KB <= 4 ? KM_W8_CT_SMALL : KM_W8_CT, KM_W8_W};
 }
+// Depth-tiled layout (deep_rows): tiles of 4 groups (128 centroids of 16-bit X,
+// 64 of fp32), two point groups per wavefront, four wavefronts; the depth is
+// walked in chunks of 4 fragment blocks (64 values).
+constexpr int kDeepCT = 4, kDeepNB = 2, kDeepW = 4, kDeepKC = 4;
+constexpr AssignCfg deep_cfg(int dt, int KB) {
+  return AssignCfg{dt == DT_F32 ? 16 : 32, KB, kDeepNB, kDeepCT, kDeepW};
+}
+inline bool is_deep_cfg(int dt, const AssignCfg& c) { return c.KB > (dt == DT_F32 ? kMaxD32 : kMaxD16) / kFragDepth; }
 // fp32 X.  `half`: tiles of half as many groups, so that a small K (e.g. 64)
 // is not padded up to a whole 128-centroid tile.  `thin`: one point group per
 // wavefront, for calls too small to fill the GPU otherwise (with half tiles).
@@ -148,6 +161,12 @@ inline AssignGeom make_assign_geom(int64_t N, int64_t D, int64_t K, int dt, int6
   g.D = D;
   g.K = K;
   g.Kpad = pad_up(K, kPadK);
+  if (deep_rows(dt, D)) {
+    g.cfg = deep_cfg(dt, (int)((D + kFragDepth - 1) / kFragDepth));
+    g.Kpad = pad_up(K, (int64_t)g.cfg.rows * g.cfg.CT);
+    g.lazy = false;
+    return g;
+  }
   if (dt == DT_F32) {
     const int kb = (int)((D + kFragDepth - 1) / kFragDepth);
     const AssignCfg full = narrow_cfg(kb), half = narrow_cfg(kb, true);
@@ -332,6 +351,7 @@ struct ReduceArgs {
   int32_t* counts;      // MODE_MEAN, nullable
   float* acc_sum;       // MODE_ACCUM: K x D running sums
   int64_t* acc_cnt;     // MODE_ACCUM: K running counts
+  int64_t strip = 0;    // column strip (reduce_strips(dt, D) of them; one launch pair per strip)
   // MODE_MEAN, optional: the fix-up also writes FlashAssign's operand
   // fragments of C_new (cluster k = centroid k % kper of problem k / kper,
   // problem fragments f_stride 16-byte slots apart, geometry cfg)
@@ -340,7 +360,8 @@ struct ReduceArgs {
   AssignCfg cfg{};
 };
 
-int64_t reduce_dc(int dt, int64_t D);   // padded row length of a carry piece
+int64_t reduce_dc(int dt, int64_t D);   // padded length of a carry piece (one column strip)
+int64_t reduce_strips(int dt, int64_t D);  // column strips of a row
 int64_t reduce_tpb(int dt, int64_t D);  // tiles per segment-reduce workgroup
 int64_t reduce_tile(int dt, int64_t D, int64_t N);         // sorted positions per segment tile for N positions
 int64_t reduce_carry_tiles(int dt, int64_t D, int64_t N);  // most segment tiles of any N' <= N positions

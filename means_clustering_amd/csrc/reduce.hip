@@ -54,20 +54,30 @@ int64_t reduce_carry_tiles(int dt, int64_t D, int64_t N) {
   return coarse > most_fine ? coarse : most_fine;
 }
 
+// A carry piece holds one column strip of a row: G lanes x 16 bytes (rows
+// longer than 64 such pieces are reduced strip by strip, see reduce_strips).
 int64_t reduce_dc(int dt, int64_t D) {
   const int64_t epl = dt == DT_F32 ? 4 : 8;
-  const int64_t nch = (D + epl - 1) / epl;
-  int64_t g = 1;
-  while (g < nch && g < 64) g <<= 1;
-  const int64_t cpl = (nch + g - 1) / g;
-  return g * cpl * epl;
+  return reduce_lanes(dt, D) * epl;
+}
+
+// Column strips of the segmented reduction: rows of at most 64 16-byte pieces
+// (512 16-bit / 256 fp32 values) are one strip; longer rows are cut into
+// strips of that width, each reduced by its own segmented-reduction and
+// fix-up launches over the same sorted order (the sorted ids and indices are
+// re-read per strip, a small fraction of the row bytes).
+int64_t reduce_strips(int dt, int64_t D) {
+  const int64_t w = reduce_dc(dt, D);
+  return (D + w - 1) / w;
 }
 
 struct SegParams {
-  const uint8_t* X;
+  const uint8_t* X;  // this strip's first column of row 0
   int dt;
   int64_t N;
-  int D;
+  int D;             // columns of this strip
+  int64_t ldx;       // row stride of X and of the centroid arrays, in elements (the full D)
+  bool first_strip;  // counts are added to running totals by the first strip only
   int64_t K;
   bool vec_ok;
   const int32_t* keys;
@@ -112,20 +122,20 @@ __device__ __forceinline__ void flush_piece(const SegParams& P, int64_t tile, in
         for (int x = 0; x < EPL; ++x) {
           const int c = c0 + x;
           if (c < P.D) {
-            const int64_t o = (int64_t)k * P.D + c;
+            const int64_t o = (int64_t)k * P.ldx + c;
             P.C_new[o] = cnt > 0 ? acc[q][x] / fcnt : P.C_prev[o];
           }
         }
       }
     } else {
-      if (j == 0) P.acc_cnt[k] += cnt;
+      if (j == 0 && P.first_strip) P.acc_cnt[k] += cnt;
 #pragma unroll
       for (int q = 0; q < CPL; ++q) {
         const int c0 = (j + q * G) * EPL;
 #pragma unroll
         for (int x = 0; x < EPL; ++x) {
           const int c = c0 + x;
-          if (c < P.D) P.acc_sum[(int64_t)k * P.D + c] += acc[q][x];
+          if (c < P.D) P.acc_sum[(int64_t)k * P.ldx + c] += acc[q][x];
         }
       }
     }
@@ -229,10 +239,10 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
             if constexpr (VEC) {  // whole 16-byte chunks: one unconditional load, masked after
               const int64_t rr = ok[u] ? row : 0;
               const int cc = c0 < P.D ? c0 : 0;
-              const u32x4_r w = *reinterpret_cast<const u32x4_r*>(P.X + ((size_t)rr * (size_t)P.D + (size_t)cc) * ES);
+              const u32x4_r w = *reinterpret_cast<const u32x4_r*>(P.X + ((size_t)rr * (size_t)P.ldx + (size_t)cc) * ES);
               xr[u][q] = (ok[u] && c0 < P.D) ? w : u32x4_r{0u, 0u, 0u, 0u};
             } else {
-              xr[u][q] = ok[u] ? load_chunk<ES>(P.X, row, P.D, c0, false) : u32x4_r{0u, 0u, 0u, 0u};
+              xr[u][q] = ok[u] ? load_chunk<ES>(P.X, row, P.D, c0, false, P.ldx) : u32x4_r{0u, 0u, 0u, 0u};
             }
           }
         }
@@ -329,7 +339,7 @@ __global__ __launch_bounds__(256) void fixup_kernel(SegParams P) {
   if (valid && s == e && P.mode == MODE_MEAN) {  // empty: keeps its centroid
     if (lane == 0 && P.counts) P.counts[k] = 0;
     if (P.C_new != P.C_prev)
-      for (int c = lane; c < P.D; c += 64) P.C_new[k * P.D + c] = P.C_prev[k * P.D + c];
+      for (int c = lane; c < P.D; c += 64) P.C_new[k * P.ldx + c] = P.C_prev[k * P.ldx + c];
   }
   float* row = rows[wave];
   if (cut) {
@@ -397,7 +407,7 @@ __global__ __launch_bounds__(256) void fixup_kernel(SegParams P) {
         for (int x = 0; x < 4; ++x) {
           const int c = (c0 + cl * lpr) * 4 + x;
           if (c >= P.D) continue;
-          const int64_t o = k * P.D + c;
+          const int64_t o = k * P.ldx + c;
           if (P.mode == MODE_MEAN) {
             const float m = n > 0 ? a[cl][x] / (float)n : P.C_prev[o];
             P.C_new[o] = m;
@@ -409,7 +419,7 @@ __global__ __launch_bounds__(256) void fixup_kernel(SegParams P) {
       if (c0 == 0) {
         if (P.mode == MODE_MEAN) {
           if (P.counts) P.counts[k] = n;
-        } else {
+        } else if (P.first_strip) {
           P.acc_cnt[k] += n;
         }
       }
@@ -420,7 +430,7 @@ __global__ __launch_bounds__(256) void fixup_kernel(SegParams P) {
   // reduction (finished clusters) or the empty rule (C_prev) left it.
   if (valid && !cut) {
     const float* src = s == e ? P.C_prev : P.C_new;
-    for (int c = lane; c < P.D; c += 64) row[c] = src[k * P.D + c];
+    for (int c = lane; c < P.D; c += 64) row[c] = src[k * P.ldx + c];
   }
   __syncthreads();
   if (valid) {
@@ -431,12 +441,16 @@ __global__ __launch_bounds__(256) void fixup_kernel(SegParams P) {
 
 static SegParams make_params(const ReduceArgs& a) {
   SegParams P;
-  P.X = (const uint8_t*)a.X;
+  const int es = dtype_size(a.dt);
+  const int64_t sw = reduce_dc(a.dt, a.D);  // strip width in columns
+  const int64_t c0 = a.strip * sw;          // first column of this strip
+  P.X = (const uint8_t*)a.X + c0 * es;
   P.dt = a.dt;
   P.N = a.N;
-  P.D = (int)a.D;
+  P.D = (int)(a.D - c0 < sw ? a.D - c0 : sw);
+  P.ldx = a.D;
+  P.first_strip = a.strip == 0;
   P.K = a.K;
-  const int es = dtype_size(a.dt);
   P.vec_ok = (((uintptr_t)a.X) % 16 == 0) && ((a.D * es) % 16 == 0);
   P.keys = a.keys;
   P.vals = a.vals;
@@ -447,16 +461,16 @@ static SegParams make_params(const ReduceArgs& a) {
   P.group_cnt = a.group_cnt;
   P.tpb = (int)reduce_tpb(a.dt, a.D);
   P.tile = (int)reduce_tile(a.dt, a.D, a.N);
-  P.frag = a.mode == MODE_MEAN ? (uint32_t*)a.frag : nullptr;
+  P.frag = a.mode == MODE_MEAN && reduce_strips(a.dt, a.D) == 1 ? (uint32_t*)a.frag : nullptr;
   P.f_stride = a.f_stride;
   P.kper = a.kper > 0 ? a.kper : a.K;
   P.cfg = a.cfg;
   P.Dc = (int)reduce_dc(a.dt, a.D);
   P.mode = a.mode;
-  P.C_prev = a.C_prev;
-  P.C_new = a.C_new;
+  P.C_prev = a.C_prev ? a.C_prev + c0 : nullptr;
+  P.C_new = a.C_new ? a.C_new + c0 : nullptr;
   P.counts = a.counts;
-  P.acc_sum = a.acc_sum;
+  P.acc_sum = a.acc_sum ? a.acc_sum + c0 : nullptr;
   P.acc_cnt = a.acc_cnt;
   return P;
 }
@@ -479,15 +493,12 @@ static void launch_seg(const SegParams& P, hipStream_t s) {
 
 hipError_t launch_segment_reduce(const ReduceArgs& a, hipStream_t stream) {
   if (a.N == 0) return hipSuccess;
+  if (a.strip < 0 || a.strip >= reduce_strips(a.dt, a.D)) return hipErrorInvalidValue;
   const SegParams P = make_params(a);
   const int es = dtype_size(a.dt);
-  const int epl = 16 / es;
-  const int64_t nch = (a.D + epl - 1) / epl;
-  int g = 1;
-  while (g < nch && g < 64) g <<= 1;
-  const int cpl = (int)((nch + g - 1) / g);
-  // D <= 512 (16-bit) or 256 (fp32) gives at most 64 chunks: cpl == 1 always.
-  if (cpl != 1) return hipErrorInvalidValue;
+  // every strip of a row takes the lane-group width of a whole strip (a narrower last strip leaves lanes idle),
+  // so all strips share one tile length and carry layout
+  const int g = (int)reduce_lanes(a.dt, a.D);
 #define KM_SEG(ES_, G_) \
   if (es == ES_ && g == G_) { launch_seg<ES_, 1, G_>(P, stream); return hipGetLastError(); }
   KM_SEG(2, 1) KM_SEG(2, 2) KM_SEG(2, 4) KM_SEG(2, 8) KM_SEG(2, 16) KM_SEG(2, 32) KM_SEG(2, 64)

@@ -31,13 +31,15 @@ __device__ __forceinline__ void widen(const u32x4_r& v, int dt, float* out) {
   }
 }
 
-// 16 bytes of row `row`, elements [c0, c0 + EPL), zero beyond D.
+// 16 bytes of row `row`, elements [c0, c0 + EPL), zero beyond D; rows are
+// `ld` elements apart (ld = 0: D).
 template <int ES>
-__device__ __forceinline__ u32x4_r load_chunk(const uint8_t* __restrict__ X, int64_t row, int D, int c0, bool vec_ok) {
+__device__ __forceinline__ u32x4_r load_chunk(const uint8_t* __restrict__ X, int64_t row, int D, int c0, bool vec_ok,
+                                              int64_t ld = 0) {
   constexpr int EPL = 16 / ES;
   u32x4_r v = {0u, 0u, 0u, 0u};
   if (c0 >= D) return v;
-  const uint8_t* r = X + (size_t)row * (size_t)D * ES;
+  const uint8_t* r = X + (size_t)row * (size_t)(ld ? ld : D) * ES;
   if (vec_ok && c0 + EPL <= D) return *reinterpret_cast<const u32x4_r*>(r + (size_t)c0 * ES);
   uint32_t w[4] = {0, 0, 0, 0};
   if (ES == 4) {

@@ -447,7 +447,7 @@ bool small_owner_fits(int64_t B, int64_t N, int64_t K) {
 hipError_t launch_small_update(const SmallArgs& a, hipStream_t stream) {
   if (a.N == 0 || a.B == 0) return hipSuccess;
   const bool owner = small_owner_fits(a.B, a.N, a.K);
-  if (a.K < 1 || (a.K > kSmallMaxK && !owner) || a.D < 1 || a.D > kMaxD16) return hipErrorInvalidValue;
+  if (a.K < 1 || (a.K > kSmallMaxK && !owner) || a.D < 1 || deep_rows(a.dt, a.D)) return hipErrorInvalidValue;
   SmallParams S;
   S.X = (const uint8_t*)a.X;
   S.dt = a.dt;

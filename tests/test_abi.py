@@ -34,8 +34,12 @@ def test_workspace_bytes(L):
     # invalid sizes give 0
     assert f(km.KM_OP_ASSIGN, -1, 128, 64, km.KM_BF16, 0) == 0
     assert f(km.KM_OP_ASSIGN, 10, 0, 64, km.KM_BF16, 0) == 0
-    assert f(km.KM_OP_ASSIGN, 10, 513, 64, km.KM_BF16, 0) == 0
-    assert f(km.KM_OP_ASSIGN, 10, 257, 64, km.KM_F32, 0) == 0
+    # any D >= 1: rows beyond the register-resident width (512 16-bit / 256 fp32 values) take the depth-tiled path
+    assert f(km.KM_OP_ASSIGN, 10, 513, 64, km.KM_BF16, 0) > 0
+    assert f(km.KM_OP_FIT, 10, 257, 64, km.KM_F32, 0) > 0
+    assert f(km.KM_OP_FIT, 1000, 4096, 1000, km.KM_BF16, 0) > 0
+    assert f(km.KM_OP_FIT_STREAMED, 10**6, 1000, 64, km.KM_F32, 1 << 16) > 0
+    assert f(km.KM_OP_ASSIGN, 10, (1 << 24) + 1, 4, km.KM_BF16, 0) == 0  # beyond 32-bit index arithmetic
     assert f(km.KM_OP_ASSIGN, 10, 8, 0, km.KM_F32, 0) == 0
     assert f(km.KM_OP_ASSIGN, 10, 8, 4, 7, 0) == 0
     assert f(km.KM_OP_FIT_STREAMED, 10, 8, 4, km.KM_F32, 0) == 0
@@ -64,7 +68,7 @@ def test_assign_validation(L):
     }
     for what, code in codes.items():
         assert code == 1, (what, code, _last(L))
-    assert a(FAKE, km.KM_BF16, 10, 600, FAKE, 4, FAKE, None, WS, 1 << 30, None) == 2  # unsupported D
+    assert a(FAKE, km.KM_BF16, 10, (1 << 24) + 1, FAKE, 4, FAKE, None, WS, 1 << 30, None) == 2  # D beyond 2^24
     assert "exceeds" in _last(L)
     assert a(FAKE, km.KM_BF16, 10, 8, FAKE, 4, FAKE, None, None, 0, None) == 3          # no workspace
     assert a(FAKE, km.KM_BF16, 10, 8, FAKE, 4, FAKE, None, WS, 16, None) == 3           # too small
@@ -98,7 +102,8 @@ def test_batched_fit_validation(L):
     assert wb(0, 10, 8, 4, km.KM_F32) == 0
     assert wb(1 << 20, 1 << 12, 8, 4, km.KM_F32) == 0      # B*N = 2^32
     assert wb(1 << 16, 10, 8, 1 << 16, km.KM_F32) == 0     # B*K = 2^32
-    assert wb(4, 10, 300, 4, km.KM_F32) == 0               # D > 256 for fp32
+    assert wb(4, 10, 300, 4, km.KM_F32) > 0                # deep fp32 rows (depth-tiled path)
+    assert wb(4, 10, (1 << 24) + 1, 4, km.KM_F32) == 0     # D beyond 2^24
     f = L.kmeans_fit_batched
     assert f(FAKE, km.KM_F32, 0, 10, 8, 4, FAKE, 1, None, None, None, WS, 1 << 30, None) == 1        # B = 0
     assert f(FAKE, km.KM_F32, 1 << 20, 1 << 12, 8, 4, FAKE, 1, None, None, None, WS, 1 << 30, None) == 2

@@ -45,8 +45,6 @@ SHAPES = [(1, 1, 1), (37, 3, 2), (1000, 32, 64), (4133, 128, 1000), (2049, 64, 6
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_assign_random(shape, xdtype):
     N, D, K = shape
-    if xdtype == "f32" and D > 256:
-        pytest.skip("fp32 supports D <= 256")
     X, C = _data(N, D, K, xdtype, seed=N * 131 + D * 7 + K)
     _run(X, C, f"random {shape} {xdtype}")
 

@@ -35,8 +35,6 @@ def _x(N, D, xdtype, seed):
                          ids=lambda s: "x".join(map(str, s)))
 def test_update_random(shape, xdtype):
     N, D, K = shape
-    if xdtype == "f32" and D > 256:
-        pytest.skip("fp32 supports D <= 256")
     X = _x(N, D, xdtype, seed=N + D + K)
     rng = np.random.default_rng(N * 3 + K)
     a = rng.integers(0, K, N)
@@ -119,8 +117,6 @@ def test_update_small_codebook(shape, xdtype):
     """K <= 64: the on-chip path (one workgroup per cluster for N <= 16384, else one chunk of 512 or 2048
     points per workgroup with the chunk sums added in order)."""
     N, D, K = shape
-    if xdtype == "f32" and D > 256:
-        pytest.skip("fp32 supports D <= 256")
     X = _x(N, D, xdtype, seed=N + 7 * D + K)
     rng = np.random.default_rng(N + K)
     w = rng.random(K) ** 3  # uneven cluster sizes, some clusters empty
@@ -141,8 +137,6 @@ def test_update_one_workgroup_per_cluster(shape, xdtype):
     each cluster's points and sums them (no sort); one point more (N = 16385) or one cluster more (K = 2049)
     than that takes the sorted path."""
     N, D, K = shape
-    if xdtype == "f32" and D > 256:
-        pytest.skip("fp32 supports D <= 256")
     X = _x(N, D, xdtype, seed=N + 3 * D + K)
     rng = np.random.default_rng(N + 2 * K)
     w = rng.random(K) ** 4  # uneven cluster sizes, many clusters empty
