@@ -229,6 +229,25 @@ km_status kmeans_fit_batched(const void* X, km_dtype dt, int64_t B, int64_t N, i
                              int32_t iters, int32_t* assign, int32_t* counts, double* objective, void* ws,
                              size_t ws_bytes, void* stream);
 
+/*
+ * kmeans_fit_noalloc -- kmeans_fit for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation, arguments and results as
+ * kmeans_fit (bit for bit), with no workspace argument.  Its scratch space is
+ * a fixed device array of KMEANS_NOALLOC_SCRATCH_BYTES inside the library
+ * (one per GPU, held from library load until the process ends); the call
+ * never allocates or frees memory.  Shapes whose kmeans_fit workspace
+ * (kmeans_workspace_bytes(KM_OP_FIT, ...)) exceeds that size are rejected
+ * with KM_ERR_UNSUPPORTED before any HIP call.  `stream` must belong to the
+ * current device (else KM_ERR_INVALID_VALUE).  All calls on one GPU share the
+ * array: calls that may overlap on one GPU (other streams, other threads)
+ * race and must be serialised by the caller; calls in order on one stream
+ * are safe.
+ */
+#define KMEANS_NOALLOC_SCRATCH_BYTES (64u << 20)
+km_status kmeans_fit_noalloc(const void* X, km_dtype dt, int64_t N, int64_t D, int64_t K, float* C, int32_t iters,
+                             int32_t* assign, int32_t* counts, double* objective, void* stream);
+
 /* Short constant description of a status code. */
 const char* kmeans_status_string(km_status s);
 

@@ -59,6 +59,7 @@ def _bind(lib):
                                         vp, vp, sz]),
         "kmeans_workspace_bytes_batched": (sz, [i64, i64, i64, i64, c_int]),
         "kmeans_fit_batched": (c_int, [vp, c_int, i64, i64, i64, i64, vp, ctypes.c_int32, vp, vp, vp, vp, sz, vp]),
+        "kmeans_fit_noalloc": (c_int, [vp, c_int, i64, i64, i64, vp, ctypes.c_int32, vp, vp, vp, vp]),
         "kmeans_status_string": (ctypes.c_char_p, [c_int]),
         "kmeans_last_error": (ctypes.c_char_p, []),
         "kmeans_timing_enable": (c_int, [c_int]),
@@ -215,6 +216,24 @@ def fit(X: torch.Tensor, C0: torch.Tensor, iters: int, objective: bool = False, 
     _check(lib().kmeans_fit(_ptr(X), _dtype(X), N, D, K, _ptr(C), int(iters), _ptr(a), _ptr(counts), _ptr(obj),
                             _ptr(w), w.numel(), ctypes.c_void_p(_stream(X.device))))
     return C, a, counts, (obj[:iters] if obj is not None else None)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # KMEANS_NOALLOC_SCRATCH_BYTES of include/kmeans.h
+
+
+def fit_noalloc(X: torch.Tensor, C: torch.Tensor, iters: int, assign_out: torch.Tensor | None = None,
+                counts_out: torch.Tensor | None = None, objective_out: torch.Tensor | None = None):
+    """kmeans_fit_noalloc: Lloyd iterations in place on C with the library's fixed scratch (no workspace).
+
+    Every tensor is the caller's (outputs may be None); the call itself allocates nothing.  Shapes whose
+    workspace exceeds NOALLOC_SCRATCH_BYTES raise KMeansError (KM_ERR_UNSUPPORTED).
+    """
+    _need(X, C)
+    N, D = X.shape
+    K = C.shape[0]
+    _check(lib().kmeans_fit_noalloc(_ptr(X), _dtype(X), N, D, K, _ptr(C), int(iters), _ptr(assign_out),
+                                    _ptr(counts_out), _ptr(objective_out), ctypes.c_void_p(_stream(X.device))))
+    return C
 
 
 def fit_batched(X: torch.Tensor, C0: torch.Tensor, iters: int, objective: bool = False, inplace: bool = False,

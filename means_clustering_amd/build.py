@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_NAME = "libkmeans_amd.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["csrc/flash_assign.hip", "csrc/sort.hip", "csrc/reduce.hip", "csrc/small_k.hip", "csrc/api.cpp"]
+SOURCES = ["csrc/flash_assign.hip", "csrc/sort.hip", "csrc/reduce.hip", "csrc/small_k.hip", "csrc/api.cpp",
+           "csrc/noalloc.hip"]
 # peak probes for the benchmark's roofline denominators, and the ablation
 # baselines (libraries of their own, not part of libkmeans_amd.so)
 EXTRA_LIBS = [("csrc/peaks.hip", os.path.join(HERE, "libkm_peaks.so"), []),

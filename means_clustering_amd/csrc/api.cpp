@@ -523,6 +523,23 @@ static km_status run_update(const void* X, km_dtype dt, int64_t N, int64_t D, co
 
 // ------------------------------------------------------------ entry points --
 
+namespace km {
+// The argument checks of kmeans_fit other than the workspace (shared with kmeans_fit_noalloc).
+km_status fit_args_check(const void* X, km_dtype dt, int64_t N, int64_t D, int64_t K, const float* C, int32_t iters,
+                         const int32_t* assign, const int32_t* counts, const double* objective) {
+  km_status st = check_sizes(N, D, K, dt, true);
+  if (st != KM_OK) return st;
+  if (iters < 0) return fail(KM_ERR_INVALID_VALUE, "iters must be >= 0");
+  if (!C || (N > 0 && !X)) return fail(KM_ERR_INVALID_VALUE, "X and C must be non-NULL");
+  if (!aligned(X, dt == KM_F32 ? 4 : 2) || !aligned(C, 4) || !aligned(assign, 4) || !aligned(counts, 4) ||
+      !aligned(objective, 8))
+    return fail(KM_ERR_INVALID_VALUE, "misaligned pointer");
+  return KM_OK;
+}
+
+km_status fail_with(km_status s, const char* msg) { return fail(s, msg); }
+}  // namespace km
+
 extern "C" {
 
 size_t kmeans_workspace_bytes(km_op op, int64_t N, int64_t D, int64_t K, km_dtype dt, int64_t chunk_rows) {
@@ -597,13 +614,8 @@ km_status kmeans_update(const void* X, km_dtype dt, int64_t N, int64_t D, const 
 
 km_status kmeans_fit(const void* X, km_dtype dt, int64_t N, int64_t D, int64_t K, float* C, int32_t iters,
                      int32_t* assign, int32_t* counts, double* objective, void* ws, size_t ws_bytes, void* stream) {
-  km_status st = check_sizes(N, D, K, dt, true);
+  km_status st = km::fit_args_check(X, dt, N, D, K, C, iters, assign, counts, objective);
   if (st != KM_OK) return st;
-  if (iters < 0) return fail(KM_ERR_INVALID_VALUE, "iters must be >= 0");
-  if (!C || (N > 0 && !X)) return fail(KM_ERR_INVALID_VALUE, "X and C must be non-NULL");
-  if (!aligned(X, dt == KM_F32 ? 4 : 2) || !aligned(C, 4) || !aligned(assign, 4) || !aligned(counts, 4) ||
-      !aligned(objective, 8))
-    return fail(KM_ERR_INVALID_VALUE, "misaligned pointer");
   st = check_ws(ws, ws_bytes, workspace_bytes_impl(KM_OP_FIT, N, D, K, dt, 0));
   if (st != KM_OK) return st;
   if (iters == 0) return KM_OK;

@@ -17,7 +17,7 @@ def test_exports_every_declared_function(L):
     assert "kmeans_assign" in declared and "kmeans_fit_streamed" in declared
     for name in declared:
         assert hasattr(L, name), name
-    assert len(declared) == 13
+    assert len(declared) == 14
 
 
 def test_status_strings(L):
@@ -147,3 +147,18 @@ def test_ablation_library_exports_and_validates():
     assert A.kmeans_abl_assign_materialized(FAKE, 1, 10, 8, FAKE, 4, FAKE, FAKE, 8, None) == -1  # scratch too small
     assert A.kmeans_abl_update_atomic(FAKE, 1, 10, 8, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == -1  # alias
 
+
+def test_fit_noalloc_validation(L):
+    """The no-allocation fit rejects bad arguments and shapes beyond its fixed scratch before any HIP call."""
+    f = L.kmeans_fit_noalloc
+    assert f(FAKE, 9, 10, 8, 4, FAKE, 1, None, None, None, None) == 1  # bad dtype
+    assert f(FAKE, km.KM_BF16, 10, 8, 4, None, 1, None, None, None, None) == 1  # null C
+    assert f(FAKE, km.KM_BF16, 10, 8, 4, FAKE, -1, None, None, None, None) == 1  # iters < 0
+    assert f(FAKE, km.KM_BF16, 10, 8, 4, FAKE, 0, None, None, None, None) == 0  # nothing to do
+    need = L.kmeans_workspace_bytes(km.KM_OP_FIT, 1 << 23, 64, 4096, km.KM_BF16, 0)
+    assert need > km.NOALLOC_SCRATCH_BYTES
+    assert f(FAKE, km.KM_BF16, 1 << 23, 64, 4096, FAKE, 1, None, None, None, None) == 2
+    assert "scratch" in _last(L)
+    # the largest shapes it serves: the 16,384 x 32 fp32 and 2^20 x 128 bf16 workloads' fits fit in the scratch
+    assert L.kmeans_workspace_bytes(km.KM_OP_FIT, 16384, 32, 64, km.KM_F32, 0) <= km.NOALLOC_SCRATCH_BYTES
+    assert L.kmeans_workspace_bytes(km.KM_OP_FIT, 1 << 20, 128, 1024, km.KM_BF16, 0) <= km.NOALLOC_SCRATCH_BYTES
