@@ -65,9 +65,18 @@
 extern "C" {
 #endif
 
-typedef enum km_dtype { KM_F32 = 0, KM_BF16 = 1, KM_F16 = 2 } km_dtype;
+/* The enumerations are plain ints on the C side (a C caller may pass any int);
+ * the C++ implementation gives them int as their fixed underlying type, so an
+ * out-of-range value from such a caller is a valid value it can reject. */
+#ifdef __cplusplus
+#define KM_ENUM_INT : int
+#else
+#define KM_ENUM_INT
+#endif
 
-typedef enum km_status {
+typedef enum km_dtype KM_ENUM_INT { KM_F32 = 0, KM_BF16 = 1, KM_F16 = 2 } km_dtype;
+
+typedef enum km_status KM_ENUM_INT {
   KM_OK = 0,
   KM_ERR_INVALID_VALUE = 1, /* null pointer, size out of range, misalignment, bad dtype */
   KM_ERR_UNSUPPORTED = 2,   /* valid but beyond a size limit (D > 2^24, K*D, B*N; no-alloc scratch) */
@@ -75,7 +84,7 @@ typedef enum km_status {
   KM_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
 } km_status;
 
-typedef enum km_op {
+typedef enum km_op KM_ENUM_INT {
   KM_OP_ASSIGN = 0,
   KM_OP_UPDATE = 1,
   KM_OP_FIT = 2,

@@ -1,6 +1,10 @@
 """The C-ABI library on the CPU: it loads, exports every declared symbol, and
 rejects bad arguments synchronously (before any HIP call), so no GPU is needed."""
 import ctypes
+import glob
+import os
+import subprocess
+import sys
 
 import pytest
 
@@ -148,6 +152,7 @@ def test_ablation_library_exports_and_validates():
     assert A.kmeans_abl_update_atomic(FAKE, 1, 10, 8, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == -1  # alias
 
 
+
 def test_fit_noalloc_validation(L):
     """The no-allocation fit rejects bad arguments and shapes beyond its fixed scratch before any HIP call."""
     f = L.kmeans_fit_noalloc
@@ -162,3 +167,57 @@ def test_fit_noalloc_validation(L):
     # the largest shapes it serves: the 16,384 x 32 fp32 and 2^20 x 128 bf16 workloads' fits fit in the scratch
     assert L.kmeans_workspace_bytes(km.KM_OP_FIT, 16384, 32, 64, km.KM_F32, 0) <= km.NOALLOC_SCRATCH_BYTES
     assert L.kmeans_workspace_bytes(km.KM_OP_FIT, 1 << 20, 128, 1024, km.KM_BF16, 0) <= km.NOALLOC_SCRATCH_BYTES
+
+
+def test_workspace_bytes_sweep(L):
+    """Workspace carving over a grid of shapes (every path: small codebooks, sorted, split sweeps, deep rows,
+    batched, streamed): sizes are positive, 256-byte multiples and grow with N."""
+    for dt in (km.KM_F32, km.KM_BF16, km.KM_F16):
+        for D in (1, 3, 16, 64, 128, 255, 256, 257, 512, 513, 1000, 4096):
+            for K in (1, 2, 63, 64, 65, 512, 2048, 2049, 8192, 8193, 65536):
+                prev = 0
+                for N in (0, 1, 100, 16384, 16385, 1 << 20):
+                    for op in (km.KM_OP_ASSIGN, km.KM_OP_UPDATE, km.KM_OP_FIT, km.KM_OP_SORT):
+                        b = L.kmeans_workspace_bytes(op, N, D, K, dt, 0)
+                        assert b > 0 and b % 256 == 0, (op, N, D, K, dt)
+                    b = L.kmeans_workspace_bytes(km.KM_OP_FIT, N, D, K, dt, 0)
+                    assert b >= prev
+                    prev = b
+                    assert L.kmeans_workspace_bytes(km.KM_OP_FIT_STREAMED, N, D, K, dt, 5000) > 0
+                assert L.kmeans_workspace_bytes_batched(3, 1000, D, K, dt) > 0
+
+
+def test_abi_checks_under_asan_ubsan(tmp_path):
+    """The host side of the library (argument validation, workspace carving, the no-allocation entry point's
+    checks: api.cpp and noalloc.hip) rebuilt with AddressSanitizer + UndefinedBehaviorSanitizer on the host
+    (device code unchanged), linked with the kernels' objects of the regular build, and this file's tests run
+    against it in a child process with the sanitizer runtime preloaded."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    objs = [os.path.join(root, "_build", f + ".o") for f in ("flash_assign.hip", "sort.hip", "reduce.hip",
+                                                             "small_k.hip")]
+    if not all(os.path.exists(o) for o in objs):
+        pytest.skip("needs the kernel objects of the regular build (__graft_entry__.build())")
+    rts = glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")
+    if not rts:
+        pytest.skip("clang AddressSanitizer runtime not found")
+    hipcc = "/opt/rocm/bin/hipcc"
+    host_san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                "-Xarch_host", "-fno-omit-frame-pointer"]
+    mine = []
+    for src in ("api.cpp", "noalloc.hip"):
+        o = str(tmp_path / (src + ".o"))
+        subprocess.run([hipcc, "-std=c++17", "-O1", "-g", "-fPIC", "--offload-arch=gfx950", *host_san,
+                        "-I", os.path.join(root, "include"), "-c",
+                        os.path.join(root, "means_clustering_amd", "csrc", src), "-o", o],
+                       check=True, capture_output=True)
+        mine.append(o)
+    lib = str(tmp_path / "libkmeans_amd_asan.so")
+    subprocess.run([hipcc, "-shared", "-fPIC", "--offload-arch=gfx950", *host_san, "-shared-libasan", *mine, *objs,
+                    "-o", lib], check=True, capture_output=True)
+    old = os.environ.get("LD_PRELOAD", "")
+    env = dict(os.environ, LD_PRELOAD=rts[0] + (":" + old if old else ""), ASAN_OPTIONS="detect_leaks=0",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    r = subprocess.run([sys.executable, os.path.join(root, "tests", "native", "run_with_lib.py"), lib,
+                        "-s", "-k", "not under_asan"], env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-3000:]
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr[-3000:]
