@@ -89,13 +89,18 @@ typedef enum km_op KM_ENUM_INT {
   KM_OP_UPDATE = 1,
   KM_OP_FIT = 2,
   KM_OP_FIT_STREAMED = 3,
-  KM_OP_SORT = 4
+  KM_OP_SORT = 4,
+  KM_OP_FIT_STREAMED_WARM = 5  /* kmeans_fit_streamed with room for every chunk's warm-start order */
 } km_op;
 
 /*
  * Workspace bytes needed by entry point `op` for the given sizes (N is the
- * number of points; for KM_OP_FIT_STREAMED `chunk_rows` is the chunk size and
- * N may be any value).  Returns 0 if the arguments are invalid.
+ * number of points; for KM_OP_FIT_STREAMED `chunk_rows` is the chunk size).
+ * KM_OP_FIT_STREAMED_WARM: the streamed fit's workspace plus 8 bytes per row
+ * of X, where each chunk keeps its sorted order from one iteration to the
+ * next so that later iterations assign it warm (faster, same results bit for
+ * bit); kmeans_fit_streamed uses that room whenever ws_bytes holds it.
+ * Returns 0 if the arguments are invalid.
  */
 size_t kmeans_workspace_bytes(km_op op, int64_t N, int64_t D, int64_t K, km_dtype dt, int64_t chunk_rows);
 

@@ -32,7 +32,7 @@ LIB_PATH = os.path.join(HERE, "libkmeans_amd.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "kmeans.h")
 
 KM_F32, KM_BF16, KM_F16 = 0, 1, 2
-KM_OP_ASSIGN, KM_OP_UPDATE, KM_OP_FIT, KM_OP_FIT_STREAMED, KM_OP_SORT = 0, 1, 2, 3, 4
+KM_OP_ASSIGN, KM_OP_UPDATE, KM_OP_FIT, KM_OP_FIT_STREAMED, KM_OP_SORT, KM_OP_FIT_STREAMED_WARM = 0, 1, 2, 3, 4, 5
 STATUS = {0: "KM_OK", 1: "KM_ERR_INVALID_VALUE", 2: "KM_ERR_UNSUPPORTED", 3: "KM_ERR_WORKSPACE", 4: "KM_ERR_HIP"}
 _DT = {torch.float32: KM_F32, torch.bfloat16: KM_BF16, torch.float16: KM_F16}
 
@@ -289,7 +289,7 @@ def staging_buffer(nbytes: int = 4 * STAGE_SLOT_BYTES) -> torch.Tensor:
 
 def fit_streamed(X_host: torch.Tensor, C0: torch.Tensor, iters: int, chunk_rows: int, copy_stream=None,
                  want_assign: bool = True, objective: bool = False, ws: Workspace | None = None,
-                 stage: torch.Tensor | None = None):
+                 stage: torch.Tensor | None = None, warm_start: bool = True):
     """Lloyd iterations with X in host memory, streamed in chunks.
 
     X_host may be pinned (uploaded directly) or pageable (uploaded through the
@@ -314,11 +314,15 @@ def fit_streamed(X_host: torch.Tensor, C0: torch.Tensor, iters: int, chunk_rows:
     a = torch.empty(N, dtype=torch.int32, pin_memory=True) if want_assign else None
     counts = torch.empty(K, dtype=torch.int32, device=dev)
     obj = torch.empty(max(iters, 1), dtype=torch.float64, device=dev) if objective else None
-    nb = workspace_bytes(KM_OP_FIT_STREAMED, N, D, K, X_host.dtype, chunk_rows)
+    # warm_start: room for every chunk's order (8 bytes a row of device memory), so iterations after the first
+    # assign each chunk warm; without it the workspace holds two chunk buffers and one chunk's scratch only
+    nb = workspace_bytes(KM_OP_FIT_STREAMED_WARM if warm_start else KM_OP_FIT_STREAMED, N, D, K, X_host.dtype,
+                         chunk_rows)
     w = _ws(ws, nb, dev)
     cs = copy_stream if copy_stream is not None else torch.cuda.Stream(dev)
+    # (the size asked for, not the buffer's: a larger reused buffer must not turn the warm start on)
     _check(lib().kmeans_fit_streamed(_ptr(X_host), _dtype(X_host), N, D, K, _ptr(C), int(iters), int(chunk_rows),
-                                     _ptr(a), _ptr(counts), _ptr(obj), _ptr(w), w.numel(),
+                                     _ptr(a), _ptr(counts), _ptr(obj), _ptr(w), nb,
                                      ctypes.c_void_p(_stream(dev)), ctypes.c_void_p(cs.cuda_stream),
                                      _ptr(stage), 0 if stage is None else stage.numel()))
     _hold_until_done(dev, X_host, stage, a)

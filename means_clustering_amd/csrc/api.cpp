@@ -233,6 +233,20 @@ struct StreamBufs {
   int64_t* acc_cnt;
 };
 
+// The streamed fit's warm-start order: every chunk's sorted ids and point order from the last iteration,
+// kept for the next (two int32 per row of X).
+struct WarmOrder {
+  int32_t* keys;
+  int32_t* vals;
+};
+static WarmOrder carve_warm_order(Carve& c, int64_t N) {
+  const size_t n = (size_t)(N > 0 ? N : 1);
+  WarmOrder w;
+  w.keys = c.take<int32_t>(n);
+  w.vals = c.take<int32_t>(n);
+  return w;
+}
+
 static StreamBufs carve_streamed(Carve& c, int64_t rows, int64_t D, int64_t K, km_dtype dt) {
   StreamBufs s;
   s.f = carve_fit(c, rows, D, K, dt, /*split=*/false);
@@ -296,9 +310,11 @@ static size_t workspace_bytes_impl(km_op op, int64_t N, int64_t D, int64_t K, km
     case KM_OP_SORT: carve_sort(c, sort_geom(N, K)); break;
     case KM_OP_UPDATE: carve_update(c, sort_geom(N, K), D, dt); break;
     case KM_OP_FIT: carve_fit(c, N, D, K, dt); break;
-    case KM_OP_FIT_STREAMED: {
+    case KM_OP_FIT_STREAMED:
+    case KM_OP_FIT_STREAMED_WARM: {
       const int64_t rows = chunk_rows < N ? chunk_rows : (N > 0 ? N : 1);
       carve_streamed(c, rows, D, K, dt);
+      if (op == KM_OP_FIT_STREAMED_WARM) carve_warm_order(c, N);
       break;
     }
     default: return 0;
@@ -356,10 +372,11 @@ static km_status run_assign(const void* X, km_dtype dt, int64_t N, int64_t D, co
 
 // Argsort (+ cluster offsets when `offsets`); returns the sorted keys and values (the inverse map).
 static km_status run_sort(const int32_t* assign, int64_t N, int64_t K, const SortBufs& b, int32_t* perm_out,
-                          int32_t** keys, int32_t** vals, hipStream_t s, bool offsets = true) {
+                          int32_t** keys, int32_t** vals, hipStream_t s, bool offsets = true,
+                          int32_t* keys_out = nullptr) {
   const SortGeom g = sort_geom(N, K);
-  // ping-pong through set a / set b; the last pass may write the caller's perm
-  int32_t* kf = (g.npass % 2) ? b.key_a : b.key_b;
+  // ping-pong through set a / set b; the last pass may write the caller's perm (and sorted ids)
+  int32_t* kf = keys_out ? keys_out : ((g.npass % 2) ? b.key_a : b.key_b);
   int32_t* vf = perm_out ? perm_out : ((g.npass % 2) ? b.val_a : b.val_b);
   KM_TIMED("sort", s, return launch_argsort(g, assign, b.key_a, b.val_a, b.key_b, b.val_b, kf, vf, b.counts,
                                             b.scan_part, s));
@@ -375,6 +392,8 @@ constexpr int64_t kFuseFragMaxK = 8192;  // largest codebook whose fix-up also w
 // assignment and the point order, valid until the workspace is used again;
 // NULL when the small-codebook path ran (it sorts on chip only).
 // B > 1: N points of B problems (N / B each) with K / B clusters each and ids b*(K/B) + k.
+// keep_keys/keep_vals (optional, sorted path): where the argsort writes the sorted ids and point order, so
+// they outlive the call (the streamed fit's per-chunk warm-start order).
 // frag/geom/prepped (optional): FlashAssign's fragment buffer and geometry for
 // the next assignment; *prepped tells whether this update already wrote the
 // fragments of C_new (then the next assignment skips its centroid preparation).
@@ -382,7 +401,8 @@ static km_status run_update(const void* X, km_dtype dt, int64_t N, int64_t D, co
                             const float* C_prev, float* C_new, int32_t* counts, const UpdateBufs& u, int mode,
                             float* acc_sum, int64_t* acc_cnt, hipStream_t s, const int32_t** sorted_keys = nullptr,
                             const int32_t** sorted_vals = nullptr, int64_t B = 1, void* frag = nullptr,
-                            const AssignGeom* geom = nullptr, bool* prepped = nullptr) {
+                            const AssignGeom* geom = nullptr, bool* prepped = nullptr, int32_t* keep_keys = nullptr,
+                            int32_t* keep_vals = nullptr) {
   if (sorted_keys) *sorted_keys = nullptr;
   if (sorted_vals) *sorted_vals = nullptr;
   if (prepped) *prepped = false;
@@ -411,7 +431,7 @@ static km_status run_update(const void* X, km_dtype dt, int64_t N, int64_t D, co
   }
   int32_t *keys = nullptr, *vals = nullptr;
   // the segmented reduction writes the cluster offsets itself (it sees every id change)
-  km_status st = run_sort(assign, N, K, u.s, nullptr, &keys, &vals, s, /*offsets=*/N == 0);
+  km_status st = run_sort(assign, N, K, u.s, keep_vals, &keys, &vals, s, /*offsets=*/N == 0, keep_keys);
   if (st != KM_OK) return st;
   if (sorted_keys) *sorted_keys = keys;
   if (sorted_vals) *sorted_vals = vals;
@@ -477,7 +497,7 @@ extern "C" {
 size_t kmeans_workspace_bytes(km_op op, int64_t N, int64_t D, int64_t K, km_dtype dt, int64_t chunk_rows) {
   const bool need_d = op != KM_OP_SORT;
   if (check_sizes(N, need_d ? D : 1, K, op == KM_OP_SORT ? KM_F32 : dt, need_d) != KM_OK) return 0;
-  if (op == KM_OP_FIT_STREAMED && chunk_rows < 1) return 0;
+  if ((op == KM_OP_FIT_STREAMED || op == KM_OP_FIT_STREAMED_WARM) && chunk_rows < 1) return 0;
   return workspace_bytes_impl(op, N, D, K, dt, chunk_rows);
 }
 
@@ -646,8 +666,12 @@ km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_
   if (iters == 0) return KM_OK;
   hipStream_t cs = (hipStream_t)compute_stream, xs = (hipStream_t)copy_stream;
   const int64_t rows = chunk_rows < N ? chunk_rows : (N > 0 ? N : 1);
+  // With room for every chunk's order (KM_OP_FIT_STREAMED_WARM), iterations after the first assign each chunk
+  // warm, in the order of its last argsort (the same results, bit for bit; only the order of work changes).
+  const bool warm = ws_bytes >= workspace_bytes_impl(KM_OP_FIT_STREAMED_WARM, N, D, K, dt, chunk_rows);
   Carve c(ws);
   const StreamBufs b = carve_streamed(c, rows, D, K, dt);
+  const WarmOrder wo = warm ? carve_warm_order(c, N) : WarmOrder{nullptr, nullptr};
   const int64_t nchunks = N > 0 ? (N + rows - 1) / rows : 0;
   const AssignGeom g = assign_geom(rows, D, K, dt);
 
@@ -709,15 +733,18 @@ km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_
       KM_HIP(hipEventRecord(ready[buf], xs));
       // compute stream: assign the chunk, then fold its per-cluster sums into the totals
       KM_HIP(hipStreamWaitEvent(cs, ready[buf], 0));
+      int32_t* ck = warm ? wo.keys + r0 : nullptr;  // this chunk's order from the last iteration
+      int32_t* cv = warm ? wo.vals + r0 : nullptr;
       KM_TIMED("assign", cs,
                return launch_flash_assign(g, b.xbuf[buf], nr, b.f.frag, b.f.assign,
-                                          objective ? b.f.min_dist : nullptr, cs));
+                                          objective ? b.f.min_dist : nullptr, cs, t > 0 ? cv : nullptr,
+                                          t > 0 ? ck : nullptr));
       if (objective)
         KM_TIMED("objective", cs,
                  return launch_objective(b.f.min_dist, nr, b.f.obj_part, objective + t, ch > 0 ? 1 : 0, cs));
       const UpdateBufs u = b.f.u;
       st = run_update(b.xbuf[buf], dt, nr, D, b.f.assign, K, nullptr, nullptr, nullptr, u, MODE_ACCUM, b.acc_sum,
-                      b.acc_cnt, cs);
+                      b.acc_cnt, cs, nullptr, nullptr, 1, nullptr, nullptr, nullptr, ck, cv);
       if (st != KM_OK) return st;
       if (assign_host && t == iters - 1)
         KM_TIMED("d2h", cs,

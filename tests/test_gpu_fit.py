@@ -109,6 +109,35 @@ def test_fit_streamed_pinned_and_pageable_agree():
     assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1]) and torch.equal(r1[2], r2[2])
 
 
+@pytest.mark.parametrize("case", [("c4", "bf16", 300_000, 64, 4096, 70_000), ("c2", "f16", 40_000, 48, 9000, 15_000),
+                                  ("c1", "f32", 50_000, 32, 200, 16_384), ("c2", "bf16", 30_000, 600, 100, 11_000),
+                                  ("c4", "bf16", 5_000, 16, 40, 1_024)],
+                         ids=lambda c: f"{c[1]}-N{c[2]}-D{c[3]}-K{c[4]}-chunk{c[5]}")
+def test_fit_streamed_warm_start_equals_cold(case):
+    """With room for every chunk's order, iterations after the first assign each chunk warm (in the order of
+    its last argsort): the results must be the cold run's bit for bit; the last iteration against the oracle."""
+    name, xdtype, N, D, K, chunk = case
+    w, Xn, C0 = _workload(name, N=N, D=D, K=K, M=min(K, 4096))
+    X = parity.x_from_numpy(Xn, w.dtype, DEV)
+    if xdtype == "f16":  # the bf16 points as fp16 values
+        X = X.float().half()
+    assert (X.dtype == torch.float32) == (xdtype == "f32")
+    Xh = X.cpu().pin_memory()
+    C0t = torch.from_numpy(C0).to(DEV)
+    print(f"[fit] streamed warm vs cold {case}", flush=True)
+    rw = km.fit_streamed(Xh, C0t, 3, chunk, objective=True, warm_start=True)
+    rc = km.fit_streamed(Xh, C0t, 3, chunk, objective=True, warm_start=False)
+    r2 = km.fit_streamed(Xh, C0t, 2, chunk, warm_start=False)
+    torch.cuda.synchronize()
+    for i in range(4):
+        assert torch.equal(rw[i], rc[i]), f"warm-started streamed fit differs from the cold one (output {i})"
+    Xs, xdt = parity.x_to_numpy(X)
+    C2 = r2[0].cpu().numpy()
+    an = rw[1].numpy()
+    parity.check_assign(Xs, xdt, C2, an, label=f"warm streamed {case}")
+    parity.check_update(Xs, xdt, an, C2, rw[0].cpu().numpy(), rw[2].cpu().numpy(), label=f"warm streamed {case}")
+
+
 def test_fit_resume_and_determinism():
     w, Xn, C0 = _workload("c2", N=50000, K=512)
     X = parity.x_from_numpy(Xn, "bf16", DEV)
