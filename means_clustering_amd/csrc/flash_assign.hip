@@ -315,6 +315,61 @@ __device__ __forceinline__ void lazy_resolve(const f32x16_t (&in)[NB], const flo
   if (__builtin_amdgcn_ballot_w64(imp)) argmax_range<0, 16, NB>(in, best, rel);
 }
 
+// Deferred argmax (the single-accumulator kernel), per group: a lane keeps only its best score and the first
+// group that reached it (one comparison and two selects, no branch); which of
+// that group's 32 centroids it was is settled once, after the sweep, by
+// resolve_deferred.  A group whose maximum does not beat the running best
+// cannot hold the lowest-index argmax, so the result is the full scan's.
+template <int NB>
+__device__ __forceinline__ void defer_take(const float (&m)[NB], float (&best)[NB], int (&qsel)[NB], int q) {
+#pragma unroll
+  for (int g = 0; g < NB; ++g) {
+    const bool up = m[g] > best[g];
+    best[g] = up ? m[g] : best[g];
+    qsel[g] = up ? q : qsel[g];
+  }
+}
+
+// After a deferred sweep each lane holds its best score `v` and the first
+// group `q` that reached it (INT32_MAX: none).  The two lanes of a point
+// agree on the point's maximum and on the first group holding it; the
+// wavefront then scores each distinct such group again with the sweep's own
+// MFMA chain (bias first, depth blocks in order, the same operands), which
+// reproduces those scores bit for bit, and the lowest row whose score equals
+// the maximum is the point's centroid.  After a warm start the 32 points of a
+// block mostly share one winning group, so this takes one or two rounds.
+// Returns the centroid index within the sweep (INT32_MAX: none); v becomes
+// the point's maximum.
+template <int DT, int KB>
+__device__ __forceinline__ int resolve_deferred(float& v, int q, const u32x4_t (&xb)[KB],
+                                                const u32x4_t* __restrict__ frag, int64_t TS, int64_t GS, int CT,
+                                                int lane, int h) {
+  const float ov = __shfl_xor(v, 32);
+  const int oq = __shfl_xor(q, 32);
+  const float vm = fmaxf(v, ov);
+  const int qa = v == vm ? q : INT32_MAX, qb = ov == vm ? oq : INT32_MAX;
+  const int qw = vm > -INFINITY ? (qa < qb ? qa : qb) : INT32_MAX;
+  v = vm;
+  int k = INT32_MAX;
+  uint64_t pending = __builtin_amdgcn_ballot_w64(qw != INT32_MAX);
+  while (pending) {
+    const int qq = __builtin_amdgcn_readlane(qw, (int)__builtin_ctzll(pending));
+    const u32x4_t* grp = frag + (int64_t)(qq / CT) * TS + (int64_t)(qq % CT) * GS;
+    f32x16_t sc = bias_of(grp + KB * 64 + h * 4);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sc = mma32<DT>(grp[kb * 64 + lane], xb[kb], sc);
+    int r = INT32_MAX;  // lowest row of this lane's half scoring the maximum
+#pragma unroll
+    for (int e = 15; e >= 0; --e) r = sc[e] == vm ? (e >> 2) * 8 + h * 4 + (e & 3) : r;
+    const bool mine = qw == qq;
+    const int kk = mine && r != INT32_MAX ? qq * 32 + r : INT32_MAX;
+    const int ok = __shfl_xor(kk, 32);
+    if (mine) k = kk < ok ? kk : ok;
+    pending &= ~__builtin_amdgcn_ballot_w64(mine);
+  }
+  return k;
+}
+
 // One pipeline stage: the MFMAs of one 32-centroid group into `out`, depth
 // block by depth block, each block fenced together with its share of the
 // running-argmax update over the previous group's scores `in`, so the matrix
@@ -435,18 +490,10 @@ __global__ __launch_bounds__(wide_cfg(KB).W * 64) __attribute__((amdgpu_waves_pe
 
   // Point fragments: read once from HBM, kept in VGPRs for the whole sweep.
   u32x4_t xb[NB][KB];
-  float xn[NB];
 #pragma unroll
-  for (int g = 0; g < NB; ++g) {
-    float s = 0.0f;
+  for (int g = 0; g < NB; ++g)
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      xb[g][kb] = load_point_frag<2>(X, pt[g], N, D, kb * kFragDepth + h * 8, vec_ok);
-      s += sumsq16<DT>(xb[g][kb]);
-    }
-    s += __shfl_xor(s, 32);
-    xn[g] = s;
-  }
+    for (int kb = 0; kb < KB; ++kb) xb[g][kb] = load_point_frag<2>(X, pt[g], N, D, kb * kFragDepth + h * 8, vec_ok);
 
   // best score per point group and lane; `rel` = selected element counted
   // from the base of the group most recently scanned (rebased by -16 a group;
@@ -530,20 +577,26 @@ __global__ __launch_bounds__(wide_cfg(KB).W * 64) __attribute__((amdgpu_waves_pe
       b = ob;
       k = ok;
     }
+    float xn = 0.0f;  // ||x||^2, only for the distance output
+    if (min_dist || (SPLIT && bt.part_xn)) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) xn += sumsq16<DT>(xb[g][kb]);
+      xn += __shfl_xor(xn, 32);
+    }
     const int64_t p = pt[g];
     if constexpr (SPLIT) {  // one range of a split sweep: its best, in problem indices
       if (h == 0 && p < N) {
         const int64_t o = (int64_t)bz * N + p;
         bt.part_s[sp * bt.part_stride + o] = b;
         bt.part_k[sp * bt.part_stride + o] = k == INT32_MAX ? INT32_MAX : k + sp * bt.split_tiles * CT * 32;
-        if (sp == 0 && bt.part_xn) bt.part_xn[o] = xn[g];
+        if (sp == 0 && bt.part_xn) bt.part_xn[o] = xn;
       }
       continue;
     }
     if (k == INT32_MAX) k = 0;  // no finite score (NaN input): index 0
     if (h == 0 && p < N) {
       assign[p] = k + id_base;
-      if (min_dist) min_dist[p] = fmaxf(xn[g] - 2.0f * b, 0.0f);
+      if (min_dist) min_dist[p] = fmaxf(xn - 2.0f * b, 0.0f);
     }
   }
 }
@@ -603,11 +656,11 @@ __global__ __launch_bounds__(wide8_cfg(KB).W * 64) __attribute__((amdgpu_waves_p
   }
 
   float best[NB];
-  int rel[NB];
+  int rel[NB];  // exact scan: selected element from the last group's base; folded: first group reaching best
 #pragma unroll
   for (int g = 0; g < NB; ++g) {
     best[g] = -INFINITY;
-    rel[g] = -(1 << 30);
+    rel[g] = FOLD ? INT32_MAX : -(1 << 30);
   }
 
   if constexpr (WARM) {
@@ -652,14 +705,14 @@ __global__ __launch_bounds__(wide8_cfg(KB).W * 64) __attribute__((amdgpu_waves_p
         for (int g = 0; g < NB; ++g) acc[g] = mma32<DT>(a, xb[g][kb], acc[g]);
         if (kb + 1 < KB) a = an;
       }
-#pragma unroll
-      for (int g = 0; g < NB; ++g) rel[g] -= 16;  // selectors now count from this group's base
       if constexpr (FOLD) {
         float m[NB];
         fold_first<NB>(acc, m);
         fold_range<2, 16, NB>(acc, m);
-        lazy_resolve<NB>(acc, m, best, rel);
+        defer_take<NB>(m, best, rel, t * CT + c);
       } else {
+#pragma unroll
+        for (int g = 0; g < NB; ++g) rel[g] -= 16;  // selectors now count from this group's base
         argmax_range_first<16, NB>(acc, best, rel);
       }
     }
@@ -673,14 +726,19 @@ __global__ __launch_bounds__(wide8_cfg(KB).W * 64) __attribute__((amdgpu_waves_p
 #pragma unroll
   for (int g = 0; g < NB; ++g) {
     float b = best[g];
-    const int sg = last_base + rel[g];
-    const bool none = b == -INFINITY || rel[g] <= -(1 << 30);
-    int k = none ? INT32_MAX : (sg >> 4) * 32 + ((sg & 15) >> 2) * 8 + h * 4 + (sg & 3);
-    const float ob = __shfl_xor(b, 32);
-    const int ok = __shfl_xor(k, 32);
-    if (ob > b || (ob == b && ok < k)) {
-      b = ob;
-      k = ok;
+    int k;
+    if constexpr (FOLD) {
+      k = resolve_deferred<DT, KB>(b, rel[g], xb[g], frag, TS, GS, CT, lane, h);
+    } else {
+      const int sg = last_base + rel[g];
+      const bool none = b == -INFINITY || rel[g] <= -(1 << 30);
+      k = none ? INT32_MAX : (sg >> 4) * 32 + ((sg & 15) >> 2) * 8 + h * 4 + (sg & 3);
+      const float ob = __shfl_xor(b, 32);
+      const int ok = __shfl_xor(k, 32);
+      if (ob > b || (ob == b && ok < k)) {
+        b = ob;
+        k = ok;
+      }
     }
     float xn = 0.0f;
     if (min_dist || (SPLIT && bt.part_xn)) {

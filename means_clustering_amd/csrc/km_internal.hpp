@@ -153,6 +153,10 @@ struct AssignGeom {
   size_t frag_bytes() const { return (size_t)ntiles() * (size_t)cfg.tile_slots() * 16; }
 };
 
+#ifndef KM_LAZY_MIN_GROUPS
+#define KM_LAZY_MIN_GROUPS 256  // cold launches fold the argmax from this many centroid groups of 32
+#endif
+
 // B: problems launched together (batched calls), for the choice of a thin layout.
 inline AssignGeom make_assign_geom(int64_t N, int64_t D, int64_t K, int dt, int64_t B = 1) {
   AssignGeom g;
@@ -187,10 +191,11 @@ inline AssignGeom make_assign_geom(int64_t N, int64_t D, int64_t K, int dt, int6
       g.cfg = wide_cfg(kb);
     }
   }
-  // A group whose maximum does not beat a lane's running best costs one max3
-  // per two scores instead of a full compare-and-select; with many groups such
-  // groups dominate (measured on gfx950: better from about 256 groups of 32).
-  g.lazy = dt != DT_F32 && g.groups() >= 256;
+  // Folded argmax (a max3 per two scores, then the index settled after the
+  // sweep) against an exact compare-and-select per score: the fold pays off
+  // with many groups (measured on gfx950: better from about 256 groups of 32);
+  // warm-started launches always fold.
+  g.lazy = dt != DT_F32 && g.groups() >= KM_LAZY_MIN_GROUPS;
   return g;
 }
 
