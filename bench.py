@@ -15,6 +15,7 @@ whole-update roofline and CPU baseline.  Prints one JSON line.
   python bench.py [--steps K] [--warmup W] [--workload c1..c5] [--extra c2,c3,c4|none] [--no-cpu-baseline]
   python bench.py --workload c1 --batch 256      (256 independent c1-shaped problems per call)
   python bench.py --ablation                     (the designs FlashAssign and Sort-Inverse Update replace)
+  python bench.py --planner-study                (the static plan against every alternative, five shapes)
 """
 from __future__ import annotations
 
@@ -527,6 +528,101 @@ def batched(args, dev):
     print(json.dumps(line), flush=True)
 
 
+# Alternatives timed by --planner-study per workload (planner keys of kmeans_plan_override); variants whose plan
+# description equals one already timed are skipped.
+STUDY_KEYS = {
+    "c1": [("small_update", 1), ("assign_split", 1), ("assign_split", 4), ("reduce_tile", 1), ("reduce_tile", 2)],
+    "default": [("assign_kernel", 1), ("assign_kernel", 2), ("assign_fold", 1), ("assign_fold", 2),
+                ("radix_items", 8), ("radix_items", 16), ("radix_items", 32), ("reduce_tile", 1), ("reduce_tile", 2)],
+}
+
+
+def planner_study(args, dev):
+    """The static planner against every alternative it could have chosen, on the five workload shapes.
+
+    For each shape: kmeans_fit of the workload's iterations with the planner's own choice, then with each single
+    override that changes the plan (kmeans_plan_override), median of several fits; the gap is the static choice's
+    time over the fastest plan's.  Time to first run: the host-side planning cost (kmeans_plan_describe +
+    kmeans_workspace_bytes, no compilation anywhere) and the first fit of each shape in the process against the
+    steady state.  The c5 shape is timed resident, one 2^26-row chunk of it (the kernels its streamed fit runs).
+    """
+    import numpy as np
+    import torch
+
+    import means_clustering_amd as km
+    import synth
+
+    L = km.lib()
+    shapes = [("c1", synth.WORKLOADS["c1"]), ("c2", synth.WORKLOADS["c2"]), ("c3", synth.WORKLOADS["c3"]),
+              ("c4", synth.WORKLOADS["c4"]), ("c5", synth.WORKLOADS["c5"].scaled(N=1 << 26, chunk_rows=0))]
+    out = {"planner_study": "static plan vs every single-choice alternative, one GPU", "shapes": {}}
+    reps = 5
+    for name, w in shapes:
+        print(f"[bench] planner study {name}: {w.description}", file=sys.stderr, flush=True)
+        tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+        X = torch.empty((w.N, w.D), dtype=tdt, device=dev)
+        synth.DeviceGenerator(w, dev).fill(X, 0)
+        C0 = torch.from_numpy(synth.init_centroids(w)).to(dev)
+        a = torch.empty(w.N, dtype=torch.int32, device=dev)
+        cnt = torch.empty(w.K, dtype=torch.int32, device=dev)
+        C = C0.clone()
+        # host planning cost: plan + workspace size, per call
+        t0 = time.perf_counter()
+        for _ in range(200):
+            km.plan_describe(w.N, w.D, w.K, tdt)
+            L.kmeans_workspace_bytes(km.KM_OP_FIT, w.N, w.D, w.K, km._DT[tdt], 0)
+        plan_us = (time.perf_counter() - t0) / 200 * 1e6
+
+        def run(ws, timing=False):
+            C.copy_(C0)
+            km.fit(X, C, w.iters, inplace=True, ws=ws, assign_out=a, counts_out=cnt)
+
+        def measure(label):
+            ws = km.Workspace(dev)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            run(ws)
+            torch.cuda.synchronize()
+            first = time.perf_counter() - t0
+            times = []
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                run(ws)
+                torch.cuda.synchronize()
+                times.append(time.perf_counter() - t0)
+            a_ref = a.clone()
+            return {"plan": km.plan_describe(w.N, w.D, w.K, tdt), "first_fit_ms": round(first * 1e3, 3),
+                    "fit_ms": round(float(np.median(times)) * 1e3, 3)}, a_ref
+
+        static, a_static = measure("static")
+        variants, seen = [], {static["plan"]}
+        for key, val in STUDY_KEYS.get(name, STUDY_KEYS["default"]):
+            km.plan_override(key, val)
+            try:
+                plan = km.plan_describe(w.N, w.D, w.K, tdt)
+                if plan in seen:
+                    continue
+                seen.add(plan)
+                r, a_var = measure(f"{key}={val}")
+                # every plan reaches the same final assignment (sums may round differently, so only counts
+                # of agreement are reported: the trajectories may part after a near tie)
+                r["override"] = {key: val}
+                r["same_final_assignment"] = bool(torch.equal(a_var, a_static))
+                variants.append(r)
+            finally:
+                km.plan_override(key, 0)
+        best = min([static] + variants, key=lambda r: r["fit_ms"])
+        out["shapes"][name] = {
+            "workload": w.description if name != "c5" else "one 2^26-row chunk of " + w.description,
+            "static": static, "alternatives": variants, "best_fit_ms": best["fit_ms"],
+            "gap_static_vs_best": round(static["fit_ms"] / best["fit_ms"] - 1.0, 4),
+            "best_override": best.get("override", "static"), "host_plan_us": round(plan_us, 2),
+            "first_fit_over_steady": round(static["first_fit_ms"] / static["fit_ms"], 3)}
+        del X
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -546,6 +642,9 @@ def main():
     ap.add_argument("--ablation", action="store_true",
                     help="only time the materialised-distance assignment and the atomic scatter update "
                          "against FlashAssign and Sort-Inverse Update (one JSON line)")
+    ap.add_argument("--planner-study", action="store_true",
+                    help="only time the static plan against every single-choice alternative on the five shapes "
+                         "(one JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -568,6 +667,10 @@ def main():
     if args.ablation:
         import torch
         ablation(torch.device("cuda:0"))
+        return
+    if args.planner_study:
+        import torch
+        planner_study(args, torch.device("cuda:0"))
         return
     if args.batch > 1:
         import torch

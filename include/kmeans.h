@@ -262,6 +262,29 @@ km_status kmeans_fit_batched(const void* X, km_dtype dt, int64_t B, int64_t N, i
 km_status kmeans_fit_noalloc(const void* X, km_dtype dt, int64_t N, int64_t D, int64_t K, float* C, int32_t iters,
                              int32_t* assign, int32_t* counts, double* objective, void* stream);
 
+/*
+ * Planner (for measurement).  The library chooses every launch shape itself
+ * from N, K, D, the dtype and the device (compute units and last-level cache
+ * size, read once per device); there is no tuning run and no compiled-at-
+ * first-use code.  kmeans_plan_override(key, value) replaces one of those
+ * choices for every later call of this process (value 0 restores the
+ * planner's choice); it is meant for comparing the static choice against
+ * the alternatives, not for production use, and must not change while a
+ * call is being enqueued.  Keys and values:
+ *   "assign_kernel"  1 pipelined four-wavefront kernel, 2 single-accumulator
+ *                    kernel (16-bit X, D <= 128)
+ *   "assign_fold"    1 exact argmax per score, 2 folded argmax (cold launches)
+ *   "assign_split"   1 never split the centroid sweep, 2..64 ranges
+ *   "reduce_tile"    1 long segment tiles, 2 short ones
+ *   "radix_items"    8, 16 or 32 keys per thread in the argsort
+ *   "small_update"   1 never the on-chip small-codebook update
+ * Every choice gives the same assignments; sums may differ in fp32 rounding.
+ * kmeans_plan_describe(N, D, K, dt, buf, len) writes a one-line description
+ * of the plan of kmeans_fit for that shape (NUL-terminated, truncated to len).
+ */
+km_status kmeans_plan_override(const char* key, int64_t value);
+km_status kmeans_plan_describe(int64_t N, int64_t D, int64_t K, km_dtype dt, char* buf, size_t len);
+
 /* Short constant description of a status code. */
 const char* kmeans_status_string(km_status s);
 

@@ -60,6 +60,8 @@ def _bind(lib):
         "kmeans_workspace_bytes_batched": (sz, [i64, i64, i64, i64, c_int]),
         "kmeans_fit_batched": (c_int, [vp, c_int, i64, i64, i64, i64, vp, ctypes.c_int32, vp, vp, vp, vp, sz, vp]),
         "kmeans_fit_noalloc": (c_int, [vp, c_int, i64, i64, i64, vp, ctypes.c_int32, vp, vp, vp, vp]),
+        "kmeans_plan_override": (c_int, [ctypes.c_char_p, i64]),
+        "kmeans_plan_describe": (c_int, [i64, i64, i64, c_int, ctypes.c_char_p, sz]),
         "kmeans_status_string": (ctypes.c_char_p, [c_int]),
         "kmeans_last_error": (ctypes.c_char_p, []),
         "kmeans_timing_enable": (c_int, [c_int]),
@@ -327,6 +329,21 @@ def fit_streamed(X_host: torch.Tensor, C0: torch.Tensor, iters: int, chunk_rows:
                                      _ptr(stage), 0 if stage is None else stage.numel()))
     _hold_until_done(dev, X_host, stage, a)
     return C, a, counts, (obj[:iters] if obj is not None else None)
+
+
+PLAN_KEYS = ("assign_kernel", "assign_fold", "assign_split", "reduce_tile", "radix_items", "small_update")
+
+
+def plan_override(key: str, value: int = 0):
+    """Replace one planner choice for later calls (0 restores the planner's choice); for measurement only."""
+    _check(lib().kmeans_plan_override(key.encode(), int(value)))
+
+
+def plan_describe(N: int, D: int, K: int, dtype=torch.bfloat16) -> str:
+    """The plan kmeans_fit makes for this shape on the current device, as one line of text."""
+    buf = ctypes.create_string_buffer(1024)
+    _check(lib().kmeans_plan_describe(N, D, K, _DT[dtype], buf, len(buf)))
+    return buf.value.decode()
 
 
 def timing_enable(on=True):

@@ -7,9 +7,12 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <condition_variable>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <fstream>
 #include <mutex>
 #include <string>
 #include <thread>
@@ -90,6 +93,101 @@ hipError_t timed(const char* phase, hipStream_t stream, F&& fn) {
     hipError_t e_ = timed(phase, stream, [&]() -> hipError_t { body; });                  \
     if (e_ != hipSuccess) return fail(KM_ERR_HIP, std::string(phase) + ": " + hipGetErrorString(e_)); \
   } while (0)
+
+// ------------------------------------------------ device and planner ----
+
+namespace {
+// The last-level cache of the GPU at PCI location (domain, bus, device), from
+// the KFD topology (the largest cache of the highest level listed for its
+// node); 0 when not found.
+int64_t kfd_llc_bytes(int domain, int bus, int dev) {
+  int64_t best = 0;
+  for (int node = 0; node < 256; ++node) {
+    const std::string base = "/sys/class/kfd/kfd/topology/nodes/" + std::to_string(node);
+    std::ifstream props(base + "/properties");
+    if (!props) {
+      if (node > 0) break;
+      continue;
+    }
+    int64_t loc = -1, dom = -1, simds = 0;
+    std::string key;
+    int64_t val;
+    while (props >> key >> val) {
+      if (key == "location_id") loc = val;
+      else if (key == "domain") dom = val;
+      else if (key == "simd_count") simds = val;
+    }
+    // location_id = bus << 8 | device << 3 | function
+    if (simds <= 0 || dom != domain || (loc >> 8) != bus || ((loc >> 3) & 31) != dev) continue;
+    int best_level = 0;
+    for (int c = 0; c < 64; ++c) {
+      std::ifstream cp(base + "/caches/" + std::to_string(c) + "/properties");
+      if (!cp) break;
+      int64_t level = 0, size_kb = 0;
+      while (cp >> key >> val) {
+        if (key == "level") level = val;
+        else if (key == "size") size_kb = val;
+      }
+      if (level > best_level || (level == best_level && size_kb * 1024 > best)) {
+        best_level = (int)level;
+        best = size_kb * 1024;
+      }
+    }
+    break;
+  }
+  return best;
+}
+
+DeviceInfo query_device(int dev) {
+  DeviceInfo d{256, 160 * 1024, 4 << 20, (int64_t)256 << 20, false};  // MI355X
+  int cus = 0, lds = 0, l2 = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return d;
+  d.cus = cus;
+  if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) == hipSuccess && lds > 0)
+    d.lds_bytes = lds;
+  if (hipDeviceGetAttribute(&l2, hipDeviceAttributeL2CacheSize, dev) == hipSuccess && l2 > 0) d.l2_bytes = l2;
+  int domain = 0, bus = 0, pdev = 0;
+  (void)hipDeviceGetAttribute(&domain, hipDeviceAttributePciDomainID, dev);
+  (void)hipDeviceGetAttribute(&bus, hipDeviceAttributePciBusId, dev);
+  (void)hipDeviceGetAttribute(&pdev, hipDeviceAttributePciDeviceId, dev);
+  const int64_t llc = kfd_llc_bytes(domain, bus, pdev);
+  d.llc_bytes = llc > d.l2_bytes ? llc : d.l2_bytes;
+  d.queried = true;
+  return d;
+}
+
+std::atomic<int> g_override[6];  // PlanOverride fields, in order
+const char* const kOverrideKeys[6] = {"assign_kernel", "assign_fold", "assign_split", "reduce_tile", "radix_items",
+                                      "small_update"};
+}  // namespace
+
+namespace km {
+const DeviceInfo& device_info() {
+  static std::mutex mu;
+  static std::vector<DeviceInfo*> cache;  // per device ordinal, kept for the life of the process
+  static const DeviceInfo fallback{256, 160 * 1024, 4 << 20, (int64_t)256 << 20, false};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fallback;
+  }
+  std::lock_guard<std::mutex> g(mu);
+  if ((int)cache.size() <= dev) cache.resize((size_t)dev + 1, nullptr);
+  if (!cache[(size_t)dev]) cache[(size_t)dev] = new DeviceInfo(query_device(dev));
+  return *cache[(size_t)dev];
+}
+
+PlanOverride plan_override() {
+  PlanOverride p;
+  p.assign_kernel = g_override[0].load(std::memory_order_relaxed);
+  p.assign_fold = g_override[1].load(std::memory_order_relaxed);
+  p.assign_split = g_override[2].load(std::memory_order_relaxed);
+  p.reduce_tile = g_override[3].load(std::memory_order_relaxed);
+  p.radix_items = g_override[4].load(std::memory_order_relaxed);
+  p.small_update = g_override[5].load(std::memory_order_relaxed);
+  return p;
+}
+}  // namespace km
 
 // ---------------------------------------------------------- validation ----
 
@@ -407,7 +505,8 @@ static km_status run_update(const void* X, km_dtype dt, int64_t N, int64_t D, co
   if (sorted_vals) *sorted_vals = nullptr;
   if (prepped) *prepped = false;
   const bool deep = deep_rows((int)dt, D);  // rows beyond one lane group: no small-codebook path, column strips
-  if (mode == MODE_MEAN && !deep && (K / B <= kSmallMaxK || small_owner_fits(B, N / B, K / B))) {
+  if (mode == MODE_MEAN && !deep && plan_override().small_update != 1 &&
+      (K / B <= kSmallMaxK || small_owner_fits(B, N / B, K / B))) {
     SmallArgs a;
     a.X = X;
     a.dt = (int)dt;
@@ -758,6 +857,55 @@ km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_
   // the staging buffer (and pageable X) can be reused as soon as this returns.
   if (stage_host)
     for (uint64_t i = 0; i < slot_seq && i < (uint64_t)kStageSlots; ++i) KM_HIP(hipEventSynchronize(slot_done[i]));
+  return KM_OK;
+}
+
+km_status kmeans_plan_override(const char* key, int64_t value) {
+  if (!key) return fail(KM_ERR_INVALID_VALUE, "key must be non-NULL");
+  for (int i = 0; i < 6; ++i)
+    if (std::strcmp(key, kOverrideKeys[i]) == 0) {
+      const bool ok = value == 0 ||
+                      (i == 0 && (value == 1 || value == 2)) || (i == 1 && (value == 1 || value == 2)) ||
+                      (i == 2 && value >= 1 && value <= 64) || (i == 3 && (value == 1 || value == 2)) ||
+                      (i == 4 && (value == 8 || value == 16 || value == 32)) || (i == 5 && value == 1);
+      if (!ok) return fail(KM_ERR_INVALID_VALUE, std::string("value out of range for ") + key);
+      g_override[i].store((int)value, std::memory_order_relaxed);
+      return KM_OK;
+    }
+  return fail(KM_ERR_INVALID_VALUE, std::string("unknown planner key ") + key);
+}
+
+km_status kmeans_plan_describe(int64_t N, int64_t D, int64_t K, km_dtype dt, char* buf, size_t len) {
+  km_status st = check_sizes(N, D, K, dt, true);
+  if (st != KM_OK) return st;
+  if (!buf || len == 0) return fail(KM_ERR_INVALID_VALUE, "buf must be non-NULL with len > 0");
+  const DeviceInfo& dv = device_info();
+  const AssignGeom g = assign_geom(N, D, K, dt);
+  auto same = [](const AssignCfg& a, const AssignCfg& b) {
+    return a.rows == b.rows && a.KB == b.KB && a.NB == b.NB && a.CT == b.CT && a.W == b.W;
+  };
+  const char* kernel = is_deep_cfg((int)dt, g.cfg)                                       ? "depth-tiled"
+                       : dt == KM_F32                                                    ? "fp32"
+                       : g.cfg.KB <= kWide8MaxKB && same(g.cfg, wide8_cfg(g.cfg.KB)) ? "single-accumulator"
+                                                                                         : "pipelined";
+  const int64_t splits = assign_splits(g, N, 1);
+  const SortGeom sg = sort_geom(N, K);
+  const bool small = !deep_rows((int)dt, D) && plan_override().small_update != 1 &&
+                     (K <= kSmallMaxK || small_owner_fits(1, N, K));
+  char upd[256];
+  if (small)
+    std::snprintf(upd, sizeof upd, "on-chip small-codebook");
+  else
+    std::snprintf(upd, sizeof upd, "sorted, %d radix pass(es) of %d keys/thread, segment tile %lld, %lld column strip(s)",
+                  sg.npass, sg.items, (long long)reduce_tile((int)dt, D, N), (long long)reduce_strips((int)dt, D));
+  char out[640];
+  std::snprintf(out, sizeof out,
+                "assign: %s kernel, %d depth blocks, %d point groups/wave, %d groups/tile, %d waves, cold argmax %s, "
+                "%lld centroid range(s); update: %s; workspace %zu bytes; device: %d CUs, LLC %lld MiB (%s)",
+                kernel, g.cfg.KB, g.cfg.NB, g.cfg.CT, g.cfg.W, g.lazy ? "folded" : "exact", (long long)splits, upd,
+                workspace_bytes_impl(KM_OP_FIT, N, D, K, dt, 0), dv.cus, (long long)(dv.llc_bytes >> 20),
+                dv.queried ? "queried" : "defaults");
+  std::snprintf(buf, len, "%s", out);
   return KM_OK;
 }
 

@@ -41,6 +41,36 @@ constexpr int64_t kMaxD = (int64_t)1 << 24;  // longest rows accepted at all (32
 // strips of kMaxD16 / kMaxD32 values.
 inline bool deep_rows(int dt, int64_t D) { return D > (dt == DT_F32 ? kMaxD32 : kMaxD16); }
 
+// ---------------------------------------------------------------------------
+// The device a plan is made for.  The launch shapes below follow from the
+// number of compute units (how many workgroups fill the GPU) and from the
+// size of the last-level cache (below which a gathered walk over the rows is
+// bound by latency rather than bandwidth).  Both are read once per device:
+// hipDeviceGetAttribute, and the KFD topology for the last-level cache, which
+// HIP does not report.  A query that no device answers (a workspace-size call
+// on a machine without a GPU) gets the MI355X values.
+// ---------------------------------------------------------------------------
+struct DeviceInfo {
+  int cus;            // compute units (256 on MI355X)
+  int64_t lds_bytes;  // LDS per compute unit (160 KiB)
+  int64_t l2_bytes;   // L2 as HIP reports it (4 MiB, per XCD)
+  int64_t llc_bytes;  // last-level cache (256 MiB Infinity Cache); the L2 if no larger level is found
+  bool queried;       // false: the MI355X defaults
+};
+const DeviceInfo& device_info();  // of the calling thread's current device
+
+// Overrides of the planner's choices, for the planner study: 0 keeps the
+// planner's choice.  Process-wide; set between calls, not during one.
+struct PlanOverride {
+  int assign_kernel;  // 1 pipelined four-wavefront kernel, 2 single-accumulator kernel (16-bit X, D <= 128)
+  int assign_fold;    // 1 exact argmax per score, 2 folded argmax (cold launches, 16-bit X)
+  int assign_split;   // 1 never split the centroid sweep; n >= 2 split it into n ranges where it can be
+  int reduce_tile;    // 1 long (128-position) segment tiles, 2 short ones
+  int radix_items;    // keys per thread of the argsort: 8, 16 or 32
+  int small_update;   // 1 no on-chip small-codebook update (always the sorted path)
+};
+PlanOverride plan_override();
+
 // Launch shape of one FlashAssign instantiation.
 struct AssignCfg {
   int rows;   // centroids per group (32 wide, 16 narrow)
@@ -132,7 +162,7 @@ constexpr AssignCfg narrow_cfg(int KB, bool half = false, bool thin = false) {
                    (KB <= 2 ? 8 : (KB <= 4 ? 4 : (KB <= 8 ? 2 : 1))) / (half && KB <= 8 ? 2 : 1), 4};
 }
 constexpr int kNarrowHalfMaxKB = 8;
-constexpr int64_t kNarrowThinBelow = 256;  // workgroups of the call at the usual point groups per wavefront
+// fp32: one point group per wavefront when the usual layout would give fewer workgroups than compute units
 
 inline int wide_kb(int64_t D) {
   const int need = (int)((D + kFragDepth - 1) / kFragDepth);
@@ -180,11 +210,13 @@ inline AssignGeom make_assign_geom(int64_t N, int64_t D, int64_t K, int dt, int6
     g.cfg = use_half ? half : full;
     g.Kpad = use_half ? kp_half : kp_full;
     const int64_t pts = (int64_t)half.W * half.NB * 16;
-    if (use_half && B * ((N + pts - 1) / pts) < kNarrowThinBelow) g.cfg = narrow_cfg(kb, true, true);
+    if (use_half && B * ((N + pts - 1) / pts) < device_info().cus) g.cfg = narrow_cfg(kb, true, true);
   } else {
     const int kb = wide_kb(D);
     const AssignCfg c8 = wide8_cfg(kb);
-    if (kb <= kWide8MaxKB && pad_up(K, kPadK) / 32 >= 256 && K >= 2 * (int64_t)c8.rows * c8.CT) {
+    const int ov = plan_override().assign_kernel;
+    const bool w8_ok = kb <= kWide8MaxKB && K >= 2 * (int64_t)c8.rows * c8.CT;
+    if (w8_ok && (ov == 2 || (ov != 1 && pad_up(K, kPadK) / 32 >= 256))) {
       g.cfg = c8;
       g.Kpad = pad_up(K, (int64_t)c8.rows * c8.CT);
     } else {
@@ -195,7 +227,8 @@ inline AssignGeom make_assign_geom(int64_t N, int64_t D, int64_t K, int dt, int6
   // sweep) against an exact compare-and-select per score: the fold pays off
   // with many groups (measured on gfx950: better from about 256 groups of 32);
   // warm-started launches always fold.
-  g.lazy = dt != DT_F32 && g.groups() >= KM_LAZY_MIN_GROUPS;
+  const int fold = plan_override().assign_fold;
+  g.lazy = dt != DT_F32 && (fold == 2 || (fold != 1 && g.groups() >= KM_LAZY_MIN_GROUPS));
   return g;
 }
 
@@ -208,21 +241,28 @@ inline AssignGeom make_assign_geom(int64_t N, int64_t D, int64_t K, int dt, int6
 #ifndef KM_SEG_U
 #define KM_SEG_U 16       // most rows in flight per lane group in the segmented reduction
 #endif
-#ifndef KM_SEG_FINE_MAX_BYTES
-#define KM_SEG_FINE_MAX_BYTES (1LL << 27)  // short segment tiles while N rows of G 16-byte pieces fit in this
-#endif
+// Short segment tiles while N rows of G 16-byte pieces fit in half the last-level cache.
+inline int64_t seg_fine_max_bytes() { return device_info().llc_bytes / 2; }
 #ifndef KM_SEG_FINE_U
 #define KM_SEG_FINE_U 16  // rows in flight per lane with short segment tiles
 #endif
 constexpr int kRadixThreads = 256;
 constexpr int kRadixMaxItems = 32;           // consecutive keys per thread: 8, 16 or 32 (block positions fit in 16 bits)
 // Keys per thread for N keys: blocks of 2048..8192 keys, small enough that
-// about a thousand blocks (four per CU) share the work when N allows.
-inline int radix_items(int64_t N) { return N >= 1024 * 8192 ? 32 : (N >= 1024 * 4096 ? 16 : 8); }
+// several blocks per compute unit share the work when N allows: 8192-key
+// blocks from 8 per compute unit, 4096-key blocks from 4 (measured on gfx950
+// by the planner study: 2^23 keys sort 1% faster in 2,048 blocks than in
+// 1,024, and 2^26 keys fastest in 8,192-key blocks).
+inline int radix_items(int64_t N) {
+  const int ov = plan_override().radix_items;
+  if (ov == 8 || ov == 16 || ov == 32) return ov;
+  const int64_t cus = device_info().cus;
+  return N >= 8 * cus * 8192 ? 32 : (N >= 4 * cus * 4096 ? 16 : 8);
+}
 constexpr int kMaxDigitBits = 6;             // digits of at most 64 values per pass
 constexpr int kSegTile = KM_SEG_TILE;
 // Short segment tiles, used while N rows of G lanes (16 bytes each) take at
-// most KM_SEG_FINE_MAX_BYTES (about half the last-level cache), where the
+// most seg_fine_max_bytes() (half the last-level cache), where the
 // walk is bound by memory latency: 16 positions (8 for rows of one lane, G
 // for rows of more than 16), so that the positions spread over many
 // workgroups and each lane group has its whole tile in flight at once.  A
@@ -266,17 +306,18 @@ struct Batch {
 
 // FlashAssign splits the centroid sweep over several workgroups per row block
 // when the row blocks alone (B problems of N points, fewer than
-// KM_SPLIT_MAX_BLOCKS workgroups) would leave most of the GPU idle: up to
-// KM_SPLIT_TARGET_BLOCKS workgroups in all, each sweeping at least
-// KM_SPLIT_MIN_TILES tiles, at most 64 ranges; a merge pass then takes the best
-// of the ranges in index order (the result is unchanged).  Measured on gfx950:
-// 2-19x faster sweeps for N up to 65,536 with 4,096 to 65,536 centroids; 4,096
-// workgroups and 4 tiles beat 1,024 / 2,048 workgroups and 8 tiles in most shapes.
-#ifndef KM_SPLIT_MAX_BLOCKS
-#define KM_SPLIT_MAX_BLOCKS 512
+// KM_SPLIT_MAX_BLOCKS_PER_CU workgroups per compute unit) would leave most of
+// the GPU idle: up to KM_SPLIT_TARGET_BLOCKS_PER_CU workgroups per compute
+// unit in all, each sweeping at least KM_SPLIT_MIN_TILES tiles, at most 64
+// ranges; a merge pass then takes the best of the ranges in index order (the
+// result is unchanged).  Measured on gfx950 (256 compute units): 2-19x faster
+// sweeps for N up to 65,536 with 4,096 to 65,536 centroids; 16 workgroups per
+// compute unit and 4 tiles beat 4 or 8 per compute unit and 8 tiles in most shapes.
+#ifndef KM_SPLIT_MAX_BLOCKS_PER_CU
+#define KM_SPLIT_MAX_BLOCKS_PER_CU 2
 #endif
-#ifndef KM_SPLIT_TARGET_BLOCKS
-#define KM_SPLIT_TARGET_BLOCKS 4096
+#ifndef KM_SPLIT_TARGET_BLOCKS_PER_CU
+#define KM_SPLIT_TARGET_BLOCKS_PER_CU 16
 #endif
 #ifndef KM_SPLIT_MIN_TILES
 #define KM_SPLIT_MIN_TILES 4
@@ -285,9 +326,16 @@ struct Batch {
 inline int64_t assign_split_tiles(const AssignGeom& g, int64_t N, int64_t B) {
   const int64_t pts = (int64_t)g.cfg.W * g.cfg.NB * g.cfg.rows;
   const int64_t blocks = B * ((N + pts - 1) / pts);
-  if (N <= 0 || blocks >= KM_SPLIT_MAX_BLOCKS) return 0;
+  const int ov = plan_override().assign_split;
+  if (N <= 0 || ov == 1) return 0;
   const int64_t nt = g.ntiles();
-  int64_t S = (KM_SPLIT_TARGET_BLOCKS + blocks - 1) / blocks;
+  if (ov >= 2) {  // a forced number of ranges (at least one tile each, at most 64)
+    const int64_t S = ov < nt ? (ov < 64 ? ov : 64) : nt;
+    return S < 2 ? 0 : (nt + S - 1) / S;
+  }
+  const int64_t cus = device_info().cus;
+  if (blocks >= KM_SPLIT_MAX_BLOCKS_PER_CU * cus) return 0;
+  int64_t S = (KM_SPLIT_TARGET_BLOCKS_PER_CU * cus + blocks - 1) / blocks;
   if (S > nt / KM_SPLIT_MIN_TILES) S = nt / KM_SPLIT_MIN_TILES;
   if (S > 64) S = 64;
   return S < 2 ? 0 : (nt + S - 1) / S;

@@ -35,11 +35,11 @@ namespace km {
 // (8192-point chunks were slower on c1-shaped problems, alone and batched.)
 constexpr int kSmallChunk = kRadixThreads * 8;
 constexpr int kSmallChunkThin = kRadixThreads * 2;
-constexpr int64_t kSmallThinBelow = 256;  // 2048-point chunks in the call
 static_assert(kSmallMaxK <= (1 << kMaxDigitBits), "one radix digit holds every id");
 
+// 512-point chunks when 2048-point chunks would give fewer workgroups than compute units
 static int small_it(int64_t B, int64_t N) {
-  return B * ((N + kSmallChunk - 1) / kSmallChunk) < kSmallThinBelow ? 2 : 8;
+  return B * ((N + kSmallChunk - 1) / kSmallChunk) < device_info().cus ? 2 : 8;
 }
 
 struct SmallParams {
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(256) void small_combine_kernel(SmallParams S, int64
   if (active) emit_fragment_row(rows[wv], S.D, S.dt, S.cfg, S.frag + 4 * b * S.f_stride, k);
 }
 
-// A few small problems (N <= 16384, at most kOwnerMaxGroups workgroups of R
+// A few small problems (N <= 16384, at most owner_max_groups() workgroups of R
 // consecutive clusters, R = 1, 2 or 4): one workgroup per (problem, R
 // clusters).  It reads all of the problem's ids at once, lists each of its
 // clusters' points in ascending index order in LDS (per-thread match counts,
@@ -300,11 +300,12 @@ __global__ __launch_bounds__(256) void small_combine_kernel(SmallParams S, int64
 // fixed order, the same for every R.
 constexpr int kOwnerMaxN = 16384;
 constexpr int kOwnerIPT = kOwnerMaxN / kRadixThreads;  // ids per thread
-#ifndef KM_OWNER_MAX_GROUPS
-#define KM_OWNER_MAX_GROUPS 512  // (measured on gfx950 with c1-shaped problems: 1.44x faster than chunk sums
-                                 //  for 1 to 4 problems, 1.25x for 8; 0.93x for 16, 0.72x for 256)
+#ifndef KM_OWNER_MAX_GROUPS_PER_CU
+#define KM_OWNER_MAX_GROUPS_PER_CU 2  // (measured on gfx950, 256 compute units, with c1-shaped problems: 1.44x
+                                      //  faster than chunk sums for 1 to 4 problems, 1.25x for 8; 0.93x for 16,
+                                      //  0.72x for 256)
 #endif
-constexpr int64_t kOwnerMaxGroups = KM_OWNER_MAX_GROUPS;
+static int64_t owner_max_groups() { return KM_OWNER_MAX_GROUPS_PER_CU * (int64_t)device_info().cus; }
 #ifndef KM_OWNER_MAX_R
 #define KM_OWNER_MAX_R 4  // (measured on gfx950, single problems of 600 to 2,048 clusters: 1.1-2.2x faster than
                           //  the sorted path with 2 or 4 clusters a workgroup, 0.87-1.0x with 8)
@@ -313,12 +314,12 @@ constexpr int kOwnerMaxR = KM_OWNER_MAX_R;  // clusters per workgroup, at most (
 
 // clusters per workgroup for B problems of K clusters (0: the layout does not apply).  Several clusters a
 // workgroup only above kSmallMaxK clusters a problem: at most kSmallMaxK the chunk-sum layout takes over
-// beyond kOwnerMaxGroups one-cluster workgroups (where it measured faster, 16 or more c1-shaped problems),
+// beyond owner_max_groups() one-cluster workgroups (where it measured faster, 16 or more c1-shaped problems),
 // and the 2- and 4-cluster workgroups were measured against the sorted path only.
 static int owner_r(int64_t B, int64_t K) {
   const int rmax = K > kSmallMaxK ? kOwnerMaxR : 1;
   for (int r = 1; r <= rmax; r *= 2)
-    if (B * ((K + r - 1) / r) <= kOwnerMaxGroups) return r;
+    if (B * ((K + r - 1) / r) <= owner_max_groups()) return r;
   return 0;
 }
 

@@ -21,7 +21,7 @@ def test_exports_every_declared_function(L):
     assert "kmeans_assign" in declared and "kmeans_fit_streamed" in declared
     for name in declared:
         assert hasattr(L, name), name
-    assert len(declared) == 14
+    assert len(declared) == 16
 
 
 def test_status_strings(L):
@@ -221,3 +221,36 @@ def test_abi_checks_under_asan_ubsan(tmp_path):
                         "-s", "-k", "not under_asan"], env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-3000:]
     assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr[-3000:]
+
+
+def test_planner_override_and_describe(L):
+    """The planner's overrides are validated and restorable; the plan description names the chosen layout."""
+    buf = ctypes.create_string_buffer(1024)
+    assert L.kmeans_plan_describe(1 << 20, 128, 1024, km.KM_BF16, buf, len(buf)) == 0
+    assert b"pipelined" in buf.value and b"sorted" in buf.value
+    assert L.kmeans_plan_describe(1 << 20, 128, 65536, km.KM_BF16, buf, len(buf)) == 0
+    assert b"single-accumulator" in buf.value
+    assert L.kmeans_plan_describe(16384, 32, 64, km.KM_F32, buf, len(buf)) == 0
+    assert b"on-chip small-codebook" in buf.value
+    assert L.kmeans_plan_describe(1000, 4096, 10, km.KM_BF16, buf, len(buf)) == 0
+    assert b"depth-tiled" in buf.value and b"8 column strip" in buf.value
+    assert L.kmeans_plan_describe(10, 0, 4, km.KM_BF16, buf, len(buf)) == 1
+    small = ctypes.create_string_buffer(8)
+    assert L.kmeans_plan_describe(10, 8, 4, km.KM_BF16, small, len(small)) == 0 and len(small.value) == 7
+    assert L.kmeans_plan_override(b"nope", 1) == 1
+    assert L.kmeans_plan_override(b"radix_items", 12) == 1
+    assert L.kmeans_plan_override(None, 1) == 1
+    base = L.kmeans_workspace_bytes(km.KM_OP_FIT, 16384, 32, 4096, km.KM_BF16, 0)
+    try:
+        assert L.kmeans_plan_override(b"assign_kernel", 2) == 0
+        L.kmeans_plan_describe(1 << 20, 128, 1024, km.KM_BF16, buf, len(buf))
+        assert b"single-accumulator" in buf.value
+        assert L.kmeans_plan_override(b"assign_split", 1) == 0
+        assert L.kmeans_workspace_bytes(km.KM_OP_FIT, 16384, 32, 4096, km.KM_BF16, 0) < base  # no split scratch
+        assert L.kmeans_plan_override(b"small_update", 1) == 0
+        L.kmeans_plan_describe(16384, 32, 64, km.KM_F32, buf, len(buf))
+        assert b"update: sorted" in buf.value
+    finally:
+        for k in km.PLAN_KEYS:
+            assert L.kmeans_plan_override(k.encode(), 0) == 0
+    assert L.kmeans_workspace_bytes(km.KM_OP_FIT, 16384, 32, 4096, km.KM_BF16, 0) == base
