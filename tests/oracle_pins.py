@@ -227,6 +227,11 @@ def pin_trajectory_1d(O):
     # the exact rational driver agrees with the golden file as well
     EC, ea, _, EJ = brute.fit([[v] for v in fr(g["X"])], [[v] for v in fr(g["C0"])], 3)
     assert [c[0] for c in EC] == fr(g["C3"]) and EJ == [fr(g[f"J{t}"])[0] for t in range(3)]
+    # J_t is the objective of assignment t against the centroids it was made with (C^t), exactly
+    Xr = [[v] for v in fr(g["X"])]
+    for t in range(3):
+        Ct = [[v] for v in fr(g[f"C{t}"])]
+        assert brute.objective(Xr, Ct, [int(v) for v in fr(g[f"a{t}"])]) == fr(g[f"J{t}"])[0], t
 
 
 def pin_symmetric_clouds(O):
