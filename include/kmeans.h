@@ -199,6 +199,14 @@ km_status kmeans_fit(const void* X, km_dtype dt, int64_t N, int64_t D, int64_t K
  * upload proceeds and returns once every byte of X has left the staging
  * buffer, so X_host and the staging buffer are free again on return; without
  * staging, keep X_host unchanged until compute_stream has been synchronised.
+ * On an error return the same holds: with staging, uploads already issued
+ * from the staging buffer have finished; work already enqueued on the two
+ * streams still runs, and the outputs are undefined until a later call
+ * succeeds (restart from the last good centroids: a fit of T - t
+ * iterations from C^t equals the uninterrupted one bit for bit).  Tests
+ * force the error path with the environment variable
+ * KM_FAULT_INJECT_UPLOAD=n, which fails the n-th chunk upload of a call
+ * before it is issued.
  * Synchronise compute_stream before reading any output.  Uploads into the
  * workspace start only after the work enqueued on compute_stream before the
  * call, so a workspace may be reused in compute-stream order.

@@ -323,11 +323,12 @@ def fit_streamed(X_host: torch.Tensor, C0: torch.Tensor, iters: int, chunk_rows:
     w = _ws(ws, nb, dev)
     cs = copy_stream if copy_stream is not None else torch.cuda.Stream(dev)
     # (the size asked for, not the buffer's: a larger reused buffer must not turn the warm start on)
-    _check(lib().kmeans_fit_streamed(_ptr(X_host), _dtype(X_host), N, D, K, _ptr(C), int(iters), int(chunk_rows),
-                                     _ptr(a), _ptr(counts), _ptr(obj), _ptr(w), nb,
-                                     ctypes.c_void_p(_stream(dev)), ctypes.c_void_p(cs.cuda_stream),
-                                     _ptr(stage), 0 if stage is None else stage.numel()))
-    _hold_until_done(dev, X_host, stage, a)
+    st = lib().kmeans_fit_streamed(_ptr(X_host), _dtype(X_host), N, D, K, _ptr(C), int(iters), int(chunk_rows),
+                                   _ptr(a), _ptr(counts), _ptr(obj), _ptr(w), nb,
+                                   ctypes.c_void_p(_stream(dev)), ctypes.c_void_p(cs.cuda_stream),
+                                   _ptr(stage), 0 if stage is None else stage.numel())
+    _hold_until_done(dev, X_host, stage, a)  # (also after a failed call: work it enqueued may still run)
+    _check(st)
     return C, a, counts, (obj[:iters] if obj is not None else None)
 
 

@@ -798,8 +798,24 @@ km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_
       events.push_back(slot_done[i]);
     }
   uint64_t slot_seq = 0;
+  // On every return, error or not, with staging: wait until the uploads already issued from the slots are
+  // done, so the caller may free or reuse the staging buffer (and pageable X) as soon as the call returns.
+  struct StagingDrain {
+    const bool on;
+    const uint64_t& seq;
+    hipEvent_t* done;
+    ~StagingDrain() {
+      if (on)
+        for (uint64_t i = 0; i < seq && i < (uint64_t)kStageSlots; ++i) (void)hipEventSynchronize(done[i]);
+    }
+  } drain{stage_host != nullptr, slot_seq, slot_done};
+  // Fault injection for tests of the error path: KM_FAULT_INJECT_UPLOAD=n makes the n-th chunk upload of
+  // this call fail before it is issued, as a failed copy would (the call returns KM_ERR_HIP).
+  int64_t fail_upload = 0, uploads = 0;
+  if (const char* e = std::getenv("KM_FAULT_INJECT_UPLOAD")) fail_upload = std::atoll(e);
   // Upload `bytes` of host X to `dst`: one copy from pinned X, or slot by slot through the staging ring.
   auto upload = [&](uint8_t* dst, const uint8_t* src, size_t bytes) -> hipError_t {
+    if (++uploads == fail_upload) return hipErrorUnknown;
     if (!stage_host) return hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, xs);
     for (size_t off = 0; off < bytes; off += slot_bytes, ++slot_seq) {
       const size_t n = std::min(slot_bytes, bytes - off);
@@ -857,7 +873,7 @@ km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_
   // the staging buffer (and pageable X) can be reused as soon as this returns.
   if (stage_host)
     for (uint64_t i = 0; i < slot_seq && i < (uint64_t)kStageSlots; ++i) KM_HIP(hipEventSynchronize(slot_done[i]));
-  return KM_OK;
+  return KM_OK;  // (the drain guard then finds every slot done)
 }
 
 km_status kmeans_plan_override(const char* key, int64_t value) {

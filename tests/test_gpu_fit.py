@@ -206,3 +206,61 @@ def test_fit_trajectory_1d():
     assert C.cpu().flatten().tolist() == [0.5, 10.5]
     assert a.cpu().tolist() == [0, 0, 1, 1]
     np.testing.assert_allclose(obj.cpu().numpy(), [181.0, 194.0 / 9.0, 1.0], rtol=1e-5)
+
+
+@pytest.mark.parametrize("pageable", [False, True])
+def test_fit_streamed_injected_upload_failure_then_restart(pageable, monkeypatch):
+    """A copy that fails mid-stream (forced from the host: KM_FAULT_INJECT_UPLOAD) returns KM_ERR_HIP without a
+    fault, with the staging buffer drained; the same call then runs cleanly and equals a fresh run bit for bit."""
+    w, Xn, C0 = _workload("c4", N=30_000, K=300)
+    X = parity.x_from_numpy(Xn, "bf16", DEV).cpu()
+    Xh = X if pageable else X.pin_memory()
+    stage = km.staging_buffer(4 * 1000 * w.D * 2) if pageable else None
+    C0t = torch.from_numpy(C0).to(DEV)
+    ws = km.Workspace(DEV)
+    monkeypatch.setenv("KM_FAULT_INJECT_UPLOAD", "5")  # the 5th of 2 x 7 chunk uploads (second iteration)
+    with pytest.raises(km.KMeansError) as e:
+        km.fit_streamed(Xh, C0t, 2, 4500, ws=ws, stage=stage)
+    assert e.value.status == 4 and "h2d" in str(e.value)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("KM_FAULT_INJECT_UPLOAD")
+    r1 = km.fit_streamed(Xh, C0t, 2, 4500, ws=ws, stage=stage)
+    r2 = km.fit_streamed(Xh, C0t, 2, 4500, ws=km.Workspace(DEV), stage=stage)
+    torch.cuda.synchronize()
+    for i in range(3):
+        assert torch.equal(r1[i], r2[i])
+    C_prev = km.fit_streamed(Xh, C0t, 1, 4500, stage=stage)[0]
+    torch.cuda.synchronize()
+    parity.check_update(Xn, "bf16", r1[1].numpy(), C_prev.cpu().numpy(), r1[0].cpu().numpy(), r1[2].cpu().numpy(),
+                        label="after an injected upload failure")
+
+
+def _poisoned(byte):
+    ws = km.Workspace(DEV)
+    ws.get(1 << 28, DEV).fill_(byte)  # every call below fits in it
+    return ws
+
+
+@pytest.mark.parametrize("case", [("c1", "f32", 16_384, 32, 64), ("c1", "f32", 40_000, 32, 50),
+                                  ("c2", "bf16", 16_384, 64, 600), ("c2", "bf16", 50_000, 128, 1024),
+                                  ("c2", "bf16", 5_000, 64, 4_800), ("c2", "bf16", 5_000, 700, 100)],
+                         ids=lambda c: f"{c[1]}-N{c[2]}-D{c[3]}-K{c[4]}")
+def test_workspace_content_is_never_read_before_written(case):
+    """The workspace may hold anything: fits with a workspace full of 0xFF bytes (NaN patterns, all ones) and
+    full of zeros give the same results bit for bit, on every update path (one-launch and chunked small
+    codebooks, sorted, split sweep, deep rows) and for the batched and streamed fits."""
+    name, xdt, N, D, K = case
+    w, Xn, C0 = _workload(name, N=N, D=D, K=K, M=min(K, 1024))
+    X = parity.x_from_numpy(Xn, w.dtype, DEV)
+    C0t = torch.from_numpy(C0).to(DEV)
+    outs = []
+    Xh = X.cpu().pin_memory()
+    for byte in (0xFF, 0x00):
+        C, a, n, J = km.fit(X, C0t, 3, objective=True, ws=_poisoned(byte))
+        Cb, ab, nb, Jb = km.fit_batched(torch.stack([X, X]), torch.stack([C0t, C0t]), 2, objective=True,
+                                        ws=_poisoned(byte))
+        Cs, as_, ns, Js = km.fit_streamed(Xh, C0t, 2, max(N // 3, 1), objective=True, ws=_poisoned(byte))
+        torch.cuda.synchronize()
+        outs.append([C, a, n, J, Cb, ab, nb, Jb, Cs, as_, ns, Js])
+    for i, (u, v) in enumerate(zip(*outs)):
+        assert torch.equal(u.cpu(), v.cpu()), f"output {i} depends on the workspace's prior content"
