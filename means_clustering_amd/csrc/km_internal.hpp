@@ -248,16 +248,16 @@ inline int64_t seg_fine_max_bytes() { return device_info().llc_bytes / 2; }
 #endif
 constexpr int kRadixThreads = 256;
 constexpr int kRadixMaxItems = 32;           // consecutive keys per thread: 8, 16 or 32 (block positions fit in 16 bits)
-// Keys per thread for N keys: blocks of 2048..8192 keys, small enough that
-// several blocks per compute unit share the work when N allows: 8192-key
-// blocks from 8 per compute unit, 4096-key blocks from 4 (measured on gfx950
-// by the planner study: 2^23 keys sort 1% faster in 2,048 blocks than in
-// 1,024, and 2^26 keys fastest in 8,192-key blocks).
+// Keys per thread for N keys: 8192-key blocks from 8 blocks per compute
+// unit, 4096-key blocks from one per compute unit, else 2048-key blocks
+// (measured on gfx950 by the planner study, whole fits: 2^20 keys 0.2-1.1%
+// faster in 4096-key blocks than in 2048, 2^23 keys 1% faster in 4096 than in
+// 8192, 2^26 keys fastest in 8192-key blocks).
 inline int radix_items(int64_t N) {
   const int ov = plan_override().radix_items;
   if (ov == 8 || ov == 16 || ov == 32) return ov;
   const int64_t cus = device_info().cus;
-  return N >= 8 * cus * 8192 ? 32 : (N >= 4 * cus * 4096 ? 16 : 8);
+  return N >= 8 * cus * 8192 ? 32 : (N >= cus * 4096 ? 16 : 8);
 }
 constexpr int kMaxDigitBits = 6;             // digits of at most 64 values per pass
 constexpr int kSegTile = KM_SEG_TILE;

@@ -192,3 +192,23 @@ def test_deep_fit_streamed(xdtype):
         parity.check_assign(Xn, xdt, Cp, an, label=f"deep streamed it{t}")
         parity.check_update(Xn, xdt, an, Cp, C.cpu().numpy(), n.cpu().numpy(), label=f"deep streamed it{t}")
     assert torch.equal(C, C_all) and torch.equal(n, n_all) and np.array_equal(a_host.numpy(), a_all.numpy())
+
+
+@pytest.mark.parametrize("case", [("bf16", 300, 20_000, 9, 2), ("f32", 200, 5_000, 6, 2), ("f16", 700, 8_192, 40, 2)],
+                         ids=lambda c: f"{c[0]}-N{c[1]}-D{c[2]}-K{c[3]}")
+def test_deep_fit_very_long_rows(case):
+    """Rows of thousands of values: tens of depth chunks per tile and up to 40 column strips per update."""
+    xdtype, N, D, K, T = case
+    X, C0 = _mixture(N, D, K, xdtype, seed=D)
+    Xn, xdt = parity.x_to_numpy(X)
+    print(f"[deep] very long rows {case}: {km.plan_describe(N, D, K, X.dtype)}", flush=True)
+    C = C0
+    for t in range(T):
+        C_prev = C
+        C, a, n, J = km.fit(X, C_prev, 1, objective=True)
+        torch.cuda.synchronize()
+        Cp = C_prev.cpu().numpy()
+        an = a.cpu().numpy()
+        parity.check_assign(Xn, xdt, Cp, an, label=f"very long rows {case} it{t}")
+        parity.check_update(Xn, xdt, an, Cp, C.cpu().numpy(), n.cpu().numpy(), label=f"very long rows {case} it{t}")
+        parity.check_objective(Xn, xdt, Cp, an, J.cpu().numpy()[0], label=f"very long rows {case} it{t}")
