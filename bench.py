@@ -16,6 +16,7 @@ whole-update roofline and CPU baseline.  Prints one JSON line.
   python bench.py --workload c1 --batch 256      (256 independent c1-shaped problems per call)
   python bench.py --ablation                     (the designs FlashAssign and Sort-Inverse Update replace)
   python bench.py --planner-study                (the static plan against every alternative, five shapes)
+  python bench.py --segment-tile-study           (update time, short vs long segment tiles, N = 2^13..2^22)
 """
 from __future__ import annotations
 
@@ -626,6 +627,54 @@ def planner_study(args, dev):
     print(json.dumps(out), flush=True)
 
 
+def segment_tile_study(dev):
+    """Sort-Inverse Update time with short (16-position) against long (128-position) segment tiles, over N.
+
+    The planner takes short tiles while N rows of G 16-byte lanes fit in half the last-level cache; this sweep
+    places that threshold.  Three row shapes (bf16 D = 128 and D = 64, fp32 D = 32) against a sorted-path
+    codebook, N = 2^13 .. 2^22, uniform random assignment; each point is the best of three runs of many updates.
+    """
+    import torch
+
+    import means_clustering_amd as km
+
+    out = {"segment_tile_study": "kmeans_update, short vs long segment tiles, one GPU", "rows": []}
+    for dt, D, K in [(torch.bfloat16, 128, 1024), (torch.bfloat16, 64, 4096), (torch.float32, 32, 1024)]:
+        lane_bytes = 16 * (1 << max(0, ((D * (4 if dt == torch.float32 else 2) + 15) // 16 - 1).bit_length()))
+        for logn in range(13, 23):
+            N = 1 << logn
+            g = torch.Generator(device=dev).manual_seed(logn)
+            X = torch.randn(N, D, device=dev, generator=g).to(dt)
+            C = torch.randn(K, D, device=dev, generator=g)
+            a = torch.randint(0, K, (N,), device=dev, generator=g, dtype=torch.int32)
+            row = {"dtype": str(dt).split(".")[1], "D": D, "K": K, "N": N, "rows_bytes": N * lane_bytes}
+            km.plan_override("small_update", 1)
+            try:
+                for tile in (1, 2):
+                    km.plan_override("reduce_tile", tile)
+                    C_new, counts = km.update(X, a, C)
+                    torch.cuda.synchronize()
+                    reps = max(20, min(2000, (1 << 24) // N))
+                    best = float("inf")
+                    for _ in range(3):
+                        t0 = time.perf_counter()
+                        for _ in range(reps):
+                            km.update(X, a, C, out=C_new, counts_out=counts)
+                        torch.cuda.synchronize()
+                        best = min(best, (time.perf_counter() - t0) / reps * 1e6)
+                    row["long_us" if tile == 1 else "short_us"] = round(best, 2)
+            finally:
+                km.plan_override("reduce_tile", 0)
+                km.plan_override("small_update", 0)
+            plan = km.plan_describe(N, D, K, dt)
+            row["planner_tile"] = int(plan.split("segment tile ")[1].split(",")[0]) if "segment tile " in plan else None
+            row["device"] = plan.split("device: ")[1]
+            print(f"[bench] segment tiles {json.dumps(row)}", file=sys.stderr, flush=True)
+            out["rows"].append(row)
+            del X, C, a
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -648,6 +697,8 @@ def main():
     ap.add_argument("--planner-study", action="store_true",
                     help="only time the static plan against every single-choice alternative on the five shapes "
                          "(one JSON line)")
+    ap.add_argument("--segment-tile-study", action="store_true",
+                    help="only time the update with short and long segment tiles over N (one JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -674,6 +725,10 @@ def main():
     if args.planner_study:
         import torch
         planner_study(args, torch.device("cuda:0"))
+        return
+    if args.segment_tile_study:
+        import torch
+        segment_tile_study(torch.device("cuda:0"))
         return
     if args.batch > 1:
         import torch

@@ -119,8 +119,10 @@ int64_t kfd_llc_bytes(int domain, int bus, int dev) {
     }
     // location_id = bus << 8 | device << 3 | function
     if (simds <= 0 || dom != domain || (loc >> 8) != bus || ((loc >> 3) & 31) != dev) continue;
+    // A gfx950 node lists every compute unit's L1 caches (over 500 entries)
+    // before its L2 and its Infinity Cache: walk them all.
     int best_level = 0;
-    for (int c = 0; c < 64; ++c) {
+    for (int c = 0; c < (1 << 16); ++c) {
       std::ifstream cp(base + "/caches/" + std::to_string(c) + "/properties");
       if (!cp) break;
       int64_t level = 0, size_kb = 0;

@@ -47,3 +47,44 @@ def test_alternative_plan_matches_oracle(case, override):
         assert torch.equal(C, C2) and torch.equal(a, a2) and torch.equal(n, n2), "2 calls != one call of 2"
     finally:
         km.plan_override(override[0], 0)
+
+
+def _kfd_largest_cache(domain, bus, dev):
+    """Size in bytes of the highest-level cache the KFD topology lists for this GPU (0 if none is found)."""
+    import glob
+    import os
+    for node in glob.glob("/sys/class/kfd/kfd/topology/nodes/*"):
+        try:
+            with open(os.path.join(node, "properties")) as f:
+                props = dict(line.split() for line in f if len(line.split()) == 2)
+        except OSError:
+            continue
+        loc = int(props.get("location_id", -1))
+        if int(props.get("simd_count", 0)) <= 0 or int(props.get("domain", -1)) != domain:
+            continue
+        if (loc >> 8) != bus or ((loc >> 3) & 31) != dev:
+            continue
+        best = (0, 0)
+        for c in glob.glob(os.path.join(node, "caches", "*", "properties")):
+            with open(c) as f:
+                p = dict(line.split() for line in f if len(line.split()) == 2)
+            best = max(best, (int(p.get("level", 0)), int(p.get("size", 0)) * 1024))
+        return best[1]
+    return 0
+
+
+def test_device_query_finds_the_last_level_cache():
+    """The planner's last-level cache is the highest cache level KFD lists for the device (the Infinity Cache on
+    MI355X, listed after hundreds of per-CU L1 entries), never less than the L2 HIP reports."""
+    props = torch.cuda.get_device_properties(0)
+    kfd = _kfd_largest_cache(props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
+    desc = km.plan_describe(1 << 20, 128, 1024, torch.bfloat16)
+    print(f"[planner] device: {desc.split('device: ')[1]}; KFD highest-level cache {kfd >> 20} MiB", flush=True)
+    llc_mib = int(desc.split("LLC ")[1].split(" MiB")[0])
+    assert "(queried)" in desc
+    assert llc_mib == max(kfd, props.L2_cache_size) >> 20
+    if kfd:
+        # the short segment tiles reach N * G * 16 bytes = half that cache: at D = 64 (G = 8), 2^20 rows on MI355X
+        n_half = (kfd // 2) // (8 * 16)
+        assert "segment tile 16" in km.plan_describe(n_half, 64, 4096, torch.bfloat16)
+        assert "segment tile 128" in km.plan_describe(2 * n_half, 64, 4096, torch.bfloat16)
