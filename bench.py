@@ -542,8 +542,8 @@ def planner_study(args, dev):
     """The static planner against every alternative it could have chosen, on the five workload shapes.
 
     For each shape: kmeans_fit of the workload's iterations with the planner's own choice, then with each single
-    override that changes the plan (kmeans_plan_override), median of several fits; the gap is the static choice's
-    time over the fastest plan's.  Time to first run: the host-side planning cost (kmeans_plan_describe +
+    override that changes the plan (kmeans_plan_override), median of several fits timed in rounds that take every
+    plan once, in rotated order; the gap is the static choice's time over the fastest plan's.  Time to first run: the host-side planning cost (kmeans_plan_describe +
     kmeans_workspace_bytes, no compilation anywhere) and the first fit of each shape in the process against the
     steady state.  The c5 shape is timed resident, one 2^26-row chunk of it (the kernels its streamed fit runs).
     """
@@ -557,7 +557,7 @@ def planner_study(args, dev):
     shapes = [("c1", synth.WORKLOADS["c1"]), ("c2", synth.WORKLOADS["c2"]), ("c3", synth.WORKLOADS["c3"]),
               ("c4", synth.WORKLOADS["c4"]), ("c5", synth.WORKLOADS["c5"].scaled(N=1 << 26, chunk_rows=0))]
     out = {"planner_study": "static plan vs every single-choice alternative, one GPU", "shapes": {}}
-    reps = 5
+    reps = 7
     for name, w in shapes:
         print(f"[bench] planner study {name}: {w.description}", file=sys.stderr, flush=True)
         tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
@@ -567,54 +567,70 @@ def planner_study(args, dev):
         a = torch.empty(w.N, dtype=torch.int32, device=dev)
         cnt = torch.empty(w.K, dtype=torch.int32, device=dev)
         C = C0.clone()
-        # host planning cost: plan + workspace size, per call
+        # host planning cost: plan + workspace size, per call (the device query, once per process, done before)
+        km.plan_describe(w.N, w.D, w.K, tdt)
         t0 = time.perf_counter()
         for _ in range(200):
             km.plan_describe(w.N, w.D, w.K, tdt)
             L.kmeans_workspace_bytes(km.KM_OP_FIT, w.N, w.D, w.K, km._DT[tdt], 0)
         plan_us = (time.perf_counter() - t0) / 200 * 1e6
 
-        def run(ws, timing=False):
+        def run(ws):
             C.copy_(C0)
             km.fit(X, C, w.iters, inplace=True, ws=ws, assign_out=a, counts_out=cnt)
-
-        def measure(label):
-            ws = km.Workspace(dev)
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            run(ws)
-            torch.cuda.synchronize()
-            first = time.perf_counter() - t0
-            times = []
-            for _ in range(reps):
-                t0 = time.perf_counter()
-                run(ws)
-                torch.cuda.synchronize()
-                times.append(time.perf_counter() - t0)
-            a_ref = a.clone()
-            return {"plan": km.plan_describe(w.N, w.D, w.K, tdt), "first_fit_ms": round(first * 1e3, 3),
-                    "fit_ms": round(float(np.median(times)) * 1e3, 3)}, a_ref
 
         def kernels_of(plan):  # the plan without its workspace size (carved for every path)
             return plan.split("; workspace")[0]
 
-        static, a_static = measure("static")
-        variants, seen = [], {kernels_of(static["plan"])}
+        # the plans: the static one, then every single override that changes the kernels
+        plans = [(None, km.plan_describe(w.N, w.D, w.K, tdt))]
+        seen = {kernels_of(plans[0][1])}
         for key, val in STUDY_KEYS.get(name, STUDY_KEYS["default"]):
             km.plan_override(key, val)
             try:
                 plan = km.plan_describe(w.N, w.D, w.K, tdt)
-                if kernels_of(plan) in seen:
-                    continue
-                seen.add(kernels_of(plan))
-                r, a_var = measure(f"{key}={val}")
-                # every plan reaches the same final assignment (sums may round differently, so only counts
-                # of agreement are reported: the trajectories may part after a near tie)
-                r["override"] = {key: val}
-                r["same_final_assignment"] = bool(torch.equal(a_var, a_static))
-                variants.append(r)
             finally:
                 km.plan_override(key, 0)
+            if kernels_of(plan) not in seen:
+                seen.add(kernels_of(plan))
+                plans.append(((key, val), plan))
+
+        def with_plan(ov, fn):
+            if ov:
+                km.plan_override(*ov)
+            try:
+                return fn()
+            finally:
+                if ov:
+                    km.plan_override(ov[0], 0)
+
+        def timed(ws):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            run(ws)
+            torch.cuda.synchronize()
+            return time.perf_counter() - t0
+
+        # first fit of each plan (the static one first: the shape's first fit in the process), then rounds that
+        # time every plan once each, in an order rotated from round to round, so that the GPU's clock drift
+        # over the study falls on all plans alike
+        wss = [km.Workspace(dev) for _ in plans]
+        first = [with_plan(ov, lambda i=i: timed(wss[i])) for i, (ov, _) in enumerate(plans)]
+        times = [[] for _ in plans]
+        finals = [None] * len(plans)
+        for r in range(reps):
+            for j in range(len(plans)):
+                i = (j + r) % len(plans)
+                times[i].append(with_plan(plans[i][0], lambda i=i: timed(wss[i])))
+                finals[i] = a.clone()
+        res = [{"plan": plan, "first_fit_ms": round(first[i] * 1e3, 3),
+                "fit_ms": round(float(np.median(times[i])) * 1e3, 3)} for i, (_, plan) in enumerate(plans)]
+        static, variants = res[0], res[1:]
+        for i, r in enumerate(variants, 1):
+            # every plan reaches the same final assignment (sums may round differently, so only agreement is
+            # reported: the trajectories may part after a near tie)
+            r["override"] = {plans[i][0][0]: plans[i][0][1]}
+            r["same_final_assignment"] = bool(torch.equal(finals[i], finals[0]))
         best = min([static] + variants, key=lambda r: r["fit_ms"])
         out["shapes"][name] = {
             "workload": w.description if name != "c5" else "one 2^26-row chunk of " + w.description,

@@ -42,7 +42,8 @@
 //     centroid; the block first scores the group of 32 centroids holding it
 //     (exact MFMA values), which gives every point a score its final best
 //     must reach, and the sweep then needs only the group maxima, scanning a
-//     group exactly when some lane's maximum beats the lane's running best.
+//     point group's scores exactly when some lane's maximum beats the lane's
+//     running best.
 //     The result is the same argmax as the full scan, bit for bit.
 #include <math.h>
 
@@ -302,17 +303,26 @@ __device__ __forceinline__ void fold_first(const f32x16_t (&in)[NB], float (&m)[
   for (int g = 0; g < NB; ++g) m[g] = fmaxf(in[g][0], in[g][1]);
 }
 
-// Lazy running argmax, slow part: only when some lane's group maximum beats
-// its running best does the wavefront scan the group's scores exactly; the
-// result is the same as scanning every group exactly (a group whose maximum
-// does not exceed the best cannot change the lowest-index argmax).
+// Lazy running argmax, slow part: a point group's scores are scanned exactly
+// only when some lane's group maximum beats its running best, each point
+// group on its own (a block where one point moves scans that point's group of
+// 32, not the wavefront's every point group).  The result is the same as
+// scanning every group exactly: a group whose maximum does not exceed the best
+// cannot change the lowest-index argmax.
+template <int E0, int E1>
+__device__ __forceinline__ void argmax_one(const f32x16_t& in, float& best, int& rel) {
+  if constexpr (E0 < E1 && E0 < 16) {
+    argmax_update<E0>(in[E0], best, rel);
+    argmax_one<E0 + 1, E1>(in, best, rel);
+  }
+}
+
 template <int NB>
 __device__ __forceinline__ void lazy_resolve(const f32x16_t (&in)[NB], const float (&m)[NB], float (&best)[NB],
                                              int (&rel)[NB]) {
-  bool imp = false;
 #pragma unroll
-  for (int g = 0; g < NB; ++g) imp |= m[g] > best[g];
-  if (__builtin_amdgcn_ballot_w64(imp)) argmax_range<0, 16, NB>(in, best, rel);
+  for (int g = 0; g < NB; ++g)
+    if (__builtin_amdgcn_ballot_w64(m[g] > best[g])) argmax_one<0, 16>(in[g], best[g], rel[g]);
 }
 
 // Deferred argmax (the single-accumulator kernel), per group: a lane keeps only its best score and the first
