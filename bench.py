@@ -73,6 +73,8 @@ def measured_peaks(dev, dtype):
                                  ctypes.POINTER(ctypes.c_double)]
     lib.km_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                  ctypes.POINTER(ctypes.c_double)]
+    lib.km_peak_lds.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_double),
+                                ctypes.POINTER(ctypes.c_double)]
     out = {}
     blocks = 512  # two workgroups (two wavefronts per SIMD) per CU
     scratch = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
@@ -94,6 +96,15 @@ def measured_peaks(dev, dtype):
                         ctypes.byref(gb)) == 0:
         out["hbm_read_GBps"] = round(gb.value, 1)
     del src, dst, rs
+    # LDS reads per compute unit (FlashAssign at D = 64 issues one 1 KiB LDS read per MFMA)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    lds_scratch = torch.empty(2 * cus * (4 * 8 + 256 * 16), dtype=torch.uint8, device=dev)
+    bpc, tb = ctypes.c_double(), ctypes.c_double()
+    if lib.km_peak_lds(40000, ctypes.c_void_p(lds_scratch.data_ptr()), lds_scratch.numel(), ctypes.byref(bpc),
+                       ctypes.byref(tb)) == 0:
+        out["lds_read_bytes_per_clock_per_cu"] = round(bpc.value, 1)
+        out["lds_read_TBps"] = round(tb.value, 1)
+    del lds_scratch
     # pinned host -> device: 1 GiB copies after two untimed ones (first-touch and mapping costs), best of 5
     h = torch.ones(1 << 30, dtype=torch.uint8, pin_memory=True)
     d = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

@@ -1,5 +1,6 @@
 // Same-run peak probes for the roofline denominators: the sustained matrix-core
-// rate of the MFMA shape FlashAssign uses, and device memory copy bandwidth.
+// rate of the MFMA shape FlashAssign uses, device memory copy and read
+// bandwidth, and LDS read bandwidth per compute unit.
 // Not part of the clustering path; the benchmark reports these next to the
 // datasheet peaks, because on a power-limited part the sustained matrix-core
 // rate with real-valued operands sits well below the datasheet figure.
@@ -97,6 +98,31 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4_t* __restrict__ s
   out[(int64_t)blockIdx.x * 256 + threadIdx.x] = x;
 }
 
+// LDS reads: every lane reads 16 bytes a step, consecutive lanes on
+// consecutive addresses (no bank conflicts), four reads in flight, from a
+// 64 KiB buffer; each wavefront records the shader clocks its loop took.
+__global__ __launch_bounds__(256) void lds_read_kernel(int iters, int64_t* __restrict__ clocks,
+                                                       u32x4_t* __restrict__ out) {
+  __shared__ u32x4_t buf[4096];
+  const int t = threadIdx.x;
+  for (int i = t; i < 4096; i += 256) buf[i] = u32x4_t{(uint32_t)i, (uint32_t)i * 3u, (uint32_t)i * 5u, (uint32_t)i * 7u};
+  __syncthreads();
+  const int lane = t & 63, wave = t >> 6;
+  const int base = (wave * 64 + lane) & 4095;
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  const int64_t c0 = clock64();
+  for (int i = 0; i < iters; i += 4) {
+    const u32x4_t v0 = buf[(base + (i + 0) * 256) & 4095];
+    const u32x4_t v1 = buf[(base + (i + 1) * 256) & 4095];
+    const u32x4_t v2 = buf[(base + (i + 2) * 256) & 4095];
+    const u32x4_t v3 = buf[(base + (i + 3) * 256) & 4095];
+    acc += v0 + v1 + v2 + v3;
+  }
+  const int64_t c1 = clock64();
+  if (lane == 0) clocks[blockIdx.x * 4 + wave] = c1 - c0;
+  out[blockIdx.x * 256 + t] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -183,6 +209,60 @@ int km_peak_read(const void* src, int64_t bytes, int reps, void* scratch, double
   if (e != hipSuccess) return (int)e;
   *gbps = (double)bytes * reps / (ms * 1e-3) / 1e9;
   return 0;
+}
+
+// LDS read bandwidth: two workgroups of 4 wavefronts per compute unit (8
+// wavefronts, 128 KiB of LDS), each wavefront reading `iters` x 1 KiB
+// (`iters` a multiple of 4).  `scratch` holds 2 * cus * (4 * 8 + 256 * 16)
+// bytes (device).  Returns the bytes read per shader clock per compute unit
+// (from the median wavefront's clock count) and the aggregate rate in TB/s.
+// Synchronous.
+int km_peak_lds(int iters, void* scratch, int64_t scratch_bytes, double* bytes_per_clock_cu, double* tbps) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return (int)e;
+  const int blocks = 2 * cus;
+  if (iters < 4 || iters % 4 || !scratch || !bytes_per_clock_cu || !tbps ||
+      scratch_bytes < (int64_t)blocks * (4 * 8 + 256 * 16))
+    return (int)hipErrorInvalidValue;
+  int64_t* clocks = static_cast<int64_t*>(scratch);
+  u32x4_t* out = reinterpret_cast<u32x4_t*>(static_cast<char*>(scratch) + (int64_t)blocks * 4 * 8);
+  hipEvent_t e0, e1;
+  if ((e = hipEventCreate(&e0)) != hipSuccess) return (int)e;
+  if ((e = hipEventCreate(&e1)) != hipSuccess) return (int)e;
+  hipLaunchKernelGGL(lds_read_kernel, dim3((unsigned)blocks), dim3(256), 0, 0, 64, clocks, out);  // warm-up
+  hipEventRecord(e0, 0);
+  hipLaunchKernelGGL(lds_read_kernel, dim3((unsigned)blocks), dim3(256), 0, 0, iters, clocks, out);
+  hipEventRecord(e1, 0);
+  e = hipEventSynchronize(e1);
+  float ms = 0.0f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (e != hipSuccess) return (int)e;
+  int64_t* host = new int64_t[(size_t)blocks * 4];
+  e = hipMemcpy(host, clocks, sizeof(int64_t) * blocks * 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) {
+    // median by counting (blocks * 4 values)
+    const int n = blocks * 4;
+    int64_t med = host[0];
+    for (int i = 0; i < n; ++i) {
+      int below = 0, equal = 0;
+      for (int j = 0; j < n; ++j) {
+        below += host[j] < host[i];
+        equal += host[j] == host[i];
+      }
+      if (below <= n / 2 && n / 2 < below + equal) {
+        med = host[i];
+        break;
+      }
+    }
+    *bytes_per_clock_cu = med > 0 ? 8.0 * iters * 1024.0 / (double)med : 0.0;
+    *tbps = (double)blocks * 4 * iters * 1024.0 / (ms * 1e-3) / 1e12;
+  }
+  delete[] host;
+  return (int)e;
 }
 
 }  // extern "C"
