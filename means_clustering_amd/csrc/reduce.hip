@@ -83,7 +83,7 @@ struct SegParams {
   int64_t ldx;       // row stride of X and of the centroid arrays, in elements (the full D)
   bool first_strip;  // counts are added to running totals by the first strip only
   int64_t K;
-  bool vec_ok;
+  bool vec_ok;  // X rows and the output rows are whole 16-byte pieces, 16-byte aligned
   const int32_t* keys;
   const int32_t* vals;
   int32_t* off;  // K+1 cluster offsets, written by the segmented reduction
@@ -110,10 +110,17 @@ struct SegParams {
 
 // Write a finished segment (or a carry piece) held by one lane group.  A
 // segment is finished here when it both starts and ends inside this tile
-// (`complete`, known from the id changes the walk has seen).
-template <int EPL, int CPL, int G>
+// (`complete`, known from the id changes the walk has seen).  A lane's EPL
+// consecutive values leave as 16-byte stores: always for a carry piece, and
+// for a finished mean when the rows are whole 16-byte pieces with 16-byte
+// aligned outputs (VEC) and span at least 8 lanes (measured on gfx950: one
+// 4-byte store per value, strided over the row, made c3's 65,536 short
+// segments cost 1.4x; narrower rows would lose a wavefront per SIMD to the
+// extra registers).
+template <int EPL, int CPL, int G, bool VEC>
 __device__ __forceinline__ void flush_piece(const SegParams& P, int64_t tile, int32_t first_key, int32_t k,
                                             bool complete, const float (&acc)[CPL][EPL], int32_t cnt, int j) {
+  static_assert(EPL % 4 == 0, "a lane's values are whole 16-byte pieces");
   if (k < 0 || k >= P.K) return;  // sorted ids lie in [0, K)
   if (complete) {
     if (P.mode == MODE_MEAN) {
@@ -122,12 +129,20 @@ __device__ __forceinline__ void flush_piece(const SegParams& P, int64_t tile, in
 #pragma unroll
       for (int q = 0; q < CPL; ++q) {
         const int c0 = (j + q * G) * EPL;
+        if (VEC && G >= 8 && cnt > 0 && c0 + EPL <= P.D) {
+          float4* dst = reinterpret_cast<float4*>(P.C_new + (int64_t)k * P.ldx + c0);
 #pragma unroll
-        for (int x = 0; x < EPL; ++x) {
-          const int c = c0 + x;
-          if (c < P.D) {
-            const int64_t o = (int64_t)k * P.ldx + c;
-            P.C_new[o] = cnt > 0 ? acc[q][x] / fcnt : P.C_prev[o];
+          for (int x = 0; x < EPL; x += 4)
+            dst[x / 4] = make_float4(acc[q][x] / fcnt, acc[q][x + 1] / fcnt, acc[q][x + 2] / fcnt,
+                                     acc[q][x + 3] / fcnt);
+        } else {
+#pragma unroll
+          for (int x = 0; x < EPL; ++x) {
+            const int c = c0 + x;
+            if (c < P.D) {
+              const int64_t o = (int64_t)k * P.ldx + c;
+              P.C_new[o] = cnt > 0 ? acc[q][x] / fcnt : P.C_prev[o];
+            }
           }
         }
       }
@@ -143,15 +158,15 @@ __device__ __forceinline__ void flush_piece(const SegParams& P, int64_t tile, in
         }
       }
     }
-  } else {  // cut by a tile edge: leave a carry piece
+  } else {  // cut by a tile edge: leave a carry piece (Dc floats, 16-byte aligned)
     const int slot = k == first_key ? 0 : 1;
     float* dst = P.carry_sum + (tile * 2 + slot) * (int64_t)P.Dc;
     if (j == 0) P.carry_cnt[tile * 2 + slot] = cnt;
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
-      const int c0 = (j + q * G) * EPL;
+      float4* d4 = reinterpret_cast<float4*>(dst + (j + q * G) * EPL);
 #pragma unroll
-      for (int x = 0; x < EPL; ++x) dst[c0 + x] = acc[q][x];
+      for (int x = 0; x < EPL; x += 4) d4[x / 4] = make_float4(acc[q][x], acc[q][x + 1], acc[q][x + 2], acc[q][x + 3]);
     }
   }
 }
@@ -255,7 +270,7 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
           if (in[u]) {
             if (kk[u] != cur) {  // the current segment ends inside the tile
               write_offsets(cur, kk[u], p0 + b0 + u);
-              flush_piece<EPL, CPL, G>(P, tile, first_key, cur, started, acc, cnt, j);
+              flush_piece<EPL, CPL, G, VEC>(P, tile, first_key, cur, started, acc, cnt, j);
               cur = kk[u];
               cnt = 0;
               started = true;
@@ -276,7 +291,7 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
         }
       }
     }
-    flush_piece<EPL, CPL, G>(P, tile, first_key, cur, started && after_key != cur, acc, cnt, j);
+    flush_piece<EPL, CPL, G, VEC>(P, tile, first_key, cur, started && after_key != cur, acc, cnt, j);
     if (pe == P.N) write_offsets(cur, P.K, P.N);  // ids after the last one start (and end) at N
   }
   if (!solid) return;
@@ -476,6 +491,8 @@ static SegParams make_params(const ReduceArgs& a) {
   P.counts = a.counts;
   P.acc_sum = a.acc_sum ? a.acc_sum + c0 : nullptr;
   P.acc_cnt = a.acc_cnt;
+  auto al16 = [](const void* q) { return q == nullptr || ((uintptr_t)q) % 16 == 0; };
+  P.vec_ok = P.vec_ok && al16(P.C_new) && al16(P.C_prev) && al16(P.acc_sum);
   return P;
 }
 
