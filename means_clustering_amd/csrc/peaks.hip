@@ -99,9 +99,10 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4_t* __restrict__ s
 }
 
 // LDS reads: every lane reads 16 bytes a step, consecutive lanes on
-// consecutive addresses (no bank conflicts), four reads in flight, from a
-// 64 KiB buffer; each wavefront records the shader clocks its loop took.
-__global__ __launch_bounds__(256) void lds_read_kernel(int iters, int64_t* __restrict__ clocks,
+// consecutive addresses (no bank conflicts; `stride` 256 slots between a
+// lane's steps), eight reads in flight, from a 64 KiB buffer; each wavefront
+// records the shader clocks its loop took.
+__global__ __launch_bounds__(256) void lds_read_kernel(int iters, int stride, int64_t* __restrict__ clocks,
                                                        u32x4_t* __restrict__ out) {
   __shared__ u32x4_t buf[4096];
   const int t = threadIdx.x;
@@ -111,12 +112,14 @@ __global__ __launch_bounds__(256) void lds_read_kernel(int iters, int64_t* __res
   const int base = (wave * 64 + lane) & 4095;
   u32x4_t acc = {0u, 0u, 0u, 0u};
   const int64_t c0 = clock64();
-  for (int i = 0; i < iters; i += 4) {
-    const u32x4_t v0 = buf[(base + (i + 0) * 256) & 4095];
-    const u32x4_t v1 = buf[(base + (i + 1) * 256) & 4095];
-    const u32x4_t v2 = buf[(base + (i + 2) * 256) & 4095];
-    const u32x4_t v3 = buf[(base + (i + 3) * 256) & 4095];
-    acc += v0 + v1 + v2 + v3;
+  for (int i = 0; i < iters; i += 8) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = buf[(base + (i + u) * stride) & 4095];
+    acc += (v[0] + v[1]) + (v[2] + v[3]) + (v[4] + v[5]) + (v[6] + v[7]);
+    // the addresses repeat and nothing writes the buffer in the loop: keep the
+    // compiler from reusing earlier loads instead of reading LDS again
+    __asm__ volatile("" ::: "memory");
   }
   const int64_t c1 = clock64();
   if (lane == 0) clocks[blockIdx.x * 4 + wave] = c1 - c0;
@@ -213,7 +216,7 @@ int km_peak_read(const void* src, int64_t bytes, int reps, void* scratch, double
 
 // LDS read bandwidth: two workgroups of 4 wavefronts per compute unit (8
 // wavefronts, 128 KiB of LDS), each wavefront reading `iters` x 1 KiB
-// (`iters` a multiple of 4).  `scratch` holds 2 * cus * (4 * 8 + 256 * 16)
+// (`iters` a multiple of 8).  `scratch` holds 2 * cus * (4 * 8 + 256 * 16)
 // bytes (device).  Returns the bytes read per shader clock per compute unit
 // (from the median wavefront's clock count) and the aggregate rate in TB/s.
 // Synchronous.
@@ -223,7 +226,7 @@ int km_peak_lds(int iters, void* scratch, int64_t scratch_bytes, double* bytes_p
   if (e != hipSuccess) return (int)e;
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return (int)e;
   const int blocks = 2 * cus;
-  if (iters < 4 || iters % 4 || !scratch || !bytes_per_clock_cu || !tbps ||
+  if (iters < 8 || iters % 8 || !scratch || !bytes_per_clock_cu || !tbps ||
       scratch_bytes < (int64_t)blocks * (4 * 8 + 256 * 16))
     return (int)hipErrorInvalidValue;
   int64_t* clocks = static_cast<int64_t*>(scratch);
@@ -231,9 +234,9 @@ int km_peak_lds(int iters, void* scratch, int64_t scratch_bytes, double* bytes_p
   hipEvent_t e0, e1;
   if ((e = hipEventCreate(&e0)) != hipSuccess) return (int)e;
   if ((e = hipEventCreate(&e1)) != hipSuccess) return (int)e;
-  hipLaunchKernelGGL(lds_read_kernel, dim3((unsigned)blocks), dim3(256), 0, 0, 64, clocks, out);  // warm-up
+  hipLaunchKernelGGL(lds_read_kernel, dim3((unsigned)blocks), dim3(256), 0, 0, 64, 256, clocks, out);  // warm-up
   hipEventRecord(e0, 0);
-  hipLaunchKernelGGL(lds_read_kernel, dim3((unsigned)blocks), dim3(256), 0, 0, iters, clocks, out);
+  hipLaunchKernelGGL(lds_read_kernel, dim3((unsigned)blocks), dim3(256), 0, 0, iters, 256, clocks, out);
   hipEventRecord(e1, 0);
   e = hipEventSynchronize(e1);
   float ms = 0.0f;
