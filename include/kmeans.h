@@ -52,8 +52,11 @@
  *     caller's next synchronisation.  No C++ exception crosses this ABI.
  *     kmeans_last_error() gives a message for the last failure on the
  *     calling thread.
- *   - Reentrancy: calls are thread-safe given distinct workspaces.  The only
- *     global state is the optional kernel-timing registry.
+ *   - Reentrancy: calls are thread-safe given distinct workspaces.  Global
+ *     state, all of it behind a lock or atomic: the per-device property
+ *     cache (filled on a device's first call), the planner overrides (for
+ *     measurement), the optional kernel-timing registry, and the
+ *     no-allocation fit's per-GPU scratch (whose overlapping calls race).
  */
 #ifndef MEANS_CLUSTERING_AMD_KMEANS_H
 #define MEANS_CLUSTERING_AMD_KMEANS_H
