@@ -206,3 +206,36 @@ def test_update_deterministic():
     c2, n2 = km.update(X, a, C_prev)
     torch.cuda.synchronize()
     assert torch.equal(c1, c2) and torch.equal(n1, n2)
+
+
+MID_N = [("bf16", 300_000, 128, 1000), ("bf16", 1 << 20, 64, 4096), ("f32", 500_000, 32, 512),
+         ("f16", 200_000, 100, 300), ("bf16", 400_000, 8, 2000)]
+
+
+@pytest.mark.parametrize("case", MID_N, ids=lambda c: f"{c[0]}-N{c[1]}-D{c[2]}-K{c[3]}")
+def test_fit_mid_n_short_segment_tiles(case):
+    """Default plans between 2 MiB and half the last-level cache of gathered rows take the short segment tiles:
+    fits there, each iteration against the oracle (the update on every point, assignments on a sample), and two
+    iterations in one call against two calls."""
+    import synth
+    xdtype, N, D, K = case
+    w = synth.WORKLOADS["c2"].scaled(N=N, D=D, K=K, M=K, dtype="f32", seed=N + D)
+    Xn = synth.points(w)
+    X = torch.from_numpy(Xn).to(TORCH_DT[xdtype]).to(DEV)
+    C0 = torch.from_numpy(synth.init_centroids(w, Xn)).to(DEV)
+    plan = km.plan_describe(N, D, K, X.dtype)
+    print(f"[update] mid N {case}: {plan}", flush=True)
+    assert "segment tile 16" in plan or "segment tile 8" in plan, "expected the short segment tiles"
+    Xs, name = parity.x_to_numpy(X)
+    rows = np.random.default_rng(D).choice(N, 4096, replace=False)
+    C = C0
+    for t in range(2):
+        C_prev = C.cpu().numpy()
+        C, a, counts, _ = km.fit(X, C, 1)
+        torch.cuda.synchronize()
+        an = a.cpu().numpy()
+        parity.check_assign(Xs, name, C_prev, an, rows=rows, label=f"mid N {case} it{t}", min_near_ties=1)
+        parity.check_update(Xs, name, an, C_prev, C.cpu().numpy(), counts.cpu().numpy(), label=f"mid N {case} it{t}")
+    C2, a2, n2, _ = km.fit(X, C0, 2)
+    torch.cuda.synchronize()
+    assert torch.equal(C2, C) and torch.equal(a2, a) and torch.equal(n2, counts)
