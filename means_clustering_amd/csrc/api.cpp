@@ -141,7 +141,7 @@ int64_t kfd_llc_bytes(int domain, int bus, int dev) {
 }
 
 DeviceInfo query_device(int dev) {
-  DeviceInfo d{256, 160 * 1024, 4 << 20, (int64_t)256 << 20, false};  // MI355X
+  DeviceInfo d{256, 160 * 1024, 4 << 20, (int64_t)256 << 20, false, "defaults"};  // MI355X
   int cus = 0, lds = 0, l2 = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return d;
   d.cus = cus;
@@ -153,8 +153,23 @@ DeviceInfo query_device(int dev) {
   (void)hipDeviceGetAttribute(&bus, hipDeviceAttributePciBusId, dev);
   (void)hipDeviceGetAttribute(&pdev, hipDeviceAttributePciDeviceId, dev);
   const int64_t llc = kfd_llc_bytes(domain, bus, pdev);
-  d.llc_bytes = llc > d.l2_bytes ? llc : d.l2_bytes;
   d.queried = true;
+  if (llc > d.l2_bytes) {
+    d.llc_bytes = llc;
+    d.llc_from = "KFD topology";
+    return d;
+  }
+  // No larger level listed (the topology hidden from this process): gfx950
+  // parts carry a 256 MiB Infinity Cache; any other device keeps its L2.
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) == hipSuccess && std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) {
+    d.llc_bytes = (int64_t)256 << 20;
+    d.llc_from = "gfx950";
+  } else {
+    (void)hipGetLastError();
+    d.llc_bytes = d.l2_bytes;
+    d.llc_from = "L2";
+  }
   return d;
 }
 
@@ -167,7 +182,7 @@ namespace km {
 const DeviceInfo& device_info() {
   static std::mutex mu;
   static std::vector<DeviceInfo*> cache;  // per device ordinal, kept for the life of the process
-  static const DeviceInfo fallback{256, 160 * 1024, 4 << 20, (int64_t)256 << 20, false};
+  static const DeviceInfo fallback{256, 160 * 1024, 4 << 20, (int64_t)256 << 20, false, "defaults"};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
     (void)hipGetLastError();
@@ -922,7 +937,7 @@ km_status kmeans_plan_describe(int64_t N, int64_t D, int64_t K, km_dtype dt, cha
                 "%lld centroid range(s); update: %s; workspace %zu bytes; device: %d CUs, LLC %lld MiB (%s)",
                 kernel, g.cfg.KB, g.cfg.NB, g.cfg.CT, g.cfg.W, g.lazy ? "folded" : "exact", (long long)splits, upd,
                 workspace_bytes_impl(KM_OP_FIT, N, D, K, dt, 0), dv.cus, (long long)(dv.llc_bytes >> 20),
-                dv.queried ? "queried" : "defaults");
+                dv.llc_from);
   std::snprintf(buf, len, "%s", out);
   return KM_OK;
 }

@@ -56,6 +56,7 @@ struct DeviceInfo {
   int64_t l2_bytes;   // L2 as HIP reports it (4 MiB, per XCD)
   int64_t llc_bytes;  // last-level cache (256 MiB Infinity Cache); the L2 if no larger level is found
   bool queried;       // false: the MI355X defaults
+  const char* llc_from;  // where llc_bytes came from: "KFD topology", "gfx950", "L2" or "defaults"
 };
 const DeviceInfo& device_info();  // of the calling thread's current device
 

@@ -75,14 +75,20 @@ def _kfd_largest_cache(domain, bus, dev):
 
 def test_device_query_finds_the_last_level_cache():
     """The planner's last-level cache is the highest cache level KFD lists for the device (the Infinity Cache on
-    MI355X, listed after hundreds of per-CU L1 entries), never less than the L2 HIP reports."""
+    MI355X, listed after hundreds of per-CU L1 entries), never less than the L2 HIP reports; with the topology
+    hidden, a gfx950 part's known 256 MiB, else the L2.  The plan description names the source."""
     props = torch.cuda.get_device_properties(0)
     kfd = _kfd_largest_cache(props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
     desc = km.plan_describe(1 << 20, 128, 1024, torch.bfloat16)
     print(f"[planner] device: {desc.split('device: ')[1]}; KFD highest-level cache {kfd >> 20} MiB", flush=True)
     llc_mib = int(desc.split("LLC ")[1].split(" MiB")[0])
-    assert "(queried)" in desc
-    assert llc_mib == max(kfd, props.L2_cache_size) >> 20
+    source = desc.split("LLC ")[1].split("(")[1].split(")")[0]
+    if kfd > props.L2_cache_size:
+        assert source == "KFD topology" and llc_mib == kfd >> 20
+    elif props.gcnArchName.startswith("gfx950"):  # topology hidden: the part's known Infinity Cache
+        assert source == "gfx950" and llc_mib == 256
+    else:
+        assert source == "L2" and llc_mib == props.L2_cache_size >> 20
     if kfd:
         # the short segment tiles reach N * G * 16 bytes = half that cache: at D = 64 (G = 8), 2^20 rows on MI355X
         n_half = (kfd // 2) // (8 * 16)
