@@ -239,3 +239,27 @@ def test_fit_mid_n_short_segment_tiles(case):
     C2, a2, n2, _ = km.fit(X, C0, 2)
     torch.cuda.synchronize()
     assert torch.equal(C2, C) and torch.equal(a2, a) and torch.equal(n2, counts)
+
+
+@pytest.mark.parametrize("xdtype", ["bf16", "f32"])
+def test_update_centroids_not_16_byte_aligned(xdtype):
+    """Centroid buffers 4-byte but not 16-byte aligned (views one float into a larger buffer): the reduction's
+    16-byte stores must step aside for them; results against the oracle and equal to the aligned call."""
+    N, D, K = 200_000, 64, 5000  # short segments: most means are written by the segmented reduction itself
+    g = torch.Generator().manual_seed(7)
+    X = torch.randn(N, D, generator=g).to(TORCH_DT[xdtype]).to(DEV)
+    C = torch.randn(K, D, generator=g).to(DEV)
+    a = torch.randint(0, K - 2, (N,), generator=g, dtype=torch.int32).to(DEV)  # the last two clusters empty
+    big_prev = torch.empty(K * D + 1, device=DEV)
+    big_new = torch.empty(K * D + 3, device=DEV)
+    C_prev = big_prev[1:].view(K, D)
+    C_prev.copy_(C)
+    C_new = big_new[3:].view(K, D)
+    assert C_prev.data_ptr() % 16 and C_new.data_ptr() % 16
+    C_ref, n_ref = km.update(X, a, C)
+    _, n = km.update(X, a, C_prev, out=C_new)
+    torch.cuda.synchronize()
+    assert torch.equal(C_new, C_ref) and torch.equal(n, n_ref), "unaligned buffers differ from the aligned call"
+    Xn, xdt = parity.x_to_numpy(X)
+    parity.check_update(Xn, xdt, a.cpu().numpy(), C.cpu().numpy(), C_new.cpu().numpy(), n.cpu().numpy(),
+                        label=f"unaligned {xdtype}")
