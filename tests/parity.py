@@ -23,10 +23,11 @@ CENTROID_TOL = {"f32": 1e-4, "bf16": 2e-3, "f16": 2e-3}
 GAP_REL = 1e-4
 MAX_NEAR_TIE_FRAC = 1e-4
 # ties at the kernel's own fp32 precision (see check_assign): not held to the 0.01% bar, but still bounded, so
-# that an excess of them (a kernel error just under the precision bound) fails: 8 per problem and iteration, or
-# 0.2% of the points
+# that a kernel deciding most of its near-ties the other way fails: at most half of the points whose oracle gap
+# lies within that precision bound (never fewer than 8).  A fixed count would not do: with dense centroids (D = 1,
+# thousands of centroids on a line) nearly every point lies within fp32 resolution of a tie.
 MAX_PRECISION_TIES = 8
-MAX_PRECISION_TIE_FRAC = 2e-3
+MAX_PRECISION_TIE_SHARE = 0.5
 
 
 def x_to_numpy(X: torch.Tensor):
@@ -55,7 +56,8 @@ def check_assign(Xn, xdtype, C_state, a_gpu, rows=None, label="", min_near_ties=
     (D + 2) * 2^-22 * (||x||^2 + ||c_oracle||^2 + ||c_gpu||^2) (fp32 accumulation of x.c - ||c||^2/2, two
     scores, distances twice the score), is a tie at the kernel's precision and is not counted against the
     0.01%: both sides take the decision in their own precision.  The gap bound still holds for it, and such
-    ties are held to their own, looser cap (MAX_PRECISION_TIES, MAX_PRECISION_TIE_FRAC)."""
+    ties are held to their own cap: at most half of the points within that bound (MAX_PRECISION_TIE_SHARE),
+    never fewer than MAX_PRECISION_TIES."""
     Xs = Xn if rows is None else Xn[rows]
     a_ref, d1, d2 = oracle.assign(Xs, np.asarray(C_state, dtype=np.float64), xdtype)
     a_gpu = np.asarray(a_gpu if rows is None else a_gpu[rows])
@@ -73,10 +75,13 @@ def check_assign(Xn, xdtype, C_state, a_gpu, rows=None, label="", min_near_ties=
         eps = (D + 2) * 2.0**-22 * (xn[mism] + cn[a_ref[mism]] + cn[a_gpu[mism]])
         counted = mism[gap[mism] > eps]
         n_prec = len(mism) - len(counted)
+        # points whose own gap lies within the bound (the second-best centroid's norm taken as the best one's)
+        near = int((gap <= (D + 2) * 2.0**-22 * (xn + 2.0 * cn[a_ref])).sum())
         if n_prec:
-            print(f"[parity] {label}: {n_prec} tie(s) at the kernel's precision of {len(Xs)} points", flush=True)
-        assert n_prec <= max(MAX_PRECISION_TIES, MAX_PRECISION_TIE_FRAC * len(Xs)), \
-            f"{label}: {n_prec} mismatches at the kernel's precision of {len(Xs)} points"
+            print(f"[parity] {label}: {n_prec} tie(s) at the kernel's precision among {near} such points of "
+                  f"{len(Xs)}", flush=True)
+        assert n_prec <= max(MAX_PRECISION_TIES, MAX_PRECISION_TIE_SHARE * near), \
+            f"{label}: {n_prec} mismatches at the kernel's precision, {near} points within it, of {len(Xs)}"
     assert len(counted) <= max(MAX_NEAR_TIE_FRAC * len(Xs), min_near_ties) + 1e-9 or len(counted) == 0, \
         f"{label}: {len(counted)} near-tie mismatches of {len(Xs)} points"
     return len(mism), a_ref

@@ -55,11 +55,11 @@ def test_precision_ties_are_capped():
     X, C, n_ties = _ties_case()
     a_ref, d1, d2 = oracle.assign(X, C, "f32")
     assert (a_ref[:n_ties] == 1).all()
-    cap = max(parity.MAX_PRECISION_TIES, parity.MAX_PRECISION_TIE_FRAC * len(X))
+    cap = max(parity.MAX_PRECISION_TIES, int(parity.MAX_PRECISION_TIE_SHARE * n_ties))  # the 40 points are the ties
     a = a_ref.copy()
-    a[: int(cap)] = 0  # exactly the cap: accepted, not counted against 0.01%
+    a[:cap] = 0  # exactly the cap: accepted, not counted against 0.01%
     parity.check_assign(X, "f32", C, a, label="at cap", precision_ties=True)
-    a[: int(cap) + 1] = 0  # one more: an excess of ties at the kernel's precision fails
+    a[: cap + 1] = 0  # one more: a kernel deciding most of its near-ties the other way fails
     with pytest.raises(AssertionError, match="at the kernel's precision"):
         parity.check_assign(X, "f32", C, a, label="over cap", precision_ties=True)
 
