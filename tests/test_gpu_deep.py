@@ -212,3 +212,24 @@ def test_deep_fit_very_long_rows(case):
         parity.check_assign(Xn, xdt, Cp, an, label=f"very long rows {case} it{t}")
         parity.check_update(Xn, xdt, an, Cp, C.cpu().numpy(), n.cpu().numpy(), label=f"very long rows {case} it{t}")
         parity.check_objective(Xn, xdt, Cp, an, J.cpu().numpy()[0], label=f"very long rows {case} it{t}")
+
+
+@pytest.mark.parametrize("case", [("bf16", 7, 712, 2000), ("f32", 1, 966, 100), ("f16", 300, 2377, 700)],
+                         ids=lambda c: f"{c[0]}-N{c[1]}-D{c[2]}-K{c[3]}")
+def test_deep_fit_more_clusters_than_points(case):
+    """K above N on the deep paths: most clusters stay empty and keep their centroids bit for bit."""
+    xdtype, N, D, K = case
+    X, C0 = _data(N, D, K, xdtype, seed=K + D)
+    Xn, xdt = parity.x_to_numpy(X)
+    print(f"[deep] K > N {case}", flush=True)
+    C = C0
+    for t in range(2):
+        C_prev = C
+        C, a, n, J = km.fit(X, C_prev, 1, objective=True)
+        torch.cuda.synchronize()
+        Cp = C_prev.cpu().numpy()
+        an = a.cpu().numpy()
+        parity.check_assign(Xn, xdt, Cp, an, label=f"K > N {case} it{t}")
+        parity.check_update(Xn, xdt, an, Cp, C.cpu().numpy(), n.cpu().numpy(), label=f"K > N {case} it{t}")
+        parity.check_objective(Xn, xdt, Cp, an, J.cpu().numpy()[0], label=f"K > N {case} it{t}")
+        assert int((n.cpu().numpy() == 0).sum()) >= K - N
