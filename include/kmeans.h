@@ -289,6 +289,11 @@ km_status kmeans_fit_noalloc(const void* X, km_dtype dt, int64_t N, int64_t D, i
  *   "reduce_tile"    1 long segment tiles, 2 short ones
  *   "radix_items"    8, 16 or 32 keys per thread in the argsort
  *   "small_update"   1 never the on-chip small-codebook update
+ *   "sort_scan"      1 scan the argsort's larger (digit, block) count
+ *                    tables as a whole (three launches), 2 scan every
+ *                    table digit by digit (one launch); by default small
+ *                    tables are summed by every scatter workgroup and
+ *                    larger ones scanned digit by digit
  * Every choice gives the same assignments; sums may differ in fp32 rounding.
  * kmeans_plan_describe(N, D, K, dt, buf, len) writes a one-line description
  * of the plan of kmeans_fit for that shape (NUL-terminated, truncated to len).

@@ -332,7 +332,8 @@ def fit_streamed(X_host: torch.Tensor, C0: torch.Tensor, iters: int, chunk_rows:
     return C, a, counts, (obj[:iters] if obj is not None else None)
 
 
-PLAN_KEYS = ("assign_kernel", "assign_fold", "assign_split", "reduce_tile", "radix_items", "small_update")
+PLAN_KEYS = ("assign_kernel", "assign_fold", "assign_split", "reduce_tile", "radix_items", "small_update",
+             "sort_scan")
 
 
 def plan_override(key: str, value: int = 0):

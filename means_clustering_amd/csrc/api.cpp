@@ -173,9 +173,9 @@ DeviceInfo query_device(int dev) {
   return d;
 }
 
-std::atomic<int> g_override[6];  // PlanOverride fields, in order
-const char* const kOverrideKeys[6] = {"assign_kernel", "assign_fold", "assign_split", "reduce_tile", "radix_items",
-                                      "small_update"};
+std::atomic<int> g_override[7];  // PlanOverride fields, in order
+const char* const kOverrideKeys[7] = {"assign_kernel", "assign_fold", "assign_split", "reduce_tile", "radix_items",
+                                      "small_update", "sort_scan"};
 }  // namespace
 
 namespace km {
@@ -202,6 +202,7 @@ PlanOverride plan_override() {
   p.reduce_tile = g_override[3].load(std::memory_order_relaxed);
   p.radix_items = g_override[4].load(std::memory_order_relaxed);
   p.small_update = g_override[5].load(std::memory_order_relaxed);
+  p.sort_scan = g_override[6].load(std::memory_order_relaxed);
   return p;
 }
 }  // namespace km
@@ -252,6 +253,7 @@ static SortGeom sort_geom(int64_t N, int64_t K) {
     if (len > m) m = len;
   }
   g.count_len = m;
+  g.scan_mode = plan_override().sort_scan;
   return g;
 }
 
@@ -895,12 +897,13 @@ km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_
 
 km_status kmeans_plan_override(const char* key, int64_t value) {
   if (!key) return fail(KM_ERR_INVALID_VALUE, "key must be non-NULL");
-  for (int i = 0; i < 6; ++i)
+  for (int i = 0; i < 7; ++i)
     if (std::strcmp(key, kOverrideKeys[i]) == 0) {
       const bool ok = value == 0 ||
                       (i == 0 && (value == 1 || value == 2)) || (i == 1 && (value == 1 || value == 2)) ||
                       (i == 2 && value >= 1 && value <= 64) || (i == 3 && (value == 1 || value == 2)) ||
-                      (i == 4 && (value == 8 || value == 16 || value == 32)) || (i == 5 && value == 1);
+                      (i == 4 && (value == 8 || value == 16 || value == 32)) || (i == 5 && value == 1) ||
+                      (i == 6 && (value == 1 || value == 2));
       if (!ok) return fail(KM_ERR_INVALID_VALUE, std::string("value out of range for ") + key);
       g_override[i].store((int)value, std::memory_order_relaxed);
       return KM_OK;
@@ -929,8 +932,10 @@ km_status kmeans_plan_describe(int64_t N, int64_t D, int64_t K, km_dtype dt, cha
   if (small)
     std::snprintf(upd, sizeof upd, "on-chip small-codebook");
   else
-    std::snprintf(upd, sizeof upd, "sorted, %d radix pass(es) of %d keys/thread, segment tile %lld, %lld column strip(s)",
-                  sg.npass, sg.items, (long long)reduce_tile((int)dt, D, N), (long long)reduce_strips((int)dt, D));
+    std::snprintf(upd, sizeof upd,
+                  "sorted, %d radix pass(es) of %d keys/thread, %s count scans, segment tile %lld, %lld column strip(s)",
+                  sg.npass, sg.items, sg.scan_mode == 1 ? "whole-table" : "per-digit", (long long)reduce_tile((int)dt, D, N),
+                  (long long)reduce_strips((int)dt, D));
   char out[640];
   std::snprintf(out, sizeof out,
                 "assign: %s kernel, %d depth blocks, %d point groups/wave, %d groups/tile, %d waves, cold argmax %s, "

@@ -69,6 +69,7 @@ struct PlanOverride {
   int reduce_tile;    // 1 long (128-position) segment tiles, 2 short ones
   int radix_items;    // keys per thread of the argsort: 8, 16 or 32
   int small_update;   // 1 no on-chip small-codebook update (always the sorted path)
+  int sort_scan;      // 1 scan larger argsort count tables as a whole, 2 scan every count table digit by digit
 };
 PlanOverride plan_override();
 
@@ -282,6 +283,7 @@ struct SortGeom {
   int items;        // keys per thread (radix_items)
   int64_t nblk;     // key blocks of kRadixThreads * items keys
   int64_t count_len;  // max over passes of (2^bits * nblk)
+  int scan_mode;    // count-table scans: 0 per digit (small tables: summed by the scatter), 1 whole table, 2 per digit
 };
 
 // Several independent problems of one shape in one launch.  Workgroup w works

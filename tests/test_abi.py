@@ -250,6 +250,11 @@ def test_planner_override_and_describe(L):
         assert L.kmeans_plan_override(b"small_update", 1) == 0
         L.kmeans_plan_describe(16384, 32, 64, km.KM_F32, buf, len(buf))
         assert b"update: sorted" in buf.value
+        assert L.kmeans_plan_override(b"sort_scan", 3) == 1
+        for v, word in ((1, b"whole-table count scans"), (2, b"per-digit count scans")):
+            assert L.kmeans_plan_override(b"sort_scan", v) == 0
+            L.kmeans_plan_describe(1 << 23, 64, 4096, km.KM_BF16, buf, len(buf))
+            assert word in buf.value
     finally:
         for k in km.PLAN_KEYS:
             assert L.kmeans_plan_override(k.encode(), 0) == 0

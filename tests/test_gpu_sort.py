@@ -74,3 +74,20 @@ def test_sort_scan_paths(N):
     workgroup) against 64 x 513 (9 tiles, scanned in three launches)."""
     rng = np.random.default_rng(N)
     _check(rng.integers(0, 4096, N), 4096, "scan paths")
+
+
+@pytest.mark.parametrize("scan", [1, 2])
+@pytest.mark.parametrize("N,K", [(1, 1), (1000, 7), (4097, 257), (100_003, 4096), (300_001, 65536),
+                                 (2**20 + 1, 4096), (8 * 2**20 + 3, 3000), (2**26 + 5, 100_000)])
+def test_sort_count_scan_modes(N, K, scan):
+    """Both ways of scanning the (digit, block) count table give the same stable argsort: the whole table (or, when
+    small, summed by every scatter workgroup) and one scan per digit row with the digits' totals added by each
+    scatter workgroup; from one block to 2^26 keys (rows of 8,192 blocks, two scan tiles a digit)."""
+    rng = np.random.default_rng(N + 7 * K)
+    a = rng.integers(0, K, N)
+    a[::997] = K + 3  # a few invalid ids
+    km.plan_override("sort_scan", scan)
+    try:
+        _check(a, K, f"count scan mode {scan}")
+    finally:
+        km.plan_override("sort_scan", 0)
