@@ -546,7 +546,8 @@ STUDY_KEYS = {
     "c1": [("small_update", 1), ("assign_split", 1), ("assign_split", 4), ("reduce_tile", 1), ("reduce_tile", 2)],
     "default": [("assign_kernel", 1), ("assign_kernel", 2), ("assign_fold", 1), ("assign_fold", 2),
                 ("radix_items", 8), ("radix_items", 16), ("radix_items", 32), ("reduce_tile", 1), ("reduce_tile", 2),
-                ("sort_scan", 1), ("sort_scan", 2)],
+                ("sort_scan", 1), ("sort_scan", 2), ("sort_rank", 1), ("sort_rank", 2), ("radix_bits", 6),
+                ("radix_bits", 8)],
 }
 
 

@@ -294,6 +294,12 @@ km_status kmeans_fit_noalloc(const void* X, km_dtype dt, int64_t N, int64_t D, i
  *                    table digit by digit (one launch); by default small
  *                    tables are summed by every scatter workgroup and
  *                    larger ones scanned digit by digit
+ *   "sort_rank"      1 rank a block's keys with per-thread digit counters,
+ *                    2 with wavefront ballots
+ *   "radix_bits"     5 to 8: the widest digit of an argsort pass (above 6
+ *                    the ballot ranking is used); by default 8 where that
+ *                    saves one of at most three passes in blocks of up to
+ *                    4,096 keys, else 6
  * Every choice gives the same assignments; sums may differ in fp32 rounding.
  * kmeans_plan_describe(N, D, K, dt, buf, len) writes a one-line description
  * of the plan of kmeans_fit for that shape (NUL-terminated, truncated to len).

@@ -333,7 +333,7 @@ def fit_streamed(X_host: torch.Tensor, C0: torch.Tensor, iters: int, chunk_rows:
 
 
 PLAN_KEYS = ("assign_kernel", "assign_fold", "assign_split", "reduce_tile", "radix_items", "small_update",
-             "sort_scan")
+             "sort_scan", "sort_rank", "radix_bits")
 
 
 def plan_override(key: str, value: int = 0):

@@ -173,9 +173,11 @@ DeviceInfo query_device(int dev) {
   return d;
 }
 
-std::atomic<int> g_override[7];  // PlanOverride fields, in order
-const char* const kOverrideKeys[7] = {"assign_kernel", "assign_fold", "assign_split", "reduce_tile", "radix_items",
-                                      "small_update", "sort_scan"};
+constexpr int kOverrides = 9;
+std::atomic<int> g_override[kOverrides];  // PlanOverride fields, in order
+const char* const kOverrideKeys[kOverrides] = {"assign_kernel", "assign_fold", "assign_split", "reduce_tile",
+                                               "radix_items", "small_update", "sort_scan", "sort_rank",
+                                               "radix_bits"};
 }  // namespace
 
 namespace km {
@@ -203,6 +205,8 @@ PlanOverride plan_override() {
   p.radix_items = g_override[4].load(std::memory_order_relaxed);
   p.small_update = g_override[5].load(std::memory_order_relaxed);
   p.sort_scan = g_override[6].load(std::memory_order_relaxed);
+  p.sort_rank = g_override[7].load(std::memory_order_relaxed);
+  p.radix_bits = g_override[8].load(std::memory_order_relaxed);
   return p;
 }
 }  // namespace km
@@ -241,10 +245,20 @@ static SortGeom sort_geom(int64_t N, int64_t K) {
   while (kb < 31 && ((int64_t)1 << kb) <= K - 1) ++kb;
   if (kb < 1) kb = 1;
   g.kbits = kb;
-  g.npass = (kb + kMaxDigitBits - 1) / kMaxDigitBits;
+  const PlanOverride ov = plan_override();
+  g.items = radix_items(N);
+  // Digits of up to 8 bits (ranked by wavefront ballots) where they save one of at most three passes and blocks
+  // hold at most 4,096 keys; otherwise up to 6 (per-thread counters, faster at an equal pass count).  (Measured on
+  // gfx950, uniform ids: 2^20 keys of 16 bits sort in 53.7 us in two 8-bit passes against 60.7 in three 6-bit
+  // ones, 2^22 in 83.5 against 90.7, 2^20 keys of 8 bits in 26.9 us in one pass against 36.4 in two; 19-bit ids
+  // in three 8-bit passes 78.2 against 75.4 in four 6-bit ones; at an equal pass count the ballot ranking is
+  // 14-20% slower, and 77% slower in 8,192-key blocks.)
+  const int p6 = (kb + kMaxDigitBits - 1) / kMaxDigitBits, p8 = (kb + kMaxWaveDigitBits - 1) / kMaxWaveDigitBits;
+  const bool wide = p8 < p6 && p6 <= 3 && g.items <= 16;
+  const int maxb = ov.radix_bits ? ov.radix_bits : (wide ? kMaxWaveDigitBits : kMaxDigitBits);
+  g.npass = (kb + maxb - 1) / maxb;
   const int base = kb / g.npass, rem = kb % g.npass;
   for (int p = 0; p < 6; ++p) g.bits[p] = p < g.npass ? base + (p < rem ? 1 : 0) : 0;
-  g.items = radix_items(N);
   const int64_t blk = (int64_t)kRadixThreads * g.items;
   g.nblk = (N + blk - 1) / blk;
   int64_t m = 1;
@@ -253,7 +267,8 @@ static SortGeom sort_geom(int64_t N, int64_t K) {
     if (len > m) m = len;
   }
   g.count_len = m;
-  g.scan_mode = plan_override().sort_scan;
+  g.scan_mode = ov.sort_scan;
+  g.wave_rank = ov.sort_rank == 2 || maxb > kMaxDigitBits;
   return g;
 }
 
@@ -897,13 +912,14 @@ km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_
 
 km_status kmeans_plan_override(const char* key, int64_t value) {
   if (!key) return fail(KM_ERR_INVALID_VALUE, "key must be non-NULL");
-  for (int i = 0; i < 7; ++i)
+  for (int i = 0; i < kOverrides; ++i)
     if (std::strcmp(key, kOverrideKeys[i]) == 0) {
       const bool ok = value == 0 ||
                       (i == 0 && (value == 1 || value == 2)) || (i == 1 && (value == 1 || value == 2)) ||
                       (i == 2 && value >= 1 && value <= 64) || (i == 3 && (value == 1 || value == 2)) ||
                       (i == 4 && (value == 8 || value == 16 || value == 32)) || (i == 5 && value == 1) ||
-                      (i == 6 && (value == 1 || value == 2));
+                      (i == 6 && (value == 1 || value == 2)) || (i == 7 && (value == 1 || value == 2)) ||
+                      (i == 8 && value >= 5 && value <= kMaxWaveDigitBits);
       if (!ok) return fail(KM_ERR_INVALID_VALUE, std::string("value out of range for ") + key);
       g_override[i].store((int)value, std::memory_order_relaxed);
       return KM_OK;
@@ -933,8 +949,10 @@ km_status kmeans_plan_describe(int64_t N, int64_t D, int64_t K, km_dtype dt, cha
     std::snprintf(upd, sizeof upd, "on-chip small-codebook");
   else
     std::snprintf(upd, sizeof upd,
-                  "sorted, %d radix pass(es) of %d keys/thread, %s count scans, segment tile %lld, %lld column strip(s)",
-                  sg.npass, sg.items, sg.scan_mode == 1 ? "whole-table" : "per-digit", (long long)reduce_tile((int)dt, D, N),
+                  "sorted, %d radix pass(es) of %d keys/thread, %s count scans, %s ranks, segment tile %lld, "
+                  "%lld column strip(s)",
+                  sg.npass, sg.items, sg.scan_mode == 1 ? "whole-table" : (sg.scan_mode == 2 ? "per-digit" : "in-scatter or per-digit"),
+                  sg.wave_rank ? "wavefront" : "thread-counter", (long long)reduce_tile((int)dt, D, N),
                   (long long)reduce_strips((int)dt, D));
   char out[640];
   std::snprintf(out, sizeof out,

@@ -70,6 +70,8 @@ struct PlanOverride {
   int radix_items;    // keys per thread of the argsort: 8, 16 or 32
   int small_update;   // 1 no on-chip small-codebook update (always the sorted path)
   int sort_scan;      // 1 scan larger argsort count tables as a whole, 2 scan every count table digit by digit
+  int sort_rank;      // 1 per-thread digit counters in the argsort's scatter, 2 wavefront ballots
+  int radix_bits;     // widest digit of an argsort pass, 5 to 8 (above 6: wavefront ballots)
 };
 PlanOverride plan_override();
 
@@ -261,7 +263,8 @@ inline int radix_items(int64_t N) {
   const int64_t cus = device_info().cus;
   return N >= 8 * cus * 8192 ? 32 : (N >= cus * 4096 ? 16 : 8);
 }
-constexpr int kMaxDigitBits = 6;             // digits of at most 64 values per pass
+constexpr int kMaxDigitBits = 6;             // digits of at most 64 values per pass (per-thread counters)
+constexpr int kMaxWaveDigitBits = 8;         // ... of at most 256 values (wavefront ballots)
 constexpr int kSegTile = KM_SEG_TILE;
 // Short segment tiles, used while N rows of G lanes (16 bytes each) take at
 // most seg_fine_max_bytes() (half the last-level cache), where the
@@ -284,6 +287,7 @@ struct SortGeom {
   int64_t nblk;     // key blocks of kRadixThreads * items keys
   int64_t count_len;  // max over passes of (2^bits * nblk)
   int scan_mode;    // count-table scans: 0 per digit (small tables: summed by the scatter), 1 whole table, 2 per digit
+  bool wave_rank;   // scatter ranks keys by wavefront ballots (always for digits of more than kMaxDigitBits)
 };
 
 // Several independent problems of one shape in one launch.  Workgroup w works

@@ -235,6 +235,143 @@ __global__ __launch_bounds__(kRadixThreads) void radix_scatter_kernel(const int3
   }
 }
 
+// Wave-ranked variant of the stable scatter, for digits of up to 8 bits.
+// Wavefront w of the block takes the 64 * IT consecutive keys from position
+// w * 64 * IT, 64 at a time (step j: positions j * 64 + lane).  In each step
+// the lanes holding the same digit find each other with one ballot per digit
+// bit; a key's rank is the wave's running count of its digit (one LDS word
+// per digit and wave, advanced by the highest such lane) plus the number of
+// such lanes below it.  The waves' counts then become per-wave offsets inside
+// each digit, the digit totals the block's digit starts.  Steps run in
+// position order and lanes in position order, so equal digits keep their
+// input order (stable).  No per-thread counters and no serial chain of LDS
+// read-modify-writes per key.
+template <int BITS, int IT, int BASES>
+__global__ __launch_bounds__(kRadixThreads) void radix_scatter_wave_kernel(const int32_t* __restrict__ keys_in,
+                                                                           const int32_t* __restrict__ vals_in,
+                                                                           int64_t N, int64_t K, int first, int shift,
+                                                                           int64_t nblk,
+                                                                           const uint32_t* __restrict__ offsets,
+                                                                           const uint32_t* __restrict__ tot,
+                                                                           int32_t* __restrict__ keys_out,
+                                                                           int32_t* __restrict__ vals_out) {
+  constexpr int R = 1 << BITS;
+  constexpr int NW = kRadixThreads / 64;
+  constexpr int BLK = kRadixThreads * IT;
+  static_assert(R <= kRadixThreads, "a thread per digit");
+  static_assert(BLK >= 3 * kRadixThreads, "the raw-count bases use the staging space");
+  __shared__ int32_t stage[BLK];
+  __shared__ uint32_t whist[NW * R];
+  __shared__ uint32_t wsum[kRadixThreads / 64];
+  __shared__ uint32_t start[R + 1];
+  __shared__ uint32_t gbase[R];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int64_t b = blockIdx.x;
+  if constexpr (BASES == kBasesRaw) {  // `offsets` holds the raw counts; the staging space is free until the keys
+    uint32_t* scr = reinterpret_cast<uint32_t*>(stage);
+    digit_bases<R>(offsets, nblk, b, scr, scr + kRadixThreads, scr + 2 * kRadixThreads, gbase);
+  } else if constexpr (BASES == kBasesPerDigit) {  // exclusive prefix of the digit totals, plus this block's entry
+    uint32_t excl;
+    block_scan_excl(t < R ? tot[t] : 0u, excl, wsum);
+    if (t < R) gbase[t] = excl + offsets[(int64_t)t * nblk + b];
+  } else {
+    for (int dd = t; dd < R; dd += kRadixThreads) gbase[dd] = offsets[(int64_t)dd * nblk + b];
+  }
+  for (int i = t; i < NW * R; i += kRadixThreads) whist[i] = 0u;
+
+  // this wavefront's keys (and values; the first pass makes them from the positions)
+  const int64_t p0 = b * BLK + (int64_t)wave * 64 * IT + lane;
+  int32_t key[IT], val[IT];
+#pragma unroll
+  for (int j = 0; j < IT; ++j) {
+    const int64_t pos = p0 + (int64_t)j * 64;
+    const bool ok = pos < N;
+    key[j] = ok ? keys_in[pos] : 0;
+    if (first) {
+      val[j] = (int32_t)pos;
+      if (ok && (uint32_t)key[j] >= (uint32_t)K) {
+        key[j] = (int32_t)(K - 1);
+        val[j] = (int32_t)((uint32_t)pos | kInvalidFlag);
+      }
+    } else {
+      val[j] = ok ? vals_in[pos] : 0;
+    }
+  }
+  __syncthreads();  // counters zeroed
+
+  uint32_t* hist = whist + wave * R;
+  const uint64_t lower = (1ull << lane) - 1ull;  // lanes below this one
+  uint32_t rank[IT];
+#pragma unroll
+  for (int j = 0; j < IT; ++j) {
+    const bool ok = p0 + (int64_t)j * 64 < N;
+    const uint32_t dg = ((uint32_t)key[j] >> shift) & (uint32_t)(R - 1);
+    uint64_t peers = __ballot(ok);
+#pragma unroll
+    for (int bit = 0; bit < BITS; ++bit) {
+      const bool on = (dg >> bit) & 1u;
+      const uint64_t m = __ballot(on);
+      peers &= on ? m : ~m;
+    }
+    const uint32_t below = (uint32_t)__popcll(peers & lower);
+    rank[j] = 0;
+    if (ok) {
+      const uint32_t c = hist[dg];
+      rank[j] = c + below;
+      if (below + 1 == (uint32_t)__popcll(peers)) hist[dg] = c + below + 1;  // the digit's highest lane
+    }
+  }
+  __syncthreads();
+  // each digit: the waves' counts become offsets inside the digit; the totals become the digit starts
+  uint32_t total = 0;
+  if (t < R) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t c = whist[w * R + t];
+      whist[w * R + t] = total;
+      total += c;
+    }
+  }
+  uint32_t excl;
+  const uint32_t nkeys = block_scan_excl(total, excl, wsum);
+  if (t < R) start[t] = excl;
+  if (t == 0) start[R] = nkeys;
+  __syncthreads();
+  // keys in sorted order; remember each striped position's destination
+#pragma unroll
+  for (int j = 0; j < IT; ++j) {
+    if (p0 + (int64_t)j * 64 < N) {
+      const uint32_t dg = ((uint32_t)key[j] >> shift) & (uint32_t)(R - 1);
+      rank[j] += start[dg] + hist[dg];
+      stage[rank[j]] = key[j];
+    }
+  }
+  __syncthreads();
+  uint32_t dst[IT];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const uint32_t p = (uint32_t)(i * kRadixThreads + t);
+    dst[i] = 0xffffffffu;
+    if (p < nkeys) {
+      const int32_t k = stage[p];
+      const uint32_t dg = ((uint32_t)k >> shift) & (uint32_t)(R - 1);
+      dst[i] = gbase[dg] + (p - start[dg]);
+      if (dst[i] < (uint64_t)N) keys_out[dst[i]] = k;  // always true for a consistent scan
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < IT; ++j)
+    if (p0 + (int64_t)j * 64 < N) stage[rank[j]] = val[j];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const uint32_t p = (uint32_t)(i * kRadixThreads + t);
+    if (p < nkeys && dst[i] < (uint64_t)N) vals_out[dst[i]] = stage[p];
+  }
+}
+
 // ------------------------------------------------------------------- scan --
 //
 // Exclusive scan of the (digit, block) counts.  A tile is 1024 threads x 4
@@ -391,7 +528,7 @@ constexpr int64_t kScanFuseMax = KM_SCAN_FUSE_TILES * kScanTile;
 // Scratch of the count scans: the tile sums of a whole-table scan, or the digit totals of per-digit scans.
 int64_t scan_part_len(int64_t n) {
   const int64_t tiles = (n + kScanTile - 1) / kScanTile + 1;
-  return tiles > (1 << kMaxDigitBits) ? tiles : (1 << kMaxDigitBits);
+  return tiles > (1 << kMaxWaveDigitBits) ? tiles : (1 << kMaxWaveDigitBits);
 }
 
 template <int B, int IT>
@@ -400,20 +537,31 @@ static void count_pass(const SortGeom& g, const int32_t* kin, int first, int shi
                      first, shift, g.nblk, counts);
 }
 
+template <int B, int IT, int BASES>
+static void scatter_launch(const SortGeom& g, const int32_t* kin, const int32_t* vin, int first, int shift,
+                           const uint32_t* counts, const uint32_t* tot, int32_t* kout, int32_t* vout, hipStream_t s) {
+  const dim3 grid((unsigned)g.nblk), block(kRadixThreads);
+  if constexpr (B <= kMaxDigitBits) {
+    if (!g.wave_rank) {
+      hipLaunchKernelGGL((radix_scatter_kernel<B, IT, BASES>), grid, block, 0, s, kin, vin, g.N, g.K, first, shift,
+                         g.nblk, counts, tot, kout, vout);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((radix_scatter_wave_kernel<B, IT, BASES>), grid, block, 0, s, kin, vin, g.N, g.K, first, shift,
+                     g.nblk, counts, tot, kout, vout);
+}
+
 template <int B, int IT>
 static void scatter_pass(const SortGeom& g, const int32_t* kin, const int32_t* vin, int first, int shift,
                          const uint32_t* counts, const uint32_t* tot, int bases, int32_t* kout, int32_t* vout,
                          hipStream_t s) {
-  const dim3 grid((unsigned)g.nblk), block(kRadixThreads);
   if (bases == kBasesRaw)
-    hipLaunchKernelGGL((radix_scatter_kernel<B, IT, kBasesRaw>), grid, block, 0, s, kin, vin, g.N, g.K, first, shift,
-                       g.nblk, counts, tot, kout, vout);
+    scatter_launch<B, IT, kBasesRaw>(g, kin, vin, first, shift, counts, tot, kout, vout, s);
   else if (bases == kBasesPerDigit)
-    hipLaunchKernelGGL((radix_scatter_kernel<B, IT, kBasesPerDigit>), grid, block, 0, s, kin, vin, g.N, g.K, first,
-                       shift, g.nblk, counts, tot, kout, vout);
+    scatter_launch<B, IT, kBasesPerDigit>(g, kin, vin, first, shift, counts, tot, kout, vout, s);
   else
-    hipLaunchKernelGGL((radix_scatter_kernel<B, IT, kBasesScanned>), grid, block, 0, s, kin, vin, g.N, g.K, first,
-                       shift, g.nblk, counts, tot, kout, vout);
+    scatter_launch<B, IT, kBasesScanned>(g, kin, vin, first, shift, counts, tot, kout, vout, s);
 }
 
 #define KM_SORT_DISPATCH(CALL)                                                               \
@@ -424,18 +572,24 @@ static void scatter_pass(const SortGeom& g, const int32_t* kin, const int32_t* v
     case 8 * 16 + 4: CALL(4, 8); break;                                                      \
     case 8 * 16 + 5: CALL(5, 8); break;                                                      \
     case 8 * 16 + 6: CALL(6, 8); break;                                                      \
+    case 8 * 16 + 7: CALL(7, 8); break;                                                      \
+    case 8 * 16 + 8: CALL(8, 8); break;                                                      \
     case 16 * 16 + 1: CALL(1, 16); break;                                                    \
     case 16 * 16 + 2: CALL(2, 16); break;                                                    \
     case 16 * 16 + 3: CALL(3, 16); break;                                                    \
     case 16 * 16 + 4: CALL(4, 16); break;                                                    \
     case 16 * 16 + 5: CALL(5, 16); break;                                                    \
     case 16 * 16 + 6: CALL(6, 16); break;                                                    \
+    case 16 * 16 + 7: CALL(7, 16); break;                                                    \
+    case 16 * 16 + 8: CALL(8, 16); break;                                                    \
     case 32 * 16 + 1: CALL(1, 32); break;                                                    \
     case 32 * 16 + 2: CALL(2, 32); break;                                                    \
     case 32 * 16 + 3: CALL(3, 32); break;                                                    \
     case 32 * 16 + 4: CALL(4, 32); break;                                                    \
     case 32 * 16 + 5: CALL(5, 32); break;                                                    \
     case 32 * 16 + 6: CALL(6, 32); break;                                                    \
+    case 32 * 16 + 7: CALL(7, 32); break;                                                    \
+    case 32 * 16 + 8: CALL(8, 32); break;                                                    \
     default: return hipErrorInvalidValue;                                                    \
   }
 

@@ -16,7 +16,8 @@ CASES = [("c2", dict(N=60_000, K=1024)), ("c4", dict(N=120_000, K=4096)), ("c3",
 OVERRIDES = [("assign_kernel", 1), ("assign_kernel", 2), ("assign_fold", 1), ("assign_fold", 2),
              ("assign_split", 1), ("assign_split", 3), ("reduce_tile", 1), ("reduce_tile", 2),
              ("radix_items", 8), ("radix_items", 16), ("radix_items", 32), ("small_update", 1),
-             ("sort_scan", 1), ("sort_scan", 2)]
+             ("sort_scan", 1), ("sort_scan", 2), ("sort_rank", 1), ("sort_rank", 2), ("radix_bits", 6),
+             ("radix_bits", 8)]
 
 
 @pytest.mark.parametrize("override", OVERRIDES, ids=lambda o: f"{o[0]}={o[1]}")

@@ -91,3 +91,51 @@ def test_sort_count_scan_modes(N, K, scan):
         _check(a, K, f"count scan mode {scan}")
     finally:
         km.plan_override("sort_scan", 0)
+
+
+@pytest.mark.parametrize("rank,bits", [(1, 0), (2, 0), (2, 7), (2, 8), (1, 5)])
+@pytest.mark.parametrize("N,K", [(1, 1), (63, 5), (1000, 7), (4097, 257), (100_003, 4096), (300_001, 65536),
+                                 (1_000_003, 100_000), (2**20 + 1, 1024), (8 * 2**20 + 3, 4096)])
+def test_sort_rank_modes(N, K, rank, bits):
+    """Every way of ranking a block's keys gives the same stable argsort: per-thread digit counters and
+    wavefront ballots, at the planner's digit widths and at digits of 7 and 8 bits (ballots only; 2-3 passes fewer
+    or more than the default), from one key to 2^23 keys (2,048- and 4,096-key blocks), with out-of-range ids."""
+    rng = np.random.default_rng(N + 13 * K + rank)
+    a = rng.integers(0, K, N)
+    a[::991] = -1  # a few invalid ids
+    km.plan_override("sort_rank", rank)
+    if bits:
+        km.plan_override("radix_bits", bits)
+    try:
+        _check(a, K, f"rank mode {rank}, digits of at most {bits or 'default'} bits")
+    finally:
+        km.plan_override("sort_rank", 0)
+        km.plan_override("radix_bits", 0)
+
+
+def test_sort_wave_rank_skewed():
+    """Wavefront ballots with every lane of a step on one digit, alternating digits and a hot cluster."""
+    K = 4096
+    a = np.zeros(300_000, dtype=np.int64)
+    a[1::2] = K - 1
+    a[::7] = 1234
+    km.plan_override("sort_rank", 2)
+    try:
+        _check(a, K, "alternating digits")
+        _check(np.full(100_001, 77), K, "one cluster")
+        rng = np.random.default_rng(5)
+        w = 1.0 / np.arange(1, K + 1) ** 1.2
+        _check(rng.choice(K, size=500_000, p=w / w.sum()), K, "zipf")
+    finally:
+        km.plan_override("sort_rank", 0)
+
+
+def test_sort_wave_rank_8bit_largest_blocks():
+    """8-bit digits ranked by ballots in 8,192-key blocks (2^26 keys: 8,193 blocks, per-digit scans of 3 tiles)."""
+    rng = np.random.default_rng(11)
+    a = rng.integers(0, 65536, 2**26 + 5)
+    km.plan_override("radix_bits", 8)
+    try:
+        _check(a, 65536, "8-bit digits, 8192-key blocks")
+    finally:
+        km.plan_override("radix_bits", 0)
