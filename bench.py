@@ -366,6 +366,40 @@ def run_resident(w, args, dev, peaks, steps, warmup, tag):
     return res
 
 
+def resident_copy_fit(w, dev, Xh, C0, stage, copy_stream):
+    """Not part of `value`: the same streamed fit with a device copy of X in the workspace (X fits in one GPU's
+    HBM), so only the first iteration crosses the host link.  Times one fit of 1 and one of the workload's
+    iteration count; the difference gives the cost of an iteration that reads X from HBM."""
+    import torch
+
+    import means_clustering_amd as km
+
+    torch.cuda.empty_cache()
+    need = km.workspace_bytes(km.KM_OP_FIT_STREAMED_RESIDENT, w.N, w.D, w.K, Xh.dtype, w.chunk_rows)
+    free, _ = torch.cuda.mem_get_info(dev)
+    if need + (4 << 30) > free:
+        return {"skipped": f"needs {need / 2**30:.1f} GiB of workspace, {free / 2**30:.1f} GiB free"}
+    rws = km.Workspace(dev)
+    times = {}
+    for it in (1, w.iters):
+        print(f"[bench] {w.name} with a resident copy of X: fit of {it} iteration(s)", file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        km.fit_streamed(Xh, C0, it, w.chunk_rows, copy_stream=copy_stream, want_assign=False, ws=rws, stage=stage,
+                        resident=True)
+        torch.cuda.synchronize()
+        times[it] = time.perf_counter() - t1
+    later = (times[w.iters] - times[1]) / max(w.iters - 1, 1)
+    del rws
+    torch.cuda.empty_cache()
+    return {"what": "kmeans_fit_streamed with a device copy of all of X in the workspace: X crosses the host link "
+                    "in the first iteration only (same results bit for bit)",
+            "workspace_GB": round(need / 1e9, 2), "fit_iterations": w.iters,
+            "fit_s": round(times[w.iters], 3), "fit_iterations_per_s": round(w.iters / times[w.iters], 4),
+            "first_iteration_s": round(times[1], 3), "later_iteration_s": round(later, 4),
+            "later_iterations_per_s": round(1.0 / later, 3) if later > 0 else None}
+
+
 def run_streamed(w, args, dev, peaks, steps, warmup):
     """The out-of-core workload: X in host memory, a step is one Lloyd iteration over every chunk."""
     import torch
@@ -416,6 +450,10 @@ def run_streamed(w, args, dev, peaks, steps, warmup):
         run_iterations(w.iters, "per-phase step")
         km.timing_enable(False)
         breakdown = read_phases(km)
+    resident = None
+    if not args.no_resident:
+        del ws  # the streamed run's workspace goes back to the allocator first
+        resident = resident_copy_fit(w, dev, Xh, C0, stage, copy_stream)
     es = 2 if w.dtype == "bf16" else 4
     e2e = w.N * w.D * es * steps / elapsed / 1e9
     stream = {"h2d_bytes_per_iteration": w.N * w.D * es, "end_to_end_GBps": round(e2e, 2),
@@ -436,7 +474,7 @@ def run_streamed(w, args, dev, peaks, steps, warmup):
            "distances_per_s": round(steps / elapsed * w.N * w.K, 1),
            "roofline": assign_roofline(w, phases, steps, peaks),
            "update_roofline": update_roofline(w, breakdown, w.iters, peaks), "streaming": stream,
-           "phases_timed_region": phases, "phase_breakdown_extra_step": breakdown}
+           "phases_timed_region": phases, "phase_breakdown_extra_step": breakdown, "resident_copy": resident}
     res["cpu_baseline"] = None
     if not args.no_cpu_baseline:
         print(f"[bench] {w.name}: cpu baseline (the oracle on a sample)", file=sys.stderr, flush=True)
@@ -718,6 +756,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for each CPU baseline")
     ap.add_argument("--no-timing", action="store_true", help="no per-kernel events (for profiler runs)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the same-run peak probes")
+    ap.add_argument("--no-resident", action="store_true",
+                    help="streamed workload: skip the extra fits with a device copy of X")
     ap.add_argument("--batch", type=int, default=1,
                     help="B > 1: time B independent problems of the workload's shape per call (batched fit)")
     ap.add_argument("--ablation", action="store_true",
@@ -794,7 +834,8 @@ def main():
         "dtype": res["dtype"], "data": "synthetic (seeded Gaussian mixtures of the workload's shape)",
         "config": res["config"], "step": res["step"], "distances_per_s": res["distances_per_s"],
         "roofline": res["roofline"], "update_roofline": res["update_roofline"],
-        "streaming": res.get("streaming"), "cpu_baseline": res["cpu_baseline"],
+        "streaming": res.get("streaming"), "resident_copy": res.get("resident_copy"),
+        "cpu_baseline": res["cpu_baseline"],
         "phases_timed_region": res["phases_timed_region"],
         "phase_breakdown_extra_step": res["phase_breakdown_extra_step"],
         "extra_configs": extras, "peaks_measured": peaks, "device": torch.cuda.get_device_name(dev),

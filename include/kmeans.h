@@ -93,7 +93,8 @@ typedef enum km_op KM_ENUM_INT {
   KM_OP_FIT = 2,
   KM_OP_FIT_STREAMED = 3,
   KM_OP_SORT = 4,
-  KM_OP_FIT_STREAMED_WARM = 5  /* kmeans_fit_streamed with room for every chunk's warm-start order */
+  KM_OP_FIT_STREAMED_WARM = 5, /* kmeans_fit_streamed with room for every chunk's warm-start order */
+  KM_OP_FIT_STREAMED_RESIDENT = 6 /* ... and for a device copy of all of X */
 } km_op;
 
 /*
@@ -103,6 +104,12 @@ typedef enum km_op KM_ENUM_INT {
  * of X, where each chunk keeps its sorted order from one iteration to the
  * next so that later iterations assign it warm (faster, same results bit for
  * bit); kmeans_fit_streamed uses that room whenever ws_bytes holds it.
+ * KM_OP_FIT_STREAMED_RESIDENT: the KM_OP_FIT_STREAMED_WARM workspace plus
+ * N * D * sizeof(dt) bytes (rounded up to 256) for a device copy of X.
+ * kmeans_fit_streamed keeps in the workspace beyond the warm layout as many
+ * leading chunks of X as fit whole: each is uploaded once, in the first
+ * iteration, and read from device memory in later ones (same results, bit
+ * for bit; only host-link traffic changes).
  * Returns 0 if the arguments are invalid.
  */
 size_t kmeans_workspace_bytes(km_op op, int64_t N, int64_t D, int64_t K, km_dtype dt, int64_t chunk_rows);

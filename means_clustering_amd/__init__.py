@@ -33,6 +33,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "kmeans.h")
 
 KM_F32, KM_BF16, KM_F16 = 0, 1, 2
 KM_OP_ASSIGN, KM_OP_UPDATE, KM_OP_FIT, KM_OP_FIT_STREAMED, KM_OP_SORT, KM_OP_FIT_STREAMED_WARM = 0, 1, 2, 3, 4, 5
+KM_OP_FIT_STREAMED_RESIDENT = 6
 STATUS = {0: "KM_OK", 1: "KM_ERR_INVALID_VALUE", 2: "KM_ERR_UNSUPPORTED", 3: "KM_ERR_WORKSPACE", 4: "KM_ERR_HIP"}
 _DT = {torch.float32: KM_F32, torch.bfloat16: KM_BF16, torch.float16: KM_F16}
 
@@ -291,11 +292,13 @@ def staging_buffer(nbytes: int = 4 * STAGE_SLOT_BYTES) -> torch.Tensor:
 
 def fit_streamed(X_host: torch.Tensor, C0: torch.Tensor, iters: int, chunk_rows: int, copy_stream=None,
                  want_assign: bool = True, objective: bool = False, ws: Workspace | None = None,
-                 stage: torch.Tensor | None = None, warm_start: bool = True):
+                 stage: torch.Tensor | None = None, warm_start: bool = True, resident: bool | int = False):
     """Lloyd iterations with X in host memory, streamed in chunks.
 
     X_host may be pinned (uploaded directly) or pageable (uploaded through the
-    pinned ``stage`` buffer, allocated here if not given).  Returns
+    pinned ``stage`` buffer, allocated here if not given).  ``resident``: True
+    keeps a device copy of all of X (uploaded in the first iteration only), an
+    int keeps that many bytes of leading chunks (needs warm_start).  Returns
     (C, assign_host int32[N] pinned or None, counts, objective-or-None).  The
     call returns once all work is enqueued on the current stream.
     """
@@ -318,8 +321,17 @@ def fit_streamed(X_host: torch.Tensor, C0: torch.Tensor, iters: int, chunk_rows:
     obj = torch.empty(max(iters, 1), dtype=torch.float64, device=dev) if objective else None
     # warm_start: room for every chunk's order (8 bytes a row of device memory), so iterations after the first
     # assign each chunk warm; without it the workspace holds two chunk buffers and one chunk's scratch only
-    nb = workspace_bytes(KM_OP_FIT_STREAMED_WARM if warm_start else KM_OP_FIT_STREAMED, N, D, K, X_host.dtype,
-                         chunk_rows)
+    if resident is True:
+        if not warm_start:
+            raise ValueError("a resident copy of X needs warm_start")
+        nb = workspace_bytes(KM_OP_FIT_STREAMED_RESIDENT, N, D, K, X_host.dtype, chunk_rows)
+    else:
+        nb = workspace_bytes(KM_OP_FIT_STREAMED_WARM if warm_start else KM_OP_FIT_STREAMED, N, D, K, X_host.dtype,
+                             chunk_rows)
+        if resident:
+            if not warm_start or int(resident) < 0:
+                raise ValueError("resident bytes must be >= 0 and need warm_start")
+            nb += int(resident)
     w = _ws(ws, nb, dev)
     cs = copy_stream if copy_stream is not None else torch.cuda.Stream(dev)
     # (the size asked for, not the buffer's: a larger reused buffer must not turn the warm start on)

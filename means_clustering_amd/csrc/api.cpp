@@ -443,10 +443,15 @@ static size_t workspace_bytes_impl(km_op op, int64_t N, int64_t D, int64_t K, km
     case KM_OP_UPDATE: carve_update(c, sort_geom(N, K), D, dt); break;
     case KM_OP_FIT: carve_fit(c, N, D, K, dt); break;
     case KM_OP_FIT_STREAMED:
-    case KM_OP_FIT_STREAMED_WARM: {
+    case KM_OP_FIT_STREAMED_WARM:
+    case KM_OP_FIT_STREAMED_RESIDENT: {
       const int64_t rows = chunk_rows < N ? chunk_rows : (N > 0 ? N : 1);
       carve_streamed(c, rows, D, K, dt);
-      if (op == KM_OP_FIT_STREAMED_WARM) carve_warm_order(c, N);
+      if (op != KM_OP_FIT_STREAMED) carve_warm_order(c, N);
+      if (op == KM_OP_FIT_STREAMED_RESIDENT) {
+        c.used = (c.used + 255) / 256 * 256;  // the resident copy starts where the warm layout's size ends
+        c.used += (size_t)N * (size_t)D * (size_t)dtype_size((int)dt);
+      }
       break;
     }
     default: return 0;
@@ -630,7 +635,9 @@ extern "C" {
 size_t kmeans_workspace_bytes(km_op op, int64_t N, int64_t D, int64_t K, km_dtype dt, int64_t chunk_rows) {
   const bool need_d = op != KM_OP_SORT;
   if (check_sizes(N, need_d ? D : 1, K, op == KM_OP_SORT ? KM_F32 : dt, need_d) != KM_OK) return 0;
-  if ((op == KM_OP_FIT_STREAMED || op == KM_OP_FIT_STREAMED_WARM) && chunk_rows < 1) return 0;
+  if ((op == KM_OP_FIT_STREAMED || op == KM_OP_FIT_STREAMED_WARM || op == KM_OP_FIT_STREAMED_RESIDENT) &&
+      chunk_rows < 1)
+    return 0;
   return workspace_bytes_impl(op, N, D, K, dt, chunk_rows);
 }
 
@@ -801,7 +808,12 @@ km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_
   const int64_t rows = chunk_rows < N ? chunk_rows : (N > 0 ? N : 1);
   // With room for every chunk's order (KM_OP_FIT_STREAMED_WARM), iterations after the first assign each chunk
   // warm, in the order of its last argsort (the same results, bit for bit; only the order of work changes).
-  const bool warm = ws_bytes >= workspace_bytes_impl(KM_OP_FIT_STREAMED_WARM, N, D, K, dt, chunk_rows);
+  const size_t warm_bytes = workspace_bytes_impl(KM_OP_FIT_STREAMED_WARM, N, D, K, dt, chunk_rows);
+  const bool warm = ws_bytes >= warm_bytes;
+  // Workspace beyond the warm layout: a device copy of the leading chunks that fit whole (uploaded in the first
+  // iteration, read from device memory afterwards).  Chunk ch is resident iff its last row is below res_rows.
+  uint8_t* const xres = warm && ws_bytes > warm_bytes ? (uint8_t*)ws + warm_bytes : nullptr;
+  const int64_t res_rows = xres ? (int64_t)((ws_bytes - warm_bytes) / row_bytes) : 0;
   Carve c(ws);
   const StreamBufs b = carve_streamed(c, rows, D, K, dt);
   const WarmOrder wo = warm ? carve_warm_order(c, N) : WarmOrder{nullptr, nullptr};
@@ -816,8 +828,8 @@ km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_
       for (hipEvent_t e : ev) (void)hipEventDestroy(e);
     }
   } guard{events};
-  hipEvent_t ready[2], freed[2], slot_done[kStageSlots], start;
-  for (hipEvent_t* e : {&ready[0], &ready[1], &freed[0], &freed[1], &start}) {
+  hipEvent_t ready[2], freed[2], slot_done[kStageSlots], start, res_ready;
+  for (hipEvent_t* e : {&ready[0], &ready[1], &freed[0], &freed[1], &start, &res_ready}) {
     KM_HIP(hipEventCreateWithFlags(e, hipEventDisableTiming));
     events.push_back(*e);
   }
@@ -864,42 +876,58 @@ km_status kmeans_fit_streamed(const void* X_host, km_dtype dt, int64_t N, int64_
     return hipSuccess;
   };
 
-  int64_t seq = 0;  // global chunk counter: buffer = seq % 2
+  int64_t seq = 0;  // counter of the chunks that go through the two chunk buffers: buffer = seq % 2
   for (int32_t t = 0; t < iters; ++t) {
     KM_TIMED("prep", cs, return launch_prep(g, C, b.f.frag, cs));
     KM_HIP(launch_zero(b.acc_sum, sizeof(float) * (size_t)(K * D), cs));
     KM_HIP(launch_zero(b.acc_cnt, sizeof(int64_t) * (size_t)K, cs));
     if (objective && nchunks == 0) KM_HIP(launch_zero(objective + t, sizeof(double), cs));
-    for (int64_t ch = 0; ch < nchunks; ++ch, ++seq) {
-      const int buf = (int)(seq % 2);
+    for (int64_t ch = 0; ch < nchunks; ++ch) {
       const int64_t r0 = ch * rows;
       const int64_t nr = (N - r0) < rows ? (N - r0) : rows;
-      // copy stream: wait until the compute of the chunk that last used this buffer is done
-      if (seq >= 2) KM_HIP(hipStreamWaitEvent(xs, freed[buf], 0));
-      KM_TIMED("h2d", xs,
-               return upload((uint8_t*)b.xbuf[buf], (const uint8_t*)X_host + (size_t)r0 * row_bytes,
-                             (size_t)nr * row_bytes));
-      KM_HIP(hipEventRecord(ready[buf], xs));
+      const bool resident = xres && r0 + nr <= res_rows;
+      const int buf = resident ? -1 : (int)(seq % 2);
+      void* xdev;
+      if (resident) {  // uploaded once, into its own place in the resident copy
+        xdev = xres + (size_t)r0 * row_bytes;
+        if (t == 0) {
+          KM_TIMED("h2d", xs,
+                   return upload((uint8_t*)xdev, (const uint8_t*)X_host + (size_t)r0 * row_bytes,
+                                 (size_t)nr * row_bytes));
+          KM_HIP(hipEventRecord(res_ready, xs));
+          KM_HIP(hipStreamWaitEvent(cs, res_ready, 0));
+        }
+      } else {
+        xdev = b.xbuf[buf];
+        // copy stream: wait until the compute of the chunk that last used this buffer is done
+        if (seq >= 2) KM_HIP(hipStreamWaitEvent(xs, freed[buf], 0));
+        KM_TIMED("h2d", xs,
+                 return upload((uint8_t*)xdev, (const uint8_t*)X_host + (size_t)r0 * row_bytes,
+                               (size_t)nr * row_bytes));
+        KM_HIP(hipEventRecord(ready[buf], xs));
+        KM_HIP(hipStreamWaitEvent(cs, ready[buf], 0));
+      }
       // compute stream: assign the chunk, then fold its per-cluster sums into the totals
-      KM_HIP(hipStreamWaitEvent(cs, ready[buf], 0));
       int32_t* ck = warm ? wo.keys + r0 : nullptr;  // this chunk's order from the last iteration
       int32_t* cv = warm ? wo.vals + r0 : nullptr;
       KM_TIMED("assign", cs,
-               return launch_flash_assign(g, b.xbuf[buf], nr, b.f.frag, b.f.assign,
-                                          objective ? b.f.min_dist : nullptr, cs, t > 0 ? cv : nullptr,
-                                          t > 0 ? ck : nullptr));
+               return launch_flash_assign(g, xdev, nr, b.f.frag, b.f.assign, objective ? b.f.min_dist : nullptr,
+                                          cs, t > 0 ? cv : nullptr, t > 0 ? ck : nullptr));
       if (objective)
         KM_TIMED("objective", cs,
                  return launch_objective(b.f.min_dist, nr, b.f.obj_part, objective + t, ch > 0 ? 1 : 0, cs));
       const UpdateBufs u = b.f.u;
-      st = run_update(b.xbuf[buf], dt, nr, D, b.f.assign, K, nullptr, nullptr, nullptr, u, MODE_ACCUM, b.acc_sum,
+      st = run_update(xdev, dt, nr, D, b.f.assign, K, nullptr, nullptr, nullptr, u, MODE_ACCUM, b.acc_sum,
                       b.acc_cnt, cs, nullptr, nullptr, 1, nullptr, nullptr, nullptr, ck, cv);
       if (st != KM_OK) return st;
       if (assign_host && t == iters - 1)
         KM_TIMED("d2h", cs,
                  return hipMemcpyAsync(assign_host + r0, b.f.assign, sizeof(int32_t) * (size_t)nr,
                                        hipMemcpyDeviceToHost, cs));
-      KM_HIP(hipEventRecord(freed[buf], cs));
+      if (!resident) {
+        KM_HIP(hipEventRecord(freed[buf], cs));
+        ++seq;
+      }
     }
     KM_TIMED("finalize", cs, return launch_finalize_accum(b.acc_sum, b.acc_cnt, K, D, C, counts, cs));
   }

@@ -184,6 +184,10 @@ def test_workspace_bytes_sweep(L):
                     assert b >= prev
                     prev = b
                     assert L.kmeans_workspace_bytes(km.KM_OP_FIT_STREAMED, N, D, K, dt, 5000) > 0
+                    warm = L.kmeans_workspace_bytes(km.KM_OP_FIT_STREAMED_WARM, N, D, K, dt, 5000)
+                    es = 4 if dt == km.KM_F32 else 2
+                    res = L.kmeans_workspace_bytes(km.KM_OP_FIT_STREAMED_RESIDENT, N, D, K, dt, 5000)
+                    assert res == warm + (N * D * es + 255) // 256 * 256, (N, D, K, dt)
                 assert L.kmeans_workspace_bytes_batched(3, 1000, D, K, dt) > 0
 
 

@@ -109,6 +109,36 @@ def test_fit_streamed_pinned_and_pageable_agree():
     assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1]) and torch.equal(r1[2], r2[2])
 
 
+@pytest.mark.parametrize("resident", [True, "2.5 chunks", "1 row short of a chunk"])
+@pytest.mark.parametrize("pageable", [False, True])
+def test_fit_streamed_resident_copy_equals_streamed(resident, pageable):
+    """A device copy of X (all of it, or the leading chunks that fit whole in the extra workspace) changes only
+    where later iterations read X from: centroids, assignment, counts and objective equal the fully streamed
+    fit's bit for bit, for pinned and pageable X, with a ragged last chunk."""
+    w, Xn, C0 = _workload("c4", N=250_003, D=64, K=1000, M=1000)
+    X = parity.x_from_numpy(Xn, "bf16", DEV).cpu()
+    chunk = 60_000
+    row = w.D * 2
+    nbytes = {True: True, "2.5 chunks": int(2.5 * chunk * row), "1 row short of a chunk": chunk * row - row}[resident]
+    Xh = X if pageable else X.pin_memory()
+    stage = km.staging_buffer(4 * 7_000 * row) if pageable else None
+    C0t = torch.from_numpy(C0).to(DEV)
+    print(f"[fit] streamed with resident copy {resident}, pageable {pageable}", flush=True)
+    rr = km.fit_streamed(Xh, C0t, 4, chunk, objective=True, stage=stage, resident=nbytes)
+    torch.cuda.synchronize()
+    rs = km.fit_streamed(Xh, C0t, 4, chunk, objective=True, stage=stage)
+    torch.cuda.synchronize()
+    for i in range(4):
+        assert torch.equal(rr[i], rs[i]), f"resident copy changes output {i}"
+    C3 = km.fit_streamed(Xh, C0t, 3, chunk, stage=stage)[0]
+    torch.cuda.synchronize()
+    Xs, xdt = parity.x_to_numpy(X)
+    an = rr[1].numpy()
+    parity.check_assign(Xs, xdt, C3.cpu().numpy(), an, label=f"resident {resident}")
+    parity.check_update(Xs, xdt, an, C3.cpu().numpy(), rr[0].cpu().numpy(), rr[2].cpu().numpy(),
+                        label=f"resident {resident}")
+
+
 @pytest.mark.parametrize("case", [("c4", "bf16", 300_000, 64, 4096, 70_000), ("c2", "f16", 40_000, 48, 9000, 15_000),
                                   ("c1", "f32", 50_000, 32, 200, 16_384), ("c2", "bf16", 30_000, 600, 100, 11_000),
                                   ("c4", "bf16", 5_000, 16, 40, 1_024)],
