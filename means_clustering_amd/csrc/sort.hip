@@ -113,7 +113,8 @@ __global__ __launch_bounds__(kRadixThreads) void radix_count_kernel(const int32_
 // block) counts, for small count tables: the keys of smaller digits anywhere,
 // plus the keys of the same digit in earlier blocks.  Thread t adds up digit
 // t / S over blocks t % S, t % S + S, ... (S = threads per digit), so a
-// wavefront reads runs of S consecutive counts.
+// wavefront reads runs of S consecutive counts; 32 of a thread's loads are
+// in flight at once (a workgroup waits on this before it can place a key).
 template <int R>
 __device__ __forceinline__ void digit_bases(const uint32_t* __restrict__ counts, int64_t nblk, int64_t b,
                                             uint32_t* part_pre, uint32_t* part_all, uint32_t* tot,
@@ -122,7 +123,7 @@ __device__ __forceinline__ void digit_bases(const uint32_t* __restrict__ counts,
   const int d = threadIdx.x / S, r = threadIdx.x % S;
   const uint32_t* row = counts + (int64_t)d * nblk;
   uint32_t pre = 0, all = 0;
-#pragma unroll 4
+#pragma unroll 32
   for (int64_t j = r; j < nblk; j += S) {
     const uint32_t c = row[j];
     all += c;
