@@ -375,7 +375,7 @@ __global__ __launch_bounds__(256) void fixup_kernel(SegParams P) {
     const int64_t nitems = nh + ng + nt;
     float a[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     int32_t n = 0;
-    constexpr int UNR = 4;  // items in flight per lane
+    constexpr int UNR = 8;  // items in flight per lane (measured on gfx950: c2 fix-up 12.2 -> 11.9 us against 4)
     for (int64_t ib = r; ib < nitems; ib += (int64_t)R * UNR) {
       float4 v[UNR][2];
       int32_t cc[UNR];

@@ -139,6 +139,33 @@ def test_fit_streamed_resident_copy_equals_streamed(resident, pageable):
                         label=f"resident {resident}")
 
 
+@pytest.mark.parametrize("case", [("c1", "f32", 10_007, 33, 50, 3_000), ("c2", "f16", 20_000, 200, 300, 7_000),
+                                  ("c4", "bf16", 5_000, 16, 6_000, 2_048), ("c2", "bf16", 9_000, 600, 64, 9_000)],
+                         ids=lambda c: f"{c[1]}-N{c[2]}-D{c[3]}-K{c[4]}-chunk{c[5]}")
+def test_fit_streamed_resident_copy_shapes(case):
+    """The resident copy across X types and shapes: fp32 and fp16 X, odd D, more clusters than points (most stay
+    empty), a single chunk; every output equal to the fully streamed fit's, bit for bit."""
+    name, xdtype, N, D, K, chunk = case
+    w, Xn, C0 = _workload(name, N=N, D=D, K=min(K, N), M=min(K, 1024))
+    if K > N:  # the extra centroids far from every point: they stay empty
+        rng = np.random.default_rng(K)
+        C0 = np.concatenate([C0, (50.0 + rng.normal(size=(K - N, D))).astype(np.float32)])
+    X = parity.x_from_numpy(Xn, w.dtype, DEV)
+    if xdtype == "f16":
+        X = X.float().half()
+    elif xdtype == "f32":
+        X = X.float()
+    Xh = X.cpu().pin_memory()
+    C0t = torch.from_numpy(C0).to(DEV)
+    print(f"[fit] streamed resident copy {case}", flush=True)
+    rr = km.fit_streamed(Xh, C0t, 3, chunk, objective=True, resident=True)
+    torch.cuda.synchronize()
+    rs = km.fit_streamed(Xh, C0t, 3, chunk, objective=True)
+    torch.cuda.synchronize()
+    for i in range(4):
+        assert torch.equal(rr[i], rs[i]), f"resident copy changes output {i}"
+
+
 @pytest.mark.parametrize("case", [("c4", "bf16", 300_000, 64, 4096, 70_000), ("c2", "f16", 40_000, 48, 9000, 15_000),
                                   ("c1", "f32", 50_000, 32, 200, 16_384), ("c2", "bf16", 30_000, 600, 100, 11_000),
                                   ("c4", "bf16", 5_000, 16, 40, 1_024)],
