@@ -161,10 +161,11 @@ enum ScatterBases {
 };
 
 // Stable scatter: destination = scanned global base of (digit, block) + rank
-// within the digit.  The block's keys, then its values, are first placed in
-// LDS in sorted order (reusing the counter space), then written out with
-// consecutive lanes on consecutive block positions, so each digit's run
-// leaves as contiguous stores rather than scattered words.
+// within the digit.  The block's keys and values are first placed in LDS in
+// sorted order (reusing the counter space: both at once in blocks of up to
+// 4,096 keys, else keys, then values), then written out with consecutive
+// lanes on consecutive block positions, so each digit's run leaves as
+// contiguous stores rather than scattered words.
 static_assert(kRadixPadded >= kRadixThreads * kRadixMaxItems, "staging reuses the counter space");
 static_assert((1 << kMaxDigitBits) <= 64, "one wavefront adds up the digit totals");
 template <int BITS, int IT, int BASES>
@@ -207,6 +208,31 @@ __global__ __launch_bounds__(kRadixThreads) void radix_scatter_kernel(const int3
   block_rank<BITS, IT>(d, valid, ctr, wsum, start, rank);
   const uint32_t nkeys = start[R];
   int32_t* stage = reinterpret_cast<int32_t*>(ctr);
+  if constexpr (2 * kRadixThreads * IT <= kRadixPadded) {
+    // keys and values staged side by side in sorted order, then written out in one round
+    int32_t* sval = stage + kRadixThreads * IT;
+#pragma unroll
+    for (int i = 0; i < IT; ++i)
+      if (valid[i]) {
+        stage[rank[i]] = key[i];
+        sval[rank[i]] = val[i];
+      }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const uint32_t p = (uint32_t)(i * kRadixThreads + threadIdx.x);
+      if (p < nkeys) {
+        const int32_t k = stage[p];
+        const uint32_t dg = ((uint32_t)k >> shift) & (uint32_t)(R - 1);
+        const uint32_t dst = gbase[dg] + (p - start[dg]);
+        if (dst < (uint64_t)N) {  // always true for a consistent scan
+          keys_out[dst] = k;
+          vals_out[dst] = sval[p];
+        }
+      }
+    }
+    return;
+  }
   // keys in sorted order; remember each striped position's destination
 #pragma unroll
   for (int i = 0; i < IT; ++i)
