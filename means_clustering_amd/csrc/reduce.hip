@@ -101,6 +101,7 @@ struct SegParams {
   AssignCfg cfg;
   int Dc;
   int mode;
+  int cpw;  // fix-up: clusters screened per wavefront (1: a wavefront per cluster)
   const float* C_prev;
   float* C_new;
   int32_t* counts;
@@ -339,29 +340,41 @@ __global__ __launch_bounds__(256) void segment_reduce_kernel(SegParams P) {
 // Lanes split into R rows x (Dc/4) float4 columns; row r takes items r,
 // r + R, ... of that list in order and the rows are combined by a fixed
 // shuffle tree, so the order of additions never depends on scheduling.
-template <int CPL>  // float4 columns per lane: 2 only when a piece has 128 of them
-__global__ __launch_bounds__(256) void fixup_kernel(SegParams P) {
-  __shared__ float rows[4][kMaxD16];  // each wavefront's final row, for the operand fragments
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Cluster k's segment [s, e) of the sorted positions and its tiles t0..t1.
+struct FixupSeg {
+  int64_t s, e, t0, t1;
+  bool valid, cut;
+};
+
+__device__ __forceinline__ FixupSeg fixup_seg(const SegParams& P, int64_t k) {
+  FixupSeg g;
+  const bool active = k < P.K;
+  g.s = active ? P.off[k] : 0;
+  g.e = active ? P.off[k + 1] : 0;
+  g.valid = active && g.s >= 0 && g.e <= P.N && g.s <= g.e;  // offsets are monotone in [0, N]
+  g.t0 = g.s / P.tile;
+  g.t1 = g.e > g.s ? (g.e - 1) / P.tile : g.t0;
+  g.cut = g.valid && g.s < g.e && g.t0 != g.t1;  // otherwise empty, or finished by segment_reduce_kernel
+  return g;
+}
+
+// One wavefront completes cluster k: an empty cluster keeps its centroid, a
+// segment cut by tile edges is summed from its pieces (row: the wavefront's
+// LDS row, filled with the new mean when fragments are written).
+template <int CPL>
+__device__ __forceinline__ void fixup_one(const SegParams& P, const FixupSeg& g, int64_t k, int lane, float* row) {
   const int gc = P.Dc / 4;                    // float4 columns of a carry piece (power of two, <= 128)
   const int lpr = gc < 64 ? gc : 64;          // lanes per row
   const int R = 64 / lpr;                     // rows
   constexpr int cpl = CPL;
   const int r = lane / lpr, c0 = lane % lpr;
-  const int64_t k = (int64_t)blockIdx.x * 4 + wave;
-  // (no early return: with fragments to write every wavefront meets the barrier below)
-  const bool active = k < P.K;
-  const int64_t s = active ? P.off[k] : 0, e = active ? P.off[k + 1] : 0;
-  const bool valid = active && s >= 0 && e <= P.N && s <= e;  // offsets are monotone in [0, N]
-  const int64_t t0 = s / P.tile, t1 = e > s ? (e - 1) / P.tile : t0;
-  const bool cut = valid && s < e && t0 != t1;  // otherwise empty, or finished by segment_reduce_kernel
-  if (valid && s == e && P.mode == MODE_MEAN) {  // empty: keeps its centroid
+  const int64_t s = g.s, e = g.e, t0 = g.t0, t1 = g.t1;
+  if (g.valid && s == e && P.mode == MODE_MEAN) {  // empty: keeps its centroid
     if (lane == 0 && P.counts) P.counts[k] = 0;
     if (P.C_new != P.C_prev)
       for (int c = lane; c < P.D; c += 64) P.C_new[k * P.ldx + c] = P.C_prev[k * P.ldx + c];
   }
-  float* row = rows[wave];
-  if (cut) {
+  if (g.cut) {
     // item list: head tiles [t0, hb), whole groups [g0, g1), tail tiles [tb, t1]
     const int64_t T = P.tpb;
     int64_t hb = (t0 / T + 1) * T;
@@ -444,15 +457,48 @@ __global__ __launch_bounds__(256) void fixup_kernel(SegParams P) {
       }
     }
   }
+}
+
+// Without fragments to write (P.cpw > 1), a wavefront screens P.cpw
+// consecutive clusters, one lane each, and completes only those that are cut
+// or empty, one after another: at 65,536 clusters of ~16 points most
+// segments were finished by the segmented reduction, and a wavefront per
+// cluster cost more to launch than the work (measured on gfx950 at c3's
+// shape: see fixup_cpw).  With fragments every cluster's row is needed:
+// one wavefront per cluster.
+template <int CPL>  // float4 columns per lane: 2 only when a piece has 128 of them
+__global__ __launch_bounds__(256) void fixup_kernel(SegParams P) {
+  __shared__ float rows[4][kMaxD16];  // each wavefront's final row, for the operand fragments
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* row = rows[wave];
+  if (P.cpw > 1) {  // (uniform; never with fragments)
+    const int64_t k0 = ((int64_t)blockIdx.x * 4 + wave) * P.cpw;
+    bool need = false;
+    if (lane < P.cpw) {
+      const FixupSeg g = fixup_seg(P, k0 + lane);
+      need = g.cut || (g.valid && g.s == g.e && P.mode == MODE_MEAN);
+    }
+    uint64_t m = __ballot(need);
+    while (m) {  // wave-uniform
+      const int i = __builtin_ctzll(m);
+      m &= m - 1;
+      fixup_one<CPL>(P, fixup_seg(P, k0 + i), k0 + i, lane, row);
+    }
+    return;
+  }
+  const int64_t k = (int64_t)blockIdx.x * 4 + wave;
+  // (no early return: with fragments to write every wavefront meets the barrier below)
+  const FixupSeg g = fixup_seg(P, k);
+  fixup_one<CPL>(P, g, k, lane, row);
   if (!P.frag) return;  // (uniform: mean mode with a fragment buffer)
   // The new centroid's row: from the sums above, else as the segmented
   // reduction (finished clusters) or the empty rule (C_prev) left it.
-  if (valid && !cut) {
-    const float* src = s == e ? P.C_prev : P.C_new;
+  if (g.valid && !g.cut) {
+    const float* src = g.s == g.e ? P.C_prev : P.C_new;
     for (int c = lane; c < P.D; c += 64) row[c] = src[k * P.ldx + c];
   }
   __syncthreads();
-  if (valid) {
+  if (g.valid) {
     const int64_t b = k / P.kper;
     emit_fragment_row(row, P.D, P.dt, P.cfg, P.frag + 4 * b * P.f_stride, k - b * P.kper);
   }
@@ -486,6 +532,7 @@ static SegParams make_params(const ReduceArgs& a) {
   P.cfg = a.cfg;
   P.Dc = (int)reduce_dc(a.dt, a.D);
   P.mode = a.mode;
+  P.cpw = 1;
   P.C_prev = a.C_prev ? a.C_prev + c0 : nullptr;
   P.C_new = a.C_new ? a.C_new + c0 : nullptr;
   P.counts = a.counts;
@@ -528,11 +575,24 @@ hipError_t launch_segment_reduce(const ReduceArgs& a, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
+// Clusters screened per fix-up wavefront when no fragments are written: enough
+// wavefronts for 8 per compute unit, at most 64 clusters each (measured on
+// gfx950 at c3's shape, 65,536 clusters: 26.8 us with a wavefront per
+// cluster; 28.6, 19.2, 20.3, 21.0 and 25.7 us with 4, 8, 16, 32 and 64
+// wavefronts per compute unit).
+static int fixup_cpw(int64_t K) {
+  const int64_t target = 8 * device_info().cus;
+  const int64_t c = K / (target > 0 ? target : 1);
+  return c < 1 ? 1 : (c > 64 ? 64 : (int)c);
+}
+
 hipError_t launch_fixup(const ReduceArgs& a, hipStream_t stream) {
   if (a.K == 0) return hipSuccess;
-  const SegParams P = make_params(a);
+  SegParams P = make_params(a);
+  P.cpw = P.frag ? 1 : fixup_cpw(a.K);
   const bool wide = P.Dc / 4 > 64;
-  const dim3 grid((unsigned)((a.K + 3) / 4));
+  const int64_t waves = (a.K + P.cpw - 1) / P.cpw;
+  const dim3 grid((unsigned)((waves + 3) / 4));
   if (wide)
     hipLaunchKernelGGL(fixup_kernel<2>, grid, dim3(256), 0, stream, P);
   else
