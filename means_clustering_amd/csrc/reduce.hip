@@ -361,7 +361,7 @@ __device__ __forceinline__ FixupSeg fixup_seg(const SegParams& P, int64_t k) {
 // One wavefront completes cluster k: an empty cluster keeps its centroid, a
 // segment cut by tile edges is summed from its pieces (row: the wavefront's
 // LDS row, filled with the new mean when fragments are written).
-template <int CPL>
+template <int CPL, int UNR>  // UNR: carry pieces in flight per lane
 __device__ __forceinline__ void fixup_one(const SegParams& P, const FixupSeg& g, int64_t k, int lane, float* row) {
   const int gc = P.Dc / 4;                    // float4 columns of a carry piece (power of two, <= 128)
   const int lpr = gc < 64 ? gc : 64;          // lanes per row
@@ -388,7 +388,6 @@ __device__ __forceinline__ void fixup_one(const SegParams& P, const FixupSeg& g,
     const int64_t nitems = nh + ng + nt;
     float a[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     int32_t n = 0;
-    constexpr int UNR = 8;  // items in flight per lane (measured on gfx950: c2 fix-up 12.2 -> 11.9 us against 4)
     for (int64_t ib = r; ib < nitems; ib += (int64_t)R * UNR) {
       float4 v[UNR][2];
       int32_t cc[UNR];
@@ -466,7 +465,7 @@ __device__ __forceinline__ void fixup_one(const SegParams& P, const FixupSeg& g,
 // cluster cost more to launch than the work (measured on gfx950 at c3's
 // shape: see fixup_cpw).  With fragments every cluster's row is needed:
 // one wavefront per cluster.
-template <int CPL>  // float4 columns per lane: 2 only when a piece has 128 of them
+template <int CPL, int UNR>  // float4 columns per lane: 2 only when a piece has 128 of them
 __global__ __launch_bounds__(256) void fixup_kernel(SegParams P) {
   __shared__ float rows[4][kMaxD16];  // each wavefront's final row, for the operand fragments
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -482,14 +481,14 @@ __global__ __launch_bounds__(256) void fixup_kernel(SegParams P) {
     while (m) {  // wave-uniform
       const int i = __builtin_ctzll(m);
       m &= m - 1;
-      fixup_one<CPL>(P, fixup_seg(P, k0 + i), k0 + i, lane, row);
+      fixup_one<CPL, UNR>(P, fixup_seg(P, k0 + i), k0 + i, lane, row);
     }
     return;
   }
   const int64_t k = (int64_t)blockIdx.x * 4 + wave;
   // (no early return: with fragments to write every wavefront meets the barrier below)
   const FixupSeg g = fixup_seg(P, k);
-  fixup_one<CPL>(P, g, k, lane, row);
+  fixup_one<CPL, UNR>(P, g, k, lane, row);
   if (!P.frag) return;  // (uniform: mean mode with a fragment buffer)
   // The new centroid's row: from the sums above, else as the segmented
   // reduction (finished clusters) or the empty rule (C_prev) left it.
@@ -593,10 +592,16 @@ hipError_t launch_fixup(const ReduceArgs& a, hipStream_t stream) {
   const bool wide = P.Dc / 4 > 64;
   const int64_t waves = (a.K + P.cpw - 1) / P.cpw;
   const dim3 grid((unsigned)((waves + 3) / 4));
+  // Carry pieces in flight per lane: 8 where a row of lanes spans at least 32 float4 columns (two rows or one a
+  // wavefront), else 4 (measured on gfx950: c2, D = 128, 12.4 -> 10.8 us with 8; c4, D = 64, four rows a
+  // wavefront, 14.3 -> 18.4 us with 8).
+  const bool deep = P.Dc / 4 >= 32;
   if (wide)
-    hipLaunchKernelGGL(fixup_kernel<2>, grid, dim3(256), 0, stream, P);
+    hipLaunchKernelGGL((fixup_kernel<2, 8>), grid, dim3(256), 0, stream, P);
+  else if (deep)
+    hipLaunchKernelGGL((fixup_kernel<1, 8>), grid, dim3(256), 0, stream, P);
   else
-    hipLaunchKernelGGL(fixup_kernel<1>, grid, dim3(256), 0, stream, P);
+    hipLaunchKernelGGL((fixup_kernel<1, 4>), grid, dim3(256), 0, stream, P);
   return hipGetLastError();
 }
 
