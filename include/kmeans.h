@@ -185,7 +185,11 @@ km_status kmeans_fit(const void* X, km_dtype dt, int64_t N, int64_t D, int64_t K
  * memory): every iteration copies X to the device in chunks of `chunk_rows`
  * rows on `copy_stream`, two device buffers in rotation, while
  * `compute_stream` assigns the previous chunk and accumulates its per-cluster
- * sums; the means are formed once per iteration.
+ * sums; the means are formed once per iteration.  A workspace of
+ * KM_OP_FIT_STREAMED_WARM size or more adds the warm start; beyond that size
+ * the leading chunks that fit whole are kept on the device after their first
+ * upload (KM_OP_FIT_STREAMED_RESIDENT: all of X), and later iterations read
+ * them there instead of copying them again.
  *   X_host       host, N x D, type dt                        (read)
  *                With stage_host == NULL it must be pinned (hipHostMalloc /
  *                torch pin_memory) and is read by the DMA engine directly.
