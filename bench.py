@@ -694,6 +694,61 @@ def planner_study(args, dev):
     print(json.dumps(out), flush=True)
 
 
+SORT_STUDY_SHAPES = [("c2", 1 << 20, 1024), ("c3", 1 << 20, 65536), ("c4", 1 << 23, 4096),
+                     ("c5 chunk", 1 << 26, 4096), ("2^22 keys, 16-bit ids", 1 << 22, 65536),
+                     ("2^20 keys, 8-bit ids", 1 << 20, 200), ("2^20 keys, 19-bit ids", 1 << 20, 300_000)]
+SORT_STUDY_VARIANTS = [("static", []), ("whole-table count scans", [("sort_scan", 1)]),
+                       ("per-digit count scans", [("sort_scan", 2)]), ("thread-counter ranks", [("sort_rank", 1)]),
+                       ("wavefront ranks", [("sort_rank", 2)]), ("digits <= 6 bits", [("radix_bits", 6)]),
+                       ("digits <= 8 bits", [("radix_bits", 8)])]
+
+
+def sort_study(dev):
+    """The argsort of the update (kmeans_sort_by_cluster) under each of its planner choices: how the (digit,
+    block) count table is scanned, how a block's keys are ranked, and the widest digit.  Uniform random ids; each
+    variant's time is the best over 3 rotated rounds of the average of 50 calls (10 for 2^26 keys).  Variants
+    whose plan equals the static one are still timed (they show the spread)."""
+    import torch
+
+    import means_clustering_amd as km
+
+    out = {"sort_study": "kmeans_sort_by_cluster per planner choice, uniform ids, one GPU", "shapes": []}
+    for name, N, K in SORT_STUDY_SHAPES:
+        print(f"[bench] sort study {name}: N={N} K={K}", file=sys.stderr, flush=True)
+        g = torch.Generator(device="cpu").manual_seed(1)
+        a = torch.randint(0, K, (N,), generator=g, dtype=torch.int32).to(dev)
+        ws = km.Workspace(dev)
+        reps = 50 if N <= (1 << 23) else 10
+        times = {v: [] for v, _ in SORT_STUDY_VARIANTS}
+        plans = {}
+        for rnd in range(3):
+            order = SORT_STUDY_VARIANTS[rnd % len(SORT_STUDY_VARIANTS):] + SORT_STUDY_VARIANTS[:rnd % len(SORT_STUDY_VARIANTS)]
+            for vname, ovs in order:
+                for k, v in ovs:
+                    km.plan_override(k, v)
+                try:
+                    plans[vname] = km.plan_describe(N, 64, K, torch.bfloat16).split("update: ")[1].split(", segment")[0]
+                    for _ in range(3):
+                        km.sort_by_cluster(a, K, ws=ws)
+                    torch.cuda.synchronize()
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(reps):
+                        km.sort_by_cluster(a, K, ws=ws)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    times[vname].append(1e3 * e0.elapsed_time(e1) / reps)
+                finally:
+                    for k, _ in ovs:
+                        km.plan_override(k, 0)
+        out["shapes"].append({"name": name, "N": N, "K": K,
+                              "us": {v: round(min(t), 2) for v, t in times.items()}, "plan": plans})
+        del a, ws
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
 def segment_tile_study(dev):
     """Sort-Inverse Update time with short (16-position) against long (128-position) segment tiles, over N.
 
@@ -768,6 +823,8 @@ def main():
                          "(one JSON line)")
     ap.add_argument("--segment-tile-study", action="store_true",
                     help="only time the update with short and long segment tiles over N (one JSON line)")
+    ap.add_argument("--sort-study", action="store_true",
+                    help="only time the update's argsort under each of its planner choices (one JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -798,6 +855,10 @@ def main():
     if args.segment_tile_study:
         import torch
         segment_tile_study(torch.device("cuda:0"))
+        return
+    if args.sort_study:
+        import torch
+        sort_study(torch.device("cuda:0"))
         return
     if args.batch > 1:
         import torch
