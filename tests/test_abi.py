@@ -274,3 +274,25 @@ def test_planner_override_and_describe(L):
         for k in km.PLAN_KEYS:
             assert L.kmeans_plan_override(k.encode(), 0) == 0
     assert L.kmeans_workspace_bytes(km.KM_OP_FIT, 16384, 32, 4096, km.KM_BF16, 0) == base
+
+
+@pytest.mark.parametrize("N,K,passes,items,rank", [
+    (1 << 20, 1024, 2, 16, b"thread-counter"),   # 10-bit ids: two 5-bit passes either way
+    (1 << 20, 65536, 2, 16, b"wavefront"),       # 16-bit ids: two 8-bit passes instead of three 6-bit ones
+    (1 << 22, 65536, 2, 16, b"wavefront"),
+    (1 << 20, 200, 1, 16, b"wavefront"),         # 8-bit ids: one pass instead of two
+    (1 << 20, 300_000, 4, 16, b"thread-counter"),  # 19-bit ids: 4 -> 3 passes does not pay
+    (1 << 23, 4096, 2, 16, b"thread-counter"),   # 12-bit ids: two 6-bit passes either way
+    (1 << 26, 65536, 3, 32, b"thread-counter"),  # 8,192-key blocks: never ballots
+    (100_003, 65536, 2, 8, b"wavefront"),
+])
+def test_plan_argsort_geometry(L, N, K, passes, items, rank):
+    """The planner's argsort geometry (host arithmetic, no GPU): 8-bit ballot-ranked digits exactly where they
+    save one of at most three passes in blocks of at most 4,096 keys, else digits of at most 6 bits."""
+    buf = ctypes.create_string_buffer(1024)
+    for k in km.PLAN_KEYS:
+        assert L.kmeans_plan_override(k.encode(), 0) == 0
+    assert L.kmeans_plan_describe(N, 64, K, km.KM_BF16, buf, len(buf)) == 0
+    d = buf.value
+    assert b"%d radix pass(es) of %d keys/thread" % (passes, items) in d, d
+    assert rank + b" ranks" in d, d
